@@ -1,0 +1,307 @@
+"""CPU oracle for the forward pass of a token-choice Mixture-of-Experts FFN layer.
+
+TEST INFRASTRUCTURE ONLY. This module is imported by tests/, by
+__graft_entry__.smoke() and by bench.py's cpu_baseline leg, and by nothing
+else. The HIP library and its Python binding never import or call it, and it
+imports nothing from them: the only code both sides share is the seeded input
+generator (moe_inputs), which holds none of the layer's arithmetic.
+
+It is the plain definition of the layer, computed slowly in float64 with numpy
+(matrix products use numpy's matmul as a library step; there is no blocking,
+fusion or reordering beyond what the definition states). Each function names
+the passage it follows. Sources:
+
+  [MATH]  "How do Mixture of Expert Models Work?" (amks.me/notes/moe), section
+          "The Math Behind MoEs": the layer output is the sum over experts of
+          the gate value times the expert's output; dense gating is
+          Softmax(x.W_g); sparse gating is Softmax(TopK(x.W_g)), the softmax
+          of only the top-K logits with every other gate set to 0; Mixtral's
+          experts are SwiGLU and it routes with Top2.
+  [CAPN]  same page, section "Load Balancing", item "Expert Capacity": each
+          expert takes at most a set number of tokens; overflow tokens skip
+          the layer or are dropped.
+  [TALK]  "[Paper Club] Upcycling Large Language Models into Mixture of
+          Experts", the MoE-layer walkthrough: routing by a plain matrix
+          multiply, permutation of each expert's tokens into one matrix
+          (dropping tokens by capacity factor), the original FFN as the
+          expert, un-permutation back to the token order, and scaling by the
+          router probability. Its upcycling part: TopK then Softmax sums to
+          one (0.7/0.3 example); copied identical experts reproduce the dense
+          model; top-1 softmax is always one.
+  [VMOE]  "Scaling Vision with Sparse Mixture of Experts" (Google Research
+          post), section "Priority Routing": a fixed buffer per expert, and
+          tokens assigned beyond it are dropped once the expert is full.
+  [ROUTE] "Take a Closer Look at the MoE LLM Routing" (OpenMoE), Introduction,
+          "Drop-towards-the-End": capacity makes tokens later in the sequence
+          drop more often, i.e. the buffers fill in token order.
+
+Readings where the pages are silent (each is listed in the design notes):
+  * top-k ties go to the lower expert index; slots are ordered by descending
+    logit (ties by ascending index);
+  * the top-k decision is taken on float32 logits, the precision in which the
+    kernel holds them; gate values use the float64 logits;
+  * capacity = ceil(cf*T*k/E) computed in double, clamped to T; cf == 0 means
+    dropless (capacity T);
+  * a dropped slot contributes 0 and the remaining gates are not renormalised;
+  * SwiGLU(x) = W_down (silu(W_gate x) * (W_up x)), silu(a) = a/(1+exp(-a)),
+    no biases;
+  * "storage" rounding: the layer stores h, o and y in its storage type. In
+    "bf16" mode the float64 value is rounded to float32 and then to bfloat16
+    (round to nearest even); in "f32" mode to float32; in "f64" mode not at
+    all (used by the self-checks).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+STORAGE_MODES = ("f64", "f32", "bf16")
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def round_to_bf16(a) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even), returned as
+    float32. bfloat16 keeps the top 16 bits of the float32 pattern; adding
+    0x7FFF plus the lowest kept bit and truncating is round-half-to-even on the
+    dropped 16 bits. Finite inputs only (the layer's inputs are finite)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u << 16).astype(np.uint32).view(np.float32)
+
+
+def store(v: np.ndarray, storage: str) -> np.ndarray:
+    """Value of v after being written in the layer's storage type, as float64."""
+    if storage == "f64":
+        return np.asarray(v, dtype=np.float64)
+    v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
+    if storage == "f32":
+        return v32.astype(np.float64)
+    if storage == "bf16":
+        return round_to_bf16(v32).astype(np.float64)
+    raise ValueError(storage)
+
+
+def as_f64(a) -> np.ndarray:
+    """float64 copy of an input array (torch tensor of any float dtype or numpy)."""
+    if hasattr(a, "detach"):
+        import torch
+        return a.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# routing  [MATH] Softmax(TopK(x.W_g)); [TALK] the router is a matrix multiply
+# ---------------------------------------------------------------------------
+
+def router_logits(x, w_router) -> np.ndarray:
+    """l[t, e] = sum_i x[t, i] * W_g[e, i]  (x.W_g with W_g stored [E, d]).
+
+    [TALK]: the router is simply a learnable matrix applied to the tokens;
+    [MATH]: the gating network's argument is x.W_g. No bias, no noise."""
+    return as_f64(x) @ as_f64(w_router).T
+
+
+def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest logits per token, in slot order.
+
+    [MATH] TopK keeps the k largest logits. The comparison is done on the
+    float32 values of the logits; ties go to the lower expert index, and slots
+    run from the largest logit down."""
+    l32 = np.asarray(logits, dtype=np.float64).astype(np.float32)
+    order = np.argsort(-l32, axis=1, kind="stable")   # stable: equal values keep index order
+    return order[:, :k].astype(np.int32)
+
+
+def topk_gates(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """g[t, j] = exp(l[t, S_j]) / sum_{j'} exp(l[t, S_j']) over the chosen k.
+
+    [MATH] the gate is the softmax of only the top-K values; the others are 0
+    (they are not represented in the [T, k] layout). The largest chosen logit
+    is subtracted before exp, which leaves the softmax unchanged."""
+    v = np.take_along_axis(np.asarray(logits, np.float64), idx.astype(np.int64), axis=1)
+    z = np.exp(v - v.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def dense_gates(logits: np.ndarray, idx: np.ndarray, gates: np.ndarray) -> np.ndarray:
+    """The full G(x) of [MATH]: gate values at the chosen experts, 0 elsewhere."""
+    T, E = logits.shape
+    G = np.zeros((T, E), dtype=np.float64)
+    np.put_along_axis(G, idx.astype(np.int64), gates, axis=1)
+    return G
+
+
+def near_tie_tokens(logits: np.ndarray, k: int, gap: float = 1e-5) -> np.ndarray:
+    """Tokens whose routing could flip under float32 rounding of the logits:
+    some adjacent gap among the sorted top-(k+1) float32 logits is below `gap`.
+    (The k-th vs (k+1)-th gap decides the chosen set; the gaps inside the top k
+    decide the slot order.)"""
+    l32 = np.sort(np.asarray(logits, np.float64).astype(np.float32), axis=1)[:, ::-1]
+    m = min(k + 1, l32.shape[1])
+    if m < 2:
+        return np.zeros(l32.shape[0], dtype=bool)
+    gaps = l32[:, : m - 1].astype(np.float64) - l32[:, 1:m].astype(np.float64)
+    return (gaps < gap).any(axis=1)
+
+
+# ---------------------------------------------------------------------------
+# capacity and permutation  [CAPN] [VMOE] [ROUTE] [TALK]
+# ---------------------------------------------------------------------------
+
+def capacity(T: int, E: int, k: int, cf: float) -> int:
+    """Per-expert buffer size. [CAPN]/[VMOE] give a pre-set per-expert buffer
+    set by a capacity factor (1 to 1.25 typical) but no formula. Reading:
+    cap = ceil(cf * T * k / E) in double precision, clamped to T; cf == 0
+    means dropless (cap = T). cf is taken as the float32 the C interface
+    receives."""
+    cf = float(np.float32(cf))
+    if cf == 0.0:
+        return int(T)
+    return int(min(T, math.ceil(cf * T * k / E)))
+
+
+def fill_in_token_order(idx: np.ndarray, E: int, cap: int):
+    """Each expert's buffer fills in token order; an assignment that arrives
+    when the expert already holds `cap` tokens is dropped ([VMOE] dropped once
+    the expert is full; [ROUTE] drops land towards the end of the sequence).
+
+    Returns (demand[E], offsets[E+1], slot_row[T,k], row_slot[R]):
+      demand[e]    tokens that chose e (kept or not)
+      offsets      exclusive prefix sum of kept[e] = min(demand[e], cap):
+                   expert e's rows are offsets[e] .. offsets[e+1]-1 ([TALK]
+                   "arrange them into a single matrix" per expert)
+      slot_row     row of (t, j) in the permuted matrix, -1 if dropped
+      row_slot     inverse map: row -> t*k + j
+    Rows inside an expert's segment are in token order."""
+    T, k = idx.shape
+    fill = np.zeros(E, dtype=np.int64)
+    rank = np.empty((T, k), dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            rank[t, j] = fill[e]
+            fill[e] += 1
+    kept = np.minimum(fill, cap)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept)
+    keep = rank < cap
+    slot_row = np.where(keep, offsets[idx.astype(np.int64)] + rank, -1)
+    R = int(offsets[E])
+    row_slot = np.full(R, -1, dtype=np.int64)
+    tt, jj = np.nonzero(keep)
+    row_slot[slot_row[tt, jj]] = tt * k + jj
+    return (fill.astype(np.int32), offsets.astype(np.int32),
+            slot_row.astype(np.int32), row_slot.astype(np.int32))
+
+
+# ---------------------------------------------------------------------------
+# expert FFN  [MATH] Mixtral's SwiGLU experts; [TALK] the expert is the FFN
+# ---------------------------------------------------------------------------
+
+def silu(a: np.ndarray) -> np.ndarray:
+    """Swish with beta = 1: a * sigmoid(a) = a / (1 + exp(-a))."""
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
+
+
+def swiglu_expert(xr, w_gate_e, w_up_e, w_down_e, storage: str):
+    """One expert on its rows xr [n, d]:
+        h = silu(xr W_gate^T) * (xr W_up^T)     stored   [n, F]
+        o = h W_down^T                           stored   [n, d]
+    with W_gate, W_up stored [F, d] and W_down stored [d, F]."""
+    xr = as_f64(xr)
+    a = xr @ as_f64(w_gate_e).T
+    b = xr @ as_f64(w_up_e).T
+    h = store(silu(a) * b, storage)
+    o = store(h @ as_f64(w_down_e).T, storage)
+    return h, o
+
+
+# ---------------------------------------------------------------------------
+# un-permute and combine  [MATH] y = sum_i G(x)_i E_i(x); [TALK] scale by the
+# router probability after arranging the tokens back; [CAPN] dropped -> 0
+# ---------------------------------------------------------------------------
+
+def combine(o_rows: np.ndarray, slot_row: np.ndarray, gates: np.ndarray,
+            storage: str, tokens=None) -> np.ndarray:
+    """y[t] = sum over kept slots j (ascending) of g[t, j] * o[slot_row[t, j]].
+    A token with no kept slot gets y = 0. `tokens` restricts the output to
+    those token indices (o_rows must then hold every row they reference)."""
+    slot_row = np.asarray(slot_row)
+    if tokens is None:
+        tokens = np.arange(slot_row.shape[0])
+    tokens = np.asarray(tokens, dtype=np.int64)
+    d = o_rows.shape[1]
+    y = np.zeros((len(tokens), d), dtype=np.float64)
+    for j in range(slot_row.shape[1]):
+        r = slot_row[tokens, j]
+        m = r >= 0
+        y[m] += gates[tokens[m], j][:, None] * o_rows[r[m]]
+    return store(y, storage)
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+
+def route(x, w_router, k: int):
+    """Routing step: logits, top-k indices (slot order), gates, near-tie mask."""
+    logits = router_logits(x, w_router)
+    idx = select_topk(logits, k)
+    gates = topk_gates(logits, idx)
+    return logits, idx, gates, near_tie_tokens(logits, k)
+
+
+def forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, storage: str,
+            tokens=None, idx=None) -> dict:
+    """The MoE layer forward pass.
+
+    tokens: optional subset of token indices whose outputs are computed (the
+            routing, capacity and permutation always cover all T tokens,
+            since capacity depends on every earlier token).
+    idx:    optional top-k indices to use instead of the router's choice
+            (the gates still come from this oracle's logits at those experts).
+    Returns a dict with logits, topk_idx, topk_gate, near_tie, demand,
+    offsets, slot_row, row_slot, cap, y (for `tokens`, or all tokens), and
+    o_rows/h_rows (rows actually computed, indexed by permuted row; NaN
+    elsewhere) when tokens is None."""
+    T = x.shape[0]
+    E = w_router.shape[0]
+    logits = router_logits(x, w_router)
+    if idx is None:
+        idx = select_topk(logits, k)
+    gates = topk_gates(logits, idx)
+    cap = capacity(T, E, k, cf)
+    demand, offsets, slot_row, row_slot = fill_in_token_order(idx, E, cap)
+    R = int(offsets[E])
+    if tokens is None:
+        need_rows = np.arange(R)
+    else:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        r = slot_row[tokens].ravel()
+        need_rows = np.unique(r[r >= 0])
+    xf = x if hasattr(x, "shape") else np.asarray(x)
+    d = xf.shape[1]
+    F = w_gate.shape[1]
+    o_rows = np.full((R, d), np.nan)
+    h_rows = np.full((R, F), np.nan) if tokens is None else None
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        rows = need_rows[(need_rows >= lo) & (need_rows < hi)]
+        if len(rows) == 0:
+            continue
+        tok = row_slot[rows] // k
+        h, o = swiglu_expert(as_f64(x[tok]), w_gate[e], w_up[e], w_down[e], storage)
+        o_rows[rows] = o
+        if h_rows is not None:
+            h_rows[rows] = h
+    y = combine(o_rows, slot_row, gates, storage, tokens)
+    return dict(logits=logits, topk_idx=idx, topk_gate=gates,
+                near_tie=near_tie_tokens(logits, k), demand=demand, offsets=offsets,
+                slot_row=slot_row, row_slot=row_slot, cap=cap, y=y,
+                o_rows=o_rows, h_rows=h_rows)

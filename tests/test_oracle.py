@@ -1,0 +1,413 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself
+(brute force on tiny inputs, closed forms, library routines in special cases,
+values the pages print, invariants the pages state). The last group plants a
+plausible mistake in the oracle and shows that some pin fails."""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from oracle import moe_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *rest = line.split()
+            vals[key] = [float(v) for v in rest]
+    return vals
+
+
+def small_layer(T=40, d=16, E=5, k=2, F=24, seed=7, dtype="f32", identical=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d)) / math.sqrt(d)
+    wg = rng.standard_normal((E, F, d)) / math.sqrt(d)
+    wu = rng.standard_normal((E, F, d)) / math.sqrt(d)
+    wd = rng.standard_normal((E, d, F)) / math.sqrt(d)
+    if identical:
+        wg[:] = wg[0]
+        wu[:] = wu[0]
+        wd[:] = wd[0]
+    if dtype == "bf16":
+        cast = lambda a: torch.from_numpy(a).to(torch.bfloat16).double().numpy()
+        x, wr, wg, wu, wd = map(cast, (x, wr, wg, wu, wd))
+    return x, wr, wg, wu, wd
+
+
+# ---------------------------------------------------------------------------
+# the pins, written as checks so that the planted-mistake tests can reuse them
+# ---------------------------------------------------------------------------
+
+def check_bf16_rounding():
+    """round_to_bf16 == torch's float32 -> bfloat16 conversion, bit for bit."""
+    rng = np.random.default_rng(0)
+    parts = [rng.standard_normal(20000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 20000).astype(np.float32)]
+    # exact ties (low 16 bits = 0x8000) with even and odd kept bit, both signs
+    hi = rng.integers(0, 0x7F7F, 4000).astype(np.uint32) << 16
+    ties = (hi | 0x8000).view(np.float32)
+    parts += [ties, -ties]
+    # just below / above a tie
+    parts += [(hi | 0x7FFF).view(np.float32), (hi | 0x8001).view(np.float32)]
+    # subnormals, zero, near overflow (rounds to inf)
+    sub = rng.integers(1, 0x007FFFFF, 2000).astype(np.uint32).view(np.float32)
+    parts += [sub, -sub, np.array([0.0, -0.0, 3.3895314e38, -3.3895314e38,
+                                   np.finfo(np.float32).max, -np.finfo(np.float32).max], np.float32)]
+    a = np.concatenate(parts).astype(np.float32)
+    a = a[np.isfinite(a)]
+    mine = orc.round_to_bf16(a).view(np.uint32)
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy().view(np.uint32)
+    assert np.array_equal(mine, ref), f"{(mine != ref).sum()} mismatches"
+
+
+def check_silu_library():
+    a = np.linspace(-60, 60, 2001)
+    assert np.allclose(orc.silu(a), torch.nn.functional.silu(torch.from_numpy(a)).numpy(),
+                       rtol=1e-14, atol=1e-300)
+
+
+def brute_topk(l, k):
+    """Max-sum subset of size k, lexicographically smallest among ties."""
+    E = len(l)
+    best, best_s = None, None
+    for s in itertools.combinations(range(E), k):
+        v = sum(l[i] for i in s)
+        if best is None or v > best:
+            best, best_s = v, s
+    return best_s
+
+
+def check_topk_bruteforce():
+    rng = np.random.default_rng(1)
+    for trial in range(300):
+        E = int(rng.integers(1, 6))
+        k = int(rng.integers(1, min(3, E) + 1))
+        T = int(rng.integers(1, 7))
+        # small integers give many exact ties
+        logits = rng.integers(-2, 3, (T, E)).astype(np.float64) * 0.5
+        if trial % 3 == 0:
+            logits = rng.standard_normal((T, E))
+        idx = orc.select_topk(logits, k)
+        for t in range(T):
+            assert tuple(sorted(idx[t].tolist())) == brute_topk(logits[t].astype(np.float32).tolist(), k)
+            v = logits[t, idx[t]]
+            # slots run from the largest logit down, ties by ascending index
+            for j in range(k - 1):
+                assert v[j] > v[j + 1] or (v[j] == v[j + 1] and idx[t, j] < idx[t, j + 1])
+
+
+def check_zero_router_closed_form():
+    """W_g = 0: every logit is 0, every token picks experts 0..k-1 with gates 1/k;
+    with a finite capacity, experts 0..k-1 keep exactly tokens 0..cap-1."""
+    T, d, E, k, F = 30, 8, 6, 3, 8
+    x, _, wg, wu, wd = small_layer(T, d, E, k, F)
+    wr = np.zeros((E, d))
+    r = orc.forward(x, wr, wg, wu, wd, k, 1.0, "f64")
+    assert np.array_equal(r["topk_idx"], np.tile(np.arange(k, dtype=np.int32), (T, 1)))
+    assert np.all(r["topk_gate"] == 1.0 / k)
+    cap = r["cap"]
+    assert cap == math.ceil(1.0 * T * k / E) == 15
+    assert np.array_equal(r["demand"], np.array([T] * k + [0] * (E - k)))
+    assert np.array_equal(r["offsets"], np.array([0] + [cap * (i + 1) for i in range(k)] + [cap * k] * (E - k)))
+    for j in range(k):
+        kept_tokens = np.nonzero(r["slot_row"][:, j] >= 0)[0]
+        assert np.array_equal(kept_tokens, np.arange(cap))
+        assert np.array_equal(r["slot_row"][:cap, j], j * cap + np.arange(cap))
+
+
+def check_gate_invariants():
+    for k in (1, 2, 3, 5):
+        x, wr, *_ = small_layer(T=50, E=5, k=k)
+        logits, idx, g, _ = orc.route(x, wr, k)
+        assert np.all(np.abs(g.sum(axis=1) - 1.0) <= k * 2.0 ** -52 * 4)
+        if k == 1:
+            assert np.all(g == 1.0)
+        G = orc.dense_gates(logits, idx, g)
+        mask = np.zeros_like(G, dtype=bool)
+        np.put_along_axis(mask, idx.astype(np.int64), True, axis=1)
+        assert np.all(G[~mask] == 0.0)
+        assert np.all(g > 0)
+        # gates follow the slot order (largest logit first)
+        assert np.all(np.diff(g, axis=1) <= 0)
+
+
+def check_k_equals_E_is_softmax():
+    x, wr, *_ = small_layer(T=50, E=5)
+    logits, idx, g, _ = orc.route(x, wr, 5)
+    ref = torch.softmax(torch.from_numpy(logits), dim=1).numpy()
+    assert np.allclose(np.take_along_axis(ref, idx.astype(np.int64), 1), g, rtol=1e-14, atol=0)
+
+
+def check_printed_gates():
+    u = read_golden("upcycling_top2_gates.txt")
+    logits = np.array([u["logits"]])
+    idx = orc.select_topk(logits, int(u["k"][0]))
+    g = orc.topk_gates(logits, idx)
+    assert idx[0].tolist() == [int(v) for v in u["expect_idx"]]
+    assert np.allclose(g[0], u["expect_gate"], rtol=1e-12)
+    s = read_golden("switch_softmax_then_top2.txt")
+    logits = np.array([s["logits"]])
+    E = int(s["E"][0])
+    idxE = orc.select_topk(logits, E)
+    gE = orc.topk_gates(logits, idxE)
+    assert idxE[0, :2].tolist() == [int(v) for v in s["expect_dense_top2_idx"]]
+    assert np.allclose(gE[0, :2], s["expect_dense_top2_gate"], rtol=1e-12)
+    assert gE[0, :2].sum() < 1.0 - 0.3
+    idx2 = orc.select_topk(logits, 2)
+    assert np.allclose(orc.topk_gates(logits, idx2)[0], s["expect_top2_gate"], rtol=1e-12)
+
+
+def check_capacity_values():
+    assert orc.capacity(64, 4, 1, 1.25) == 20          # the tiny fp32 workload
+    assert orc.capacity(8192, 32, 2, 1.25) == 640      # the OpenMoE-shaped workload
+    assert orc.capacity(4096, 8, 2, 0.0) == 4096       # dropless
+    assert orc.capacity(10, 3, 1, 1.0) == 4            # ceil(3.33)
+    assert orc.capacity(7, 2, 1, 1.1) == 4             # ceil(3.85)
+    assert orc.capacity(10, 2, 2, 4.0) == 10           # clamped to T
+    assert orc.capacity(100, 64, 1, 0.01) == 1         # never below one once cf > 0
+
+
+def counting_ranks(idx, E):
+    """rank(t, e) = #{t' < t : e in S_t'} from the definition, via a cumulative count."""
+    T, k = idx.shape
+    onehot = np.zeros((T, E), dtype=np.int64)
+    for j in range(k):
+        onehot[np.arange(T), idx[:, j]] += 1
+    before = np.cumsum(onehot, axis=0) - onehot
+    return np.take_along_axis(before, idx.astype(np.int64), axis=1)
+
+
+def check_permutation(idx, E, cap):
+    T, k = idx.shape
+    demand, offsets, slot_row, row_slot = orc.fill_in_token_order(idx, E, cap)
+    rank = counting_ranks(idx, E)
+    keep = rank < cap
+    assert np.array_equal(slot_row >= 0, keep)
+    assert np.array_equal(demand, np.bincount(idx.ravel(), minlength=E))
+    kept = np.minimum(demand, cap)
+    assert np.array_equal(np.diff(offsets), kept)
+    assert offsets[0] == 0 and offsets[E] == keep.sum() == len(row_slot)
+    assert np.all(kept <= cap)
+    tt, jj = np.nonzero(keep)
+    e = idx[tt, jj]
+    assert np.array_equal(slot_row[tt, jj], offsets[e] + rank[tt, jj])
+    # mutual inverses
+    assert np.array_equal(row_slot[slot_row[tt, jj]], tt * k + jj)
+    assert np.array_equal(np.sort(slot_row[keep]), np.arange(offsets[E]))
+    # segments hold their expert, in token order
+    tok = row_slot // k
+    for ex in range(E):
+        seg = row_slot[offsets[ex]:offsets[ex + 1]]
+        assert np.all(idx.ravel()[seg] == ex)
+        assert np.all(np.diff(tok[offsets[ex]:offsets[ex + 1]]) > 0)
+    # drop-towards-the-end: once (t, e) is dropped every later (t', e) is dropped
+    for ex in range(E):
+        m = (idx == ex)
+        kept_t = np.nonzero((m & keep).any(1))[0]
+        drop_t = np.nonzero((m & ~keep).any(1))[0]
+        if len(kept_t) and len(drop_t):
+            assert kept_t.max() < drop_t.min()
+
+
+def queue_simulation(idx, E, cap):
+    """Brute force: explicit per-expert queues that refuse arrivals once full."""
+    T, k = idx.shape
+    queues = [[] for _ in range(E)]
+    for t in range(T):
+        for j in range(k):
+            q = queues[idx[t, j]]
+            if len(q) < cap:
+                q.append(t)
+    return queues
+
+
+def check_permutation_bruteforce():
+    rng = np.random.default_rng(3)
+    for trial in range(40):
+        E = int(rng.integers(1, 7))
+        k = int(rng.integers(1, E + 1))
+        T = int(rng.integers(1, 13))
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        for cap in range(1, T + 1):
+            check_permutation(idx, E, cap)
+            _, offsets, _, row_slot = orc.fill_in_token_order(idx, E, cap)
+            q = queue_simulation(idx, E, cap)
+            for e in range(E):
+                assert (row_slot[offsets[e]:offsets[e + 1]] // k).tolist() == q[e]
+
+
+def dense_reference_y(x, wr, wg, wu, wd, k, cf, storage):
+    """Every expert on every token (torch, library silu), times the dense G with
+    dropped slots set to 0, summed over experts. Shares only the routing
+    decision (indices and gates) with the oracle; no permutation at all."""
+    r = orc.forward(x, wr, wg, wu, wd, k, cf, storage)
+    T, E = r["logits"].shape
+    G = np.zeros((T, E))
+    for j in range(k):
+        kept = r["slot_row"][:, j] >= 0
+        G[np.nonzero(kept)[0], r["topk_idx"][kept, j]] = r["topk_gate"][kept, j]
+
+    def st(t):
+        if storage == "f64":
+            return t
+        t32 = t.to(torch.float32)
+        if storage == "bf16":
+            t32 = t32.to(torch.bfloat16)
+        return t32.to(torch.float64)
+
+    xt = torch.from_numpy(np.asarray(x, np.float64))
+    y = torch.zeros_like(xt)
+    for e in range(E):
+        h = st(torch.nn.functional.silu(xt @ torch.from_numpy(wg[e]).T) * (xt @ torch.from_numpy(wu[e]).T))
+        o = st(h @ torch.from_numpy(wd[e]).T)
+        y += torch.from_numpy(G[:, e])[:, None] * o
+    return r, st(y).numpy()
+
+
+def check_dense_identity():
+    for (T, E, k, cf, storage, dt) in [(40, 5, 2, 0.0, "f64", "f32"), (40, 5, 2, 1.0, "f64", "f32"),
+                                       (33, 4, 1, 1.25, "f64", "f32"), (40, 6, 3, 0.75, "f64", "f32"),
+                                       (40, 5, 2, 1.0, "bf16", "bf16"), (40, 4, 4, 0.0, "f32", "f32")]:
+        x, wr, wg, wu, wd = small_layer(T=T, E=E, k=k, dtype=dt)
+        r, yd = dense_reference_y(x, wr, wg, wu, wd, k, cf, storage)
+        if storage == "f64":
+            assert np.allclose(r["y"], yd, rtol=1e-12, atol=1e-14)
+        else:
+            # same rounding points; summation order differs only in float64
+            assert np.allclose(r["y"], yd, rtol=2.0 ** -7, atol=1e-12)
+            assert np.mean(r["y"] == yd) > 0.99
+        # fully dropped tokens give 0
+        dropped = (r["slot_row"] < 0).all(axis=1)
+        assert np.all(r["y"][dropped] == 0.0)
+
+
+def check_identical_experts_dense_ffn():
+    """Copies of one FFN with Softmax(TopK) gates reproduce the dense FFN
+    (the upcycling property in the talk): the gates sum to one."""
+    for (E, k) in [(4, 2), (6, 3), (4, 1), (1, 1)]:
+        x, wr, wg, wu, wd = small_layer(T=30, E=E, identical=True)
+        r = orc.forward(x, wr, wg, wu, wd, k, 0.0, "f64")
+        xt = torch.from_numpy(x)
+        dense = (torch.nn.functional.silu(xt @ torch.from_numpy(wg[0]).T)
+                 * (xt @ torch.from_numpy(wu[0]).T)) @ torch.from_numpy(wd[0]).T
+        # BLAS sums row blocks in its own order, so equality is to float64 rounding
+        assert np.allclose(r["y"], dense.numpy(), rtol=1e-13, atol=1e-13)
+        if k == 1:
+            assert np.all(r["topk_gate"] == 1.0)
+
+
+def check_near_tie():
+    logits = np.array([[1.0, 1.0 + 5e-6, 0.0, -1.0],     # top-2 order near tie
+                       [1.0, 0.5, 0.5 + 2e-6, -1.0],     # 2nd vs 3rd near tie
+                       [1.0, 0.5, 0.0, -1.0],            # clear
+                       [2.0, 0.5, 0.5 - 1e-4, -1.0]])    # 1e-4 apart: clear
+    assert orc.near_tie_tokens(logits, 2).tolist() == [True, True, False, False]
+    assert orc.near_tie_tokens(logits, 1).tolist() == [True, False, False, False]
+
+
+ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
+            check_zero_router_closed_form, check_gate_invariants, check_k_equals_E_is_softmax,
+            check_printed_gates, check_capacity_values, check_permutation_bruteforce,
+            check_dense_identity, check_identical_experts_dense_ffn, check_near_tie]
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+def test_permutation_random_mid():
+    rng = np.random.default_rng(11)
+    for (T, E, k) in [(500, 8, 2), (300, 64, 8), (257, 3, 3)]:
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        for cap in (1, 7, T * k // E, T):
+            check_permutation(idx, E, cap)
+
+
+def test_skewed_workload_drops_towards_the_end():
+    """The Zipf token-id workload: capacity 640, imbalanced demand, and the
+    drops fall in the later part of the sequence (Drop-towards-the-End)."""
+    w = mi.WORKLOADS["openmoe_bf16"]
+    a = mi.generate(w, expert_weights=False)
+    logits, idx, g, tie = orc.route(a["x"], a["w_router"], w.k)
+    cap = orc.capacity(w.T, w.E, w.k, w.cf)
+    assert cap == 640
+    demand, offsets, slot_row, row_slot = orc.fill_in_token_order(idx, w.E, cap)
+    assert demand.max() > cap                   # imbalanced: some expert overflows
+    dropped = slot_row < 0
+    n_drop = int(dropped.sum())
+    assert 0 < n_drop < w.T * w.k // 4
+    drop_tokens = np.nonzero(dropped.any(1))[0]
+    assert np.median(drop_tokens) > w.T * 0.6
+    assert drop_tokens.min() > w.T // 4
+
+
+def test_workload_shapes_and_seeds():
+    w = mi.WORKLOADS["tiny_fp32"]
+    a = mi.generate(w)
+    b = mi.generate(w)
+    for key in ("x", "w_router", "w_gate", "w_up", "w_down"):
+        assert torch.equal(a[key], b[key])
+    assert a["x"].shape == (64, 64) and a["w_gate"].shape == (4, 128, 64)
+    assert a["w_down"].shape == (4, 64, 128)
+    # scale: weights ~ N(0, 1/d)
+    assert abs(a["w_gate"].double().std().item() * math.sqrt(64) - 1.0) < 0.05
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must make some pin fail
+# ---------------------------------------------------------------------------
+
+def _swap_gate_up(xr, w_gate_e, w_up_e, w_down_e, storage, _orig=orc.swiglu_expert):
+    return _orig(xr, w_up_e, w_gate_e, w_down_e, storage)
+
+
+MUTANTS = {
+    "topk_smallest": ("select_topk", lambda logits, k: np.argsort(np.asarray(logits, np.float32), axis=1, kind="stable")[:, :k].astype(np.int32),
+                      [check_topk_bruteforce]),
+    "ties_to_higher_index": ("select_topk", lambda logits, k: (logits.shape[1] - 1 - np.argsort(-np.asarray(logits, np.float32)[:, ::-1], axis=1, kind="stable"))[:, :k].astype(np.int32),
+                             [check_zero_router_closed_form]),
+    "softmax_then_topk": ("topk_gates", lambda logits, idx: np.take_along_axis(
+        np.exp(logits - logits.max(1, keepdims=True)) / np.exp(logits - logits.max(1, keepdims=True)).sum(1, keepdims=True),
+        idx.astype(np.int64), 1), [check_gate_invariants]),
+    "capacity_floor": ("capacity", lambda T, E, k, cf: T if cf == 0 else int(min(T, math.floor(cf * T * k / E))),
+                       [check_capacity_values]),
+    "silu_sign": ("silu", lambda a: a / (1.0 + np.exp(a)), [check_silu_library, check_identical_experts_dense_ffn]),
+    "gate_up_swapped": ("swiglu_expert", _swap_gate_up, [check_dense_identity]),
+    "combine_ignores_gates": ("combine", lambda o_rows, slot_row, gates, storage, tokens=None, _o=orc.combine:
+                              _o(o_rows, slot_row, np.ones_like(gates), storage, tokens), [check_dense_identity]),
+    "bf16_truncates": ("round_to_bf16", lambda a: (np.ascontiguousarray(a, np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32),
+                       [check_bf16_rounding]),
+}
+
+
+def _fill_reverse(idx, E, cap, _orig=orc.fill_in_token_order):
+    T = idx.shape[0]
+    demand, offsets, slot_row, row_slot = _orig(idx[::-1].copy(), E, cap)
+    return demand, offsets, slot_row[::-1].copy(), (T - 1 - row_slot // idx.shape[1]) * idx.shape[1] + row_slot % idx.shape[1]
+
+
+MUTANTS["fill_from_the_end"] = ("fill_in_token_order", _fill_reverse, [check_permutation_bruteforce])
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn, pins = MUTANTS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    caught = False
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught = True
+    assert caught, f"planted mistake {name} passed every pin"
