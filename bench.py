@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""MoE layer forward throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload mixtral_bf16]
+
+One step is one moe_forward call (router, permutation, both grouped GEMMs,
+combine) over one batch of T tokens already resident in HBM. The headline
+value is T / (wall time per step), timed over exactly K steps bracketed by
+torch.cuda.synchronize(). A second pass runs the same kernels stage by stage
+(moe_route, moe_permute, moe_expert_gate_up, moe_expert_down,
+moe_unpermute_combine) with HIP events between the launches on the launch
+stream, and a 512 MiB buffer written before each step so the HBM-bound stages
+do not read from cache; it gives each stage's duration and the roofline
+figures. The CPU oracle is timed on a bounded sample of the same workload.
+Prints one JSON line on stdout (progress goes to stderr).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd tokens/s + % bf16 MFMA peak (grouped FFN), Mixtral-shape, 1 GPU"
+PEAK = {"bf16_tflops": 2500.0, "f32_tflops": 157.3, "hbm_gbs": 8000.0}
+DOMINANT_KERNEL_SRC = os.path.join(ROOT, "sparse_mixture_experts_09_amd", "csrc", "ffn_bf16.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload):
+    """HBM bytes per launch of the gate/up kernel from rocprofv3 counters, if
+    they were taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != source_digest(DOMINANT_KERNEL_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, a, target_s):
+    """The oracle, as it is, on the first S tokens of the workload."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as orc
+
+    def run(S):
+        t = time.perf_counter()
+        orc.forward(a["x"][:S], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], w.k, w.cf, w.dtype)
+        return time.perf_counter() - t
+
+    S = min(w.T, 128)
+    t = run(S)
+    log(f"cpu oracle: {S} tokens in {t:.2f} s")
+    S2 = min(w.T, int(S * target_s / max(t, 1e-3)))
+    if S2 > 1.5 * S:
+        S = S2
+        t = run(S)
+        log(f"cpu oracle: {S} tokens in {t:.2f} s")
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    drop = "dropless, so routing and outputs equal the full layer's for these tokens" if w.cf == 0 else \
+        f"capacity recomputed for {S} tokens"
+    return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {S} of {w.T} tokens of {w.name} ({drop}); whole layer forward in float64 "
+                      f"numpy (BLAS matmul), {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-flush", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path (sharding over GPUs is "
+              "a design note, not code). Run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    from sparse_mixture_experts_09_amd import moe
+
+    if not os.path.exists(moe.LIB_PATH):
+        from sparse_mixture_experts_09_amd.build import build
+        build()
+    w = mi.WORKLOADS[args.workload]
+    T, d, E, k, F, cf = w.T, w.d, w.E, w.k, w.F, w.cf
+    s = 2 if w.dtype == "bf16" else 4
+    K, W = args.steps, args.warmup
+    log(f"generating {w.name} ...")
+    a = mi.generate(w)
+    g = {n: v.cuda() for n, v in a.items() if v is not None and n != "token_ids"}
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    # ---- headline: K x moe_forward ----
+    y = torch.empty_like(g["x"])
+    ws = torch.empty(moe.moe_workspace_bytes(T, d, E, k, cf, F, g["x"].dtype), dtype=torch.uint8, device="cuda")
+
+    def forward():
+        moe.moe_forward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], k, cf, y=y, ws=ws)
+
+    for _ in range(W):
+        forward()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(K):
+        forward()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    gpu_ms_step = e0.elapsed_time(e1) / K
+    log(f"moe_forward: {ms_step:.3f} ms/step wall, {gpu_ms_step:.3f} ms/step events")
+
+    # ---- stage pass: same kernels, events between launches ----
+    R_max = moe.moe_rows_max(T, E, k, cf)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    perm = {"expert_counts": torch.empty(E, dtype=torch.int32, device="cuda"),
+            "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+            "slot_row": torch.empty((T, k), dtype=torch.int32, device="cuda"),
+            "row_slot": torch.empty(R_max, dtype=torch.int32, device="cuda"),
+            "x_perm": torch.empty((R_max, d), dtype=g["x"].dtype, device="cuda"),
+            "ws": torch.empty(max(moe.moe_permute_workspace_bytes(T, E), 16), dtype=torch.uint8, device="cuda")}
+    h = torch.empty((R_max, F), dtype=g["x"].dtype, device="cuda")
+    o = torch.empty((R_max, d), dtype=g["x"].dtype, device="cuda")
+    y2 = torch.empty_like(g["x"])
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    names = ["route", "permute", "gate_up", "down", "combine"]
+    samples = {n: [] for n in names}
+    for it in range(W + K):
+        if flush is not None:
+            flush.fill_(it & 0xFF)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record(stream)
+        moe.moe_route(g["x"], g["w_router"], k, topk_idx=idx, topk_gate=gate, stream=stream)
+        ev[1].record(stream)
+        moe.moe_permute(g["x"], idx, E, cf, out=perm, stream=stream)
+        ev[2].record(stream)
+        moe.moe_expert_gate_up(perm["x_perm"], perm["expert_offsets"], g["w_gate"], g["w_up"], T, k, cf, h=h,
+                               stream=stream)
+        ev[3].record(stream)
+        moe.moe_expert_down(h, perm["expert_offsets"], g["w_down"], T, k, cf, out_perm=o, stream=stream)
+        ev[4].record(stream)
+        moe.moe_unpermute_combine(o, perm["slot_row"], gate, E, cf, y=y2, stream=stream)
+        ev[5].record(stream)
+        if it >= W:
+            samples["_ev"] = samples.get("_ev", []) + [ev]
+    torch.cuda.synchronize()
+    for ev in samples.pop("_ev"):
+        for i, n in enumerate(names):
+            samples[n].append(ev[i].elapsed_time(ev[i + 1]))
+    st_ms = {n: float(np.mean(v)) for n, v in samples.items()}
+    same_as_forward = bool(torch.equal(y, y2))
+
+    offsets = perm["expert_offsets"].cpu().numpy().astype(np.int64)
+    slot_row = perm["slot_row"].cpu().numpy()
+    kept = np.diff(offsets)
+    R = int(offsets[-1])
+    active = int((kept > 0).sum())
+    T_read = int((slot_row >= 0).any(axis=1).sum())
+    alg = {
+        "route": dict(bytes=T * d * s + E * d * s + T * k * 8, flops=2 * T * d * E),
+        "permute": dict(bytes=T_read * d * s + R * d * s + 4 * (2 * T * k + R + 2 * E), flops=0),
+        "gate_up": dict(bytes=active * 2 * F * d * s + R * d * s + R * F * s, flops=4 * d * F * R),
+        "down": dict(bytes=active * d * F * s + R * F * s + R * d * s, flops=2 * d * F * R),
+        "combine": dict(bytes=R * d * s + T * k * 8 + T * d * s, flops=2 * R * d),
+    }
+    peak_mm = PEAK["bf16_tflops"] if w.dtype == "bf16" else PEAK["f32_tflops"]
+    stages = {}
+    for n in names:
+        t = st_ms[n] * 1e-3
+        stages[n] = {"us": st_ms[n] * 1e3, "GB/s": alg[n]["bytes"] / t / 1e9,
+                     "TFLOP/s": alg[n]["flops"] / t / 1e12,
+                     "hbm_frac": alg[n]["bytes"] / t / 1e9 / PEAK["hbm_gbs"]}
+        log(f"  {n:8s} {st_ms[n] * 1e3:9.1f} us  {stages[n]['GB/s']:8.0f} GB/s  {stages[n]['TFLOP/s']:8.1f} TFLOP/s")
+    ffn_t = (st_ms["gate_up"] + st_ms["down"]) * 1e-3
+    ffn_frac = (alg["gate_up"]["flops"] + alg["down"]["flops"]) / ffn_t / 1e12 / peak_mm
+    hbm_t = (st_ms["route"] + st_ms["permute"] + st_ms["combine"]) * 1e-3
+    hbm_frac = (alg["route"]["bytes"] + alg["permute"]["bytes"] + alg["combine"]["bytes"]) / hbm_t / 1e9 / PEAK["hbm_gbs"]
+    gu_t = st_ms["gate_up"] * 1e-3
+    achieved = alg["gate_up"]["flops"] / gu_t / 1e12
+    roofline = {"bound": "mfma", "kernel": "ffn_bf16_kernel<128,64,true> (grouped gate/up GEMM + SwiGLU)",
+                "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s", "frac": achieved / peak_mm,
+                "traffic": load_traffic(w.name), "alg_flops_per_launch": alg["gate_up"]["flops"],
+                "avg_launch_us": st_ms["gate_up"] * 1e3}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline(w, a, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "T": T, "d": d, "E": E, "k": k, "F": F, "cf": cf, "kept_rows": R,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "ffn_mfma_frac": ffn_frac,
+        "route_permute_combine_hbm_frac": hbm_frac,
+        "layer_tflops": (alg["route"]["flops"] + alg["gate_up"]["flops"] + alg["down"]["flops"]) / (ms_step * 1e-3) / 1e12,
+        "gpu_ms_per_step_events": gpu_ms_step,
+        "stages": stages,
+        "stage_path_equals_forward": same_as_forward,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

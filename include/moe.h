@@ -1,0 +1,184 @@
+/*
+ * moe.h -- C interface of libmoe: the forward pass of a token-choice
+ * Mixture-of-Experts FFN layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages define it:
+ *   - "How do Mixture of Expert Models Work?", section "The Math Behind MoEs":
+ *     y = sum_i G(x)_i E_i(x) with G(x) = Softmax(TopK(x.W_g)) -- the softmax
+ *     of only the k largest router logits, every other gate 0 -- and, for
+ *     Mixtral, SwiGLU experts with Top2.
+ *   - "[Paper Club] Upcycling Large Language Models into Mixture of Experts",
+ *     the MoE-layer walkthrough: route (the router is a plain matrix multiply),
+ *     permute (gather each expert's tokens into one matrix, dropping tokens by
+ *     capacity factor), run the experts (a grouped GEMM over any number of
+ *     experts and tokens in one operation), un-permute back to the token
+ *     order, and scale by the router probability.
+ *   - Capacity: "How do Mixture of Expert Models Work?", section "Load
+ *     Balancing" (Expert Capacity); "Scaling Vision with Sparse Mixture of
+ *     Experts", section "Priority Routing" (a fixed buffer per expert; tokens
+ *     beyond it are dropped once the expert is full); "Take a Closer Look at
+ *     the MoE LLM Routing", Introduction (drops land towards the end of the
+ *     sequence, i.e. buffers fill in token order).
+ *
+ * Conventions for every entry point:
+ *   - Problem scalars: T tokens, hidden size d, E experts, top-k, capacity
+ *     factor cf, expert FFN width F.
+ *   - Layouts are row-major. Weight matrices are [out, in] with the input
+ *     dimension contiguous: w_router [E, d], w_gate and w_up [E, F, d],
+ *     w_down [E, d, F].
+ *   - dtype: MOE_BF16 stores x, weights, x_perm, h, out_perm and y as
+ *     bfloat16 (accumulation in fp32); MOE_F32 stores them as fp32. Logits and
+ *     gates are always fp32; indices and row maps are int32.
+ *   - Capacity: cap = T if cf == 0 (dropless), else min(T, ceil(cf*T*k/E))
+ *     computed in double. Expert e keeps its first min(demand_e, cap)
+ *     assignments in token order; later ones are dropped and contribute 0
+ *     to y (the remaining gates are not renormalised).
+ *   - R_max = min(T*k, E*cap) bounds the number of kept rows R; permuted
+ *     buffers (x_perm, h, out_perm, row_slot) have R_max rows. The actual R
+ *     = expert_offsets[E] stays on the device; rows at or beyond it are left
+ *     untouched.
+ *   - Ownership: the caller allocates every device buffer; the library never
+ *     allocates or frees device memory and keeps no state between calls.
+ *     Device pointers must be 16-byte aligned. Inputs and outputs must not
+ *     overlap.
+ *   - Asynchrony: every call only enqueues kernels on `stream` (NULL = the
+ *     null stream) and returns; it never synchronises. Outputs are valid once
+ *     the caller has synchronised the stream.
+ *   - Errors: arguments are checked on the host before any launch; a failing
+ *     check returns its status and enqueues nothing. MOE_ERR_HIP reports a
+ *     launch error (hipGetLastError after the launches); faults during
+ *     execution surface at the caller's synchronisation, as usual in HIP.
+ *   - T == 0 is a valid empty problem: the call returns MOE_OK and enqueues
+ *     nothing (pointers are not inspected).
+ *   - Compiled limits (MOE_ERR_UNSUPPORTED beyond them): E <= 256, k <= 8,
+ *     T*k < 2^31; d and F multiples of 8 (bf16) or 4 (fp32); for bf16 the
+ *     grouped FFN also needs d and F to be multiples of 64.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null pointer, bad scalar, overlapping buffers */
+  MOE_ERR_UNSUPPORTED = 2,   /* outside the compiled limits, or misaligned pointer */
+  MOE_ERR_WORKSPACE = 3,     /* workspace too small */
+  MOE_ERR_HIP = 4            /* a HIP runtime call failed */
+} moe_status;
+
+/* Per-expert capacity for the given problem (host only, pure).
+ * Returns -1 if T < 0, E < 1, k not in [1, E] or cf negative / not finite. */
+int64_t moe_capacity(int64_t T, int32_t E, int32_t k, float cf);
+
+/* R_max = min(T*k, E*cap): the row count to allocate for x_perm, h, out_perm
+ * and row_slot. Host only. */
+int moe_rows_max(int64_t T, int32_t E, int32_t k, float cf, int64_t* rows);
+
+/* Workspace bytes needed by moe_permute (per-chunk expert histograms). */
+int moe_permute_workspace_bytes(int64_t T, int32_t E, size_t* bytes);
+
+/* Workspace bytes needed by moe_forward (routing outputs, row maps, x_perm,
+ * h, out_perm and the permutation's histograms, each 256-byte aligned). */
+int moe_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf,
+                        int32_t F, moe_dtype dt, size_t* bytes);
+
+/* Router: logits l = x . W_g^T (fp32 accumulation), the k largest per token
+ * in slot order (descending logit, ties to the lower expert index) and their
+ * softmax gates ("The Math Behind MoEs": Softmax(TopK(x.W_g))).
+ *   x          [T, d]  dt        input tokens
+ *   w_router   [E, d]  dt        router weight
+ *   topk_idx   [T, k]  int32     out: chosen experts
+ *   topk_gate  [T, k]  fp32      out: gates, summing to 1 per token
+ *   logits_opt [T, E]  fp32      out (optional, NULL to skip): router logits */
+int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt,
+              const void* x, const void* w_router,
+              int32_t* topk_idx, float* topk_gate, float* logits_opt,
+              hipStream_t stream);
+
+/* Permutation with token-order capacity (the walkthrough's permute step).
+ *   topk_idx        [T, k]      int32  in: from moe_route (values in [0, E))
+ *   expert_counts   [E]         int32  out: demand, tokens that chose e
+ *   expert_offsets  [E + 1]     int32  out: exclusive prefix sum of
+ *                                      kept_e = min(demand_e, cap)
+ *   slot_row        [T, k]      int32  out: row of (t, j) in x_perm, -1 if dropped
+ *   row_slot        [R_max]     int32  out: t*k + j for each kept row
+ *   x_perm          [R_max, d]  dt     out: x_perm[slot_row[t,j]] = x[t];
+ *                                      expert-major, token order inside an expert
+ *   ws, ws_bytes                       scratch, >= moe_permute_workspace_bytes */
+int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+                const void* x, const int32_t* topk_idx,
+                int32_t* expert_counts, int32_t* expert_offsets,
+                int32_t* slot_row, int32_t* row_slot, void* x_perm,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Grouped SwiGLU expert FFN over the permuted rows, one launch per
+ * projection for all experts (the walkthrough's grouped GEMM; Mixtral's
+ * SwiGLU experts in "The Math Behind MoEs"). For each expert e and each row r
+ * in [expert_offsets[e], expert_offsets[e+1]):
+ *   h[r, :]        = store(silu(x_perm[r] . W_gate[e]^T) * (x_perm[r] . W_up[e]^T))
+ *   out_perm[r, :] = store(h[r] . W_down[e]^T)
+ * silu(a) = a / (1 + exp(-a)); "store" rounds the fp32 accumulator to dt.
+ *   x_perm          [R_max, d]  dt
+ *   expert_offsets  [E + 1]     int32 (device; read by the kernels)
+ *   h_ws            [R_max, F]  dt    caller scratch, holds h on return
+ *   out_perm        [R_max, d]  dt    out */
+int moe_grouped_ffn(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
+                    moe_dtype dt, const void* x_perm, const int32_t* expert_offsets,
+                    const void* w_gate, const void* w_up, const void* w_down,
+                    void* h_ws, void* out_perm, hipStream_t stream);
+
+/* The two launches of moe_grouped_ffn, for callers that schedule (or time)
+ * them separately. Same arguments, layouts and arithmetic as above:
+ *   moe_expert_gate_up: h = store(silu(x_perm . W_gate^T) * (x_perm . W_up^T))
+ *   moe_expert_down:    out_perm = store(h . W_down^T)                       */
+int moe_expert_gate_up(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
+                       moe_dtype dt, const void* x_perm, const int32_t* expert_offsets,
+                       const void* w_gate, const void* w_up, void* h, hipStream_t stream);
+int moe_expert_down(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
+                    moe_dtype dt, const void* h, const int32_t* expert_offsets,
+                    const void* w_down, void* out_perm, hipStream_t stream);
+
+/* Un-permute and gate-weighted combine ("The Math Behind MoEs":
+ * y = sum_i G(x)_i E_i(x); the walkthrough's un-permute then scale):
+ *   y[t, :] = store(sum over kept slots j, ascending, of
+ *                   topk_gate[t, j] * out_perm[slot_row[t, j], :])
+ * summed in fp32 from +0; a token with every slot dropped gets y = 0.
+ *   out_perm   [R_max, d]  dt
+ *   slot_row   [T, k]      int32
+ *   topk_gate  [T, k]      fp32
+ *   y          [T, d]      dt    out */
+int moe_unpermute_combine(int64_t T, int32_t d, int32_t E, int32_t k, float cf,
+                          moe_dtype dt, const void* out_perm, const int32_t* slot_row,
+                          const float* topk_gate, void* y, hipStream_t stream);
+
+/* The whole layer: moe_route, moe_permute, moe_grouped_ffn and
+ * moe_unpermute_combine in sequence on one stream, with every intermediate
+ * in the caller's workspace (no host synchronisation, no allocation).
+ *   y                [T, d]  dt     out
+ *   topk_idx_opt     [T, k]  int32  out (optional; NULL keeps it in ws)
+ *   topk_gate_opt    [T, k]  fp32   out (optional)
+ *   slot_row_opt     [T, k]  int32  out (optional)
+ *   ws, ws_bytes                    scratch, >= moe_workspace_bytes */
+int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
+                moe_dtype dt, const void* x, const void* w_router,
+                const void* w_gate, const void* w_up, const void* w_down, void* y,
+                int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* slot_row_opt,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

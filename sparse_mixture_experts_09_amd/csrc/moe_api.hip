@@ -1,0 +1,319 @@
+// libmoe C interface: argument checks, capacity and workspace arithmetic,
+// and the launch sequence of the layer. No device memory is allocated here and
+// no call synchronises; see include/moe.h for the contract of each entry point.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "moe.h"
+#include "moe_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 8;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(int dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+struct Range {
+  const void* p;
+  size_t n;
+};
+
+bool overlap(Range a, Range b) {
+  if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// The first nout ranges are outputs; each must be disjoint from every other
+// listed range (inputs and the other outputs).
+bool any_overlap(const Range* all, int nout, int nall) {
+  for (int i = 0; i < nout; ++i)
+    for (int j = 0; j < nall; ++j)
+      if (j != i && overlap(all[i], all[j])) return true;
+  return false;
+}
+
+int64_t capacity_of(int64_t T, int E, int k, float cf) {
+  if (cf == 0.0f) return T;
+  const double c = ceil((double)cf * (double)T * (double)k / (double)E);
+  return c >= (double)T ? T : (int64_t)c;
+}
+
+int64_t rows_max_of(int64_t T, int E, int k, int64_t cap) {
+  const int64_t a = T * k, b = (int64_t)E * cap;
+  return a < b ? a : b;
+}
+
+// Scalar checks shared by every entry point. F < 0 means "not used".
+int check_scalars(int64_t T, int d, int E, int k, float cf, int F, int dt, bool ffn) {
+  if (T < 0 || d < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (F != -1 && F < 1) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(cf) || cf < 0.0f) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE || k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  const int vec = dt == MOE_BF16 ? 8 : 4;
+  if (d % vec != 0) return MOE_ERR_UNSUPPORTED;
+  if (F > 0 && F % vec != 0) return MOE_ERR_UNSUPPORTED;
+  if (ffn && dt == MOE_BF16 && (d % 64 != 0 || F % 64 != 0)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+struct ForwardLayout {
+  size_t topk_idx, topk_gate, slot_row, row_slot, counts, offsets, chunks, x_perm, h, out_perm, total;
+};
+
+ForwardLayout forward_layout(int64_t T, int d, int E, int k, int64_t R_max, int F, int dt) {
+  ForwardLayout L;
+  const size_t s = elem_bytes(dt);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round_up(bytes);
+    return at;
+  };
+  L.topk_idx = take((size_t)T * k * 4);
+  L.topk_gate = take((size_t)T * k * 4);
+  L.slot_row = take((size_t)T * k * 4);
+  L.row_slot = take((size_t)R_max * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.chunks = take((size_t)moe::permute_chunks(T) * E * 4);
+  L.x_perm = take((size_t)R_max * d * s);
+  L.h = take((size_t)R_max * F * s);
+  L.out_perm = take((size_t)R_max * d * s);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_capacity(int64_t T, int32_t E, int32_t k, float cf) {
+  if (T < 0 || E < 1 || k < 1 || k > E || !isfinite(cf) || cf < 0.0f) return -1;
+  return capacity_of(T, E, k, cf);
+}
+
+int moe_rows_max(int64_t T, int32_t E, int32_t k, float cf, int64_t* rows) {
+  if (rows == nullptr) return MOE_ERR_INVALID_ARG;
+  const int64_t cap = moe_capacity(T, E, k, cf);
+  if (cap < 0) return MOE_ERR_INVALID_ARG;
+  *rows = rows_max_of(T, E, k, cap);
+  return MOE_OK;
+}
+
+int moe_permute_workspace_bytes(int64_t T, int32_t E, size_t* bytes) {
+  if (bytes == nullptr || T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  *bytes = round_up((size_t)moe::permute_chunks(T) * E * 4);
+  return MOE_OK;
+}
+
+int moe_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+                        size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  const int st = check_scalars(T, d, E, k, cf, F, dt, true);
+  if (st != MOE_OK) return st;
+  const int64_t R_max = rows_max_of(T, E, k, capacity_of(T, E, k, cf));
+  *bytes = forward_layout(T, d, E, k, R_max, F, dt).total;
+  return MOE_OK;
+}
+
+int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, const void* x,
+              const void* w_router, int32_t* topk_idx, float* topk_gate, float* logits_opt,
+              hipStream_t stream) {
+  int st = check_scalars(T, d, E, k, 0.0f, -1, dt, false);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_idx) || !aligned16(topk_gate) ||
+      !aligned16(logits_opt))
+    return MOE_ERR_UNSUPPORTED;
+  const size_t s = elem_bytes(dt);
+  const Range all[] = {{topk_idx, (size_t)T * k * 4}, {topk_gate, (size_t)T * k * 4},
+                       {logits_opt, (size_t)T * E * 4}, {x, (size_t)T * d * s},
+                       {w_router, (size_t)E * d * s}};
+  if (any_overlap(all, 3, 5)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_router(dt == MOE_BF16, T, d, E, k, x, w_router, topk_idx, topk_gate,
+                                       logits_opt, stream));
+}
+
+int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
+                const int32_t* topk_idx, int32_t* expert_counts, int32_t* expert_offsets,
+                int32_t* slot_row, int32_t* row_slot, void* x_perm, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  int st = check_scalars(T, d, E, k, cf, -1, dt, false);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !topk_idx || !expert_counts || !expert_offsets || !slot_row || !row_slot || !x_perm || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(topk_idx) || !aligned16(expert_counts) || !aligned16(expert_offsets) ||
+      !aligned16(slot_row) || !aligned16(row_slot) || !aligned16(x_perm) || !aligned16(ws))
+    return MOE_ERR_UNSUPPORTED;
+  size_t need = 0;
+  moe_permute_workspace_bytes(T, E, &need);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const int64_t cap = capacity_of(T, E, k, cf);
+  const int64_t R_max = rows_max_of(T, E, k, cap);
+  const size_t s = elem_bytes(dt);
+  const Range all[] = {{expert_counts, (size_t)E * 4}, {expert_offsets, (size_t)(E + 1) * 4},
+                       {slot_row, (size_t)T * k * 4},  {row_slot, (size_t)R_max * 4},
+                       {x_perm, (size_t)R_max * d * s}, {ws, need},
+                       {x, (size_t)T * d * s},          {topk_idx, (size_t)T * k * 4}};
+  if (any_overlap(all, 6, 8)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_permute(dt == MOE_BF16, T, d, E, k, cap, x, topk_idx, expert_counts,
+                                        expert_offsets, slot_row, row_slot, x_perm,
+                                        reinterpret_cast<int32_t*>(ws), stream));
+}
+
+int moe_grouped_ffn(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+                    const void* x_perm, const int32_t* expert_offsets, const void* w_gate,
+                    const void* w_up, const void* w_down, void* h_ws, void* out_perm,
+                    hipStream_t stream) {
+  int st = check_scalars(T, d, E, k, cf, F, dt, true);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x_perm || !expert_offsets || !w_gate || !w_up || !w_down || !h_ws || !out_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(expert_offsets) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(h_ws) || !aligned16(out_perm))
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t R_max = rows_max_of(T, E, k, capacity_of(T, E, k, cf));
+  const size_t s = elem_bytes(dt);
+  const size_t wbytes = (size_t)E * F * d * s;
+  const Range all[] = {{h_ws, (size_t)R_max * F * s}, {out_perm, (size_t)R_max * d * s},
+                       {x_perm, (size_t)R_max * d * s}, {expert_offsets, (size_t)(E + 1) * 4},
+                       {w_gate, wbytes}, {w_up, wbytes}, {w_down, wbytes}};
+  if (any_overlap(all, 2, 7)) return MOE_ERR_INVALID_ARG;
+  hipError_t e = dt == MOE_BF16
+                     ? moe::launch_ffn_bf16(R_max, d, E, F, x_perm, expert_offsets, w_gate, w_up,
+                                            w_down, h_ws, out_perm, stream)
+                     : moe::launch_ffn_f32(R_max, d, E, F, x_perm, expert_offsets, w_gate, w_up,
+                                           w_down, h_ws, out_perm, stream);
+  return hip_status(e);
+}
+
+static int expert_gemm(int which, int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
+                       moe_dtype dt, const void* in, const int32_t* expert_offsets, const void* w0,
+                       const void* w1, void* out, hipStream_t stream) {
+  int st = check_scalars(T, d, E, k, cf, F, dt, true);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!in || !expert_offsets || !w0 || (which == 1 && !w1) || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(in) || !aligned16(expert_offsets) || !aligned16(w0) || !aligned16(w1) || !aligned16(out))
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t R_max = rows_max_of(T, E, k, capacity_of(T, E, k, cf));
+  const size_t s = elem_bytes(dt);
+  const size_t wbytes = (size_t)E * F * d * s;
+  const size_t in_cols = which == 1 ? d : F, out_cols = which == 1 ? F : d;
+  const Range all[] = {{out, (size_t)R_max * out_cols * s}, {in, (size_t)R_max * in_cols * s},
+                       {expert_offsets, (size_t)(E + 1) * 4}, {w0, wbytes}, {w1, which == 1 ? wbytes : 0}};
+  if (any_overlap(all, 1, 5)) return MOE_ERR_INVALID_ARG;
+  hipError_t e = dt == MOE_BF16
+                     ? moe::launch_gemm_bf16(which, R_max, d, E, F, in, expert_offsets, w0, w1, out, stream)
+                     : moe::launch_gemm_f32(which, R_max, d, E, F, in, expert_offsets, w0, w1, out, stream);
+  return hip_status(e);
+}
+
+int moe_expert_gate_up(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+                       const void* x_perm, const int32_t* expert_offsets, const void* w_gate,
+                       const void* w_up, void* h, hipStream_t stream) {
+  return expert_gemm(1, T, d, E, k, cf, F, dt, x_perm, expert_offsets, w_gate, w_up, h, stream);
+}
+
+int moe_expert_down(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+                    const void* h, const int32_t* expert_offsets, const void* w_down, void* out_perm,
+                    hipStream_t stream) {
+  return expert_gemm(2, T, d, E, k, cf, F, dt, h, expert_offsets, w_down, nullptr, out_perm, stream);
+}
+
+int moe_unpermute_combine(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+                          const void* out_perm, const int32_t* slot_row, const float* topk_gate,
+                          void* y, hipStream_t stream) {
+  int st = check_scalars(T, d, E, k, cf, -1, dt, false);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!out_perm || !slot_row || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(out_perm) || !aligned16(slot_row) || !aligned16(topk_gate) || !aligned16(y))
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t R_max = rows_max_of(T, E, k, capacity_of(T, E, k, cf));
+  const size_t s = elem_bytes(dt);
+  const Range all[] = {{y, (size_t)T * d * s}, {out_perm, (size_t)R_max * d * s},
+                       {slot_row, (size_t)T * k * 4}, {topk_gate, (size_t)T * k * 4}};
+  if (any_overlap(all, 1, 4)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(dt == MOE_BF16, T, d, k, out_perm, slot_row, topk_gate, y, stream));
+}
+
+int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+                const void* x, const void* w_router, const void* w_gate, const void* w_up,
+                const void* w_down, void* y, int32_t* topk_idx_opt, float* topk_gate_opt,
+                int32_t* slot_row_opt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_scalars(T, d, E, k, cf, F, dt, true);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(y) || !aligned16(ws) || !aligned16(topk_idx_opt) ||
+      !aligned16(topk_gate_opt) || !aligned16(slot_row_opt))
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t cap = capacity_of(T, E, k, cf);
+  const int64_t R_max = rows_max_of(T, E, k, cap);
+  const ForwardLayout L = forward_layout(T, d, E, k, R_max, F, dt);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const size_t s = elem_bytes(dt);
+  const size_t wbytes = (size_t)E * F * d * s;
+  const Range all[] = {{y, (size_t)T * d * s},        {topk_idx_opt, (size_t)T * k * 4},
+                       {topk_gate_opt, (size_t)T * k * 4}, {slot_row_opt, (size_t)T * k * 4},
+                       {ws, L.total},                 {x, (size_t)T * d * s},
+                       {w_router, (size_t)E * d * s}, {w_gate, wbytes},
+                       {w_up, wbytes},                {w_down, wbytes}};
+  if (any_overlap(all, 5, 10)) return MOE_ERR_INVALID_ARG;
+
+  char* w = reinterpret_cast<char*>(ws);
+  int32_t* idx = topk_idx_opt ? topk_idx_opt : reinterpret_cast<int32_t*>(w + L.topk_idx);
+  float* gate = topk_gate_opt ? topk_gate_opt : reinterpret_cast<float*>(w + L.topk_gate);
+  int32_t* srow = slot_row_opt ? slot_row_opt : reinterpret_cast<int32_t*>(w + L.slot_row);
+  int32_t* rslot = reinterpret_cast<int32_t*>(w + L.row_slot);
+  int32_t* counts = reinterpret_cast<int32_t*>(w + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(w + L.offsets);
+  int32_t* chunks = reinterpret_cast<int32_t*>(w + L.chunks);
+  void* x_perm = w + L.x_perm;
+  void* h = w + L.h;
+  void* out_perm = w + L.out_perm;
+  const bool bf16 = dt == MOE_BF16;
+
+  hipError_t e = moe::launch_router(bf16, T, d, E, k, x, w_router, idx, gate, nullptr, stream);
+  if (e == hipSuccess)
+    e = moe::launch_permute(bf16, T, d, E, k, cap, x, idx, counts, offsets, srow, rslot, x_perm, chunks,
+                            stream);
+  if (e == hipSuccess)
+    e = bf16 ? moe::launch_ffn_bf16(R_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, h, out_perm,
+                                    stream)
+             : moe::launch_ffn_f32(R_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, h, out_perm,
+                                   stream);
+  if (e == hipSuccess) e = moe::launch_combine(bf16, T, d, k, out_perm, srow, gate, y, stream);
+  return hip_status(e);
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape, limit or alignment";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

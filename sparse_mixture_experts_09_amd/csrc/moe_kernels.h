@@ -1,0 +1,40 @@
+// Kernel launchers of libmoe (internal; the public interface is include/moe.h).
+// Every launcher only enqueues work on stream s and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_router(bool bf16, int64_t T, int d, int E, int k, const void* x, const void* wr,
+                         int32_t* idx, float* gate, float* logits, hipStream_t s);
+
+// Chunks of tokens used by the permutation's histogram (one int per expert each).
+int64_t permute_chunks(int64_t T);
+
+hipError_t launch_permute(bool bf16, int64_t T, int d, int E, int k, int64_t cap, const void* x,
+                          const int32_t* idx, int32_t* expert_counts, int32_t* expert_offsets,
+                          int32_t* slot_row, int32_t* row_slot, void* x_perm, int32_t* chunk_counts,
+                          hipStream_t s);
+
+// The two grouped GEMMs (which = 1: gate/up with the SwiGLU epilogue, 2: down).
+hipError_t launch_gemm_bf16(int which, int64_t R_max, int d, int E, int F, const void* in,
+                            const int32_t* offsets, const void* w0, const void* w1, void* out,
+                            hipStream_t s);
+hipError_t launch_gemm_f32(int which, int64_t R_max, int d, int E, int F, const void* in,
+                           const int32_t* offsets, const void* w0, const void* w1, void* out,
+                           hipStream_t s);
+
+hipError_t launch_ffn_bf16(int64_t R_max, int d, int E, int F, const void* x_perm,
+                           const int32_t* offsets, const void* wg, const void* wu, const void* wd,
+                           void* h, void* out, hipStream_t s);
+
+hipError_t launch_ffn_f32(int64_t R_max, int d, int E, int F, const void* x_perm,
+                          const int32_t* offsets, const void* wg, const void* wu, const void* wd,
+                          void* h, void* out, hipStream_t s);
+
+hipError_t launch_combine(bool bf16, int64_t T, int d, int k, const void* out_perm,
+                          const int32_t* slot_row, const float* gate, void* y, hipStream_t s);
+
+}  // namespace moe

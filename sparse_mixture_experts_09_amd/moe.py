@@ -1,0 +1,235 @@
+"""ctypes binding of libmoe (include/moe.h).
+
+Argument marshalling only: shapes are read off the tensors, device pointers and
+the current HIP stream are passed through, and outputs that the caller does not
+supply are allocated with torch (device memory is the only thing torch provides
+here). Every step of the layer runs in the HIP kernels of libmoe.so; there is
+no fallback: if the library is not built, importing works but every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+
+_lib = None
+
+_i64, _i32, _f32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_SIGS = {
+    "moe_capacity": (_i64, [_i64, _i32, _i32, _f32]),
+    "moe_rows_max": (ctypes.c_int, [_i64, _i32, _i32, _f32, ctypes.POINTER(_i64)]),
+    "moe_permute_workspace_bytes": (ctypes.c_int, [_i64, _i32, ctypes.POINTER(_sz)]),
+    "moe_workspace_bytes": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int,
+                                           ctypes.POINTER(_sz)]),
+    "moe_route": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_permute": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _vp, _vp, _sz, _vp]),
+    "moe_grouped_ffn": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp,
+                                       _vp, _vp, _vp, _vp, _vp]),
+    "moe_expert_gate_up": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp,
+                                          _vp, _vp, _vp]),
+    "moe_expert_down": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp,
+                                       _vp, _vp]),
+    "moe_unpermute_combine": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, ctypes.c_int, _vp, _vp, _vp,
+                                             _vp, _vp]),
+    "moe_forward": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                   _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m sparse_mixture_experts_09_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def _check(fn: str, st: int) -> None:
+    if st != MOE_OK:
+        raise MoeError(fn, st)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def moe_capacity(T: int, E: int, k: int, cf: float) -> int:
+    return int(lib().moe_capacity(T, E, k, cf))
+
+
+def moe_rows_max(T: int, E: int, k: int, cf: float) -> int:
+    r = _i64()
+    _check("moe_rows_max", lib().moe_rows_max(T, E, k, cf, ctypes.byref(r)))
+    return int(r.value)
+
+
+def moe_permute_workspace_bytes(T: int, E: int) -> int:
+    b = _sz()
+    _check("moe_permute_workspace_bytes", lib().moe_permute_workspace_bytes(T, E, ctypes.byref(b)))
+    return int(b.value)
+
+
+def moe_workspace_bytes(T: int, d: int, E: int, k: int, cf: float, F: int, dtype) -> int:
+    dt = MOE_BF16 if dtype in (torch.bfloat16, MOE_BF16) else MOE_F32
+    b = _sz()
+    _check("moe_workspace_bytes", lib().moe_workspace_bytes(T, d, E, k, cf, F, dt, ctypes.byref(b)))
+    return int(b.value)
+
+
+def moe_route(x, w_router, k: int, topk_idx=None, topk_gate=None, logits=None, want_logits=False,
+              stream=None):
+    """Returns (topk_idx [T,k] int32, topk_gate [T,k] fp32, logits [T,E] fp32 or None)."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_gate is None:
+        topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if logits is None and want_logits:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    st = lib().moe_route(T, d, E, k, _dt(x), _ptr(x), _ptr(w_router), _ptr(topk_idx), _ptr(topk_gate),
+                         _ptr(logits), _stream(stream))
+    _check("moe_route", st)
+    return topk_idx, topk_gate, logits
+
+
+def moe_permute(x, topk_idx, E: int, cf: float, stream=None, out=None):
+    """Returns dict(expert_counts, expert_offsets, slot_row, row_slot, x_perm)."""
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    R_max = moe_rows_max(T, E, k, cf)
+    o = out or {}
+
+    def get(name, shape, dtype):
+        t = o.get(name)
+        return t if t is not None else torch.empty(shape, dtype=dtype, device=dev)
+
+    counts = get("expert_counts", E, torch.int32)
+    offsets = get("expert_offsets", E + 1, torch.int32)
+    slot_row = get("slot_row", (T, k), torch.int32)
+    row_slot = get("row_slot", max(R_max, 1), torch.int32)
+    x_perm = get("x_perm", (max(R_max, 1), d), x.dtype)
+    ws = get("ws", max(moe_permute_workspace_bytes(T, E), 16), torch.uint8)
+    st = lib().moe_permute(T, d, E, k, cf, _dt(x), _ptr(x), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                           _ptr(slot_row), _ptr(row_slot), _ptr(x_perm), _ptr(ws), ws.numel(),
+                           _stream(stream))
+    _check("moe_permute", st)
+    return dict(expert_counts=counts, expert_offsets=offsets, slot_row=slot_row, row_slot=row_slot,
+                x_perm=x_perm)
+
+
+def moe_grouped_ffn(x_perm, expert_offsets, w_gate, w_up, w_down, T: int, k: int, cf: float,
+                    h=None, out_perm=None, stream=None):
+    """Returns (h [R_max,F], out_perm [R_max,d])."""
+    E, F, d = w_gate.shape
+    R_max = moe_rows_max(T, E, k, cf)
+    dev = x_perm.device
+    if h is None:
+        h = torch.empty((max(R_max, 1), F), dtype=x_perm.dtype, device=dev)
+    if out_perm is None:
+        out_perm = torch.empty((max(R_max, 1), d), dtype=x_perm.dtype, device=dev)
+    st = lib().moe_grouped_ffn(T, d, E, k, cf, F, _dt(x_perm), _ptr(x_perm), _ptr(expert_offsets),
+                               _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(out_perm),
+                               _stream(stream))
+    _check("moe_grouped_ffn", st)
+    return h, out_perm
+
+
+def moe_expert_gate_up(x_perm, expert_offsets, w_gate, w_up, T: int, k: int, cf: float, h=None,
+                       stream=None):
+    """First grouped GEMM with the SwiGLU epilogue. Returns h [R_max, F]."""
+    E, F, d = w_gate.shape
+    if h is None:
+        h = torch.empty((max(moe_rows_max(T, E, k, cf), 1), F), dtype=x_perm.dtype, device=x_perm.device)
+    st = lib().moe_expert_gate_up(T, d, E, k, cf, F, _dt(x_perm), _ptr(x_perm), _ptr(expert_offsets),
+                                  _ptr(w_gate), _ptr(w_up), _ptr(h), _stream(stream))
+    _check("moe_expert_gate_up", st)
+    return h
+
+
+def moe_expert_down(h, expert_offsets, w_down, T: int, k: int, cf: float, out_perm=None, stream=None):
+    """Second grouped GEMM. Returns out_perm [R_max, d]."""
+    E, d, F = w_down.shape
+    if out_perm is None:
+        out_perm = torch.empty((max(moe_rows_max(T, E, k, cf), 1), d), dtype=h.dtype, device=h.device)
+    st = lib().moe_expert_down(T, d, E, k, cf, F, _dt(h), _ptr(h), _ptr(expert_offsets), _ptr(w_down),
+                               _ptr(out_perm), _stream(stream))
+    _check("moe_expert_down", st)
+    return out_perm
+
+
+def moe_unpermute_combine(out_perm, slot_row, topk_gate, E: int, cf: float, y=None, stream=None):
+    T, k = slot_row.shape
+    d = out_perm.shape[1]
+    if y is None:
+        y = torch.empty((T, d), dtype=out_perm.dtype, device=out_perm.device)
+    st = lib().moe_unpermute_combine(T, d, E, k, cf, _dt(out_perm), _ptr(out_perm), _ptr(slot_row),
+                                     _ptr(topk_gate), _ptr(y), _stream(stream))
+    _check("moe_unpermute_combine", st)
+    return y
+
+
+def moe_forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, y=None, topk_idx=None,
+                topk_gate=None, slot_row=None, ws=None, stream=None):
+    """The whole layer. Returns y [T, d] (topk_idx / topk_gate / slot_row are
+    filled when given)."""
+    T, d = x.shape
+    E, F, _ = w_gate.shape
+    if y is None:
+        y = torch.empty_like(x)
+    if ws is None:
+        ws = torch.empty(max(moe_workspace_bytes(T, d, E, k, cf, F, x.dtype), 16), dtype=torch.uint8,
+                         device=x.device)
+    st = lib().moe_forward(T, d, E, k, cf, F, _dt(x), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
+                           _ptr(w_down), _ptr(y), _ptr(topk_idx), _ptr(topk_gate), _ptr(slot_row),
+                           _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_forward", st)
+    return y
