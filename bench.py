@@ -63,12 +63,13 @@ def cpu_baseline(w, a, target_s):
         orc.forward(a["x"][:S], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], w.k, w.cf, w.dtype)
         return time.perf_counter() - t
 
+    # grow the sample (x4) until it takes about target_s or covers the whole batch;
+    # each run includes the oracle's fixed cost of widening the weights to float64
     S = min(w.T, 128)
     t = run(S)
     log(f"cpu oracle: {S} tokens in {t:.2f} s")
-    S2 = min(w.T, int(S * target_s / max(t, 1e-3)))
-    if S2 > 1.5 * S:
-        S = S2
+    while S < w.T and t < target_s / 2:
+        S = min(w.T, 4 * S)
         t = run(S)
         log(f"cpu oracle: {S} tokens in {t:.2f} s")
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])

@@ -9,7 +9,7 @@
 // consecutive tokens. Lane l covers the 16-byte slices l, l+64, l+128, ... of
 // a token row, so every x row is read once with coalesced 16-byte loads. The
 // experts are processed in passes of 8: a lane accumulates TW x 8 partial dot
-// products (bf16 pairs through v_dot2, fp32 through fma), then one transposed
+// products (bf16 widened exactly to fp32, then fma), then one transposed
 // wave reduction leaves every (token, expert) total in some lane. The logits
 // go to LDS and the arg-top-k runs per token over one wavefront: each lane
 // holds up to four experts (E <= 256), and k rounds of a 64-lane butterfly
@@ -24,12 +24,12 @@ namespace {
 constexpr int kRouterWaves = 4;
 constexpr int kEPass = 8;
 
+// bf16 values widen exactly to fp32; products and sums are plain fp32 fma.
 __device__ __forceinline__ float dot16(BF16, const u32x4& xv, const u32x4& wv, float acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    bf16x2 a = __builtin_bit_cast(bf16x2, xv[i]);
-    bf16x2 b = __builtin_bit_cast(bf16x2, wv[i]);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+    acc = fmaf(bf16_lo(xv[i]), bf16_lo(wv[i]), acc);
+    acc = fmaf(bf16_hi(xv[i]), bf16_hi(wv[i]), acc);
   }
   return acc;
 }
