@@ -89,6 +89,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run K device-to-device copies of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -98,6 +100,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": args.steps}), flush=True)
+        return
 
     import moe_inputs as mi
     from sparse_mixture_experts_09_amd import moe
@@ -205,7 +217,7 @@ def main():
     hbm_frac = (alg["route"]["bytes"] + alg["permute"]["bytes"] + alg["combine"]["bytes"]) / hbm_t / 1e9 / PEAK["hbm_gbs"]
     gu_t = st_ms["gate_up"] * 1e-3
     achieved = alg["gate_up"]["flops"] / gu_t / 1e12
-    roofline = {"bound": "mfma", "kernel": "ffn_bf16_kernel<128,64,true> (grouped gate/up GEMM + SwiGLU)",
+    roofline = {"bound": "mfma", "kernel": "ffn_bf16_dma_kernel<128,true> (grouped gate/up GEMM + SwiGLU epilogue)",
                 "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s", "frac": achieved / peak_mm,
                 "traffic": load_traffic(w.name), "alg_flops_per_launch": alg["gate_up"]["flops"],
                 "avg_launch_us": st_ms["gate_up"] * 1e3}

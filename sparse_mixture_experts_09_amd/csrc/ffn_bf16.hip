@@ -15,16 +15,15 @@
 // activations its second, so each lane's accumulator holds 4 consecutive output
 // features of one row, stored as one 8-byte write.
 //
-// Block tile BM rows x BN output features, K step 64, 4 wavefronts in 2 x 2;
-// a wavefront owns (BM/2) x (BN/2) outputs (and, in GEMM1, the gate and the up
-// accumulator of each). The weight tile of GEMM1 holds BN gate rows followed by
-// BN up rows, so the two products for one h element sit in the same lane and
-// register, and the SwiGLU epilogue needs no data exchange.
-//
-// LDS: double-buffered A and B tiles, rows of 128 bytes split into eight
-// 16-byte chunks; chunk c of row r lives at chunk position c ^ (r & 7), so the
-// 8 lanes that read one chunk column of 8 consecutive rows hit 8 different
-// 16-byte bank groups.
+// Two kernels share the fragment layout and epilogue:
+//   ffn_bf16_dma_kernel  256-row tiles, 8 wavefronts (2 per SIMD), K step 64,
+//                        global -> LDS DMA into two stages (the main path);
+//   ffn_bf16_kernel      128-row tiles, 4 wavefronts, register-staged loads
+//                        (small problems, where big tiles waste work on the
+//                        ragged last tile of each expert).
+// In GEMM1 the weight tile holds BN gate rows followed by BN up rows, so the
+// two products for one h element sit in the same lane and register and the
+// SwiGLU epilogue needs no data exchange.
 #include "ffn_sched.h"
 #include "moe_common.h"
 #include "moe_kernels.h"
@@ -36,31 +35,37 @@ namespace {
 constexpr int kBK = 64;            // bf16 elements per K step (128 bytes per row)
 constexpr int kRowBytes = kBK * 2;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk c of row r sits at position c ^ (r & 7) ^ ((r >> 3) & 1): the lanes of one ds_read_b128
+// phase (rows r..r+15, one chunk column) then hit distinct 16-byte bank groups whether the LDS
+// serves 8 lanes over 32 banks or 16 lanes over 64 banks per cycle, and so do the row-major writes.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+}
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 
-template <int BM, int BN, bool SWIGLU>
-__global__ __launch_bounds__(256) void ffn_bf16_kernel(int E, const int32_t* __restrict__ offsets, int N,
+template <int BM, int BN, bool SWIGLU, int NWM, int NWN>
+__global__ __launch_bounds__(64 * NWM * NWN) void ffn_bf16_kernel(int E, const int32_t* __restrict__ offsets, int N,
                                                        int K, const uint16_t* __restrict__ A,
                                                        const uint16_t* __restrict__ B0,
                                                        const uint16_t* __restrict__ B1,
                                                        uint16_t* __restrict__ C, int NT) {
   constexpr int BROWS = SWIGLU ? 2 * BN : BN;    // weight rows staged per K step
-  constexpr int WM = BM / 2, WN = BN / 2;        // wave tile (output rows x output features)
+  constexpr int NT_ = 64 * NWM * NWN;            // threads per block
+  constexpr int WM = BM / NWM, WN = BN / NWN;    // wave tile (output rows x output features)
   constexpr int MB = WM / 32, NB = WN / 32;      // 32x32 MFMA blocks per wave
   constexpr int NACC = (SWIGLU ? 2 : 1) * MB * NB;
-  constexpr int A_LD = BM * 8 / 256;             // 16-byte chunks per thread per K step
-  constexpr int B_LD = BROWS * 8 / 256;
+  constexpr int A_LD = BM * 8 / NT_;             // 16-byte chunks per thread per K step
+  constexpr int B_LD = BROWS * 8 / NT_;
   constexpr int STAGE = (BM + BROWS) * kRowBytes;
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && (BM * 8) % NT_ == 0 && (BROWS * 8) % NT_ == 0, "tile");
   extern __shared__ __align__(16) char smem[];
 
   TileCoord tc;
   if (!find_tile(offsets, E, BM, NT, blockIdx.x, tc)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int n0 = tc.n_tile * BN;
   const size_t ldk = (size_t)K;   // elements per row for both operands
 
@@ -70,7 +75,7 @@ __global__ __launch_bounds__(256) void ffn_bf16_kernel(int E, const int32_t* __r
   int a_lds[A_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int q = tid + 256 * i, row = q >> 3, c = q & 7;
+    const int q = tid + NT_ * i, row = q >> 3, c = q & 7;
     const int r = min(tc.m0 + row, tc.seg_rows - 1);
     a_src[i] = A + (size_t)(tc.seg_start + r) * ldk + c * 8;
     a_lds[i] = swz(row, c);
@@ -80,7 +85,7 @@ __global__ __launch_bounds__(256) void ffn_bf16_kernel(int E, const int32_t* __r
   const size_t wofs = (size_t)tc.e * (size_t)N * ldk;
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    const int q = tid + 256 * i, row = q >> 3, c = q & 7;
+    const int q = tid + NT_ * i, row = q >> 3, c = q & 7;
     const uint16_t* base = B0;
     int n = row;
     if (SWIGLU && row >= BN) {
@@ -112,42 +117,58 @@ __global__ __launch_bounds__(256) void ffn_bf16_kernel(int E, const int32_t* __r
     for (int i = 0; i < B_LD; ++i) st16(st + b_lds[i], rb[i]);
   };
 
+  // Fragments for one 16-deep substep: MB activation blocks and NBF weight
+  // blocks (gate blocks, then up blocks in GEMM1). Two register sets: the
+  // reads for substep s+1 are issued before the MFMAs of substep s, so the LDS
+  // latency hides behind MB*NBF matrix instructions.
+  constexpr int NBF = (SWIGLU ? 2 : 1) * NB;
+  bf16x8 fa[2][MB], fb[2][NBF];
+  auto read_frags = [&](const char* buf, int s, bf16x8(&A_)[MB], bf16x8(&B_)[NBF]) {
+    const int chunk = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      A_[mb] = __builtin_bit_cast(bf16x8, ld16(buf + swz(wm * WM + mb * 32 + (lane & 31), chunk)));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int row = wn * WN + nb * 32 + (lane & 31);
+      B_[nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowBytes + swz(row, chunk)));
+      if (SWIGLU) B_[NB + nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowBytes + swz(BN + row, chunk)));
+    }
+  };
+  auto mma = [&](const bf16x8(&A_)[MB], const bf16x8(&B_)[NBF]) {
+#pragma unroll
+    for (int nb = 0; nb < NBF; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        // accumulator order: [gate|plain][mb][nb], then [up][mb][nb]
+        const int a = (nb / NB) * MB * NB + mb * NB + (nb % NB);
+        acc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B_[nb], A_[mb], acc[a], 0, 0, 0);
+      }
+  };
+  static_assert(kBK / 16 == 4, "the substep schedule below assumes four 16-deep substeps");
+
   const int KT = K / kBK;
   gload(0);
   lstore(smem);
   __syncthreads();
+  read_frags(smem, 0, fa[0], fb[0]);
 
   for (int kt = 0; kt < KT; ++kt) {
-    char* cur = smem + (kt & 1) * STAGE;
-    if (kt + 1 < KT) gload((kt + 1) * kBK);
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      const int chunk = 2 * s + (lane >> 5);
-      bf16x8 xa[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int row = wm * WM + mb * 32 + (lane & 31);
-        xa[mb] = __builtin_bit_cast(bf16x8, ld16(cur + swz(row, chunk)));
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int row = wn * WN + nb * 32 + (lane & 31);
-        const bf16x8 wg = __builtin_bit_cast(bf16x8, ld16(cur + BM * kRowBytes + swz(row, chunk)));
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb * NB + nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wg, xa[mb], acc[mb * NB + nb], 0, 0, 0);
-        if (SWIGLU) {
-          const bf16x8 wu =
-              __builtin_bit_cast(bf16x8, ld16(cur + BM * kRowBytes + swz(BN + row, chunk)));
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            acc[MB * NB + mb * NB + nb] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(wu, xa[mb], acc[MB * NB + mb * NB + nb], 0, 0, 0);
-        }
-      }
-    }
-    if (kt + 1 < KT) lstore(smem + ((kt + 1) & 1) * STAGE);
+    const char* cur = smem + (kt & 1) * STAGE;
+    char* nxt = smem + ((kt + 1) & 1) * STAGE;
+    const bool more = kt + 1 < KT;
+    if (more) gload((kt + 1) * kBK);
+    read_frags(cur, 1, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    read_frags(cur, 2, fa[0], fb[0]);
+    mma(fa[1], fb[1]);
+    read_frags(cur, 3, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    // the next buffer was last read before the previous barrier
+    if (more) lstore(nxt);
+    mma(fa[1], fb[1]);
     __syncthreads();
+    if (more) read_frags(nxt, 0, fa[0], fb[0]);
   }
 
   // epilogue: lane holds, for its row (lane & 31), features 8*g + 4*(lane>>5) + 0..3
@@ -177,18 +198,237 @@ __global__ __launch_bounds__(256) void ffn_bf16_kernel(int E, const int32_t* __r
   }
 }
 
-template <int BM, int BN, bool SWIGLU>
+// ---------------------------------------------------------------------------
+// Main kernel: operand tiles go straight from global memory into LDS with
+// global_load_lds_dwordx4 (no staging registers, no ds_write), K step 64, two
+// LDS stages of 256 + BROWS rows x 128 bytes.
+//
+// One DMA instruction writes 1 KB of LDS contiguously (lane L at +16 L, i.e.
+// 8 rows of 128 bytes), so the bank swizzle is applied on the global side:
+// the lane that lands on chunk position p of tile row r fetches chunk
+// p ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1). Full 128-byte rows keep every
+// global request a whole cache line.
+//
+// Schedule of one K step (tile kt in stage kt & 1, tile kt + 1 in flight):
+//   substeps 0..2: read the next substep's fragments, then 16 MFMAs per wave
+//   wait for my LDS reads and for tile kt + 1's DMA, s_barrier
+//   DMA tile kt + 2 into stage kt & 1 (every wave is done reading it)
+//   read fragments of tile kt + 1, substep 0; MFMAs of substep 3
+// The barrier is a bare s_barrier: __syncthreads() would also wait for the
+// DMA just issued. The loop body has no branches (the prefetch past the last
+// tile reloads the last tile into a stage nobody reads); the last K step is
+// peeled.
+// ---------------------------------------------------------------------------
+
+constexpr int kRowB = kBK * 2;                  // 128 bytes per LDS row
+__device__ __forceinline__ int dswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int daddr(int r, int chunk) { return r * kRowB + ((chunk ^ dswz(r)) << 4); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N & 0x30) << 10) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt lgkmcnt(0), other counters untouched
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte-per-lane global -> LDS DMA (global_load_lds_dwordx4). The LDS
+// address must be wave-uniform; lane L lands at lds + 16 L. The builtin only
+// exists for the device, so the host pass sees an empty body (otherwise it
+// drops the host stubs of kernel templates that use it).
+__device__ __forceinline__ void dma16(const void* g, char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+#endif
+}
+
+template <int BN, bool SWIGLU>
+__global__ __launch_bounds__(512) void ffn_bf16_dma_kernel(
+    int E, const int32_t* __restrict__ offsets, int N, int K, const uint16_t* __restrict__ A,
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT) {
+  constexpr int BM = 256, NWM = 2, NWN = 4, NW = NWM * NWN;
+  constexpr int BROWS = SWIGLU ? 2 * BN : BN;
+  constexpr int WM = BM / NWM, WN = BN / NWN;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int NBF = (SWIGLU ? 2 : 1) * NB;
+  constexpr int NACC = MB * NBF;
+  constexpr int A_PW = BM / 8 / NW, B_PW = BROWS / 8 / NW;   // 1 KB DMA pieces per wave per K step
+  constexpr int LOADS = A_PW + B_PW;
+  constexpr int STAGE = (BM + BROWS) * kRowB;
+  static_assert(BM % (8 * NW) == 0 && BROWS % (8 * NW) == 0 && WN % 32 == 0, "tile");
+  extern __shared__ __align__(16) char smem[];
+
+  TileCoord tc;
+  if (!find_tile(offsets, E, BM, NT, blockIdx.x, tc)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int n0 = tc.n_tile * BN;
+
+  // per-lane byte offsets of the 16-byte pieces this lane fetches (row clamped
+  // into the expert's segment / below N: duplicates feed no stored output)
+  const char* Ab = reinterpret_cast<const char*>(A);
+  const char* B0b = reinterpret_cast<const char*>(B0);
+  const char* B1b = reinterpret_cast<const char*>(B1);
+  const size_t wofs = (size_t)tc.e * (size_t)N * K * 2;
+  size_t a_off[A_PW], b_off[B_PW];
+#pragma unroll
+  for (int i = 0; i < A_PW; ++i) {
+    const int row = (wave * A_PW + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ dswz(row);
+    const int r = min(tc.m0 + row, tc.seg_rows - 1);
+    a_off[i] = (size_t)(tc.seg_start + r) * K * 2 + c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < B_PW; ++i) {
+    const int row = (wave * B_PW + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ dswz(row);
+    const int n = min(n0 + (SWIGLU && row >= BN ? row - BN : row), N - 1);
+    b_off[i] = wofs + (size_t)n * K * 2 + c * 16;
+  }
+  const int KT = K / kBK;
+  auto dma = [&](int kt) {
+    const int kc = kt < KT ? kt : KT - 1;
+    char* st = smem + (kt & 1) * STAGE;
+    const size_t koff = (size_t)kc * kRowB;
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) dma16(Ab + a_off[i] + koff, st + (wave * A_PW + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i) {
+      const int row = (wave * B_PW + i) * 8;   // first row of this piece (wave-uniform)
+      const char* base = (SWIGLU && row >= BN) ? B1b : B0b;
+      dma16(base + b_off[i] + koff, st + BM * kRowB + (wave * B_PW + i) * 1024);
+    }
+  };
+
+  f32x16 acc[NACC];
+#pragma unroll
+  for (int i = 0; i < NACC; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  bf16x8 fa[2][MB], fb[2][NBF];
+  auto read_frags = [&](int stage, int s, bf16x8(&A_)[MB], bf16x8(&B_)[NBF]) {
+    const char* buf = smem + stage * STAGE;
+    const int chunk = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      A_[mb] = __builtin_bit_cast(bf16x8, ld16(buf + daddr(wm * WM + mb * 32 + (lane & 31), chunk)));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int row = wn * WN + nb * 32 + (lane & 31);
+      B_[nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(row, chunk)));
+      if (SWIGLU) B_[NB + nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(BN + row, chunk)));
+    }
+  };
+  auto mma = [&](const bf16x8(&A_)[MB], const bf16x8(&B_)[NBF]) {
+#pragma unroll
+    for (int nb = 0; nb < NBF; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        // accumulator order: [gate | plain][mb][nb], then [up][mb][nb]
+        const int a = (nb / NB) * MB * NB + mb * NB + (nb % NB);
+        acc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B_[nb], A_[mb], acc[a], 0, 0, 0);
+      }
+  };
+
+  dma(0);
+  dma(1);
+  wait_vmcnt<LOADS>();          // tile 0 landed (tile 1 may be in flight)
+  __builtin_amdgcn_s_barrier();
+  read_frags(0, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < KT - 1; ++kt) {
+    const int cur = kt & 1;
+    read_frags(cur, 1, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    read_frags(cur, 2, fa[0], fb[0]);
+    mma(fa[1], fb[1]);
+    read_frags(cur, 3, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    wait_lgkm0();               // this wave's reads of stage cur are done
+    wait_vmcnt<0>();            // tile kt + 1 landed
+    __builtin_amdgcn_s_barrier();
+    dma(kt + 2);                // into stage cur
+    read_frags(cur ^ 1, 0, fa[0], fb[0]);
+    mma(fa[1], fb[1]);
+  }
+  {
+    const int cur = (KT - 1) & 1;
+    read_frags(cur, 1, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    read_frags(cur, 2, fa[0], fb[0]);
+    mma(fa[1], fb[1]);
+    read_frags(cur, 3, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    mma(fa[1], fb[1]);
+  }
+  // the redundant prefetch of tile KT may still be landing in a stage nobody reads;
+  // drain it so no DMA outlives the block's LDS allocation
+  wait_vmcnt<0>();
+
+  // epilogue: lane holds, for its row (lane & 31), features 8*g + 4*(lane>>5) + 0..3
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int rloc = tc.m0 + wm * WM + mb * 32 + (lane & 31);
+    if (rloc >= tc.seg_rows) continue;
+    uint16_t* crow = C + (size_t)(tc.seg_start + rloc) * (size_t)N;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = n0 + wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
+        if (col >= N) continue;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = acc[mb * NB + nb][4 * g + i];
+          v[i] = SWIGLU ? silu(a) * acc[MB * NB + mb * NB + nb][4 * g + i] : a;
+        }
+        uint2 w;
+        w.x = pack_bf16x2(v[0], v[1]);
+        w.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(crow + col) = w;
+      }
+    }
+  }
+}
+
+template <int BN, bool SWIGLU>
+hipError_t launch_dma(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A,
+                      const void* B0, const void* B1, void* C, hipStream_t s) {
+  constexpr int BM = 256;
+  constexpr int BROWS = SWIGLU ? 2 * BN : BN;
+  constexpr size_t kLds = 2 * (size_t)(BM + BROWS) * kRowB;
+  auto kern = &ffn_bf16_dma_kernel<BN, SWIGLU>;
+  // opt in to more than 64 KiB of dynamic LDS once per instantiation
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (attr != hipSuccess) return attr;
+  const int NT = (N + BN - 1) / BN;
+  const int64_t blocks = ((R_max + BM - 1) / BM + E) * NT;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(512), kLds, s, E, offsets, N, K,
+                     reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B0),
+                     reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C), NT);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, bool SWIGLU, int NWM = 2, int NWN = 2>
 hipError_t launch_gemm(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A,
                        const void* B0, const void* B1, void* C, hipStream_t s) {
+  constexpr int BROWS = SWIGLU ? 2 * BN : BN;
+  constexpr size_t kLds = 2 * (size_t)(BM + BROWS) * kRowBytes;
+  auto kern = &ffn_bf16_kernel<BM, BN, SWIGLU, NWM, NWN>;
+  // opt in to more than 64 KiB of dynamic LDS once per instantiation
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (attr != hipSuccess) return attr;
   const int NT = (N + BN - 1) / BN;
   const int64_t mt_max = (R_max + BM - 1) / BM + E;
   const int64_t blocks = mt_max * NT;
-  constexpr int BROWS = SWIGLU ? 2 * BN : BN;
-  const size_t lds = 2 * (size_t)(BM + BROWS) * kRowBytes;
-  hipLaunchKernelGGL((ffn_bf16_kernel<BM, BN, SWIGLU>), dim3((unsigned)blocks), dim3(256), lds, s, E,
-                     offsets, N, K, reinterpret_cast<const uint16_t*>(A),
-                     reinterpret_cast<const uint16_t*>(B0), reinterpret_cast<const uint16_t*>(B1),
-                     reinterpret_cast<uint16_t*>(C), NT);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * NWM * NWN), kLds, s, E, offsets, N, K,
+                     reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B0),
+                     reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C), NT);
   return hipGetLastError();
 }
 
@@ -197,6 +437,13 @@ hipError_t launch_gemm(int64_t R_max, int E, const int32_t* offsets, int N, int 
 hipError_t launch_gemm_bf16(int which, int64_t R_max, int d, int E, int F, const void* in,
                             const int32_t* offsets, const void* w0, const void* w1, void* out,
                             hipStream_t s) {
+  // 256-row DMA tiles once experts average at least 128 rows; below that the
+  // 128-row tiles waste less work on the ragged last tile of each expert.
+  const bool big = R_max >= 128 * (int64_t)E;
+  if (big) {
+    if (which == 1) return launch_dma<128, true>(R_max, E, offsets, F, d, in, w0, w1, out, s);
+    return launch_dma<256, false>(R_max, E, offsets, d, F, in, w0, nullptr, out, s);
+  }
   if (which == 1) return launch_gemm<128, 64, true>(R_max, E, offsets, F, d, in, w0, w1, out, s);
   return launch_gemm<128, 128, false>(R_max, E, offsets, d, F, in, w0, nullptr, out, s);
 }
