@@ -86,8 +86,16 @@ int moe_rows_max(int64_t T, int32_t E, int32_t k, float cf, int64_t* rows);
 /* Workspace bytes needed by moe_permute (per-chunk expert histograms). */
 int moe_permute_workspace_bytes(int64_t T, int32_t E, size_t* bytes);
 
+/* Workspace bytes of moe_grouped_ffn / moe_expert_down: fp32 partial tiles
+ * for the down projection's split tail (one 256 x 256 tile per compute unit
+ * of the current device at most; 0 when the problem uses no split). Query it
+ * with the device the calls will run on current. */
+int moe_ffn_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
+                            moe_dtype dt, size_t* bytes);
+
 /* Workspace bytes needed by moe_forward (routing outputs, row maps, x_perm,
- * h, out_perm and the permutation's histograms, each 256-byte aligned). */
+ * h, out_perm, the permutation's histograms and the FFN's split-tail
+ * partials, each 256-byte aligned; depends on the current device). */
 int moe_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf,
                         int32_t F, moe_dtype dt, size_t* bytes);
 
@@ -130,11 +138,18 @@ int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype 
  *   x_perm          [R_max, d]  dt
  *   expert_offsets  [E + 1]     int32 (device; read by the kernels)
  *   h_ws            [R_max, F]  dt    caller scratch, holds h on return
- *   out_perm        [R_max, d]  dt    out */
+ *   out_perm        [R_max, d]  dt    out
+ *   ws, ws_bytes                      scratch of moe_ffn_workspace_bytes; NULL
+ *                                     runs the down projection without the
+ *                                     split tail (same result, longer tail)
+ * Scheduling: when the tile count of the down projection leaves a partial
+ * last round on the device's compute units, each tile of that round is split
+ * into K-slices whose fp32 partial sums are added in slice order before the
+ * single rounding to dt, so results are deterministic. */
 int moe_grouped_ffn(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
                     moe_dtype dt, const void* x_perm, const int32_t* expert_offsets,
                     const void* w_gate, const void* w_up, const void* w_down,
-                    void* h_ws, void* out_perm, hipStream_t stream);
+                    void* h_ws, void* out_perm, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* The two launches of moe_grouped_ffn, for callers that schedule (or time)
  * them separately. Same arguments, layouts and arithmetic as above:
@@ -145,7 +160,8 @@ int moe_expert_gate_up(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int
                        const void* w_gate, const void* w_up, void* h, hipStream_t stream);
 int moe_expert_down(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
                     moe_dtype dt, const void* h, const int32_t* expert_offsets,
-                    const void* w_down, void* out_perm, hipStream_t stream);
+                    const void* w_down, void* out_perm, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
 
 /* Un-permute and gate-weighted combine ("The Math Behind MoEs":
  * y = sum_i G(x)_i E_i(x); the walkthrough's un-permute then scale):

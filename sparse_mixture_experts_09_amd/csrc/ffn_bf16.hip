@@ -221,6 +221,7 @@ __global__ __launch_bounds__(64 * NWM * NWN) void ffn_bf16_kernel(int E, const i
 // ---------------------------------------------------------------------------
 
 constexpr int kRowB = kBK * 2;                  // 128 bytes per LDS row
+constexpr int kMaxSplit = 8;                    // most K-slices per split tail tile
 __device__ __forceinline__ int dswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int daddr(int r, int chunk) { return r * kRowB + ((chunk ^ dswz(r)) << 4); }
 
@@ -247,7 +248,8 @@ __device__ __forceinline__ void dma16(const void* g, char* lds) {
 template <int BN, bool SWIGLU>
 __global__ __launch_bounds__(512) void ffn_bf16_dma_kernel(
     int E, const int32_t* __restrict__ offsets, int N, int K, const uint16_t* __restrict__ A,
-    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT) {
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT,
+    int P, int max_split, float* __restrict__ partials) {
   constexpr int BM = 256, NWM = 2, NWN = 4, NW = NWM * NWN;
   constexpr int BROWS = SWIGLU ? 2 * BN : BN;
   constexpr int WM = BM / NWM, WN = BN / NWN;
@@ -260,8 +262,17 @@ __global__ __launch_bounds__(512) void ffn_bf16_dma_kernel(
   static_assert(BM % (8 * NW) == 0 && BROWS % (8 * NW) == 0 && WN % 32 == 0, "tile");
   extern __shared__ __align__(16) char smem[];
 
-  TileCoord tc;
-  if (!find_tile(offsets, E, BM, NT, blockIdx.x, tc)) return;
+  const int KTall = K / kBK;
+  WorkItem w;
+  if (!find_item(offsets, E, BM, NT, P, max_split, KTall, blockIdx.x, w)) return;
+  const TileCoord tc = w.tc;
+  // K steps [kb, kb + KT) of this item (a slice of K for a split tail tile)
+  int kb = 0, KT = KTall;
+  if (w.split >= 0) {
+    const int ns = make_plan(offsets, E, BM, NT, P, max_split, KTall).s;
+    kb = w.slice * KTall / ns;
+    KT = (w.slice + 1) * KTall / ns - kb;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / NWN, wn = wave % NWN;
   const int n0 = tc.n_tile * BN;
@@ -287,9 +298,8 @@ __global__ __launch_bounds__(512) void ffn_bf16_dma_kernel(
     const int n = min(n0 + (SWIGLU && row >= BN ? row - BN : row), N - 1);
     b_off[i] = wofs + (size_t)n * K * 2 + c * 16;
   }
-  const int KT = K / kBK;
   auto dma = [&](int kt) {
-    const int kc = kt < KT ? kt : KT - 1;
+    const int kc = kb + (kt < KT ? kt : KT - 1);
     char* st = smem + (kt & 1) * STAGE;
     const size_t koff = (size_t)kc * kRowB;
 #pragma unroll
@@ -367,6 +377,27 @@ __global__ __launch_bounds__(512) void ffn_bf16_dma_kernel(
   // drain it so no DMA outlives the block's LDS allocation
   wait_vmcnt<0>();
 
+  if (!SWIGLU && w.split >= 0) {
+    // K-slice of a split tail tile: the fp32 partial tile [BM][BN], reduced later
+    const int ns = make_plan(offsets, E, BM, NT, P, max_split, KTall).s;
+    float* pt = partials + (size_t)(w.split * ns + w.slice) * BM * BN;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = wm * WM + mb * 32 + (lane & 31);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[mb * NB + nb][4 * g + i];
+          *reinterpret_cast<f32x4*>(pt + (size_t)row * BN + col) = v;
+        }
+    }
+    return;
+  }
+
   // epilogue: lane holds, for its row (lane & 31), features 8*g + 4*(lane>>5) + 0..3
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -394,9 +425,41 @@ __global__ __launch_bounds__(512) void ffn_bf16_dma_kernel(
   }
 }
 
+// Sum the K-slice partials of each split tail tile in slice order and store
+// the bf16 result (rows inside the expert's segment, columns below N).
+// One block per (split tile, 16-row group); a thread owns 16 columns.
+__global__ __launch_bounds__(256) void split_reduce_kernel(int E, const int32_t* __restrict__ offsets, int N,
+                                                           int K, int NT, int P, int max_split,
+                                                           const float* __restrict__ partials,
+                                                           uint16_t* __restrict__ C) {
+  constexpr int BM = 256, BN = 256;
+  const WorkPlan p = make_plan(offsets, E, BM, NT, P, max_split, K / kBK);
+  const int t = blockIdx.x / (BM / 16);
+  if (t >= p.r) return;
+  TileCoord tc;
+  if (!locate_tile(offsets, E, BM, NT, p.full + t, tc)) return;
+  const int row = (blockIdx.x % (BM / 16)) * 16 + (threadIdx.x >> 4);
+  const int rloc = tc.m0 + row;
+  if (rloc >= tc.seg_rows) return;
+  const int c0 = (threadIdx.x & 15) * 16;
+  uint16_t* crow = C + (size_t)(tc.seg_start + rloc) * (size_t)N + (size_t)tc.n_tile * BN;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int col = c0 + 4 * q;
+    if (tc.n_tile * BN + col >= N) break;
+    f32x4 sum = *reinterpret_cast<const f32x4*>(partials + ((size_t)(t * p.s) * BM + row) * BN + col);
+    for (int j = 1; j < p.s; ++j)
+      sum += *reinterpret_cast<const f32x4*>(partials + ((size_t)(t * p.s + j) * BM + row) * BN + col);
+    uint2 w;
+    w.x = pack_bf16x2(sum[0], sum[1]);
+    w.y = pack_bf16x2(sum[2], sum[3]);
+    *reinterpret_cast<uint2*>(crow + col) = w;
+  }
+}
+
 template <int BN, bool SWIGLU>
 hipError_t launch_dma(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A,
-                      const void* B0, const void* B1, void* C, hipStream_t s) {
+                      const void* B0, const void* B1, void* C, float* partials, int P, hipStream_t s) {
   constexpr int BM = 256;
   constexpr int BROWS = SWIGLU ? 2 * BN : BN;
   constexpr size_t kLds = 2 * (size_t)(BM + BROWS) * kRowB;
@@ -406,10 +469,16 @@ hipError_t launch_dma(int64_t R_max, int E, const int32_t* offsets, int N, int K
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
   const int NT = (N + BN - 1) / BN;
-  const int64_t blocks = ((R_max + BM - 1) / BM + E) * NT;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(512), kLds, s, E, offsets, N, K,
+  const int64_t tiles_ub = ((R_max + BM - 1) / BM + E) * NT;
+  const bool split = !SWIGLU && partials != nullptr && P > 0;
+  const int max_split = split ? kMaxSplit : 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid_blocks(tiles_ub, P, split)), dim3(512), kLds, s, E, offsets, N, K,
                      reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B0),
-                     reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C), NT);
+                     reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C), NT, P, max_split,
+                     partials);
+  if (split)
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(P * (BM / 16))), dim3(256), 0, s, E, offsets, N, K, NT,
+                       P, max_split, partials, reinterpret_cast<uint16_t*>(C));
   return hipGetLastError();
 }
 
@@ -434,15 +503,35 @@ hipError_t launch_gemm(int64_t R_max, int E, const int32_t* offsets, int N, int 
 
 }  // namespace
 
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+bool ffn_bf16_big_tiles(int64_t R_max, int E) { return R_max >= 128 * (int64_t)E; }
+
+size_t ffn_bf16_workspace_bytes(int64_t R_max, int E) {
+  // partial tiles of the down projection's split tail: at most one per compute unit
+  if (!ffn_bf16_big_tiles(R_max, E)) return 0;
+  return (size_t)compute_units() * 256 * 256 * sizeof(float);
+}
+
 hipError_t launch_gemm_bf16(int which, int64_t R_max, int d, int E, int F, const void* in,
                             const int32_t* offsets, const void* w0, const void* w1, void* out,
-                            hipStream_t s) {
+                            void* ws, hipStream_t s) {
   // 256-row DMA tiles once experts average at least 128 rows; below that the
   // 128-row tiles waste less work on the ragged last tile of each expert.
-  const bool big = R_max >= 128 * (int64_t)E;
-  if (big) {
-    if (which == 1) return launch_dma<128, true>(R_max, E, offsets, F, d, in, w0, w1, out, s);
-    return launch_dma<256, false>(R_max, E, offsets, d, F, in, w0, nullptr, out, s);
+  if (ffn_bf16_big_tiles(R_max, E)) {
+    if (which == 1) return launch_dma<128, true>(R_max, E, offsets, F, d, in, w0, w1, out, nullptr, 0, s);
+    return launch_dma<256, false>(R_max, E, offsets, d, F, in, w0, nullptr, out, reinterpret_cast<float*>(ws),
+                                  ws ? compute_units() : 0, s);
   }
   if (which == 1) return launch_gemm<128, 64, true>(R_max, E, offsets, F, d, in, w0, w1, out, s);
   return launch_gemm<128, 128, false>(R_max, E, offsets, d, F, in, w0, nullptr, out, s);
@@ -450,10 +539,10 @@ hipError_t launch_gemm_bf16(int which, int64_t R_max, int d, int E, int F, const
 
 hipError_t launch_ffn_bf16(int64_t R_max, int d, int E, int F, const void* x_perm,
                            const int32_t* offsets, const void* wg, const void* wu, const void* wd,
-                           void* h, void* out, hipStream_t s) {
-  hipError_t err = launch_gemm_bf16(1, R_max, d, E, F, x_perm, offsets, wg, wu, h, s);
+                           void* h, void* out, void* ws, hipStream_t s) {
+  hipError_t err = launch_gemm_bf16(1, R_max, d, E, F, x_perm, offsets, wg, wu, h, nullptr, s);
   if (err != hipSuccess) return err;
-  return launch_gemm_bf16(2, R_max, d, E, F, h, offsets, wd, nullptr, out, s);
+  return launch_gemm_bf16(2, R_max, d, E, F, h, offsets, wd, nullptr, out, ws, s);
 }
 
 }  // namespace moe

@@ -69,8 +69,12 @@ int check_scalars(int64_t T, int d, int E, int k, float cf, int F, int dt, bool 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 struct ForwardLayout {
-  size_t topk_idx, topk_gate, slot_row, row_slot, counts, offsets, chunks, x_perm, h, out_perm, total;
+  size_t topk_idx, topk_gate, slot_row, row_slot, counts, offsets, chunks, x_perm, h, out_perm, ffn, total;
 };
+
+size_t ffn_ws_bytes(int64_t R_max, int E, int dt) {
+  return dt == MOE_BF16 ? moe::ffn_bf16_workspace_bytes(R_max, E) : 0;
+}
 
 ForwardLayout forward_layout(int64_t T, int d, int E, int k, int64_t R_max, int F, int dt) {
   ForwardLayout L;
@@ -91,6 +95,7 @@ ForwardLayout forward_layout(int64_t T, int d, int E, int k, int64_t R_max, int 
   L.x_perm = take((size_t)R_max * d * s);
   L.h = take((size_t)R_max * F * s);
   L.out_perm = take((size_t)R_max * d * s);
+  L.ffn = take(ffn_ws_bytes(R_max, E, dt));
   L.total = o;
   return L;
 }
@@ -126,6 +131,15 @@ int moe_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, in
   if (st != MOE_OK) return st;
   const int64_t R_max = rows_max_of(T, E, k, capacity_of(T, E, k, cf));
   *bytes = forward_layout(T, d, E, k, R_max, F, dt).total;
+  return MOE_OK;
+}
+
+int moe_ffn_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+                            size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  const int st = check_scalars(T, d, E, k, cf, F, dt, true);
+  if (st != MOE_OK) return st;
+  *bytes = ffn_ws_bytes(rows_max_of(T, E, k, capacity_of(T, E, k, cf)), E, dt);
   return MOE_OK;
 }
 
@@ -178,26 +192,29 @@ int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype 
 
 int moe_grouped_ffn(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
                     const void* x_perm, const int32_t* expert_offsets, const void* w_gate,
-                    const void* w_up, const void* w_down, void* h_ws, void* out_perm,
-                    hipStream_t stream) {
+                    const void* w_up, const void* w_down, void* h_ws, void* out_perm, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
   int st = check_scalars(T, d, E, k, cf, F, dt, true);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!x_perm || !expert_offsets || !w_gate || !w_up || !w_down || !h_ws || !out_perm)
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x_perm) || !aligned16(expert_offsets) || !aligned16(w_gate) || !aligned16(w_up) ||
-      !aligned16(w_down) || !aligned16(h_ws) || !aligned16(out_perm))
+      !aligned16(w_down) || !aligned16(h_ws) || !aligned16(out_perm) || !aligned16(ws))
     return MOE_ERR_UNSUPPORTED;
   const int64_t R_max = rows_max_of(T, E, k, capacity_of(T, E, k, cf));
   const size_t s = elem_bytes(dt);
   const size_t wbytes = (size_t)E * F * d * s;
+  const size_t need = ffn_ws_bytes(R_max, E, dt);
+  if (ws != nullptr && ws_bytes < need) return MOE_ERR_WORKSPACE;
   const Range all[] = {{h_ws, (size_t)R_max * F * s}, {out_perm, (size_t)R_max * d * s},
+                       {ws, need},
                        {x_perm, (size_t)R_max * d * s}, {expert_offsets, (size_t)(E + 1) * 4},
                        {w_gate, wbytes}, {w_up, wbytes}, {w_down, wbytes}};
-  if (any_overlap(all, 2, 7)) return MOE_ERR_INVALID_ARG;
+  if (any_overlap(all, 3, 8)) return MOE_ERR_INVALID_ARG;
   hipError_t e = dt == MOE_BF16
                      ? moe::launch_ffn_bf16(R_max, d, E, F, x_perm, expert_offsets, w_gate, w_up,
-                                            w_down, h_ws, out_perm, stream)
+                                            w_down, h_ws, out_perm, need ? ws : nullptr, stream)
                      : moe::launch_ffn_f32(R_max, d, E, F, x_perm, expert_offsets, w_gate, w_up,
                                            w_down, h_ws, out_perm, stream);
   return hip_status(e);
@@ -205,22 +222,26 @@ int moe_grouped_ffn(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_
 
 static int expert_gemm(int which, int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
                        moe_dtype dt, const void* in, const int32_t* expert_offsets, const void* w0,
-                       const void* w1, void* out, hipStream_t stream) {
+                       const void* w1, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_scalars(T, d, E, k, cf, F, dt, true);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!in || !expert_offsets || !w0 || (which == 1 && !w1) || !out) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(in) || !aligned16(expert_offsets) || !aligned16(w0) || !aligned16(w1) || !aligned16(out))
+  if (!aligned16(in) || !aligned16(expert_offsets) || !aligned16(w0) || !aligned16(w1) || !aligned16(out) ||
+      !aligned16(ws))
     return MOE_ERR_UNSUPPORTED;
   const int64_t R_max = rows_max_of(T, E, k, capacity_of(T, E, k, cf));
   const size_t s = elem_bytes(dt);
   const size_t wbytes = (size_t)E * F * d * s;
+  const size_t need = which == 2 ? ffn_ws_bytes(R_max, E, dt) : 0;
+  if (which == 2 && ws != nullptr && ws_bytes < need) return MOE_ERR_WORKSPACE;
   const size_t in_cols = which == 1 ? d : F, out_cols = which == 1 ? F : d;
-  const Range all[] = {{out, (size_t)R_max * out_cols * s}, {in, (size_t)R_max * in_cols * s},
+  const Range all[] = {{out, (size_t)R_max * out_cols * s}, {ws, need}, {in, (size_t)R_max * in_cols * s},
                        {expert_offsets, (size_t)(E + 1) * 4}, {w0, wbytes}, {w1, which == 1 ? wbytes : 0}};
-  if (any_overlap(all, 1, 5)) return MOE_ERR_INVALID_ARG;
+  if (any_overlap(all, 2, 6)) return MOE_ERR_INVALID_ARG;
   hipError_t e = dt == MOE_BF16
-                     ? moe::launch_gemm_bf16(which, R_max, d, E, F, in, expert_offsets, w0, w1, out, stream)
+                     ? moe::launch_gemm_bf16(which, R_max, d, E, F, in, expert_offsets, w0, w1, out,
+                                             need ? ws : nullptr, stream)
                      : moe::launch_gemm_f32(which, R_max, d, E, F, in, expert_offsets, w0, w1, out, stream);
   return hip_status(e);
 }
@@ -228,13 +249,14 @@ static int expert_gemm(int which, int64_t T, int32_t d, int32_t E, int32_t k, fl
 int moe_expert_gate_up(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
                        const void* x_perm, const int32_t* expert_offsets, const void* w_gate,
                        const void* w_up, void* h, hipStream_t stream) {
-  return expert_gemm(1, T, d, E, k, cf, F, dt, x_perm, expert_offsets, w_gate, w_up, h, stream);
+  return expert_gemm(1, T, d, E, k, cf, F, dt, x_perm, expert_offsets, w_gate, w_up, h, nullptr, 0, stream);
 }
 
 int moe_expert_down(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
                     const void* h, const int32_t* expert_offsets, const void* w_down, void* out_perm,
-                    hipStream_t stream) {
-  return expert_gemm(2, T, d, E, k, cf, F, dt, h, expert_offsets, w_down, nullptr, out_perm, stream);
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  return expert_gemm(2, T, d, E, k, cf, F, dt, h, expert_offsets, w_down, nullptr, out_perm, ws, ws_bytes,
+                     stream);
 }
 
 int moe_unpermute_combine(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
@@ -290,6 +312,7 @@ int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
   void* x_perm = w + L.x_perm;
   void* h = w + L.h;
   void* out_perm = w + L.out_perm;
+  void* ffn_ws = w + L.ffn;
   const bool bf16 = dt == MOE_BF16;
 
   hipError_t e = moe::launch_router(bf16, T, d, E, k, x, w_router, idx, gate, nullptr, stream);
@@ -298,7 +321,7 @@ int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
                             stream);
   if (e == hipSuccess)
     e = bf16 ? moe::launch_ffn_bf16(R_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, h, out_perm,
-                                    stream)
+                                    ffn_ws_bytes(R_max, E, dt) ? ffn_ws : nullptr, stream)
              : moe::launch_ffn_f32(R_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, h, out_perm,
                                    stream);
   if (e == hipSuccess) e = moe::launch_combine(bf16, T, d, k, out_perm, srow, gate, y, stream);

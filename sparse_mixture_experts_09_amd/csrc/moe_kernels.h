@@ -19,16 +19,20 @@ hipError_t launch_permute(bool bf16, int64_t T, int d, int E, int k, int64_t cap
                           hipStream_t s);
 
 // The two grouped GEMMs (which = 1: gate/up with the SwiGLU epilogue, 2: down).
+// ws (bf16 down projection only, may be NULL): ffn_bf16_workspace_bytes() of
+// scratch for the partial tiles of its split tail.
 hipError_t launch_gemm_bf16(int which, int64_t R_max, int d, int E, int F, const void* in,
                             const int32_t* offsets, const void* w0, const void* w1, void* out,
-                            hipStream_t s);
+                            void* ws, hipStream_t s);
+size_t ffn_bf16_workspace_bytes(int64_t R_max, int E);
+int compute_units();
 hipError_t launch_gemm_f32(int which, int64_t R_max, int d, int E, int F, const void* in,
                            const int32_t* offsets, const void* w0, const void* w1, void* out,
                            hipStream_t s);
 
 hipError_t launch_ffn_bf16(int64_t R_max, int d, int E, int F, const void* x_perm,
                            const int32_t* offsets, const void* wg, const void* wu, const void* wd,
-                           void* h, void* out, hipStream_t s);
+                           void* h, void* out, void* ws, hipStream_t s);
 
 hipError_t launch_ffn_f32(int64_t R_max, int d, int E, int F, const void* x_perm,
                           const int32_t* offsets, const void* wg, const void* wu, const void* wd,

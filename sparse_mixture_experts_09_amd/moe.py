@@ -31,12 +31,14 @@ _SIGS = {
     "moe_route": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_permute": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _vp, _vp, _sz, _vp]),
+    "moe_ffn_workspace_bytes": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int,
+                                               ctypes.POINTER(_sz)]),
     "moe_grouped_ffn": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp,
-                                       _vp, _vp, _vp, _vp, _vp]),
+                                       _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_expert_gate_up": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp,
                                           _vp, _vp, _vp]),
     "moe_expert_down": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp,
-                                       _vp, _vp]),
+                                       _vp, _vp, _sz, _vp]),
     "moe_unpermute_combine": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, ctypes.c_int, _vp, _vp, _vp,
                                              _vp, _vp]),
     "moe_forward": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp,
@@ -122,6 +124,20 @@ def moe_workspace_bytes(T: int, d: int, E: int, k: int, cf: float, F: int, dtype
     return int(b.value)
 
 
+def moe_ffn_workspace_bytes(T: int, d: int, E: int, k: int, cf: float, F: int, dtype) -> int:
+    dt = MOE_BF16 if dtype in (torch.bfloat16, MOE_BF16) else MOE_F32
+    b = _sz()
+    _check("moe_ffn_workspace_bytes", lib().moe_ffn_workspace_bytes(T, d, E, k, cf, F, dt, ctypes.byref(b)))
+    return int(b.value)
+
+
+def _ffn_ws(ws, T, d, E, k, cf, F, dtype, device):
+    if ws is None:
+        n = moe_ffn_workspace_bytes(T, d, E, k, cf, F, dtype)
+        ws = torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    return ws
+
+
 def moe_route(x, w_router, k: int, topk_idx=None, topk_gate=None, logits=None, want_logits=False,
               stream=None):
     """Returns (topk_idx [T,k] int32, topk_gate [T,k] fp32, logits [T,E] fp32 or None)."""
@@ -167,8 +183,9 @@ def moe_permute(x, topk_idx, E: int, cf: float, stream=None, out=None):
 
 
 def moe_grouped_ffn(x_perm, expert_offsets, w_gate, w_up, w_down, T: int, k: int, cf: float,
-                    h=None, out_perm=None, stream=None):
-    """Returns (h [R_max,F], out_perm [R_max,d])."""
+                    h=None, out_perm=None, ws=None, stream=None):
+    """Returns (h [R_max,F], out_perm [R_max,d]). ws: FFN scratch (allocated
+    when None; pass False to run without the split tail)."""
     E, F, d = w_gate.shape
     R_max = moe_rows_max(T, E, k, cf)
     dev = x_perm.device
@@ -176,9 +193,10 @@ def moe_grouped_ffn(x_perm, expert_offsets, w_gate, w_up, w_down, T: int, k: int
         h = torch.empty((max(R_max, 1), F), dtype=x_perm.dtype, device=dev)
     if out_perm is None:
         out_perm = torch.empty((max(R_max, 1), d), dtype=x_perm.dtype, device=dev)
+    ws = None if ws is False else _ffn_ws(ws, T, d, E, k, cf, F, x_perm.dtype, dev)
     st = lib().moe_grouped_ffn(T, d, E, k, cf, F, _dt(x_perm), _ptr(x_perm), _ptr(expert_offsets),
-                               _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(out_perm),
-                               _stream(stream))
+                               _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(out_perm), _ptr(ws),
+                               ws.numel() if ws is not None else 0, _stream(stream))
     _check("moe_grouped_ffn", st)
     return h, out_perm
 
@@ -195,13 +213,16 @@ def moe_expert_gate_up(x_perm, expert_offsets, w_gate, w_up, T: int, k: int, cf:
     return h
 
 
-def moe_expert_down(h, expert_offsets, w_down, T: int, k: int, cf: float, out_perm=None, stream=None):
-    """Second grouped GEMM. Returns out_perm [R_max, d]."""
+def moe_expert_down(h, expert_offsets, w_down, T: int, k: int, cf: float, out_perm=None, ws=None,
+                    stream=None):
+    """Second grouped GEMM. Returns out_perm [R_max, d]. ws: FFN scratch
+    (allocated when None; pass False to run without the split tail)."""
     E, d, F = w_down.shape
     if out_perm is None:
         out_perm = torch.empty((max(moe_rows_max(T, E, k, cf), 1), d), dtype=h.dtype, device=h.device)
+    ws = None if ws is False else _ffn_ws(ws, T, d, E, k, cf, F, h.dtype, h.device)
     st = lib().moe_expert_down(T, d, E, k, cf, F, _dt(h), _ptr(h), _ptr(expert_offsets), _ptr(w_down),
-                               _ptr(out_perm), _stream(stream))
+                               _ptr(out_perm), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
     _check("moe_expert_down", st)
     return out_perm
 

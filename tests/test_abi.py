@@ -27,7 +27,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -121,8 +121,12 @@ def test_stage_entry_points_validate():
     a = list(args); a[7] = None
     assert L.moe_permute(*a) == INV
     # grouped ffn: bf16 F not a multiple of 64, h overlapping a weight
-    assert L.moe_grouped_ffn(64, 64, 4, 2, 1.0, 72, BF16, A[0], A[1], A[2], A[3], A[4], A[5], A[6], None) == UNS
-    assert L.moe_grouped_ffn(64, 64, 4, 2, 1.0, 128, BF16, A[0], A[1], A[2], A[3], A[4], A[2], A[6], None) == INV
+    assert L.moe_grouped_ffn(64, 64, 4, 2, 1.0, 72, BF16, A[0], A[1], A[2], A[3], A[4], A[5], A[6], None, 0, None) == UNS
+    assert L.moe_grouped_ffn(64, 64, 4, 2, 1.0, 128, BF16, A[0], A[1], A[2], A[3], A[4], A[2], A[6], None, 0, None) == INV
+    # misaligned scratch
+    assert L.moe_grouped_ffn(64, 64, 4, 2, 1.0, 128, BF16, A[0], A[1], A[2], A[3], A[4], A[5], A[6], A[7] + 8, 1 << 30, None) == UNS
+    assert L.moe_expert_down(64, 64, 4, 2, 1.0, 128, BF16, A[0], A[1], A[2], A[3], A[4] + 4, 1 << 30, None) == UNS
+    assert L.moe_ffn_workspace_bytes(64, 64, 4, 2, 1.0, 128, BF16, ctypes.byref(ctypes.c_size_t())) == OK
     # combine: y overlapping out_perm
     assert L.moe_unpermute_combine(64, 64, 4, 2, 1.0, F32, A[0], A[1], A[2], A[0], None) == INV
     assert L.moe_unpermute_combine(64, 64, 4, 2, 1.0, F32, A[0], A[1], None, A[3], None) == INV

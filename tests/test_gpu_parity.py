@@ -335,3 +335,42 @@ def test_full_size_combine(name):
     torch.cuda.synchronize()
     y_ref = orc.combine(o[:R].double().numpy(), ref["slot_row"], gate32.astype(np.float64), w.dtype)
     assert_close_rows(host(y), y_ref, w.dtype)
+
+
+# ---------------------------------------------------------------------------
+# the down projection's split tail (256-row tiles): every output row compared
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", [
+    (2048, 512, 8, 2, 1024, 0.0, "bf16", 31),    # fewer tiles than compute units: every tile split
+    (4096, 2048, 8, 2, 1024, 0.0, "bf16", 32),   # whole rounds plus a split tail
+    (3000, 1024, 6, 2, 512, 1.1, "bf16", 33),    # drops, ragged experts
+], ids=case_id)
+def test_grouped_ffn_split_tail(case):
+    w, a = mi.random_small(*case)
+    logits, idx, gates, tie = orc.route(a["x"], a["w_router"], w.k)
+    cap = orc.capacity(w.T, w.E, w.k, w.cf)
+    demand, offsets, slot_row, row_slot = orc.fill_in_token_order(idx, w.E, cap)
+    R = int(offsets[-1])
+    R_max = moe.moe_rows_max(w.T, w.E, w.k, w.cf)
+    assert R_max >= 128 * w.E   # the 256-row tile path
+    rows_tok = torch.from_numpy(row_slot.astype(np.int64)) // w.k
+    x_perm = torch.zeros((R_max, w.d), dtype=torch.bfloat16)
+    x_perm[:R] = a["x"][rows_tok]
+    g = {n: dev(a[n]) for n in ("w_gate", "w_up", "w_down")}
+    xp, off = dev(x_perm), dev(torch.from_numpy(offsets))
+    h1, o1 = moe.moe_grouped_ffn(xp, off, g["w_gate"], g["w_up"], g["w_down"], w.T, w.k, w.cf)
+    h2, o2 = moe.moe_grouped_ffn(xp, off, g["w_gate"], g["w_up"], g["w_down"], w.T, w.k, w.cf)
+    h3, o3 = moe.moe_grouped_ffn(xp, off, g["w_gate"], g["w_up"], g["w_down"], w.T, w.k, w.cf, ws=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:R], o2[:R])          # deterministic
+    hh = np.empty((R, w.F))
+    oo = np.empty((R, w.d))
+    for e in range(w.E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            hh[lo:hi], oo[lo:hi] = orc.swiglu_expert(a["x"][rows_tok[lo:hi]], a["w_gate"][e], a["w_up"][e],
+                                                     a["w_down"][e], "bf16")
+    assert_close_rows(host(h1[:R]), hh, "bf16", "h")
+    assert_close_rows(host(o1[:R]), oo, "bf16", "o (split tail)")
+    assert_close_rows(host(o3[:R]), oo, "bf16", "o (no split)")
