@@ -5,15 +5,6 @@
 // every other gate 0. "[Paper Club] Upcycling Large Language Models into
 // Mixture of Experts": the router is a plain learnable matrix multiply.
 //
-// Layout of the work: a block is 4 wavefronts; each wavefront owns TW
-// consecutive tokens. Lane l covers the 16-byte slices l, l+64, l+128, ... of
-// a token row, so every x row is read once with coalesced 16-byte loads. The
-// experts are processed in passes of 8: a lane accumulates TW x 8 partial dot
-// products (bf16 widened exactly to fp32, then fma), then one transposed
-// wave reduction leaves every (token, expert) total in some lane. The logits
-// go to LDS and the arg-top-k runs per token over one wavefront: each lane
-// holds up to four experts (E <= 256), and k rounds of a 64-lane butterfly
-// argmax on (value desc, index asc) pick the experts in slot order.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -21,27 +12,28 @@ namespace moe {
 
 namespace {
 
+// (v1, i1) beats (v2, i2): larger value, ties to the lower index.
+__device__ __forceinline__ bool beats(float v1, int i1, float v2, int i2) {
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+
+// ---------------------------------------------------------------------------
+// fp32 router: a wavefront owns TW consecutive tokens and
+// lane l covers the 16-byte slices l, l+64, ... of each token row, so x is read
+// once with coalesced loads; experts go in passes of 8, each lane accumulating
+// TW x 8 partial dot products that one transposed wave reduction completes.
+// The W_g slices come from L2/L1; TW tokens share every W_g load. bf16 data
+// goes to the matrix-core kernel below.
+// ---------------------------------------------------------------------------
+
 constexpr int kRouterWaves = 4;
 constexpr int kEPass = 8;
 
-// bf16 values widen exactly to fp32; products and sums are plain fp32 fma.
-__device__ __forceinline__ float dot16(BF16, const u32x4& xv, const u32x4& wv, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc = fmaf(bf16_lo(xv[i]), bf16_lo(wv[i]), acc);
-    acc = fmaf(bf16_hi(xv[i]), bf16_hi(wv[i]), acc);
-  }
-  return acc;
-}
 __device__ __forceinline__ float dot16(F32, const u32x4& xv, const u32x4& wv, float acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(xv[i]), __uint_as_float(wv[i]), acc);
   return acc;
-}
-
-// (v1, i1) beats (v2, i2): larger value, ties to the lower index.
-__device__ __forceinline__ bool beats(float v1, int i1, float v2, int i2) {
-  return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
 template <typename S, int TW>
@@ -168,24 +160,240 @@ hipError_t launch_router_tw(int64_t T, int d, int E, int k, const void* x, const
   return hipGetLastError();
 }
 
-template <typename S>
-hipError_t launch_router_s(int64_t T, int d, int E, int k, const void* x, const void* wr,
-                           int32_t* idx, float* gate, float* logits, hipStream_t s) {
-  // Tokens per wavefront: enough waves to fill the chip first, then reuse of
-  // each W_g load across tokens.
+// ---------------------------------------------------------------------------
+// bf16 router on the matrix cores. The logits are a [T, d] x [d, E] product
+// with E small, so the work is bound by reading x from HBM once. A block owns
+// BT = 16 * MT tokens; its NW wavefronts split d: the 128-column steps of d go
+// round-robin to the wavefronts, which issue the x loads of D steps at once
+// before computing on them. In a step, lane l of a wavefront holds row l % 16
+// of each 16-token tile and of each 16-expert tile of W_g, with the 16-byte
+// pieces at columns 32 j + 8 (l / 16) (j = 0..3), which is the operand layout
+// of v_mfma_f32_16x16x32_bf16 for the 32 columns of piece j. W_g is the first
+// operand, so lane l ends up holding experts 4 (l / 16) .. + 3 of token l % 16.
+// bf16 products are exact in fp32 and the sums are fp32, as in the plain dot
+// product. The NW partial logit tiles meet in LDS and are added in wavefront
+// order (a fixed order: the logits do not depend on timing). Arg-top-k then
+// runs per token on LPT lanes that hold EPL experts each.
+// ---------------------------------------------------------------------------
+
+constexpr int kRStep = 128;   // d columns per step
+
+template <int NT>
+struct RouterSel {   // lanes per token and experts per lane for the arg-top-k
+  static constexpr int LPT = NT <= 4 ? 16 : (NT == 8 ? 32 : 64);
+  static constexpr int EPL = 16 * NT / LPT;
+};
+
+template <int NT, int MT, int NW>
+constexpr size_t router_mfma_lds() {
+  return (size_t)NW * 16 * MT * (16 * NT + 4) * sizeof(float);
+}
+
+template <int NT, int MT, int NW, int D>
+__global__ __launch_bounds__(NW * 64) void router_mfma_kernel(int64_t T, int d, int E, int k,
+                                                              const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ wr,
+                                                              int32_t* __restrict__ topk_idx,
+                                                              float* __restrict__ topk_gate,
+                                                              float* __restrict__ logits_out) {
+  constexpr int BT = 16 * MT;
+  constexpr int EP = 16 * NT;
+  constexpr int RS = EP + 4;   // floats per LDS row of partial logits
+  constexpr int LPT = RouterSel<NT>::LPT, EPL = RouterSel<NT>::EPL;
+  extern __shared__ __align__(16) float red[];   // [NW][BT][RS]
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * BT;
+  const size_t rb = (size_t)d * 2;
+  const char* xr[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int64_t t = min<int64_t>(t0 + mt * 16 + r16, T - 1);   // rows past T: results unused
+    xr[mt] = reinterpret_cast<const char*>(x) + (size_t)t * rb;
+  }
+  const char* wrow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int e = min(nt * 16 + r16, E - 1);   // experts past E: results unused
+    wrow[nt] = reinterpret_cast<const char*>(wr) + (size_t)e * rb;
+  }
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int S = (d + kRStep - 1) / kRStep;
+  for (int s0 = wave; s0 < S; s0 += NW * D) {
+    bf16x8 a[D][MT][4];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int c = (s0 + i * NW) * kRStep + 8 * g;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = s0 + i * NW < S && c + 32 * j < d;   // d is a multiple of 8: whole pieces
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          a[i][mt][j] = __builtin_bit_cast(bf16x8, in ? ld16(xr[mt] + (size_t)(c + 32 * j) * 2) : zero);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (s0 + i * NW >= S) break;
+      const int c = (s0 + i * NW) * kRStep + 8 * g;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        bf16x8 b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          b[j] = __builtin_bit_cast(bf16x8, c + 32 * j < d ? ld16(wrow[nt] + (size_t)(c + 32 * j) * 2) : zero);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i][mt][j], acc[mt][nt], 0, 0, 0);
+      }
+    }
+  }
+
+  // partial tiles to LDS, then the sum over wavefronts in wavefront order
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<f32x4*>(&red[(wave * BT + mt * 16 + r16) * RS + nt * 16 + 4 * g]) = acc[mt][nt];
+  __syncthreads();
+  for (int q = threadIdx.x; q < BT * EP; q += NW * 64) {
+    const int row = q / EP, col = q % EP;
+    float v = red[row * RS + col];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += red[(w * BT + row) * RS + col];
+    red[row * RS + col] = v;   // only this thread touches (row, col) of any wavefront
+  }
+  __syncthreads();
+
+  // arg-top-k and softmax, one token per LPT lanes
+  constexpr int TS = 64 / LPT;
+  const int slot = lane / LPT, el = lane % LPT;
+  for (int tb = wave * TS; tb < BT; tb += NW * TS) {
+    const int tl = tb + slot;
+    const int64_t t = t0 + tl;
+    const bool live = tl < BT && t < T;
+    float v[EPL];
+    bool taken[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = el + LPT * j;
+      taken[j] = e >= E;
+      v[j] = (tl < BT && e < E) ? red[tl * RS + e] : 0.f;
+      if (logits_out != nullptr && live && e < E) logits_out[t * E + e] = v[j];
+    }
+    float sel_v[8];
+    int sel_i[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if (r >= k) break;
+      float bv = -INFINITY;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = el + LPT * j;
+        if (!taken[j] && beats(v[j], e, bv, bi)) {
+          bv = v[j];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = LPT / 2; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (beats(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      sel_v[r] = bv;
+      sel_i[r] = bi;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (el + LPT * j == bi) taken[j] = true;
+    }
+    float ssum = 0.f;
+    float ex[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if (r < k) {
+        ex[r] = expf(sel_v[r] - sel_v[0]);
+        ssum += ex[r];
+      }
+    }
+    if (live) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        if (r < k && el == r) {
+          topk_idx[t * k + r] = sel_i[r];
+          topk_gate[t * k + r] = ex[r] / ssum;
+        }
+      }
+    }
+  }
+}
+
+template <int NT, int MT, int NW, int D>
+hipError_t launch_router_mfma(int64_t T, int d, int E, int k, const void* x, const void* wr, int32_t* idx,
+                              float* gate, float* logits, hipStream_t s) {
+  constexpr size_t kLds = router_mfma_lds<NT, MT, NW>();
+  auto kern = &router_mfma_kernel<NT, MT, NW, D>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (attr != hipSuccess) return attr;
+  const int64_t blocks = (T + 16 * MT - 1) / (16 * MT);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), kLds, s, T, d, E, k,
+                     reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(wr), idx, gate,
+                     logits);
+  return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_router_nt(int64_t T, int d, int E, int k, const void* x, const void* wr, int32_t* idx,
+                            float* gate, float* logits, hipStream_t s) {
+  // 32-token blocks once they still give every compute unit a block: each
+  // block reads all of W_g, so larger blocks halve that traffic
+  constexpr int NW = NT <= 4 ? 8 : 4;
+  if (T >= 32 * (int64_t)compute_units())
+    return launch_router_mfma<NT, 2, NW, 2>(T, d, E, k, x, wr, idx, gate, logits, s);
+  return launch_router_mfma<NT, 1, NW, 4>(T, d, E, k, x, wr, idx, gate, logits, s);
+}
+
+hipError_t launch_router_f32(int64_t T, int d, int E, int k, const void* x, const void* wr, int32_t* idx,
+                             float* gate, float* logits, hipStream_t s) {
+  // tokens per wavefront: enough waves to fill the chip first, then reuse of
+  // each W_g load across tokens
   const int64_t waves_wanted = 4096;
-  if (T >= waves_wanted * 8) return launch_router_tw<S, 8>(T, d, E, k, x, wr, idx, gate, logits, s);
-  if (T >= waves_wanted * 4) return launch_router_tw<S, 4>(T, d, E, k, x, wr, idx, gate, logits, s);
-  if (T >= waves_wanted * 2) return launch_router_tw<S, 2>(T, d, E, k, x, wr, idx, gate, logits, s);
-  return launch_router_tw<S, 1>(T, d, E, k, x, wr, idx, gate, logits, s);
+  if (T >= waves_wanted * 8) return launch_router_tw<F32, 8>(T, d, E, k, x, wr, idx, gate, logits, s);
+  if (T >= waves_wanted * 4) return launch_router_tw<F32, 4>(T, d, E, k, x, wr, idx, gate, logits, s);
+  if (T >= waves_wanted * 2) return launch_router_tw<F32, 2>(T, d, E, k, x, wr, idx, gate, logits, s);
+  return launch_router_tw<F32, 1>(T, d, E, k, x, wr, idx, gate, logits, s);
+}
+
+hipError_t launch_router_bf16(int64_t T, int d, int E, int k, const void* x, const void* wr, int32_t* idx,
+                              float* gate, float* logits, hipStream_t s) {
+  if (E <= 16) return launch_router_nt<1>(T, d, E, k, x, wr, idx, gate, logits, s);
+  if (E <= 32) return launch_router_nt<2>(T, d, E, k, x, wr, idx, gate, logits, s);
+  if (E <= 64) return launch_router_nt<4>(T, d, E, k, x, wr, idx, gate, logits, s);
+  if (E <= 128) return launch_router_nt<8>(T, d, E, k, x, wr, idx, gate, logits, s);
+  return launch_router_nt<16>(T, d, E, k, x, wr, idx, gate, logits, s);
 }
 
 }  // namespace
 
 hipError_t launch_router(bool bf16, int64_t T, int d, int E, int k, const void* x, const void* wr,
                          int32_t* idx, float* gate, float* logits, hipStream_t s) {
-  if (bf16) return launch_router_s<BF16>(T, d, E, k, x, wr, idx, gate, logits, s);
-  return launch_router_s<F32>(T, d, E, k, x, wr, idx, gate, logits, s);
+  if (bf16) return launch_router_bf16(T, d, E, k, x, wr, idx, gate, logits, s);
+  return launch_router_f32(T, d, E, k, x, wr, idx, gate, logits, s);
 }
 
 }  // namespace moe

@@ -92,6 +92,34 @@ def test_route(case):
         assert np.all(host(gate) == 1.0)
 
 
+# Router-only shapes: every expert-tile width of the bf16 kernel (E up to 256),
+# one- and two-tile token blocks with a ragged last block, d down to one
+# 16-byte piece and d ending inside a 128-column step; fp32 with large E.
+ROUTE_SHAPES = [
+    (1000, 200, 256, 8, "bf16", 30),
+    (8200, 264, 200, 2, "bf16", 31),
+    (9000, 136, 100, 3, "bf16", 32),
+    (8193, 64, 40, 5, "bf16", 33),
+    (5000, 8, 2, 2, "bf16", 34),
+    (17, 1032, 16, 1, "bf16", 35),
+    (70, 72, 200, 8, "f32", 36),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_SHAPES, ids=lambda c: "T{}_d{}_E{}_k{}_{}".format(*c[:5]))
+def test_route_shapes(case):
+    T, d, E, k, dtype, seed = case
+    w = mi.Workload(f"route_T{T}_d{d}_E{E}", T=T, d=d, E=E, k=k, F=8, cf=0.0, dtype=dtype, seed=seed)
+    a = mi.generate(w, expert_weights=False)
+    logits, idx_ref, gate_ref, near = orc.route(a["x"], a["w_router"], k)
+    idx, gate, lg = moe.moe_route(dev(a["x"]), dev(a["w_router"]), k, want_logits=True)
+    torch.cuda.synchronize()
+    flips = compare_routing(host(idx), host(gate), {"topk_idx": idx_ref, "topk_gate": gate_ref, "near_tie": near})
+    assert flips <= int(near.sum())
+    l = host(lg)
+    assert np.all(np.abs(l - logits) <= 1e-5 * (1.0 + np.abs(logits)))
+
+
 @pytest.mark.parametrize("case", SMALL + NAMED_SMALL, ids=case_id)
 def test_permute(case):
     w, a = workload(case)
