@@ -45,6 +45,17 @@ Readings where the pages are silent (each is listed in the design notes):
   * a dropped slot contributes 0 and the remaining gates are not renormalised;
   * SwiGLU(x) = W_down (silu(W_gate x) * (W_up x)), silu(a) = a/(1+exp(-a)),
     no biases;
+  * Switch gating ([TALK] upcycling part): softmax over all E logits, then
+    the k chosen probabilities as gates (no renormalisation); the E/k
+    output rescale is applied to each kept gate, which is the same as
+    scaling the expert outputs since the combine is linear. The chosen set
+    is the same as for Softmax(TopK) (softmax is monotone), decided on the
+    float32 logits as above;
+  * Batch Priority Routing ([VMOE] "Priority Routing"): the pages do not
+    define the importance score; the layer uses each token's top-1 gate.
+    Buffers fill in descending score order (the score taken as float32, the
+    precision the kernels hold gates in), ties to the lower token index;
+    rows inside an expert's segment follow that fill order;
   * "storage" rounding: the layer stores h, o and y in its storage type. In
     "bf16" mode the float64 value is rounded to float32 and then to bfloat16
     (round to nearest even); in "f32" mode to float32; in "f64" mode not at
@@ -128,6 +139,40 @@ def topk_gates(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return z / z.sum(axis=1, keepdims=True)
 
 
+def switch_gates(logits: np.ndarray, idx: np.ndarray, scaled: bool) -> np.ndarray:
+    """Switch-Transformer order ([TALK], upcycling part): p = softmax over all
+    E logits first, then the gate of slot j is p[t, S_j]. The kept gates no
+    longer sum to one (the talk's 0.4 / 0.2 example). With scaled=True every
+    kept gate is multiplied by E/k: the talk's fix scales the expert (MLP)
+    output by the number of experts over top-k, and the combine is linear in
+    the gate, so scaling the gate is the same operation."""
+    l = np.asarray(logits, np.float64)
+    z = np.exp(l - l.max(axis=1, keepdims=True))
+    p = z / z.sum(axis=1, keepdims=True)
+    g = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    if scaled:
+        E, k = l.shape[1], idx.shape[1]
+        g = g * (E / k)
+    return g
+
+
+GATINGS = ("topk_softmax", "softmax_topk", "softmax_topk_scaled")
+
+
+def gates_for(logits: np.ndarray, idx: np.ndarray, gating: str) -> np.ndarray:
+    """Gate values of the chosen slots under one of the gating rules:
+    topk_softmax        Softmax(TopK(l)) ([MATH]; the layer's default)
+    softmax_topk        TopK(Softmax(l)) (Switch order, [TALK])
+    softmax_topk_scaled the same times E/k ([TALK]'s rescale)"""
+    if gating == "topk_softmax":
+        return topk_gates(logits, idx)
+    if gating == "softmax_topk":
+        return switch_gates(logits, idx, False)
+    if gating == "softmax_topk_scaled":
+        return switch_gates(logits, idx, True)
+    raise ValueError(f"unknown gating {gating!r}")
+
+
 def dense_gates(logits: np.ndarray, idx: np.ndarray, gates: np.ndarray) -> np.ndarray:
     """The full G(x) of [MATH]: gate values at the chosen experts, 0 elsewhere."""
     T, E = logits.shape
@@ -165,10 +210,11 @@ def capacity(T: int, E: int, k: int, cf: float) -> int:
     return int(min(T, math.ceil(cf * T * k / E)))
 
 
-def fill_in_token_order(idx: np.ndarray, E: int, cap: int):
-    """Each expert's buffer fills in token order; an assignment that arrives
-    when the expert already holds `cap` tokens is dropped ([VMOE] dropped once
-    the expert is full; [ROUTE] drops land towards the end of the sequence).
+def fill_in_order(idx: np.ndarray, E: int, cap: int, order):
+    """Each expert's buffer fills as the tokens arrive in `order` (a
+    permutation of 0..T-1); an assignment that arrives when the expert
+    already holds `cap` tokens is dropped ([VMOE] dropped once the expert is
+    full). A token's k slots arrive together, in slot order.
 
     Returns (demand[E], offsets[E+1], slot_row[T,k], row_slot[R]):
       demand[e]    tokens that chose e (kept or not)
@@ -177,11 +223,12 @@ def fill_in_token_order(idx: np.ndarray, E: int, cap: int):
                    "arrange them into a single matrix" per expert)
       slot_row     row of (t, j) in the permuted matrix, -1 if dropped
       row_slot     inverse map: row -> t*k + j
-    Rows inside an expert's segment are in token order."""
+    Rows inside an expert's segment are in arrival order."""
     T, k = idx.shape
     fill = np.zeros(E, dtype=np.int64)
     rank = np.empty((T, k), dtype=np.int64)
-    for t in range(T):
+    for t in order:
+        t = int(t)
         for j in range(k):
             e = int(idx[t, j])
             rank[t, j] = fill[e]
@@ -197,6 +244,26 @@ def fill_in_token_order(idx: np.ndarray, E: int, cap: int):
     row_slot[slot_row[tt, jj]] = tt * k + jj
     return (fill.astype(np.int32), offsets.astype(np.int32),
             slot_row.astype(np.int32), row_slot.astype(np.int32))
+
+
+def fill_in_token_order(idx: np.ndarray, E: int, cap: int):
+    """Buffers fill in token order ([ROUTE] drops land towards the end of the
+    sequence): fill_in_order with the identity order."""
+    return fill_in_order(idx, E, cap, range(idx.shape[0]))
+
+
+def priority_order(score) -> np.ndarray:
+    """[VMOE] Batch Priority Routing: tokens are taken by descending
+    importance score instead of position. The score is compared as float32
+    (the precision of the gates the kernels hold); equal scores keep token
+    order (a stable sort of the negated score)."""
+    s32 = np.asarray(score, np.float64).astype(np.float32).astype(np.float64)
+    return np.argsort(-s32, kind="stable")
+
+
+def fill_in_priority_order(idx: np.ndarray, E: int, cap: int, score):
+    """Batch Priority Routing: fill_in_order in descending score order."""
+    return fill_in_order(idx, E, cap, priority_order(score))
 
 
 # ---------------------------------------------------------------------------
@@ -249,16 +316,16 @@ def combine(o_rows: np.ndarray, slot_row: np.ndarray, gates: np.ndarray,
 # whole layer
 # ---------------------------------------------------------------------------
 
-def route(x, w_router, k: int):
+def route(x, w_router, k: int, gating: str = "topk_softmax"):
     """Routing step: logits, top-k indices (slot order), gates, near-tie mask."""
     logits = router_logits(x, w_router)
     idx = select_topk(logits, k)
-    gates = topk_gates(logits, idx)
+    gates = gates_for(logits, idx, gating)
     return logits, idx, gates, near_tie_tokens(logits, k)
 
 
 def forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, storage: str,
-            tokens=None, idx=None) -> dict:
+            tokens=None, idx=None, gating: str = "topk_softmax", bpr: bool = False) -> dict:
     """The MoE layer forward pass.
 
     tokens: optional subset of token indices whose outputs are computed (the
@@ -266,6 +333,9 @@ def forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, storage: str,
             since capacity depends on every earlier token).
     idx:    optional top-k indices to use instead of the router's choice
             (the gates still come from this oracle's logits at those experts).
+    gating: one of GATINGS (see gates_for).
+    bpr:    Batch Priority Routing: buffers fill in descending order of each
+            token's top-1 gate instead of token order.
     Returns a dict with logits, topk_idx, topk_gate, near_tie, demand,
     offsets, slot_row, row_slot, cap, y (for `tokens`, or all tokens), and
     o_rows/h_rows (rows actually computed, indexed by permuted row; NaN
@@ -275,9 +345,12 @@ def forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, storage: str,
     logits = router_logits(x, w_router)
     if idx is None:
         idx = select_topk(logits, k)
-    gates = topk_gates(logits, idx)
+    gates = gates_for(logits, idx, gating)
     cap = capacity(T, E, k, cf)
-    demand, offsets, slot_row, row_slot = fill_in_token_order(idx, E, cap)
+    if bpr:
+        demand, offsets, slot_row, row_slot = fill_in_priority_order(idx, E, cap, gates[:, 0])
+    else:
+        demand, offsets, slot_row, row_slot = fill_in_token_order(idx, E, cap)
     R = int(offsets[E])
     if tokens is None:
         need_rows = np.arange(R)

@@ -246,11 +246,11 @@ def check_permutation_bruteforce():
                 assert (row_slot[offsets[e]:offsets[e + 1]] // k).tolist() == q[e]
 
 
-def dense_reference_y(x, wr, wg, wu, wd, k, cf, storage):
+def dense_reference_y(x, wr, wg, wu, wd, k, cf, storage, **kw):
     """Every expert on every token (torch, library silu), times the dense G with
     dropped slots set to 0, summed over experts. Shares only the routing
     decision (indices and gates) with the oracle; no permutation at all."""
-    r = orc.forward(x, wr, wg, wu, wd, k, cf, storage)
+    r = orc.forward(x, wr, wg, wu, wd, k, cf, storage, **kw)
     T, E = r["logits"].shape
     G = np.zeros((T, E))
     for j in range(k):
@@ -275,11 +275,15 @@ def dense_reference_y(x, wr, wg, wu, wd, k, cf, storage):
 
 
 def check_dense_identity():
-    for (T, E, k, cf, storage, dt) in [(40, 5, 2, 0.0, "f64", "f32"), (40, 5, 2, 1.0, "f64", "f32"),
-                                       (33, 4, 1, 1.25, "f64", "f32"), (40, 6, 3, 0.75, "f64", "f32"),
-                                       (40, 5, 2, 1.0, "bf16", "bf16"), (40, 4, 4, 0.0, "f32", "f32")]:
+    for case in [(40, 5, 2, 0.0, "f64", "f32"), (40, 5, 2, 1.0, "f64", "f32"),
+                 (33, 4, 1, 1.25, "f64", "f32"), (40, 6, 3, 0.75, "f64", "f32"),
+                 (40, 5, 2, 1.0, "bf16", "bf16"), (40, 4, 4, 0.0, "f32", "f32"),
+                 (40, 5, 2, 0.75, "f64", "f32", "softmax_topk_scaled", True),
+                 (40, 6, 3, 1.0, "bf16", "bf16", "softmax_topk", True)]:
+        T, E, k, cf, storage, dt = case[:6]
+        kw = {} if len(case) == 6 else dict(gating=case[6], bpr=case[7])
         x, wr, wg, wu, wd = small_layer(T=T, E=E, k=k, dtype=dt)
-        r, yd = dense_reference_y(x, wr, wg, wu, wd, k, cf, storage)
+        r, yd = dense_reference_y(x, wr, wg, wu, wd, k, cf, storage, **kw)
         if storage == "f64":
             assert np.allclose(r["y"], yd, rtol=1e-12, atol=1e-14)
         else:
@@ -315,10 +319,166 @@ def check_near_tie():
     assert orc.near_tie_tokens(logits, 1).tolist() == [True, False, False, False]
 
 
+# ---------------------------------------------------------------------------
+# Switch gating (softmax over all experts, then top-k; optional E/k rescale)
+# ---------------------------------------------------------------------------
+
+def check_switch_printed_gates():
+    """The talk's Switch example: softmax first over E = 8 experts, then the two
+    kept probabilities are 0.4 and 0.2 (they no longer sum to one); the E/k = 4
+    rescale multiplies them by 4."""
+    s = read_golden("switch_softmax_then_top2.txt")
+    logits = np.array([s["logits"]])
+    E = int(s["E"][0])
+    idx = orc.select_topk(logits, 2)
+    assert idx[0].tolist() == [int(v) for v in s["expect_dense_top2_idx"]]
+    g = orc.switch_gates(logits, idx, scaled=False)
+    assert np.allclose(g[0], s["expect_dense_top2_gate"], rtol=1e-12)
+    assert g[0].sum() < 0.61
+    gs = orc.switch_gates(logits, idx, scaled=True)
+    assert np.allclose(gs[0], np.array(s["expect_dense_top2_gate"]) * E / 2, rtol=1e-12)
+    assert np.array_equal(orc.gates_for(logits, idx, "softmax_topk"), g)
+    assert np.array_equal(orc.gates_for(logits, idx, "softmax_topk_scaled"), gs)
+
+
+def check_switch_library_softmax():
+    """Library routine: every Switch gate is torch.softmax over all E at the
+    chosen expert; k = E gives the whole softmax; and each gate equals the
+    Softmax(TopK) gate times the probability mass of the chosen set."""
+    for k in (1, 2, 3, 5):
+        x, wr, *_ = small_layer(T=50, E=5, k=k)
+        logits, idx, g, _ = orc.route(x, wr, k, gating="softmax_topk")
+        p = torch.softmax(torch.from_numpy(logits), dim=1).numpy()
+        pk = np.take_along_axis(p, idx.astype(np.int64), 1)
+        assert np.allclose(g, pk, rtol=1e-14, atol=0)
+        assert np.allclose(orc.topk_gates(logits, idx) * pk.sum(1, keepdims=True), g, rtol=1e-13, atol=0)
+        _, _, gs, _ = orc.route(x, wr, k, gating="softmax_topk_scaled")
+        assert np.allclose(gs, g * 5 / k, rtol=1e-15, atol=0)
+        if k == 5:
+            assert np.allclose(g.sum(1), 1.0, rtol=1e-14)
+        else:
+            assert np.all(g.sum(1) < 1.0)
+
+
+def check_switch_scaled_zero_router_is_dense():
+    """The talk's claim for the E/k rescale: with copied experts the model
+    behaves like the dense one. With W_g = 0 every probability is 1/E, so the
+    rescaled gates are 1/k and k copies of the FFN add up to the dense FFN;
+    without the rescale the output is k/E of it. For a general router the
+    output is (E/k) * (kept probability mass) * FFN(x)."""
+    for (E, k) in [(4, 2), (8, 2), (6, 3), (5, 5)]:
+        x, wr, wg, wu, wd = small_layer(T=30, E=E, identical=True)
+        xt = torch.from_numpy(x)
+        dense = ((torch.nn.functional.silu(xt @ torch.from_numpy(wg[0]).T)
+                  * (xt @ torch.from_numpy(wu[0]).T)) @ torch.from_numpy(wd[0]).T).numpy()
+        zero = np.zeros_like(wr)
+        r = orc.forward(x, zero, wg, wu, wd, k, 0.0, "f64", gating="softmax_topk_scaled")
+        assert np.allclose(r["topk_gate"], 1.0 / k, rtol=1e-15, atol=0)
+        assert np.allclose(r["y"], dense, rtol=1e-13, atol=1e-13)
+        r = orc.forward(x, zero, wg, wu, wd, k, 0.0, "f64", gating="softmax_topk")
+        assert np.allclose(r["topk_gate"], 1.0 / E, rtol=1e-15, atol=0)
+        assert np.allclose(r["y"], dense * k / E, rtol=1e-13, atol=1e-13)
+        r = orc.forward(x, wr, wg, wu, wd, k, 0.0, "f64", gating="softmax_topk_scaled")
+        p = torch.softmax(torch.from_numpy(r["logits"]), dim=1).numpy()
+        mass = np.take_along_axis(p, r["topk_idx"].astype(np.int64), 1).sum(1, keepdims=True)
+        assert np.allclose(r["y"], dense * mass * E / k, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Batch Priority Routing (buffers fill in descending score order)
+# ---------------------------------------------------------------------------
+
+def bpr_sets(idx, E, cap, score):
+    """Brute force from the definition, per expert and without a sequential
+    fill: among the tokens that chose e, the kept ones are the cap best by
+    (float32 score descending, token ascending), in that order."""
+    T, k = idx.shape
+    s32 = np.asarray(score, np.float64).astype(np.float32).tolist()
+    out = []
+    for e in range(E):
+        dem = [t for t in range(T) if e in idx[t].tolist()]
+        dem.sort(key=lambda t: (-s32[t], t))
+        out.append(dem[:cap])
+    return out
+
+
+def check_bpr_bruteforce():
+    rng = np.random.default_rng(5)
+    for trial in range(60):
+        E = int(rng.integers(1, 7))
+        k = int(rng.integers(1, E + 1))
+        T = int(rng.integers(1, 14))
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        if trial % 2:
+            score = rng.integers(0, 3, T).astype(np.float64) * 0.25   # many exact ties
+        else:
+            score = rng.random(T)
+        for cap in range(1, T + 1):
+            demand, offsets, slot_row, row_slot = orc.fill_in_priority_order(idx, E, cap, score)
+            sets = bpr_sets(idx, E, cap, score)
+            assert np.array_equal(demand, np.bincount(idx.ravel(), minlength=E))
+            assert np.array_equal(np.diff(offsets), np.minimum(demand, cap))
+            for e in range(E):
+                assert (row_slot[offsets[e]:offsets[e + 1]] // k).tolist() == sets[e]
+            keep = slot_row >= 0
+            tt, jj = np.nonzero(keep)
+            assert np.array_equal(row_slot[slot_row[tt, jj]], tt * k + jj)
+            assert np.array_equal(np.sort(slot_row[keep]), np.arange(offsets[E]))
+
+
+def check_bpr_reduces_to_token_order():
+    """Equal scores: priority order is token order, so BPR is the vanilla fill."""
+    rng = np.random.default_rng(6)
+    for trial in range(20):
+        E, k, T = 5, 2, 37
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        for cap in (1, 5, 9, 37):
+            a = orc.fill_in_priority_order(idx, E, cap, np.full(T, 0.5))
+            b = orc.fill_in_token_order(idx, E, cap)
+            for u, v in zip(a, b):
+                assert np.array_equal(u, v)
+    # and a strictly decreasing score is token order too, an increasing one reverses it
+    idx = np.zeros((6, 1), dtype=np.int32)
+    _, _, sr, _ = orc.fill_in_priority_order(idx, 1, 2, np.arange(6, 0, -1))
+    assert sr[:, 0].tolist() == [0, 1, -1, -1, -1, -1]
+    _, _, sr, _ = orc.fill_in_priority_order(idx, 1, 2, np.arange(6))
+    assert sr[:, 0].tolist() == [-1, -1, -1, -1, 1, 0]
+
+
+def check_bpr_float32_decision():
+    """Scores are compared as float32: two scores equal in float32 tie, and
+    the tie goes to the lower token index even if the float64 values differ."""
+    idx = np.zeros((3, 1), dtype=np.int32)
+    score = np.array([0.5, 0.5 + 1e-12, 0.25])
+    _, _, sr, _ = orc.fill_in_priority_order(idx, 1, 1, score)
+    assert sr[:, 0].tolist() == [0, -1, -1]
+    _, _, sr, _ = orc.fill_in_priority_order(idx, 1, 2, np.array([0.25, 0.5 + 1e-12, 0.5]))
+    assert sr[:, 0].tolist() == [-1, 0, 1]
+
+
+def check_bpr_forward_keeps_high_gates():
+    """Forward with BPR on a capacity-bound layer: for every expert, no dropped
+    assignment has a larger top-1 gate than a kept one."""
+    x, wr, wg, wu, wd = small_layer(T=60, E=4, k=2)
+    r = orc.forward(x, wr, wg, wu, wd, 2, 0.5, "f64", bpr=True)
+    s = r["topk_gate"][:, 0].astype(np.float32)
+    assert (r["slot_row"] < 0).any()
+    for e in range(4):
+        m = r["topk_idx"] == e
+        kept = s[(m & (r["slot_row"] >= 0)).any(1)]
+        drop = s[(m & (r["slot_row"] < 0)).any(1)]
+        if len(kept) and len(drop):
+            assert kept.min() >= drop.max()
+
+
 ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
             check_zero_router_closed_form, check_gate_invariants, check_k_equals_E_is_softmax,
             check_printed_gates, check_capacity_values, check_permutation_bruteforce,
-            check_dense_identity, check_identical_experts_dense_ffn, check_near_tie]
+            check_dense_identity, check_identical_experts_dense_ffn, check_near_tie,
+            check_switch_printed_gates, check_switch_library_softmax,
+            check_switch_scaled_zero_router_is_dense, check_bpr_bruteforce,
+            check_bpr_reduces_to_token_order, check_bpr_float32_decision,
+            check_bpr_forward_keeps_high_gates]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -398,6 +558,18 @@ def _fill_reverse(idx, E, cap, _orig=orc.fill_in_token_order):
 
 
 MUTANTS["fill_from_the_end"] = ("fill_in_token_order", _fill_reverse, [check_permutation_bruteforce])
+MUTANTS["switch_renormalised"] = ("switch_gates", lambda logits, idx, scaled: orc.topk_gates(logits, idx),
+                                  [check_switch_printed_gates])
+MUTANTS["switch_scale_k_over_E"] = ("switch_gates", lambda logits, idx, scaled, _o=orc.switch_gates:
+                                    _o(logits, idx, False) * (idx.shape[1] / logits.shape[1] if scaled else 1.0),
+                                    [check_switch_scaled_zero_router_is_dense])
+MUTANTS["bpr_ascending"] = ("priority_order", lambda score: np.argsort(
+    np.asarray(score, np.float64).astype(np.float32), kind="stable"), [check_bpr_bruteforce])
+MUTANTS["bpr_ties_to_later_token"] = ("priority_order", lambda score: np.lexsort(
+    (-np.arange(len(score)), -np.asarray(score, np.float64).astype(np.float32).astype(np.float64))),
+    [check_bpr_bruteforce])
+MUTANTS["bpr_score_as_float64"] = ("priority_order", lambda score: np.argsort(
+    -np.asarray(score, np.float64), kind="stable"), [check_bpr_float32_decision])
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
