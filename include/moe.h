@@ -67,6 +67,32 @@ extern "C" {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Gate rule of the router (the chosen experts are the same under every rule;
+ * softmax is monotone):
+ *   MOE_GATING_TOPK_SOFTMAX        Softmax(TopK(l)): the softmax of the k
+ *       chosen logits, summing to 1 ("The Math Behind MoEs"; Mixtral).
+ *   MOE_GATING_SOFTMAX_TOPK        TopK(Softmax(l)): the softmax over all E
+ *       logits at the chosen experts, which no longer sum to 1 (the
+ *       Switch-Transformer order in the upcycling talk, its 0.4 / 0.2
+ *       example).
+ *   MOE_GATING_SOFTMAX_TOPK_SCALED the same, times E/k: the talk's rescale
+ *       of the expert outputs by the number of experts over top-k, applied to
+ *       the gates (the combine is linear in them). */
+typedef enum {
+  MOE_GATING_TOPK_SOFTMAX = 0,
+  MOE_GATING_SOFTMAX_TOPK = 1,
+  MOE_GATING_SOFTMAX_TOPK_SCALED = 2
+} moe_gating;
+
+/* Order in which the expert buffers fill up to capacity:
+ *   MOE_FILL_TOKEN_ORDER  by token index (drops land towards the end of the
+ *       sequence: "Take a Closer Look at the MoE LLM Routing", Introduction).
+ *   MOE_FILL_PRIORITY     Batch Priority Routing ("Scaling Vision with Sparse
+ *       Mixture of Experts", section "Priority Routing"): tokens are taken
+ *       by descending importance score; equal scores (compared as float32,
+ *       -0 equal to +0) keep token order. NaN scores are not supported. */
+typedef enum { MOE_FILL_TOKEN_ORDER = 0, MOE_FILL_PRIORITY = 1 } moe_fill_order;
+
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,   /* null pointer, bad scalar, overlapping buffers */
@@ -86,6 +112,10 @@ int moe_rows_max(int64_t T, int32_t E, int32_t k, float cf, int64_t* rows);
 /* Workspace bytes needed by moe_permute (per-chunk expert histograms). */
 int moe_permute_workspace_bytes(int64_t T, int32_t E, size_t* bytes);
 
+/* Workspace bytes needed by moe_permute_priority (the histograms, the
+ * priority order and the radix sort's key / value buffers). */
+int moe_permute_priority_workspace_bytes(int64_t T, int32_t E, size_t* bytes);
+
 /* Workspace bytes of moe_grouped_ffn / moe_expert_down: fp32 partial tiles
  * for the down projection's split tail (one 256 x 256 tile per compute unit
  * of the current device at most; 0 when the problem uses no split). Query it
@@ -93,9 +123,10 @@ int moe_permute_workspace_bytes(int64_t T, int32_t E, size_t* bytes);
 int moe_ffn_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
                             moe_dtype dt, size_t* bytes);
 
-/* Workspace bytes needed by moe_forward (routing outputs, row maps, x_perm,
- * h, out_perm, the permutation's histograms and the FFN's split-tail
- * partials, each 256-byte aligned; depends on the current device). */
+/* Workspace bytes needed by moe_forward and moe_forward_ex (routing outputs,
+ * row maps, x_perm, h, out_perm, the permutation's histograms, the priority
+ * sort's buffers and the FFN's split-tail partials, each 256-byte aligned;
+ * depends on the current device). */
 int moe_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf,
                         int32_t F, moe_dtype dt, size_t* bytes);
 
@@ -112,6 +143,16 @@ int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt,
               int32_t* topk_idx, float* topk_gate, float* logits_opt,
               hipStream_t stream);
 
+/* moe_route with a selectable gate rule (moe_gating); moe_route is
+ * gating = MOE_GATING_TOPK_SOFTMAX. Same indices for every rule; under the
+ * softmax-first rules topk_gate[t, j] = p[t, S_j] (times E/k when scaled)
+ * with p the softmax over all E logits. An unknown rule is
+ * MOE_ERR_INVALID_ARG. */
+int moe_route_gating(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, int32_t gating,
+                     const void* x, const void* w_router,
+                     int32_t* topk_idx, float* topk_gate, float* logits_opt,
+                     hipStream_t stream);
+
 /* Permutation with token-order capacity (the walkthrough's permute step).
  *   topk_idx        [T, k]      int32  in: from moe_route (values in [0, E))
  *   expert_counts   [E]         int32  out: demand, tokens that chose e
@@ -127,6 +168,21 @@ int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype 
                 int32_t* expert_counts, int32_t* expert_offsets,
                 int32_t* slot_row, int32_t* row_slot, void* x_perm,
                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_permute with Batch Priority Routing (MOE_FILL_PRIORITY): token t's
+ * importance is score[t * score_stride] (fp32, device; pass topk_gate with
+ * stride k for the top-1 gate). Each expert keeps, among the tokens that
+ * chose it, the min(demand, cap) of highest score (ties to the lower token
+ * index), and its rows in x_perm follow that order instead of token order.
+ * Counts and offsets are as for moe_permute.
+ *   score, score_stride  fp32 device array, 4-byte aligned; stride >= 1
+ *   ws, ws_bytes         scratch, >= moe_permute_priority_workspace_bytes */
+int moe_permute_priority(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+                         const void* x, const int32_t* topk_idx,
+                         const float* score, int64_t score_stride,
+                         int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* slot_row, int32_t* row_slot, void* x_perm,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Grouped SwiGLU expert FFN over the permuted rows, one launch per
  * projection for all experts (the walkthrough's grouped GEMM; Mixtral's
@@ -189,6 +245,18 @@ int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
                 const void* w_gate, const void* w_up, const void* w_down, void* y,
                 int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* slot_row_opt,
                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_forward with a gate rule (moe_gating) and a capacity fill order
+ * (moe_fill_order). With MOE_FILL_PRIORITY the importance score of a token
+ * is its top-1 gate under the chosen rule (the pages leave the score open).
+ * moe_forward is (MOE_GATING_TOPK_SOFTMAX, MOE_FILL_TOKEN_ORDER). Unknown
+ * values are MOE_ERR_INVALID_ARG. */
+int moe_forward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
+                   moe_dtype dt, int32_t gating, int32_t fill_order,
+                   const void* x, const void* w_router,
+                   const void* w_gate, const void* w_up, const void* w_down, void* y,
+                   int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* slot_row_opt,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* moe_status_string(int status);

@@ -68,8 +68,22 @@ int check_scalars(int64_t T, int d, int E, int k, float cf, int F, int dt, bool 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+bool valid_gating(int g) {
+  return g == MOE_GATING_TOPK_SOFTMAX || g == MOE_GATING_SOFTMAX_TOPK || g == MOE_GATING_SOFTMAX_TOPK_SCALED;
+}
+bool valid_fill(int f) { return f == MOE_FILL_TOKEN_ORDER || f == MOE_FILL_PRIORITY; }
+
+// Permutation workspace: chunk histograms, then (priority fill only) the
+// order and the sort's buffers, each 256-byte aligned.
+size_t permute_ws_bytes(int64_t T, int E, bool priority) {
+  size_t b = round_up((size_t)moe::permute_chunks(T) * E * 4);
+  if (priority) b += round_up((size_t)T * 4) + round_up(moe::priority_sort_bytes(T));
+  return b;
+}
+
 struct ForwardLayout {
-  size_t topk_idx, topk_gate, slot_row, row_slot, counts, offsets, chunks, x_perm, h, out_perm, ffn, total;
+  size_t topk_idx, topk_gate, slot_row, row_slot, counts, offsets, chunks, order, sort, x_perm, h, out_perm,
+      ffn, total;
 };
 
 size_t ffn_ws_bytes(int64_t R_max, int E, int dt) {
@@ -92,6 +106,8 @@ ForwardLayout forward_layout(int64_t T, int d, int E, int k, int64_t R_max, int 
   L.counts = take((size_t)E * 4);
   L.offsets = take((size_t)(E + 1) * 4);
   L.chunks = take((size_t)moe::permute_chunks(T) * E * 4);
+  L.order = take((size_t)T * 4);
+  L.sort = take(moe::priority_sort_bytes(T));
   L.x_perm = take((size_t)R_max * d * s);
   L.h = take((size_t)R_max * F * s);
   L.out_perm = take((size_t)R_max * d * s);
@@ -120,7 +136,14 @@ int moe_rows_max(int64_t T, int32_t E, int32_t k, float cf, int64_t* rows) {
 int moe_permute_workspace_bytes(int64_t T, int32_t E, size_t* bytes) {
   if (bytes == nullptr || T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
   if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
-  *bytes = round_up((size_t)moe::permute_chunks(T) * E * 4);
+  *bytes = permute_ws_bytes(T, E, false);
+  return MOE_OK;
+}
+
+int moe_permute_priority_workspace_bytes(int64_t T, int32_t E, size_t* bytes) {
+  if (bytes == nullptr || T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  *bytes = permute_ws_bytes(T, E, true);
   return MOE_OK;
 }
 
@@ -143,11 +166,12 @@ int moe_ffn_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf
   return MOE_OK;
 }
 
-int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, const void* x,
-              const void* w_router, int32_t* topk_idx, float* topk_gate, float* logits_opt,
-              hipStream_t stream) {
+int moe_route_gating(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, int32_t gating,
+                     const void* x, const void* w_router, int32_t* topk_idx, float* topk_gate,
+                     float* logits_opt, hipStream_t stream) {
   int st = check_scalars(T, d, E, k, 0.0f, -1, dt, false);
   if (st != MOE_OK) return st;
+  if (!valid_gating(gating)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !topk_idx || !topk_gate) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_idx) || !aligned16(topk_gate) ||
@@ -158,24 +182,33 @@ int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, const vo
                        {logits_opt, (size_t)T * E * 4}, {x, (size_t)T * d * s},
                        {w_router, (size_t)E * d * s}};
   if (any_overlap(all, 3, 5)) return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_router(dt == MOE_BF16, T, d, E, k, x, w_router, topk_idx, topk_gate,
+  return hip_status(moe::launch_router(dt == MOE_BF16, T, d, E, k, gating, x, w_router, topk_idx, topk_gate,
                                        logits_opt, stream));
 }
 
-int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
-                const int32_t* topk_idx, int32_t* expert_counts, int32_t* expert_offsets,
-                int32_t* slot_row, int32_t* row_slot, void* x_perm, void* ws, size_t ws_bytes,
-                hipStream_t stream) {
+int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, const void* x,
+              const void* w_router, int32_t* topk_idx, float* topk_gate, float* logits_opt,
+              hipStream_t stream) {
+  return moe_route_gating(T, d, E, k, dt, MOE_GATING_TOPK_SOFTMAX, x, w_router, topk_idx, topk_gate,
+                          logits_opt, stream);
+}
+
+static int permute_impl(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
+                        const int32_t* topk_idx, const float* score, int64_t score_stride,
+                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot_row,
+                        int32_t* row_slot, void* x_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_scalars(T, d, E, k, cf, -1, dt, false);
   if (st != MOE_OK) return st;
+  const bool priority = score != nullptr;
+  if (priority && score_stride < 1) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !topk_idx || !expert_counts || !expert_offsets || !slot_row || !row_slot || !x_perm || !ws)
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(topk_idx) || !aligned16(expert_counts) || !aligned16(expert_offsets) ||
-      !aligned16(slot_row) || !aligned16(row_slot) || !aligned16(x_perm) || !aligned16(ws))
+      !aligned16(slot_row) || !aligned16(row_slot) || !aligned16(x_perm) || !aligned16(ws) ||
+      (reinterpret_cast<uintptr_t>(score) & 3u) != 0)
     return MOE_ERR_UNSUPPORTED;
-  size_t need = 0;
-  moe_permute_workspace_bytes(T, E, &need);
+  const size_t need = permute_ws_bytes(T, E, priority);
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   const int64_t cap = capacity_of(T, E, k, cf);
   const int64_t R_max = rows_max_of(T, E, k, cap);
@@ -183,11 +216,39 @@ int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype 
   const Range all[] = {{expert_counts, (size_t)E * 4}, {expert_offsets, (size_t)(E + 1) * 4},
                        {slot_row, (size_t)T * k * 4},  {row_slot, (size_t)R_max * 4},
                        {x_perm, (size_t)R_max * d * s}, {ws, need},
-                       {x, (size_t)T * d * s},          {topk_idx, (size_t)T * k * 4}};
-  if (any_overlap(all, 6, 8)) return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_permute(dt == MOE_BF16, T, d, E, k, cap, x, topk_idx, expert_counts,
-                                        expert_offsets, slot_row, row_slot, x_perm,
-                                        reinterpret_cast<int32_t*>(ws), stream));
+                       {x, (size_t)T * d * s},          {topk_idx, (size_t)T * k * 4},
+                       {score, priority ? (size_t)((T - 1) * score_stride + 1) * 4 : 0}};
+  if (any_overlap(all, 6, 9)) return MOE_ERR_INVALID_ARG;
+  char* w = reinterpret_cast<char*>(ws);
+  int32_t* chunks = reinterpret_cast<int32_t*>(w);
+  int32_t* order = nullptr;
+  hipError_t e = hipSuccess;
+  if (priority) {
+    const size_t at = round_up((size_t)moe::permute_chunks(T) * E * 4);
+    order = reinterpret_cast<int32_t*>(w + at);
+    e = moe::launch_priority_order(T, score, score_stride, order, w + at + round_up((size_t)T * 4), stream);
+  }
+  if (e == hipSuccess)
+    e = moe::launch_permute(dt == MOE_BF16, T, d, E, k, cap, x, topk_idx, order, expert_counts,
+                            expert_offsets, slot_row, row_slot, x_perm, chunks, stream);
+  return hip_status(e);
+}
+
+int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
+                const int32_t* topk_idx, int32_t* expert_counts, int32_t* expert_offsets,
+                int32_t* slot_row, int32_t* row_slot, void* x_perm, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  return permute_impl(T, d, E, k, cf, dt, x, topk_idx, nullptr, 0, expert_counts, expert_offsets, slot_row,
+                      row_slot, x_perm, ws, ws_bytes, stream);
+}
+
+int moe_permute_priority(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
+                         const int32_t* topk_idx, const float* score, int64_t score_stride,
+                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot_row,
+                         int32_t* row_slot, void* x_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (score == nullptr) return MOE_ERR_INVALID_ARG;
+  return permute_impl(T, d, E, k, cf, dt, x, topk_idx, score, score_stride, expert_counts, expert_offsets,
+                      slot_row, row_slot, x_perm, ws, ws_bytes, stream);
 }
 
 int moe_grouped_ffn(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
@@ -276,12 +337,14 @@ int moe_unpermute_combine(int64_t T, int32_t d, int32_t E, int32_t k, float cf, 
   return hip_status(moe::launch_combine(dt == MOE_BF16, T, d, k, out_perm, slot_row, topk_gate, y, stream));
 }
 
-int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
-                const void* x, const void* w_router, const void* w_gate, const void* w_up,
-                const void* w_down, void* y, int32_t* topk_idx_opt, float* topk_gate_opt,
-                int32_t* slot_row_opt, void* ws, size_t ws_bytes, hipStream_t stream) {
+int moe_forward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+                   int32_t gating, int32_t fill_order, const void* x, const void* w_router,
+                   const void* w_gate, const void* w_up, const void* w_down, void* y, int32_t* topk_idx_opt,
+                   float* topk_gate_opt, int32_t* slot_row_opt, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
   int st = check_scalars(T, d, E, k, cf, F, dt, true);
   if (st != MOE_OK) return st;
+  if (!valid_gating(gating) || !valid_fill(fill_order)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !w_gate || !w_up || !w_down || !y || !ws) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
@@ -309,16 +372,19 @@ int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
   int32_t* counts = reinterpret_cast<int32_t*>(w + L.counts);
   int32_t* offsets = reinterpret_cast<int32_t*>(w + L.offsets);
   int32_t* chunks = reinterpret_cast<int32_t*>(w + L.chunks);
+  int32_t* order = fill_order == MOE_FILL_PRIORITY ? reinterpret_cast<int32_t*>(w + L.order) : nullptr;
   void* x_perm = w + L.x_perm;
   void* h = w + L.h;
   void* out_perm = w + L.out_perm;
   void* ffn_ws = w + L.ffn;
   const bool bf16 = dt == MOE_BF16;
 
-  hipError_t e = moe::launch_router(bf16, T, d, E, k, x, w_router, idx, gate, nullptr, stream);
+  hipError_t e = moe::launch_router(bf16, T, d, E, k, gating, x, w_router, idx, gate, nullptr, stream);
+  // Batch Priority Routing: the importance score is each token's top-1 gate
+  if (e == hipSuccess && order) e = moe::launch_priority_order(T, gate, k, order, w + L.sort, stream);
   if (e == hipSuccess)
-    e = moe::launch_permute(bf16, T, d, E, k, cap, x, idx, counts, offsets, srow, rslot, x_perm, chunks,
-                            stream);
+    e = moe::launch_permute(bf16, T, d, E, k, cap, x, idx, order, counts, offsets, srow, rslot, x_perm,
+                            chunks, stream);
   if (e == hipSuccess)
     e = bf16 ? moe::launch_ffn_bf16(R_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, h, out_perm,
                                     ffn_ws_bytes(R_max, E, dt) ? ffn_ws : nullptr, stream)
@@ -326,6 +392,15 @@ int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
                                    stream);
   if (e == hipSuccess) e = moe::launch_combine(bf16, T, d, k, out_perm, srow, gate, y, stream);
   return hip_status(e);
+}
+
+int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+                const void* x, const void* w_router, const void* w_gate, const void* w_up,
+                const void* w_down, void* y, int32_t* topk_idx_opt, float* topk_gate_opt,
+                int32_t* slot_row_opt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return moe_forward_ex(T, d, E, k, cf, F, dt, MOE_GATING_TOPK_SOFTMAX, MOE_FILL_TOKEN_ORDER, x, w_router,
+                        w_gate, w_up, w_down, y, topk_idx_opt, topk_gate_opt, slot_row_opt, ws, ws_bytes,
+                        stream);
 }
 
 const char* moe_status_string(int status) {

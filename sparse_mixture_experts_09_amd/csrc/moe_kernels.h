@@ -7,16 +7,25 @@
 
 namespace moe {
 
-hipError_t launch_router(bool bf16, int64_t T, int d, int E, int k, const void* x, const void* wr,
+// gating: 0 Softmax(TopK), 1 TopK(Softmax), 2 TopK(Softmax) * E/k
+hipError_t launch_router(bool bf16, int64_t T, int d, int E, int k, int gating, const void* x, const void* wr,
                          int32_t* idx, float* gate, float* logits, hipStream_t s);
 
 // Chunks of tokens used by the permutation's histogram (one int per expert each).
 int64_t permute_chunks(int64_t T);
 
+// order: token at each position of the arrival sequence for the capacity
+// fill (nullptr: token order)
 hipError_t launch_permute(bool bf16, int64_t T, int d, int E, int k, int64_t cap, const void* x,
-                          const int32_t* idx, int32_t* expert_counts, int32_t* expert_offsets,
-                          int32_t* slot_row, int32_t* row_slot, void* x_perm, int32_t* chunk_counts,
-                          hipStream_t s);
+                          const int32_t* idx, const int32_t* order, int32_t* expert_counts,
+                          int32_t* expert_offsets, int32_t* slot_row, int32_t* row_slot, void* x_perm,
+                          int32_t* chunk_counts, hipStream_t s);
+
+// Priority order for Batch Priority Routing: order[0..T) = tokens by score[t * stride]
+// descending (as float32), equal scores by ascending token. ws: priority_sort_bytes(T).
+size_t priority_sort_bytes(int64_t T);
+hipError_t launch_priority_order(int64_t T, const float* score, int64_t stride, int32_t* order, void* ws,
+                                 hipStream_t s);
 
 // The two grouped GEMMs (which = 1: gate/up with the SwiGLU epilogue, 2: down).
 // ws (bf16 down projection only, may be NULL): ffn_bf16_workspace_bytes() of

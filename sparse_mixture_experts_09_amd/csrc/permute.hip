@@ -1,4 +1,4 @@
-// Permutation with token-order capacity.
+// Permutation with token-order or priority-order capacity.
 //
 // "[Paper Club] Upcycling Large Language Models into Mixture of Experts", the
 // MoE-layer walkthrough: after routing, every expert's tokens are arranged
@@ -22,6 +22,17 @@
 //               slot_row (row or -1) and row_slot.
 //   4. scatter: one wavefront per token reads the x row once with 16-byte
 //               loads and writes it to each of its kept rows.
+//
+// Batch Priority Routing ("Scaling Vision with Sparse Mixture of Experts",
+// section "Priority Routing": tokens are taken by an importance score rather
+// than by position): steps 1 and 3 walk the tokens in a given order instead
+// of 0..T-1, so ranks count the assignments that arrive earlier in that
+// order. The order (score descending as float32, equal scores by ascending
+// token) comes from a stable least-significant-digit radix sort: four passes
+// of 8 bits over an order-preserving integer image of the score, each pass a
+// per-chunk digit histogram, one exclusive scan over (digit, chunk), and a
+// stable scatter whose in-chunk rank comes from ballots (lanes with the same
+// digit) and per-wavefront digit counts in LDS.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -31,15 +42,18 @@ namespace {
 
 constexpr int kChunk = 256;   // tokens per chunk = threads per block in hist / rank
 
+// order: token at each position of the arrival sequence (nullptr: identity)
 __global__ __launch_bounds__(256) void perm_hist_kernel(int64_t T, int E, int k,
                                                         const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ order,
                                                         int32_t* __restrict__ chunk_counts) {
   __shared__ int cnt[256];
   const int tid = threadIdx.x;
   cnt[tid] = 0;
   __syncthreads();
-  const int64_t t = (int64_t)blockIdx.x * kChunk + tid;
-  if (t < T) {
+  const int64_t p = (int64_t)blockIdx.x * kChunk + tid;
+  if (p < T) {
+    const int64_t t = order ? (int64_t)order[p] : p;
     for (int j = 0; j < k; ++j) {
       const int e = idx[t * k + j];
       if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
@@ -90,14 +104,16 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int nchunks, int E, int6
 
 __global__ __launch_bounds__(256) void perm_rank_kernel(int64_t T, int E, int k, int64_t cap,
                                                         const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ order,
                                                         const int32_t* __restrict__ chunk_base,
                                                         const int32_t* __restrict__ expert_offsets,
                                                         int32_t* __restrict__ slot_row,
                                                         int32_t* __restrict__ row_slot) {
   __shared__ int wave_cnt[4][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t = (int64_t)blockIdx.x * kChunk + tid;
-  const bool valid = t < T;
+  const int64_t p = (int64_t)blockIdx.x * kChunk + tid;
+  const bool valid = p < T;
+  const int64_t t = !valid ? 0 : (order ? (int64_t)order[p] : p);
   int ex[8], rk[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -160,20 +176,138 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(int64_t T, int k, siz
   }
 }
 
+// ---------------------------------------------------------------------------
+// Priority order: stable radix sort of the positions 0..T-1 by score
+// ---------------------------------------------------------------------------
+
+// Order-preserving image of a float: larger score -> smaller key, so an
+// ascending sort gives descending scores. -0 is taken as +0 (they compare
+// equal as numbers, so they must tie).
+__device__ __forceinline__ uint32_t desc_key(float f) {
+  uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
+  u ^= (u & 0x80000000u) ? 0xFFFFFFFFu : 0x80000000u;   // ascending image
+  return ~u;
+}
+
+__global__ __launch_bounds__(256) void rsort_prep_kernel(int64_t T, const float* __restrict__ score,
+                                                         int64_t stride, uint32_t* __restrict__ keys,
+                                                         int32_t* __restrict__ vals) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= T) return;
+  keys[p] = desc_key(score[p * stride]);
+  vals[p] = (int32_t)p;
+}
+
+// hist[digit * nchunks + chunk] = elements of the chunk with that digit
+__global__ __launch_bounds__(256) void rsort_hist_kernel(int64_t T, int shift, int64_t nchunks,
+                                                         const uint32_t* __restrict__ keys,
+                                                         int32_t* __restrict__ hist) {
+  __shared__ int cnt[256];
+  const int tid = threadIdx.x;
+  cnt[tid] = 0;
+  __syncthreads();
+  const int64_t p = (int64_t)blockIdx.x * 256 + tid;
+  if (p < T) atomicAdd(&cnt[(keys[p] >> shift) & 255u], 1);
+  __syncthreads();
+  hist[(int64_t)tid * nchunks + blockIdx.x] = cnt[tid];
+}
+
+// Exclusive scan of n ints in place, one block: thread i owns a contiguous
+// segment, the segment totals are scanned across the block.
+__global__ __launch_bounds__(256) void rsort_scan_kernel(int64_t n, int32_t* __restrict__ a) {
+  __shared__ int sh_wave[4];
+  const int tid = threadIdx.x;
+  const int64_t per = (n + 255) / 256;
+  const int64_t lo = min<int64_t>(n, tid * per), hi = min<int64_t>(n, lo + per);
+  int sum = 0;
+  for (int64_t i = lo; i < hi; ++i) sum += a[i];
+  const int incl = block_inclusive_scan(sum, sh_wave);
+  int run = incl - sum;
+  for (int64_t i = lo; i < hi; ++i) {
+    const int v = a[i];
+    a[i] = run;
+    run += v;
+  }
+}
+
+__global__ __launch_bounds__(256) void rsort_scatter_kernel(int64_t T, int shift, int64_t nchunks,
+                                                            const uint32_t* __restrict__ keys_in,
+                                                            const int32_t* __restrict__ vals_in,
+                                                            const int32_t* __restrict__ base,
+                                                            uint32_t* __restrict__ keys_out,
+                                                            int32_t* __restrict__ vals_out) {
+  __shared__ int wave_cnt[4][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 4 * 256; i += 256) (&wave_cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int64_t p = (int64_t)blockIdx.x * 256 + tid;
+  const bool valid = p < T;
+  const uint32_t key = valid ? keys_in[p] : 0u;
+  const int dg = (int)((key >> shift) & 255u);
+  // lanes of this wavefront holding the same digit
+  uint64_t same = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const uint64_t m = __ballot((dg >> b) & 1);
+    same &= ((dg >> b) & 1) ? m : ~m;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int r = __popcll(same & below);
+  // the last lane of each digit group publishes the group's size
+  if (valid && (same >> lane) == 1ull) wave_cnt[wave][dg] = __popcll(same);
+  __syncthreads();
+  if (!valid) return;
+  int pos = base[(int64_t)dg * nchunks + blockIdx.x] + r;
+  for (int w = 0; w < wave; ++w) pos += wave_cnt[w][dg];
+  keys_out[pos] = key;
+  vals_out[pos] = vals_in[p];
+}
+
 }  // namespace
 
 int64_t permute_chunks(int64_t T) { return (T + kChunk - 1) / kChunk; }
 
-hipError_t launch_permute(bool bf16, int64_t T, int d, int E, int k, int64_t cap, const void* x,
-                          const int32_t* idx, int32_t* expert_counts, int32_t* expert_offsets,
-                          int32_t* slot_row, int32_t* row_slot, void* x_perm, int32_t* chunk_counts,
-                          hipStream_t s) {
+size_t priority_sort_bytes(int64_t T) {
+  // keys and values, twice (ping-pong), plus the (digit, chunk) histogram
   const int64_t nchunks = permute_chunks(T);
-  hipLaunchKernelGGL(perm_hist_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, E, k, idx,
+  return (size_t)T * 16 + (size_t)nchunks * 256 * 4;
+}
+
+hipError_t launch_priority_order(int64_t T, const float* score, int64_t stride, int32_t* order, void* ws,
+                                 hipStream_t s) {
+  const int64_t nchunks = permute_chunks(T);
+  char* w = reinterpret_cast<char*>(ws);
+  uint32_t* ka = reinterpret_cast<uint32_t*>(w);
+  uint32_t* kb = ka + T;
+  int32_t* vb = reinterpret_cast<int32_t*>(kb + T);
+  int32_t* hist = vb + T;
+  // the values start in `order`; four passes end there again
+  hipLaunchKernelGGL(rsort_prep_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, score, stride, ka, order);
+  for (int pass = 0; pass < 4; ++pass) {
+    const bool even = (pass & 1) == 0;
+    const uint32_t* kin = even ? ka : kb;
+    uint32_t* kout = even ? kb : ka;
+    const int32_t* vin = even ? order : vb;
+    int32_t* vout = even ? vb : order;
+    hipLaunchKernelGGL(rsort_hist_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, 8 * pass, nchunks, kin,
+                       hist);
+    hipLaunchKernelGGL(rsort_scan_kernel, dim3(1), dim3(256), 0, s, nchunks * 256, hist);
+    hipLaunchKernelGGL(rsort_scatter_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, 8 * pass, nchunks, kin,
+                       vin, hist, kout, vout);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(bool bf16, int64_t T, int d, int E, int k, int64_t cap, const void* x,
+                          const int32_t* idx, const int32_t* order, int32_t* expert_counts,
+                          int32_t* expert_offsets, int32_t* slot_row, int32_t* row_slot, void* x_perm,
+                          int32_t* chunk_counts, hipStream_t s) {
+  const int64_t nchunks = permute_chunks(T);
+  hipLaunchKernelGGL(perm_hist_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, E, k, idx, order,
                      chunk_counts);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, s, (int)nchunks, E, cap, chunk_counts,
                      expert_counts, expert_offsets);
-  hipLaunchKernelGGL(perm_rank_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, E, k, cap, idx,
+  hipLaunchKernelGGL(perm_rank_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, E, k, cap, idx, order,
                      chunk_counts, expert_offsets, slot_row, row_slot);
   const size_t row_bytes = (size_t)d * (bf16 ? 2 : 4);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, T, k,

@@ -3,7 +3,13 @@
 // "How do Mixture of Expert Models Work?", section "The Math Behind MoEs":
 // G(x) = Softmax(TopK(x.W_g)), the softmax of only the k largest logits with
 // every other gate 0. "[Paper Club] Upcycling Large Language Models into
-// Mixture of Experts": the router is a plain learnable matrix multiply.
+// Mixture of Experts": the router is a plain learnable matrix multiply; its
+// upcycling part also gives the Switch-Transformer order (softmax over all E
+// experts first, then the top k, whose probabilities no longer sum to one)
+// and the E/k rescale of the expert outputs, applied here to the kept gates.
+//
+// gating: 0 = Softmax(TopK(l)); 1 = TopK(Softmax(l)); 2 = the same times E/k.
+// The chosen experts are the same in every mode (softmax is monotone).
 //
 #include "moe_common.h"
 #include "moe_kernels.h"
@@ -15,6 +21,17 @@ namespace {
 // (v1, i1) beats (v2, i2): larger value, ties to the lower index.
 __device__ __forceinline__ bool beats(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// Softmax denominator over all E logits of one token held by a group of L
+// lanes (lane bits below L), each lane adding exp(v - vmax) over its own
+// experts (part). The group's first lane's total is broadcast, so every gate
+// of the token uses one value.
+template <int L>
+__device__ __forceinline__ float group_sum(float part, int lane) {
+#pragma unroll
+  for (int o = L / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+  return __shfl(part, lane & ~(L - 1));
 }
 
 
@@ -37,7 +54,7 @@ __device__ __forceinline__ float dot16(F32, const u32x4& xv, const u32x4& wv, fl
 }
 
 template <typename S, int TW>
-__global__ __launch_bounds__(256) void router_kernel(int64_t T, int d, int E, int k,
+__global__ __launch_bounds__(256) void router_kernel(int64_t T, int d, int E, int k, int gating,
                                                      const typename S::elem* __restrict__ x,
                                                      const typename S::elem* __restrict__ wr,
                                                      int32_t* __restrict__ topk_idx,
@@ -129,7 +146,7 @@ __global__ __launch_bounds__(256) void router_kernel(int64_t T, int d, int E, in
       for (int q = 0; q < 4; ++q)
         if (lane + 64 * q == bi) taken[q] = true;
     }
-    // softmax over the k chosen logits, largest first
+    // softmax over the k chosen logits (largest first), or over all E
     float s = 0.f;
     float ex[8];
 #pragma unroll
@@ -139,22 +156,31 @@ __global__ __launch_bounds__(256) void router_kernel(int64_t T, int d, int E, in
         s += ex[j];
       }
     }
+    float scale = 1.f;
+    if (gating != 0) {
+      float part = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (lane + 64 * q < E) part += expf(v[q] - sel_v[0]);
+      s = group_sum<64>(part, lane);
+      if (gating == 2) scale = (float)E / (float)k;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < k && lane == j) {
         topk_idx[t * k + j] = sel_i[j];
-        topk_gate[t * k + j] = ex[j] / s;
+        topk_gate[t * k + j] = ex[j] / s * scale;
       }
     }
   }
 }
 
 template <typename S, int TW>
-hipError_t launch_router_tw(int64_t T, int d, int E, int k, const void* x, const void* wr,
+hipError_t launch_router_tw(int64_t T, int d, int E, int k, int gating, const void* x, const void* wr,
                             int32_t* idx, float* gate, float* logits, hipStream_t s) {
   const int64_t per_block = (int64_t)kRouterWaves * TW;
   const int64_t blocks = (T + per_block - 1) / per_block;
-  hipLaunchKernelGGL((router_kernel<S, TW>), dim3((unsigned)blocks), dim3(256), 0, s, T, d, E, k,
+  hipLaunchKernelGGL((router_kernel<S, TW>), dim3((unsigned)blocks), dim3(256), 0, s, T, d, E, k, gating,
                      reinterpret_cast<const typename S::elem*>(x),
                      reinterpret_cast<const typename S::elem*>(wr), idx, gate, logits);
   return hipGetLastError();
@@ -190,7 +216,7 @@ constexpr size_t router_mfma_lds() {
 }
 
 template <int NT, int MT, int NW, int D>
-__global__ __launch_bounds__(NW * 64) void router_mfma_kernel(int64_t T, int d, int E, int k,
+__global__ __launch_bounds__(NW * 64) void router_mfma_kernel(int64_t T, int d, int E, int k, int gating,
                                                               const uint16_t* __restrict__ x,
                                                               const uint16_t* __restrict__ wr,
                                                               int32_t* __restrict__ topk_idx,
@@ -330,12 +356,21 @@ __global__ __launch_bounds__(NW * 64) void router_mfma_kernel(int64_t T, int d, 
         ssum += ex[r];
       }
     }
+    float scale = 1.f;
+    if (gating != 0) {
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (el + LPT * j < E) part += expf(v[j] - sel_v[0]);
+      ssum = group_sum<LPT>(part, lane);
+      if (gating == 2) scale = (float)E / (float)k;
+    }
     if (live) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         if (r < k && el == r) {
           topk_idx[t * k + r] = sel_i[r];
-          topk_gate[t * k + r] = ex[r] / ssum;
+          topk_gate[t * k + r] = ex[r] / ssum * scale;
         }
       }
     }
@@ -343,57 +378,57 @@ __global__ __launch_bounds__(NW * 64) void router_mfma_kernel(int64_t T, int d, 
 }
 
 template <int NT, int MT, int NW, int D>
-hipError_t launch_router_mfma(int64_t T, int d, int E, int k, const void* x, const void* wr, int32_t* idx,
-                              float* gate, float* logits, hipStream_t s) {
+hipError_t launch_router_mfma(int64_t T, int d, int E, int k, int gating, const void* x, const void* wr,
+                              int32_t* idx, float* gate, float* logits, hipStream_t s) {
   constexpr size_t kLds = router_mfma_lds<NT, MT, NW>();
   auto kern = &router_mfma_kernel<NT, MT, NW, D>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
   const int64_t blocks = (T + 16 * MT - 1) / (16 * MT);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), kLds, s, T, d, E, k,
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), kLds, s, T, d, E, k, gating,
                      reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(wr), idx, gate,
                      logits);
   return hipGetLastError();
 }
 
 template <int NT>
-hipError_t launch_router_nt(int64_t T, int d, int E, int k, const void* x, const void* wr, int32_t* idx,
-                            float* gate, float* logits, hipStream_t s) {
+hipError_t launch_router_nt(int64_t T, int d, int E, int k, int gating, const void* x, const void* wr,
+                            int32_t* idx, float* gate, float* logits, hipStream_t s) {
   // 32-token blocks once they still give every compute unit a block: each
   // block reads all of W_g, so larger blocks halve that traffic
   constexpr int NW = NT <= 4 ? 8 : 4;
   if (T >= 32 * (int64_t)compute_units())
-    return launch_router_mfma<NT, 2, NW, 2>(T, d, E, k, x, wr, idx, gate, logits, s);
-  return launch_router_mfma<NT, 1, NW, 4>(T, d, E, k, x, wr, idx, gate, logits, s);
+    return launch_router_mfma<NT, 2, NW, 2>(T, d, E, k, gating, x, wr, idx, gate, logits, s);
+  return launch_router_mfma<NT, 1, NW, 4>(T, d, E, k, gating, x, wr, idx, gate, logits, s);
 }
 
-hipError_t launch_router_f32(int64_t T, int d, int E, int k, const void* x, const void* wr, int32_t* idx,
+hipError_t launch_router_f32(int64_t T, int d, int E, int k, int g, const void* x, const void* wr, int32_t* idx,
                              float* gate, float* logits, hipStream_t s) {
   // tokens per wavefront: enough waves to fill the chip first, then reuse of
   // each W_g load across tokens
   const int64_t waves_wanted = 4096;
-  if (T >= waves_wanted * 8) return launch_router_tw<F32, 8>(T, d, E, k, x, wr, idx, gate, logits, s);
-  if (T >= waves_wanted * 4) return launch_router_tw<F32, 4>(T, d, E, k, x, wr, idx, gate, logits, s);
-  if (T >= waves_wanted * 2) return launch_router_tw<F32, 2>(T, d, E, k, x, wr, idx, gate, logits, s);
-  return launch_router_tw<F32, 1>(T, d, E, k, x, wr, idx, gate, logits, s);
+  if (T >= waves_wanted * 8) return launch_router_tw<F32, 8>(T, d, E, k, g, x, wr, idx, gate, logits, s);
+  if (T >= waves_wanted * 4) return launch_router_tw<F32, 4>(T, d, E, k, g, x, wr, idx, gate, logits, s);
+  if (T >= waves_wanted * 2) return launch_router_tw<F32, 2>(T, d, E, k, g, x, wr, idx, gate, logits, s);
+  return launch_router_tw<F32, 1>(T, d, E, k, g, x, wr, idx, gate, logits, s);
 }
 
-hipError_t launch_router_bf16(int64_t T, int d, int E, int k, const void* x, const void* wr, int32_t* idx,
-                              float* gate, float* logits, hipStream_t s) {
-  if (E <= 16) return launch_router_nt<1>(T, d, E, k, x, wr, idx, gate, logits, s);
-  if (E <= 32) return launch_router_nt<2>(T, d, E, k, x, wr, idx, gate, logits, s);
-  if (E <= 64) return launch_router_nt<4>(T, d, E, k, x, wr, idx, gate, logits, s);
-  if (E <= 128) return launch_router_nt<8>(T, d, E, k, x, wr, idx, gate, logits, s);
-  return launch_router_nt<16>(T, d, E, k, x, wr, idx, gate, logits, s);
+hipError_t launch_router_bf16(int64_t T, int d, int E, int k, int g, const void* x, const void* wr,
+                              int32_t* idx, float* gate, float* logits, hipStream_t s) {
+  if (E <= 16) return launch_router_nt<1>(T, d, E, k, g, x, wr, idx, gate, logits, s);
+  if (E <= 32) return launch_router_nt<2>(T, d, E, k, g, x, wr, idx, gate, logits, s);
+  if (E <= 64) return launch_router_nt<4>(T, d, E, k, g, x, wr, idx, gate, logits, s);
+  if (E <= 128) return launch_router_nt<8>(T, d, E, k, g, x, wr, idx, gate, logits, s);
+  return launch_router_nt<16>(T, d, E, k, g, x, wr, idx, gate, logits, s);
 }
 
 }  // namespace
 
-hipError_t launch_router(bool bf16, int64_t T, int d, int E, int k, const void* x, const void* wr,
+hipError_t launch_router(bool bf16, int64_t T, int d, int E, int k, int gating, const void* x, const void* wr,
                          int32_t* idx, float* gate, float* logits, hipStream_t s) {
-  if (bf16) return launch_router_bf16(T, d, E, k, x, wr, idx, gate, logits, s);
-  return launch_router_f32(T, d, E, k, x, wr, idx, gate, logits, s);
+  if (bf16) return launch_router_bf16(T, d, E, k, gating, x, wr, idx, gate, logits, s);
+  return launch_router_f32(T, d, E, k, gating, x, wr, idx, gate, logits, s);
 }
 
 }  // namespace moe

@@ -17,6 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
+GATINGS = {"topk_softmax": 0, "softmax_topk": 1, "softmax_topk_scaled": 2}
+FILL_ORDERS = {"token": 0, "priority": 1}
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 
 _lib = None
@@ -29,6 +31,13 @@ _SIGS = {
     "moe_workspace_bytes": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int,
                                            ctypes.POINTER(_sz)]),
     "moe_route": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_route_gating": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _vp,
+                                        _vp]),
+    "moe_permute_priority_workspace_bytes": (ctypes.c_int, [_i64, _i32, ctypes.POINTER(_sz)]),
+    "moe_permute_priority": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, ctypes.c_int, _vp, _vp, _vp, _i64,
+                                            _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_forward_ex": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _i32, _i32, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_permute": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _vp, _vp, _sz, _vp]),
     "moe_ffn_workspace_bytes": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int,
@@ -117,6 +126,13 @@ def moe_permute_workspace_bytes(T: int, E: int) -> int:
     return int(b.value)
 
 
+def moe_permute_priority_workspace_bytes(T: int, E: int) -> int:
+    b = _sz()
+    _check("moe_permute_priority_workspace_bytes",
+           lib().moe_permute_priority_workspace_bytes(T, E, ctypes.byref(b)))
+    return int(b.value)
+
+
 def moe_workspace_bytes(T: int, d: int, E: int, k: int, cf: float, F: int, dtype) -> int:
     dt = MOE_BF16 if dtype in (torch.bfloat16, MOE_BF16) else MOE_F32
     b = _sz()
@@ -139,8 +155,10 @@ def _ffn_ws(ws, T, d, E, k, cf, F, dtype, device):
 
 
 def moe_route(x, w_router, k: int, topk_idx=None, topk_gate=None, logits=None, want_logits=False,
-              stream=None):
-    """Returns (topk_idx [T,k] int32, topk_gate [T,k] fp32, logits [T,E] fp32 or None)."""
+              stream=None, gating: str = "topk_softmax"):
+    """Returns (topk_idx [T,k] int32, topk_gate [T,k] fp32, logits [T,E] fp32 or None).
+    gating: "topk_softmax" (moe_route), "softmax_topk" or "softmax_topk_scaled"
+    (moe_route_gating)."""
     T, d = x.shape
     E = w_router.shape[0]
     dev = x.device
@@ -150,14 +168,22 @@ def moe_route(x, w_router, k: int, topk_idx=None, topk_gate=None, logits=None, w
         topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
     if logits is None and want_logits:
         logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-    st = lib().moe_route(T, d, E, k, _dt(x), _ptr(x), _ptr(w_router), _ptr(topk_idx), _ptr(topk_gate),
-                         _ptr(logits), _stream(stream))
-    _check("moe_route", st)
+    if gating == "topk_softmax":
+        st = lib().moe_route(T, d, E, k, _dt(x), _ptr(x), _ptr(w_router), _ptr(topk_idx), _ptr(topk_gate),
+                             _ptr(logits), _stream(stream))
+        _check("moe_route", st)
+    else:
+        st = lib().moe_route_gating(T, d, E, k, _dt(x), GATINGS[gating], _ptr(x), _ptr(w_router),
+                                    _ptr(topk_idx), _ptr(topk_gate), _ptr(logits), _stream(stream))
+        _check("moe_route_gating", st)
     return topk_idx, topk_gate, logits
 
 
-def moe_permute(x, topk_idx, E: int, cf: float, stream=None, out=None):
-    """Returns dict(expert_counts, expert_offsets, slot_row, row_slot, x_perm)."""
+def moe_permute(x, topk_idx, E: int, cf: float, stream=None, out=None, score=None, score_stride: int = 1):
+    """Returns dict(expert_counts, expert_offsets, slot_row, row_slot, x_perm).
+    score: fp32 device tensor of importance scores (token t's score at
+    flat index t * score_stride) for Batch Priority Routing (moe_permute_priority);
+    None fills in token order (moe_permute)."""
     T, d = x.shape
     k = topk_idx.shape[1]
     dev = x.device
@@ -173,11 +199,20 @@ def moe_permute(x, topk_idx, E: int, cf: float, stream=None, out=None):
     slot_row = get("slot_row", (T, k), torch.int32)
     row_slot = get("row_slot", max(R_max, 1), torch.int32)
     x_perm = get("x_perm", (max(R_max, 1), d), x.dtype)
-    ws = get("ws", max(moe_permute_workspace_bytes(T, E), 16), torch.uint8)
-    st = lib().moe_permute(T, d, E, k, cf, _dt(x), _ptr(x), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
-                           _ptr(slot_row), _ptr(row_slot), _ptr(x_perm), _ptr(ws), ws.numel(),
-                           _stream(stream))
-    _check("moe_permute", st)
+    if score is None:
+        ws = get("ws", max(moe_permute_workspace_bytes(T, E), 16), torch.uint8)
+        st = lib().moe_permute(T, d, E, k, cf, _dt(x), _ptr(x), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                               _ptr(slot_row), _ptr(row_slot), _ptr(x_perm), _ptr(ws), ws.numel(),
+                               _stream(stream))
+        _check("moe_permute", st)
+    else:
+        if score.dtype != torch.float32:
+            raise ValueError("score must be float32")
+        ws = get("ws", max(moe_permute_priority_workspace_bytes(T, E), 16), torch.uint8)
+        st = lib().moe_permute_priority(T, d, E, k, cf, _dt(x), _ptr(x), _ptr(topk_idx), _ptr(score),
+                                        score_stride, _ptr(counts), _ptr(offsets), _ptr(slot_row),
+                                        _ptr(row_slot), _ptr(x_perm), _ptr(ws), ws.numel(), _stream(stream))
+        _check("moe_permute_priority", st)
     return dict(expert_counts=counts, expert_offsets=offsets, slot_row=slot_row, row_slot=row_slot,
                 x_perm=x_perm)
 
@@ -239,9 +274,11 @@ def moe_unpermute_combine(out_perm, slot_row, topk_gate, E: int, cf: float, y=No
 
 
 def moe_forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, y=None, topk_idx=None,
-                topk_gate=None, slot_row=None, ws=None, stream=None):
+                topk_gate=None, slot_row=None, ws=None, stream=None, gating: str = "topk_softmax",
+                fill_order: str = "token"):
     """The whole layer. Returns y [T, d] (topk_idx / topk_gate / slot_row are
-    filled when given)."""
+    filled when given). The defaults call moe_forward; another gating or
+    fill_order ("priority" = Batch Priority Routing) calls moe_forward_ex."""
     T, d = x.shape
     E, F, _ = w_gate.shape
     if y is None:
@@ -249,8 +286,15 @@ def moe_forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, y=None, to
     if ws is None:
         ws = torch.empty(max(moe_workspace_bytes(T, d, E, k, cf, F, x.dtype), 16), dtype=torch.uint8,
                          device=x.device)
-    st = lib().moe_forward(T, d, E, k, cf, F, _dt(x), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
-                           _ptr(w_down), _ptr(y), _ptr(topk_idx), _ptr(topk_gate), _ptr(slot_row),
-                           _ptr(ws), ws.numel(), _stream(stream))
-    _check("moe_forward", st)
+    if gating == "topk_softmax" and fill_order == "token":
+        st = lib().moe_forward(T, d, E, k, cf, F, _dt(x), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
+                               _ptr(w_down), _ptr(y), _ptr(topk_idx), _ptr(topk_gate), _ptr(slot_row),
+                               _ptr(ws), ws.numel(), _stream(stream))
+        _check("moe_forward", st)
+    else:
+        st = lib().moe_forward_ex(T, d, E, k, cf, F, _dt(x), GATINGS[gating], FILL_ORDERS[fill_order], _ptr(x),
+                                  _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y),
+                                  _ptr(topk_idx), _ptr(topk_gate), _ptr(slot_row), _ptr(ws), ws.numel(),
+                                  _stream(stream))
+        _check("moe_forward_ex", st)
     return y

@@ -27,7 +27,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 17
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -135,3 +135,42 @@ def test_stage_entry_points_validate():
     assert L.moe_workspace_bytes(64, 64, 4, 5, 1.0, 128, F32, ctypes.byref(b)) == INV
     assert L.moe_workspace_bytes(64, 64, 4, 2, 1.0, 128, F32, None) == INV
     assert L.moe_permute_workspace_bytes(64, 300, ctypes.byref(b)) == UNS
+
+
+def test_gating_and_priority_entry_points_validate():
+    L = moe.lib()
+    # unknown gate rule; valid rules reach the overlap check
+    assert L.moe_route_gating(8, 64, 4, 2, F32, 3, A[0], A[1], A[2], A[3], None, None) == INV
+    assert L.moe_route_gating(8, 64, 4, 2, F32, -1, A[0], A[1], A[2], A[3], None, None) == INV
+    for g in (0, 1, 2):
+        assert L.moe_route_gating(8, 64, 4, 2, F32, g, A[0], A[1], A[0], A[3], None, None) == INV
+        assert L.moe_route_gating(0, 64, 4, 2, F32, g, None, None, None, None, None, None) == OK
+    # priority permute: null or misaligned score, bad stride, small workspace, score overlapping an output
+    args = [64, 64, 4, 2, 1.0, F32, A[0], A[1], A[8], 2, A[2], A[3], A[4], A[5], A[6], A[7], 1 << 30, None]
+    a = list(args); a[8] = None
+    assert L.moe_permute_priority(*a) == INV
+    a = list(args); a[8] = A[8] + 2
+    assert L.moe_permute_priority(*a) == UNS
+    a = list(args); a[9] = 0
+    assert L.moe_permute_priority(*a) == INV
+    need = ctypes.c_size_t()
+    assert L.moe_permute_priority_workspace_bytes(64, 4, ctypes.byref(need)) == OK
+    plain = ctypes.c_size_t()
+    assert L.moe_permute_workspace_bytes(64, 4, ctypes.byref(plain)) == OK
+    assert need.value >= plain.value + 64 * 4 + 64 * 16
+    a = list(args); a[16] = need.value - 1
+    assert L.moe_permute_priority(*a) == WS
+    a = list(args); a[8] = A[4] + 16
+    assert L.moe_permute_priority(*a) == INV
+    a = list(args); a[0] = 0
+    assert L.moe_permute_priority(*a) == OK
+    # forward_ex: unknown gate rule or fill order
+    fx = [64, 64, 4, 1, 1.25, 128, F32, 0, 0, A[0], A[1], A[2], A[3], A[4], A[5], None, None, None, A[6], 1 << 40, None]
+    a = list(fx); a[7] = 5
+    assert L.moe_forward_ex(*a) == INV
+    a = list(fx); a[8] = 2
+    assert L.moe_forward_ex(*a) == INV
+    a = list(fx); a[14] = A[0]          # y overlapping x
+    assert L.moe_forward_ex(*a) == INV
+    a = list(fx); a[0] = 0
+    assert L.moe_forward_ex(*a) == OK
