@@ -2,6 +2,8 @@
 """MoE layer forward throughput on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload mixtral_bf16]
+                    [--gating topk_softmax|softmax_topk|softmax_topk_scaled]
+                    [--fill token|priority]
 
 One step is one moe_forward call (router, permutation, both grouped GEMMs,
 combine) over one batch of T tokens already resident in HBM. The headline
@@ -12,6 +14,9 @@ moe_unpermute_combine) with HIP events between the launches on the launch
 stream, and a 512 MiB buffer written before each step so the HBM-bound stages
 do not read from cache; it gives each stage's duration and the roofline
 figures. The CPU oracle is timed on a bounded sample of the same workload.
+--gating / --fill select a gate rule and a capacity fill order (Batch
+Priority Routing); the step is then moe_forward_ex, and the permute stage
+includes the priority sort.
 Prints one JSON line on stdout (progress goes to stderr).
 """
 import argparse
@@ -52,7 +57,7 @@ def load_traffic(workload):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, a, target_s):
+def cpu_baseline(w, a, target_s, gating="topk_softmax", bpr=False):
     """The oracle, as it is, on the first S tokens of the workload."""
     from threadpoolctl import threadpool_info
 
@@ -60,7 +65,8 @@ def cpu_baseline(w, a, target_s):
 
     def run(S):
         t = time.perf_counter()
-        orc.forward(a["x"][:S], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], w.k, w.cf, w.dtype)
+        orc.forward(a["x"][:S], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], w.k, w.cf, w.dtype,
+                    gating=gating, bpr=bpr)
         return time.perf_counter() - t
 
     # grow the sample (x4) until it takes about target_s or covers the whole batch;
@@ -89,6 +95,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--gating", default="topk_softmax", choices=["topk_softmax", "softmax_topk", "softmax_topk_scaled"])
+    ap.add_argument("--fill", default="token", choices=["token", "priority"])
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run K device-to-device copies of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -131,8 +139,12 @@ def main():
     y = torch.empty_like(g["x"])
     ws = torch.empty(moe.moe_workspace_bytes(T, d, E, k, cf, F, g["x"].dtype), dtype=torch.uint8, device="cuda")
 
+    gating, fill = args.gating, args.fill
+    bpr = fill == "priority"
+
     def forward():
-        moe.moe_forward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], k, cf, y=y, ws=ws)
+        moe.moe_forward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], k, cf, y=y, ws=ws,
+                        gating=gating, fill_order=fill)
 
     for _ in range(W):
         forward()
@@ -158,7 +170,8 @@ def main():
             "slot_row": torch.empty((T, k), dtype=torch.int32, device="cuda"),
             "row_slot": torch.empty(R_max, dtype=torch.int32, device="cuda"),
             "x_perm": torch.empty((R_max, d), dtype=g["x"].dtype, device="cuda"),
-            "ws": torch.empty(max(moe.moe_permute_workspace_bytes(T, E), 16), dtype=torch.uint8, device="cuda")}
+            "ws": torch.empty(max(moe.moe_permute_priority_workspace_bytes(T, E) if bpr else
+                                  moe.moe_permute_workspace_bytes(T, E), 16), dtype=torch.uint8, device="cuda")}
     h = torch.empty((R_max, F), dtype=g["x"].dtype, device="cuda")
     o = torch.empty((R_max, d), dtype=g["x"].dtype, device="cuda")
     y2 = torch.empty_like(g["x"])
@@ -170,9 +183,9 @@ def main():
             flush.fill_(it & 0xFF)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         ev[0].record(stream)
-        moe.moe_route(g["x"], g["w_router"], k, topk_idx=idx, topk_gate=gate, stream=stream)
+        moe.moe_route(g["x"], g["w_router"], k, topk_idx=idx, topk_gate=gate, stream=stream, gating=gating)
         ev[1].record(stream)
-        moe.moe_permute(g["x"], idx, E, cf, out=perm, stream=stream)
+        moe.moe_permute(g["x"], idx, E, cf, out=perm, stream=stream, score=gate if bpr else None, score_stride=k)
         ev[2].record(stream)
         moe.moe_expert_gate_up(perm["x_perm"], perm["expert_offsets"], g["w_gate"], g["w_up"], T, k, cf, h=h,
                                stream=stream)
@@ -225,14 +238,14 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        cpu = cpu_baseline(w, a, args.cpu_seconds)
+        cpu = cpu_baseline(w, a, args.cpu_seconds, gating, bpr)
 
     out = {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "T": T, "d": d, "E": E, "k": k, "F": F, "cf": cf, "kept_rows": R,
-                   "parallelism": "none (1 GPU)"},
+                   "gating": gating, "fill": fill, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ffn_mfma_frac": ffn_frac,

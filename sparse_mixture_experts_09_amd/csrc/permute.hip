@@ -28,7 +28,9 @@
 // than by position): steps 1 and 3 walk the tokens in a given order instead
 // of 0..T-1, so ranks count the assignments that arrive earlier in that
 // order. The order (score descending as float32, equal scores by ascending
-// token) comes from a stable least-significant-digit radix sort: four passes
+// token) comes, for T <= 16384, from counting for every token the tokens
+// with a smaller 64-bit (score image, token) key, and beyond that from a
+// stable least-significant-digit radix sort: four passes
 // of 8 bits over an order-preserving integer image of the score, each pass a
 // per-chunk digit histogram, one exclusive scan over (digit, chunk), and a
 // stable scatter whose in-chunk rank comes from ballots (lanes with the same
@@ -212,22 +214,80 @@ __global__ __launch_bounds__(256) void rsort_hist_kernel(int64_t T, int shift, i
   hist[(int64_t)tid * nchunks + blockIdx.x] = cnt[tid];
 }
 
-// Exclusive scan of n ints in place, one block: thread i owns a contiguous
-// segment, the segment totals are scanned across the block.
-__global__ __launch_bounds__(256) void rsort_scan_kernel(int64_t n, int32_t* __restrict__ a) {
-  __shared__ int sh_wave[4];
-  const int tid = threadIdx.x;
-  const int64_t per = (n + 255) / 256;
-  const int64_t lo = min<int64_t>(n, tid * per), hi = min<int64_t>(n, lo + per);
-  int sum = 0;
-  for (int64_t i = lo; i < hi; ++i) sum += a[i];
-  const int incl = block_inclusive_scan(sum, sh_wave);
-  int run = incl - sum;
-  for (int64_t i = lo; i < hi; ++i) {
-    const int v = a[i];
-    a[i] = run;
-    run += v;
+// Exclusive scan of n ints in place, one block of 1024 threads walking the
+// array in coalesced tiles of 1024 with a running carry.
+__global__ __launch_bounds__(1024) void rsort_scan_kernel(int64_t n, int32_t* __restrict__ a) {
+  __shared__ int sh[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry = 0;
+  for (int64_t base = 0; base < n; base += 1024) {
+    const int64_t i = base + tid;
+    const int v = i < n ? a[i] : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
+    }
+    if (lane == 63) sh[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int t = sh[w];
+      before += w < wave ? t : 0;
+      total += t;
+    }
+    if (i < n) a[i] = carry + before + incl - v;
+    carry += total;
+    __syncthreads();   // sh is rewritten by the next tile
   }
+}
+
+// Small problems (T <= 16384): the position of token t in the order is the
+// number of tokens whose 64-bit key (score image << 32 | token) is below
+// t's; keys are distinct, so the positions are a permutation. Block (b, sp)
+// counts, for the 256 tokens of tile b, the keys of split sp of the token
+// range (staged through LDS); the per-split counts are added in split order
+// by the scatter kernel, so no atomics and no zeroing are needed.
+constexpr int kSmallSort = 16384;
+constexpr int kCountTile = 1024;
+
+__device__ __forceinline__ uint64_t full_key(const float* score, int64_t stride, int64_t t) {
+  return ((uint64_t)desc_key(score[t * stride]) << 32) | (uint32_t)t;
+}
+
+__global__ __launch_bounds__(256) void rank_count_kernel(int64_t T, int splits, const float* __restrict__ score,
+                                                         int64_t stride, int32_t* __restrict__ partial) {
+  __shared__ uint64_t tile[kCountTile];
+  const int tid = threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * 256 + tid;
+  const uint64_t mine = t < T ? full_key(score, stride, t) : 0ull;
+  const int sp = blockIdx.y;
+  const int64_t lo = T * sp / splits, hi = T * (sp + 1) / splits;
+  int cnt = 0;
+  for (int64_t base = lo; base < hi; base += kCountTile) {
+    const int n = (int)min<int64_t>(kCountTile, hi - base);
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) tile[i] = full_key(score, stride, base + i);
+    __syncthreads();
+    for (int i = 0; i < n; ++i) cnt += tile[i] < mine ? 1 : 0;
+  }
+  if (t < T) partial[(int64_t)sp * T + t] = cnt;
+}
+
+__global__ __launch_bounds__(256) void rank_scatter_kernel(int64_t T, int splits, const int32_t* __restrict__ partial,
+                                                           int32_t* __restrict__ order) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int pos = 0;
+  for (int sp = 0; sp < splits; ++sp) pos += partial[(int64_t)sp * T + t];
+  order[pos] = (int32_t)t;
+}
+
+int small_sort_splits(int64_t T) {
+  const int64_t s = T / 512;
+  return s < 1 ? 1 : (s > 32 ? 32 : (int)s);
 }
 
 __global__ __launch_bounds__(256) void rsort_scatter_kernel(int64_t T, int shift, int64_t nchunks,
@@ -268,13 +328,24 @@ __global__ __launch_bounds__(256) void rsort_scatter_kernel(int64_t T, int shift
 int64_t permute_chunks(int64_t T) { return (T + kChunk - 1) / kChunk; }
 
 size_t priority_sort_bytes(int64_t T) {
-  // keys and values, twice (ping-pong), plus the (digit, chunk) histogram
+  // small T: per-split partial positions; otherwise keys and values, twice
+  // (ping-pong), plus the (digit, chunk) histogram
+  if (T <= kSmallSort) return (size_t)small_sort_splits(T) * T * 4;
   const int64_t nchunks = permute_chunks(T);
   return (size_t)T * 16 + (size_t)nchunks * 256 * 4;
 }
 
 hipError_t launch_priority_order(int64_t T, const float* score, int64_t stride, int32_t* order, void* ws,
                                  hipStream_t s) {
+  if (T <= kSmallSort) {
+    const int splits = small_sort_splits(T);
+    int32_t* partial = reinterpret_cast<int32_t*>(ws);
+    const unsigned tiles = (unsigned)((T + 255) / 256);
+    hipLaunchKernelGGL(rank_count_kernel, dim3(tiles, (unsigned)splits), dim3(256), 0, s, T, splits, score, stride,
+                       partial);
+    hipLaunchKernelGGL(rank_scatter_kernel, dim3(tiles), dim3(256), 0, s, T, splits, partial, order);
+    return hipGetLastError();
+  }
   const int64_t nchunks = permute_chunks(T);
   char* w = reinterpret_cast<char*>(ws);
   uint32_t* ka = reinterpret_cast<uint32_t*>(w);
@@ -291,7 +362,7 @@ hipError_t launch_priority_order(int64_t T, const float* score, int64_t stride, 
     int32_t* vout = even ? vb : order;
     hipLaunchKernelGGL(rsort_hist_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, 8 * pass, nchunks, kin,
                        hist);
-    hipLaunchKernelGGL(rsort_scan_kernel, dim3(1), dim3(256), 0, s, nchunks * 256, hist);
+    hipLaunchKernelGGL(rsort_scan_kernel, dim3(1), dim3(1024), 0, s, nchunks * 256, hist);
     hipLaunchKernelGGL(rsort_scatter_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, 8 * pass, nchunks, kin,
                        vin, hist, kout, vout);
   }

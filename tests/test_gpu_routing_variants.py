@@ -135,10 +135,13 @@ def test_permute_priority(case, stride_k):
     (5000, 64, 8, 0.3, 51),
     (257, 3, 2, 0.5, 52),
     (1, 4, 2, 1.0, 53),
+    (16384, 8, 2, 0.5, 54),      # largest single-workgroup sort
+    (16385, 8, 2, 0.5, 55),      # smallest radix sort
 ])
 def test_permute_priority_ties_and_sizes(T, E, k, cf, seed):
     """Many exact ties (a handful of score values, with -0 and +0 equal), the
-    top bit of every radix digit used (negative scores), several sizes."""
+    top bit of every radix digit used (negative scores), several sizes on both
+    sides of the switch from the one-workgroup sort to the radix sort."""
     w = mi.Workload("bpr", T=T, d=64, E=E, k=k, F=8, cf=cf, dtype="f32", seed=seed)
     a = mi.generate(w, expert_weights=False)
     rng = np.random.default_rng(seed)
