@@ -56,6 +56,14 @@ Readings where the pages are silent (each is listed in the design notes):
     Buffers fill in descending score order (the score taken as float32, the
     precision the kernels hold gates in), ties to the lower token index;
     rows inside an expert's segment follow that fill order;
+  * expert choice ([TALK] "the selection is reversed": each expert takes a
+    fixed number of tokens, so a token gets from zero to all experts): the
+    token-expert score is the dense gate Softmax(x.W_g) of [MATH]; expert e
+    takes the C = capacity(T, E, k, cf) tokens with the largest score[t, e]
+    (k read as the average number of experts per token), compared as
+    float32, ties to the lower token index; its rows list them in ascending
+    token order; the gate of (t, e) is score[t, e] (not renormalised) and
+    y[t] sums over the experts that chose t, in ascending expert order;
   * "storage" rounding: the layer stores h, o and y in its storage type. In
     "bf16" mode the float64 value is rounded to float32 and then to bfloat16
     (round to nearest even); in "f32" mode to float32; in "f64" mode not at
@@ -310,6 +318,81 @@ def combine(o_rows: np.ndarray, slot_row: np.ndarray, gates: np.ndarray,
         m = r >= 0
         y[m] += gates[tokens[m], j][:, None] * o_rows[r[m]]
     return store(y, storage)
+
+
+# ---------------------------------------------------------------------------
+# expert choice  [TALK] the experts select the tokens; [MATH] dense gating
+# ---------------------------------------------------------------------------
+
+def softmax_scores(logits: np.ndarray) -> np.ndarray:
+    """[MATH] dense gating G(x) = Softmax(x.W_g): per token, the softmax over
+    all E logits (the largest logit subtracted first)."""
+    l = np.asarray(logits, np.float64)
+    z = np.exp(l - l.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def expert_choice_select(scores: np.ndarray, C: int):
+    """Each expert takes the C tokens with the largest score in its column,
+    compared as float32, equal scores to the lower token index ([TALK]: each
+    expert selects a fixed number of tokens). Returns
+      tokens [E, C]  the chosen tokens of each expert, ascending
+      slot   [T, E]  row of (t, e) in the expert-major matrix (e*C + position
+                     in tokens[e]), -1 if e did not choose t."""
+    T, E = scores.shape
+    s32 = np.asarray(scores, np.float64).astype(np.float32).astype(np.float64)
+    tokens = np.empty((E, C), dtype=np.int32)
+    slot = np.full((T, E), -1, dtype=np.int32)
+    for e in range(E):
+        best = np.argsort(-s32[:, e], kind="stable")[:C]
+        chosen = np.sort(best)
+        tokens[e] = chosen
+        slot[chosen, e] = e * C + np.arange(C)
+    return tokens, slot
+
+
+def expert_choice_boundary_ties(scores: np.ndarray, C: int, gap: float = 2e-6) -> np.ndarray:
+    """Experts whose C-th and (C+1)-th largest float32 scores are closer than
+    `gap` (an ulp of difference in the kernel's float32 score could change
+    the chosen set there)."""
+    T, E = scores.shape
+    if C >= T:
+        return np.zeros(E, dtype=bool)
+    s32 = np.sort(np.asarray(scores, np.float64).astype(np.float32).astype(np.float64), axis=0)[::-1]
+    return (s32[C - 1] - s32[C]) < gap
+
+
+def expert_choice_forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, storage: str,
+                          tokens=None) -> dict:
+    """The layer with expert-choice routing. C = capacity(T, E, k, cf) tokens
+    per expert (cf == 0: C = T, every expert takes every token).
+    y[t] = store(sum over experts e that chose t, ascending, of
+                 score[t, e] * FFN_e(x_t)); a token no expert chose gets 0.
+    `tokens` restricts y to those tokens (every expert still runs its rows)."""
+    T = x.shape[0]
+    E = w_router.shape[0]
+    logits = router_logits(x, w_router)
+    S = softmax_scores(logits)
+    C = capacity(T, E, k, cf)
+    tok, slot = expert_choice_select(S, C)
+    d = x.shape[1]
+    F = w_gate.shape[1]
+    o_rows = np.empty((E * C, d))
+    h_rows = np.empty((E * C, F))
+    for e in range(E):
+        h, o = swiglu_expert(as_f64(x[tok[e]]), w_gate[e], w_up[e], w_down[e], storage)
+        o_rows[e * C:(e + 1) * C] = o
+        h_rows[e * C:(e + 1) * C] = h
+    if tokens is None:
+        tokens = np.arange(T)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    y = np.zeros((len(tokens), d))
+    for e in range(E):
+        r = slot[tokens, e]
+        m = r >= 0
+        y[m] += S[tokens[m], e][:, None] * o_rows[r[m]]
+    return dict(logits=logits, scores=S, cap=C, tokens=tok, slot=slot, y=store(y, storage),
+                o_rows=o_rows, h_rows=h_rows, boundary_tie=expert_choice_boundary_ties(S, C))
 
 
 # ---------------------------------------------------------------------------

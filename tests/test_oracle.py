@@ -471,6 +471,88 @@ def check_bpr_forward_keeps_high_gates():
             assert kept.min() >= drop.max()
 
 
+# ---------------------------------------------------------------------------
+# expert choice (each expert takes its C best tokens by softmax score)
+# ---------------------------------------------------------------------------
+
+def check_ec_bruteforce():
+    rng = np.random.default_rng(8)
+    for trial in range(60):
+        E = int(rng.integers(1, 6))
+        T = int(rng.integers(1, 12))
+        if trial % 2:
+            logits = rng.integers(-1, 2, (T, E)).astype(np.float64)   # many exact ties
+        else:
+            logits = rng.standard_normal((T, E))
+        S = orc.softmax_scores(logits)
+        assert np.allclose(S, torch.softmax(torch.from_numpy(logits), dim=1).numpy(), rtol=1e-14, atol=0)
+        s32 = S.astype(np.float32).tolist()
+        for C in range(1, T + 1):
+            tok, slot = orc.expert_choice_select(S, C)
+            assert tok.shape == (E, C)
+            for e in range(E):
+                want = sorted(sorted(range(T), key=lambda t: (-s32[t][e], t))[:C])
+                assert tok[e].tolist() == want
+                for i, t in enumerate(want):
+                    assert slot[t, e] == e * C + i
+            assert (slot >= 0).sum() == E * C
+            assert np.array_equal(np.sort(slot[slot >= 0]), np.arange(E * C))
+
+
+def check_ec_selects_by_score_not_logit():
+    """Token A has logits (5, 5), token B (1, -5). Expert 0 with C = 1 takes B:
+    its score 1/(1+e^-6) = 0.9975 beats A's 0.5, although A's logit is larger;
+    expert 1 takes A (0.5 against B's 0.0025)."""
+    logits = np.array([[5.0, 5.0], [1.0, -5.0]])
+    S = orc.softmax_scores(logits)
+    assert abs(S[1, 0] - 1.0 / (1.0 + math.exp(-6.0))) < 1e-15 and S[0, 0] == 0.5
+    tok, slot = orc.expert_choice_select(S, 1)
+    assert tok[:, 0].tolist() == [1, 0]
+    assert slot.tolist() == [[-1, 1], [0, -1]]
+
+
+def check_ec_full_capacity_is_dense_gating():
+    """C = T (cf = 0): every expert takes every token, so the layer is the dense
+    softmax-gated mixture of [MATH]: y = sum_e Softmax(x.W_g)_e FFN_e(x),
+    evaluated densely with torch (library softmax and silu)."""
+    for (E, k) in [(4, 2), (3, 1), (5, 5)]:
+        x, wr, wg, wu, wd = small_layer(T=25, E=E)
+        r = orc.expert_choice_forward(x, wr, wg, wu, wd, k, 0.0, "f64")
+        assert r["cap"] == 25
+        xt = torch.from_numpy(x)
+        G = torch.softmax(xt @ torch.from_numpy(wr).T, dim=1)
+        y = torch.zeros_like(xt)
+        for e in range(E):
+            h = torch.nn.functional.silu(xt @ torch.from_numpy(wg[e]).T) * (xt @ torch.from_numpy(wu[e]).T)
+            y += G[:, e:e + 1] * (h @ torch.from_numpy(wd[e]).T)
+        assert np.allclose(r["y"], y.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def check_ec_zero_router():
+    """W_g = 0: every score is 1/E, so every expert takes tokens 0..C-1; with
+    copied experts those tokens get exactly the dense FFN (E gates of 1/E) and
+    the others 0."""
+    T, E, k, cf = 30, 4, 2, 0.5
+    x, _, wg, wu, wd = small_layer(T=T, E=E, identical=True)
+    wr = np.zeros((E, x.shape[1]))
+    r = orc.expert_choice_forward(x, wr, wg, wu, wd, k, cf, "f64")
+    C = r["cap"]
+    assert C == math.ceil(cf * T * k / E) == 8
+    assert np.array_equal(r["tokens"], np.tile(np.arange(C), (E, 1)))
+    xt = torch.from_numpy(x)
+    dense = ((torch.nn.functional.silu(xt @ torch.from_numpy(wg[0]).T) * (xt @ torch.from_numpy(wu[0]).T))
+             @ torch.from_numpy(wd[0]).T).numpy()
+    assert np.allclose(r["y"][:C], dense[:C], rtol=1e-13, atol=1e-13)
+    assert np.all(r["y"][C:] == 0.0)
+
+
+def check_ec_float32_decision():
+    """Scores equal in float32 tie (lower token wins) even if float64 differs."""
+    S = np.array([[0.5, 0.5], [0.5 + 1e-12, 0.5 - 1e-12], [0.25, 0.75]])
+    tok, _ = orc.expert_choice_select(S, 1)
+    assert tok[:, 0].tolist() == [0, 2]
+
+
 ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
             check_zero_router_closed_form, check_gate_invariants, check_k_equals_E_is_softmax,
             check_printed_gates, check_capacity_values, check_permutation_bruteforce,
@@ -478,7 +560,8 @@ ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
             check_switch_printed_gates, check_switch_library_softmax,
             check_switch_scaled_zero_router_is_dense, check_bpr_bruteforce,
             check_bpr_reduces_to_token_order, check_bpr_float32_decision,
-            check_bpr_forward_keeps_high_gates]
+            check_bpr_forward_keeps_high_gates, check_ec_bruteforce, check_ec_selects_by_score_not_logit,
+            check_ec_full_capacity_is_dense_gating, check_ec_zero_router, check_ec_float32_decision]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -568,8 +651,37 @@ MUTANTS["bpr_ascending"] = ("priority_order", lambda score: np.argsort(
 MUTANTS["bpr_ties_to_later_token"] = ("priority_order", lambda score: np.lexsort(
     (-np.arange(len(score)), -np.asarray(score, np.float64).astype(np.float32).astype(np.float64))),
     [check_bpr_bruteforce])
+MUTANTS["ec_selects_by_logit"] = ("softmax_scores", lambda logits: np.asarray(logits, np.float64),
+                                  [check_ec_selects_by_score_not_logit])
+MUTANTS["ec_ties_to_later_token"] = ("expert_choice_select", lambda S, C, _o=orc.expert_choice_select:
+                                     _ec_reversed(S, C, _o), [check_ec_zero_router])
+MUTANTS["ec_rows_in_score_order"] = ("expert_choice_select", lambda S, C: _ec_score_order(S, C),
+                                     [check_ec_bruteforce])
 MUTANTS["bpr_score_as_float64"] = ("priority_order", lambda score: np.argsort(
     -np.asarray(score, np.float64), kind="stable"), [check_bpr_float32_decision])
+
+
+def _ec_reversed(S, C, orig):
+    """Ties to the later token: select on the reversed token order."""
+    T = S.shape[0]
+    tok, _ = orig(S[::-1].copy(), C)
+    tok = np.sort(T - 1 - tok, axis=1)
+    slot = np.full(S.shape, -1, dtype=np.int32)
+    for e in range(S.shape[1]):
+        slot[tok[e], e] = e * C + np.arange(C)
+    return tok.astype(np.int32), slot
+
+
+def _ec_score_order(S, C):
+    """Rows in descending score order instead of token order."""
+    s32 = np.asarray(S, np.float64).astype(np.float32).astype(np.float64)
+    T, E = S.shape
+    tok = np.empty((E, C), dtype=np.int32)
+    slot = np.full((T, E), -1, dtype=np.int32)
+    for e in range(E):
+        tok[e] = np.argsort(-s32[:, e], kind="stable")[:C]
+        slot[tok[e], e] = e * C + np.arange(C)
+    return tok, slot
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
