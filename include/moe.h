@@ -258,6 +258,73 @@ int moe_forward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t
                    int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* slot_row_opt,
                    void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Expert-choice routing ("[Paper Club] Upcycling Large Language Models into
+ * Mixture of Experts": the selection is reversed, each expert takes a fixed
+ * number of tokens, so a token gets from zero to all E experts).
+ *   score[t, e] = Softmax(x_t . W_g^T)[e], the dense gate of "The Math Behind
+ *                 MoEs" (fp32; the softmax over all E logits of token t).
+ *   C = moe_capacity(T, E, k, cf) tokens per expert, k read as the average
+ *                 number of experts per token (cf == 0: C = T, every expert
+ *                 takes every token, i.e. dense softmax gating).
+ *   Expert e takes the C tokens with the largest score[:, e], compared as
+ *   float32, equal scores to the lower token index. Its rows e*C .. e*C+C-1
+ *   list them in ascending token order.
+ *   y[t] = store(sum over the experts e that chose t, ascending, of
+ *                score[t, e] * FFN_e(x_t)), fp32 from +0; y = 0 for a token
+ *   no expert chose. Gates are not renormalised.
+ * Limit: E * C < 2^31 (MOE_ERR_UNSUPPORTED beyond).
+ * ------------------------------------------------------------------------- */
+
+/* Scratch of moe_route_expert_choice (one key row of T per expert). */
+int moe_route_expert_choice_workspace_bytes(int64_t T, int32_t E, size_t* bytes);
+
+/* Router scores and the per-expert selection.
+ *   scores          [T, E]     fp32   out: the dense gate
+ *   expert_tokens   [E * C]    int32  out: token of each row (expert-major,
+ *                                     ascending token inside an expert)
+ *   slot            [T, E]     int32  out: row of (t, e), -1 if e did not take t
+ *   expert_offsets  [E + 1]    int32  out: e * C (for the grouped FFN)
+ *   ws, ws_bytes                      scratch, >= moe_route_expert_choice_workspace_bytes */
+int moe_route_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+                            const void* x, const void* w_router, float* scores,
+                            int32_t* expert_tokens, int32_t* slot, int32_t* expert_offsets,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Row gather: x_perm[r, :] = x[row_token[r], :] for r < R (a token index
+ * outside [0, T) gives a zero row). x [T, d], x_perm [R, d], both dt. */
+int moe_gather_rows(int64_t T, int32_t d, int64_t R, moe_dtype dt, const void* x,
+                    const int32_t* row_token, void* x_perm, hipStream_t stream);
+
+/* The grouped SwiGLU FFN of moe_grouped_ffn over any expert-major row set of
+ * at most R_max rows (expert e owns rows expert_offsets[e] ..
+ * expert_offsets[e+1]-1, offsets non-decreasing, expert_offsets[E] <= R_max).
+ * Same arithmetic, layouts and split-tail workspace rules; the workspace
+ * size comes from moe_ffn_rows_workspace_bytes. */
+int moe_ffn_rows_workspace_bytes(int64_t R_max, int32_t d, int32_t E, int32_t F, moe_dtype dt,
+                                 size_t* bytes);
+int moe_grouped_ffn_rows(int64_t R_max, int32_t d, int32_t E, int32_t F, moe_dtype dt,
+                         const void* x_perm, const int32_t* expert_offsets,
+                         const void* w_gate, const void* w_up, const void* w_down,
+                         void* h_ws, void* out_perm, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Combine with a variable fan-in (y as above; rows outside [0, E*C) count as
+ * not chosen).
+ *   out_perm [E*C, d] dt, slot [T, E] int32, scores [T, E] fp32, y [T, d] dt out */
+int moe_combine_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+                              const void* out_perm, const int32_t* slot, const float* scores,
+                              void* y, hipStream_t stream);
+
+/* The whole expert-choice layer on one stream, intermediates in ws.
+ *   scores_opt [T, E] fp32 and slot_opt [T, E] int32 are optional outputs. */
+int moe_forward_expert_choice_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf,
+                                              int32_t F, moe_dtype dt, size_t* bytes);
+int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
+                              moe_dtype dt, const void* x, const void* w_router,
+                              const void* w_gate, const void* w_up, const void* w_down, void* y,
+                              float* scores_opt, int32_t* slot_opt,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* moe_status_string(int status);
 

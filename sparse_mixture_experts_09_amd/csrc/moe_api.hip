@@ -403,6 +403,193 @@ int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
                         stream);
 }
 
+// ---------------------------------------------------------------------------
+// expert choice
+// ---------------------------------------------------------------------------
+
+// Rows of the expert-choice layer: C tokens per expert (C = capacity).
+static int ec_rows(int64_t T, int E, int k, float cf, int64_t* C, int64_t* R) {
+  *C = capacity_of(T, E, k, cf);
+  *R = (int64_t)E * *C;
+  return *R < ((int64_t)1 << 31) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
+int moe_route_expert_choice_workspace_bytes(int64_t T, int32_t E, size_t* bytes) {
+  if (bytes == nullptr || T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  *bytes = round_up(moe::ec_select_bytes(T, E));
+  return MOE_OK;
+}
+
+int moe_route_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
+                            const void* w_router, float* scores, int32_t* expert_tokens, int32_t* slot,
+                            int32_t* expert_offsets, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_scalars(T, d, E, k, cf, -1, dt, false);
+  if (st != MOE_OK) return st;
+  int64_t C, R;
+  if ((st = ec_rows(T, E, k, cf, &C, &R)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !scores || !expert_tokens || !slot || !expert_offsets || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(scores) || !aligned16(expert_tokens) ||
+      !aligned16(slot) || !aligned16(expert_offsets) || !aligned16(ws))
+    return MOE_ERR_UNSUPPORTED;
+  const size_t need = round_up(moe::ec_select_bytes(T, E));
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const size_t s = elem_bytes(dt);
+  const Range all[] = {{scores, (size_t)T * E * 4}, {expert_tokens, (size_t)R * 4}, {slot, (size_t)T * E * 4},
+                       {expert_offsets, (size_t)(E + 1) * 4}, {ws, need},
+                       {x, (size_t)T * d * s}, {w_router, (size_t)E * d * s}};
+  if (any_overlap(all, 5, 7)) return MOE_ERR_INVALID_ARG;
+  hipError_t e = moe::launch_router(dt == MOE_BF16, T, d, E, k, 3, x, w_router, nullptr, nullptr, scores, stream);
+  if (e == hipSuccess) e = moe::launch_ec_select(T, E, (int)C, scores, ws, expert_tokens, slot, expert_offsets, stream);
+  return hip_status(e);
+}
+
+int moe_gather_rows(int64_t T, int32_t d, int64_t R, moe_dtype dt, const void* x, const int32_t* row_token,
+                    void* x_perm, hipStream_t stream) {
+  if (T < 0 || d < 1 || R < 0 || (dt != MOE_F32 && dt != MOE_BF16)) return MOE_ERR_INVALID_ARG;
+  if (d % (dt == MOE_BF16 ? 8 : 4) != 0) return MOE_ERR_UNSUPPORTED;
+  if (R == 0) return MOE_OK;
+  if (!x || !row_token || !x_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(row_token) || !aligned16(x_perm)) return MOE_ERR_UNSUPPORTED;
+  const size_t s = elem_bytes(dt);
+  const Range all[] = {{x_perm, (size_t)R * d * s}, {x, (size_t)T * d * s}, {row_token, (size_t)R * 4}};
+  if (any_overlap(all, 1, 3)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_gather_rows(dt == MOE_BF16, T, R, d, x, row_token, x_perm, stream));
+}
+
+int moe_ffn_rows_workspace_bytes(int64_t R_max, int32_t d, int32_t E, int32_t F, moe_dtype dt, size_t* bytes) {
+  if (bytes == nullptr || R_max < 0) return MOE_ERR_INVALID_ARG;
+  const int st = check_scalars(0, d, E, 1, 0.0f, F, dt, true);
+  if (st != MOE_OK) return st;
+  *bytes = ffn_ws_bytes(R_max, E, dt);
+  return MOE_OK;
+}
+
+int moe_grouped_ffn_rows(int64_t R_max, int32_t d, int32_t E, int32_t F, moe_dtype dt, const void* x_perm,
+                         const int32_t* expert_offsets, const void* w_gate, const void* w_up, const void* w_down,
+                         void* h_ws, void* out_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (R_max < 0) return MOE_ERR_INVALID_ARG;
+  int st = check_scalars(0, d, E, 1, 0.0f, F, dt, true);
+  if (st != MOE_OK) return st;
+  if (R_max >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (R_max == 0) return MOE_OK;
+  if (!x_perm || !expert_offsets || !w_gate || !w_up || !w_down || !h_ws || !out_perm)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(expert_offsets) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(w_down) || !aligned16(h_ws) || !aligned16(out_perm) || !aligned16(ws))
+    return MOE_ERR_UNSUPPORTED;
+  const size_t s = elem_bytes(dt);
+  const size_t wbytes = (size_t)E * F * d * s;
+  const size_t need = ffn_ws_bytes(R_max, E, dt);
+  if (ws != nullptr && ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const Range all[] = {{h_ws, (size_t)R_max * F * s}, {out_perm, (size_t)R_max * d * s},
+                       {ws, need},
+                       {x_perm, (size_t)R_max * d * s}, {expert_offsets, (size_t)(E + 1) * 4},
+                       {w_gate, wbytes}, {w_up, wbytes}, {w_down, wbytes}};
+  if (any_overlap(all, 3, 8)) return MOE_ERR_INVALID_ARG;
+  hipError_t e = dt == MOE_BF16
+                     ? moe::launch_ffn_bf16(R_max, d, E, F, x_perm, expert_offsets, w_gate, w_up,
+                                            w_down, h_ws, out_perm, need ? ws : nullptr, stream)
+                     : moe::launch_ffn_f32(R_max, d, E, F, x_perm, expert_offsets, w_gate, w_up,
+                                           w_down, h_ws, out_perm, stream);
+  return hip_status(e);
+}
+
+int moe_combine_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+                              const void* out_perm, const int32_t* slot, const float* scores, void* y,
+                              hipStream_t stream) {
+  int st = check_scalars(T, d, E, k, cf, -1, dt, false);
+  if (st != MOE_OK) return st;
+  int64_t C, R;
+  if ((st = ec_rows(T, E, k, cf, &C, &R)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!out_perm || !slot || !scores || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(out_perm) || !aligned16(slot) || !aligned16(scores) || !aligned16(y)) return MOE_ERR_UNSUPPORTED;
+  const size_t s = elem_bytes(dt);
+  const Range all[] = {{y, (size_t)T * d * s}, {out_perm, (size_t)R * d * s}, {slot, (size_t)T * E * 4},
+                       {scores, (size_t)T * E * 4}};
+  if (any_overlap(all, 1, 4)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_ec_combine(dt == MOE_BF16, T, d, E, R, out_perm, slot, scores, y, stream));
+}
+
+struct EcLayout {
+  size_t scores, tokens, slot, offsets, select, x_perm, h, out_perm, ffn, total;
+};
+
+static EcLayout ec_layout(int64_t T, int d, int E, int64_t R, int F, int dt) {
+  EcLayout L;
+  const size_t s = elem_bytes(dt);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round_up(bytes);
+    return at;
+  };
+  L.scores = take((size_t)T * E * 4);
+  L.tokens = take((size_t)R * 4);
+  L.slot = take((size_t)T * E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.select = take(moe::ec_select_bytes(T, E));
+  L.x_perm = take((size_t)R * d * s);
+  L.h = take((size_t)R * F * s);
+  L.out_perm = take((size_t)R * d * s);
+  L.ffn = take(ffn_ws_bytes(R, E, dt));
+  L.total = o;
+  return L;
+}
+
+int moe_forward_expert_choice_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
+                                              moe_dtype dt, size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  int st = check_scalars(T, d, E, k, cf, F, dt, true);
+  if (st != MOE_OK) return st;
+  int64_t C, R;
+  if ((st = ec_rows(T, E, k, cf, &C, &R)) != MOE_OK) return st;
+  *bytes = ec_layout(T, d, E, R, F, dt).total;
+  return MOE_OK;
+}
+
+int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+                              const void* x, const void* w_router, const void* w_gate, const void* w_up,
+                              const void* w_down, void* y, float* scores_opt, int32_t* slot_opt, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  int st = check_scalars(T, d, E, k, cf, F, dt, true);
+  if (st != MOE_OK) return st;
+  int64_t C, R;
+  if ((st = ec_rows(T, E, k, cf, &C, &R)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(y) || !aligned16(ws) || !aligned16(scores_opt) || !aligned16(slot_opt))
+    return MOE_ERR_UNSUPPORTED;
+  const EcLayout L = ec_layout(T, d, E, R, F, dt);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const size_t s = elem_bytes(dt);
+  const size_t wbytes = (size_t)E * F * d * s;
+  const Range all[] = {{y, (size_t)T * d * s}, {scores_opt, (size_t)T * E * 4}, {slot_opt, (size_t)T * E * 4},
+                       {ws, L.total},
+                       {x, (size_t)T * d * s}, {w_router, (size_t)E * d * s}, {w_gate, wbytes},
+                       {w_up, wbytes}, {w_down, wbytes}};
+  if (any_overlap(all, 4, 9)) return MOE_ERR_INVALID_ARG;
+  char* w = reinterpret_cast<char*>(ws);
+  float* scores = scores_opt ? scores_opt : reinterpret_cast<float*>(w + L.scores);
+  int32_t* slot = slot_opt ? slot_opt : reinterpret_cast<int32_t*>(w + L.slot);
+  int32_t* tokens = reinterpret_cast<int32_t*>(w + L.tokens);
+  int32_t* offsets = reinterpret_cast<int32_t*>(w + L.offsets);
+  const bool bf16 = dt == MOE_BF16;
+  hipError_t e = moe::launch_router(bf16, T, d, E, k, 3, x, w_router, nullptr, nullptr, scores, stream);
+  if (e == hipSuccess) e = moe::launch_ec_select(T, E, (int)C, scores, w + L.select, tokens, slot, offsets, stream);
+  if (e == hipSuccess) e = moe::launch_gather_rows(bf16, T, R, d, x, tokens, w + L.x_perm, stream);
+  if (e == hipSuccess)
+    e = bf16 ? moe::launch_ffn_bf16(R, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w_down, w + L.h,
+                                    w + L.out_perm, ffn_ws_bytes(R, E, dt) ? w + L.ffn : nullptr, stream)
+             : moe::launch_ffn_f32(R, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w_down, w + L.h,
+                                   w + L.out_perm, stream);
+  if (e == hipSuccess) e = moe::launch_ec_combine(bf16, T, d, E, R, w + L.out_perm, slot, scores, y, stream);
+  return hip_status(e);
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -7,7 +7,8 @@
 
 namespace moe {
 
-// gating: 0 Softmax(TopK), 1 TopK(Softmax), 2 TopK(Softmax) * E/k
+// gating: 0 Softmax(TopK), 1 TopK(Softmax), 2 TopK(Softmax) * E/k,
+// 3 expert-choice scores: Softmax over all E written to logits (idx, gate unused)
 hipError_t launch_router(bool bf16, int64_t T, int d, int E, int k, int gating, const void* x, const void* wr,
                          int32_t* idx, float* gate, float* logits, hipStream_t s);
 
@@ -49,5 +50,15 @@ hipError_t launch_ffn_f32(int64_t R_max, int d, int E, int F, const void* x_perm
 
 hipError_t launch_combine(bool bf16, int64_t T, int d, int k, const void* out_perm,
                           const int32_t* slot_row, const float* gate, void* y, hipStream_t s);
+
+// Expert choice: per-expert selection of C tokens from the [T, E] scores
+// (ws: ec_select_bytes), the row gather, and the variable fan-in combine.
+size_t ec_select_bytes(int64_t T, int E);
+hipError_t launch_ec_select(int64_t T, int E, int C, const float* scores, void* ws, int32_t* tokens,
+                            int32_t* slot, int32_t* offsets, hipStream_t s);
+hipError_t launch_gather_rows(bool bf16, int64_t T, int64_t R, int d, const void* x, const int32_t* row_token,
+                              void* x_perm, hipStream_t s);
+hipError_t launch_ec_combine(bool bf16, int64_t T, int d, int E, int64_t R, const void* out_perm,
+                             const int32_t* slot, const float* scores, void* y, hipStream_t s);
 
 }  // namespace moe

@@ -10,6 +10,9 @@
 //
 // gating: 0 = Softmax(TopK(l)); 1 = TopK(Softmax(l)); 2 = the same times E/k.
 // The chosen experts are the same in every mode (softmax is monotone).
+// gating 3 (expert choice): no top-k; logits_out receives the dense gate
+// Softmax(l) over all E experts ("How do Mixture of Expert Models Work?",
+// "The Math Behind MoEs"), the score each expert ranks the tokens by.
 //
 #include "moe_common.h"
 #include "moe_kernels.h"
@@ -112,7 +115,24 @@ __global__ __launch_bounds__(256) void router_kernel(int64_t T, int d, int E, in
       const int e = lane + 64 * q;
       v[q] = e < E ? lg[wave][i][e] : 0.f;
       taken[q] = e >= E;
-      if (logits_out != nullptr && e < E) logits_out[t * E + e] = v[q];
+      if (gating != 3 && logits_out != nullptr && e < E) logits_out[t * E + e] = v[q];
+    }
+    if (gating == 3) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (lane + 64 * q < E) mx = fmaxf(mx, v[q]);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      float part = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (lane + 64 * q < E) part += expf(v[q] - mx);
+      const float den = group_sum<64>(part, lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (lane + 64 * q < E) logits_out[t * E + lane + 64 * q] = expf(v[q] - mx) / den;
+      continue;
     }
     float sel_v[8];
     int sel_i[8];
@@ -315,7 +335,26 @@ __global__ __launch_bounds__(NW * 64) void router_mfma_kernel(int64_t T, int d, 
       const int e = el + LPT * j;
       taken[j] = e >= E;
       v[j] = (tl < BT && e < E) ? red[tl * RS + e] : 0.f;
-      if (logits_out != nullptr && live && e < E) logits_out[t * E + e] = v[j];
+      if (gating != 3 && logits_out != nullptr && live && e < E) logits_out[t * E + e] = v[j];
+    }
+    if (gating == 3) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (el + LPT * j < E) mx = fmaxf(mx, v[j]);
+#pragma unroll
+      for (int o = LPT / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (el + LPT * j < E) part += expf(v[j] - mx);
+      const float den = group_sum<LPT>(part, lane);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = el + LPT * j;
+        if (live && e < E) logits_out[t * E + e] = expf(v[j] - mx) / den;
+      }
+      continue;
     }
     float sel_v[8];
     int sel_i[8];

@@ -52,6 +52,19 @@ _SIGS = {
                                              _vp, _vp]),
     "moe_forward": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp,
                                    _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_route_expert_choice_workspace_bytes": (ctypes.c_int, [_i64, _i32, ctypes.POINTER(_sz)]),
+    "moe_route_expert_choice": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                               _vp, _vp, _vp, _sz, _vp]),
+    "moe_gather_rows": (ctypes.c_int, [_i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp]),
+    "moe_ffn_rows_workspace_bytes": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.c_int, ctypes.POINTER(_sz)]),
+    "moe_grouped_ffn_rows": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _vp, _vp, _sz, _vp]),
+    "moe_combine_expert_choice": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                                 _vp]),
+    "moe_forward_expert_choice_workspace_bytes": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32,
+                                                                 ctypes.c_int, ctypes.POINTER(_sz)]),
+    "moe_forward_expert_choice": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp,
+                                                 _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -297,4 +310,93 @@ def moe_forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, y=None, to
                                   _ptr(topk_idx), _ptr(topk_gate), _ptr(slot_row), _ptr(ws), ws.numel(),
                                   _stream(stream))
         _check("moe_forward_ex", st)
+    return y
+
+
+# ---------------------------------------------------------------------------
+# expert choice
+# ---------------------------------------------------------------------------
+
+def _size_query(fn, *args) -> int:
+    b = _sz()
+    _check(fn, getattr(lib(), fn)(*args, ctypes.byref(b)))
+    return int(b.value)
+
+
+def moe_route_expert_choice(x, w_router, k: int, cf: float, stream=None):
+    """Scores and per-expert selection. Returns dict(scores [T,E] fp32,
+    expert_tokens [E*C] int32, slot [T,E] int32, expert_offsets [E+1] int32, C)."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    C = moe_capacity(T, E, k, cf)
+    dev = x.device
+    out = dict(scores=torch.empty((T, E), dtype=torch.float32, device=dev),
+               expert_tokens=torch.empty(max(E * C, 1), dtype=torch.int32, device=dev),
+               slot=torch.empty((T, E), dtype=torch.int32, device=dev),
+               expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev), C=C)
+    ws = torch.empty(max(_size_query("moe_route_expert_choice_workspace_bytes", T, E), 16), dtype=torch.uint8,
+                     device=dev)
+    st = lib().moe_route_expert_choice(T, d, E, k, cf, _dt(x), _ptr(x), _ptr(w_router), _ptr(out["scores"]),
+                                       _ptr(out["expert_tokens"]), _ptr(out["slot"]), _ptr(out["expert_offsets"]),
+                                       _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_route_expert_choice", st)
+    return out
+
+
+def moe_gather_rows(x, row_token, R: int, x_perm=None, stream=None):
+    """x_perm[r] = x[row_token[r]] for r < R."""
+    T, d = x.shape
+    if x_perm is None:
+        x_perm = torch.empty((max(R, 1), d), dtype=x.dtype, device=x.device)
+    _check("moe_gather_rows", lib().moe_gather_rows(T, d, R, _dt(x), _ptr(x), _ptr(row_token), _ptr(x_perm),
+                                                    _stream(stream)))
+    return x_perm
+
+
+def moe_grouped_ffn_rows(x_perm, expert_offsets, w_gate, w_up, w_down, R_max: int, h=None, out_perm=None,
+                         ws=None, stream=None):
+    """Grouped SwiGLU FFN over at most R_max expert-major rows. Returns (h, out_perm)."""
+    E, F, d = w_gate.shape
+    dev = x_perm.device
+    if h is None:
+        h = torch.empty((max(R_max, 1), F), dtype=x_perm.dtype, device=dev)
+    if out_perm is None:
+        out_perm = torch.empty((max(R_max, 1), d), dtype=x_perm.dtype, device=dev)
+    if ws is None:
+        n = _size_query("moe_ffn_rows_workspace_bytes", R_max, d, E, F, _dt(x_perm))
+        ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+    elif ws is False:
+        ws = None
+    st = lib().moe_grouped_ffn_rows(R_max, d, E, F, _dt(x_perm), _ptr(x_perm), _ptr(expert_offsets), _ptr(w_gate),
+                                    _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(out_perm), _ptr(ws),
+                                    ws.numel() if ws is not None else 0, _stream(stream))
+    _check("moe_grouped_ffn_rows", st)
+    return h, out_perm
+
+
+def moe_combine_expert_choice(out_perm, slot, scores, k: int, cf: float, y=None, stream=None):
+    T, E = slot.shape
+    d = out_perm.shape[1]
+    if y is None:
+        y = torch.empty((T, d), dtype=out_perm.dtype, device=out_perm.device)
+    st = lib().moe_combine_expert_choice(T, d, E, k, cf, _dt(out_perm), _ptr(out_perm), _ptr(slot), _ptr(scores),
+                                         _ptr(y), _stream(stream))
+    _check("moe_combine_expert_choice", st)
+    return y
+
+
+def moe_forward_expert_choice(x, w_router, w_gate, w_up, w_down, k: int, cf: float, y=None, scores=None,
+                              slot=None, ws=None, stream=None):
+    """The whole expert-choice layer. Returns y [T, d] (scores / slot filled when given)."""
+    T, d = x.shape
+    E, F, _ = w_gate.shape
+    if y is None:
+        y = torch.empty_like(x)
+    if ws is None:
+        n = _size_query("moe_forward_expert_choice_workspace_bytes", T, d, E, k, cf, F, _dt(x))
+        ws = torch.empty(max(n, 16), dtype=torch.uint8, device=x.device)
+    st = lib().moe_forward_expert_choice(T, d, E, k, cf, F, _dt(x), _ptr(x), _ptr(w_router), _ptr(w_gate),
+                                         _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(scores), _ptr(slot), _ptr(ws),
+                                         ws.numel(), _stream(stream))
+    _check("moe_forward_expert_choice", st)
     return y

@@ -27,7 +27,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 25
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -76,8 +76,22 @@ def test_workspace_sizes():
     assert moe.moe_permute_workspace_bytes(4096, 8) >= 16 * 8 * 4
 
 
-# Fake device addresses: 16-byte aligned, far apart, never dereferenced.
+# Fake device addresses: 16-byte aligned, far apart, never dereferenced. The
+# tests that pass them expect a failing check before any launch; should a check
+# ever pass, the call would launch kernels on these addresses, so they only
+# run where no GPU is visible.
 A = [0x7F0000000000 + i * 0x100000000 for i in range(16)]
+
+
+@pytest.fixture(autouse=True)
+def _no_fake_pointers_on_a_gpu(request):
+    import torch
+    if "fake" in request.node.name or request.node.name.startswith(("test_forward_validation",
+                                                                   "test_stage_entry_points",
+                                                                   "test_gating_and_priority",
+                                                                   "test_expert_choice_entry")):
+        if torch.cuda.device_count() > 0:
+            pytest.skip("fake device pointers are only passed where no GPU is visible")
 
 
 def fwd(T=64, d=64, E=4, k=1, cf=1.25, F=128, dt=F32, x=A[0], wr=A[1], wg=A[2], wu=A[3], wd=A[4], y=A[5],
@@ -174,3 +188,46 @@ def test_gating_and_priority_entry_points_validate():
     assert L.moe_forward_ex(*a) == INV
     a = list(fx); a[0] = 0
     assert L.moe_forward_ex(*a) == OK
+
+
+def test_expert_choice_entry_points_validate():
+    L = moe.lib()
+    b = ctypes.c_size_t()
+    assert L.moe_route_expert_choice_workspace_bytes(100, 8, ctypes.byref(b)) == OK and b.value >= 100 * 8 * 4
+    assert L.moe_route_expert_choice_workspace_bytes(100, 300, ctypes.byref(b)) == UNS
+    # route: k > E, small workspace, scores overlapping x, T = 0
+    r = [64, 64, 4, 2, 1.0, F32, A[0], A[1], A[2], A[3], A[4], A[5], A[6], 1 << 30, None]
+    a = list(r); a[3] = 5
+    assert L.moe_route_expert_choice(*a) == INV
+    a = list(r); a[13] = 16
+    assert L.moe_route_expert_choice(*a) == WS
+    a = list(r); a[8] = A[0]
+    assert L.moe_route_expert_choice(*a) == INV
+    a = list(r); a[0] = 0
+    assert L.moe_route_expert_choice(*a) == OK
+    # E * C beyond int32 rows
+    a = list(r); a[0] = 1 << 24; a[2] = 256; a[3] = 200; a[4] = 1.0
+    assert L.moe_route_expert_choice(*a) == UNS
+    # gather: misaligned, overlap, R = 0
+    assert L.moe_gather_rows(64, 64, 10, F32, A[0], A[1] + 4, A[2], None) == UNS
+    assert L.moe_gather_rows(64, 64, 10, F32, A[0], A[1], A[0], None) == INV
+    assert L.moe_gather_rows(64, 64, 0, F32, None, None, None, None) == OK
+    assert L.moe_gather_rows(64, 66, 10, F32, A[0], A[1], A[2], None) == UNS
+    # grouped ffn over rows: bf16 F not a multiple of 64, h overlapping out
+    assert L.moe_grouped_ffn_rows(100, 64, 4, 72, BF16, A[0], A[1], A[2], A[3], A[4], A[5], A[6], None, 0, None) == UNS
+    assert L.moe_grouped_ffn_rows(100, 64, 4, 128, BF16, A[0], A[1], A[2], A[3], A[4], A[5], A[5], None, 0, None) == INV
+    assert L.moe_grouped_ffn_rows(0, 64, 4, 128, BF16, None, None, None, None, None, None, None, None, 0, None) == OK
+    assert L.moe_ffn_rows_workspace_bytes(100, 64, 4, 128, BF16, ctypes.byref(b)) == OK
+    # combine: y overlapping out_perm
+    assert L.moe_combine_expert_choice(64, 64, 4, 2, 1.0, F32, A[0], A[1], A[2], A[0], None) == INV
+    # forward
+    assert L.moe_forward_expert_choice_workspace_bytes(64, 64, 4, 2, 1.0, 128, F32, ctypes.byref(b)) == OK
+    f = [64, 64, 4, 2, 1.0, 128, F32, A[0], A[1], A[2], A[3], A[4], A[5], None, None, A[6], 1 << 40, None]
+    a = list(f); a[15] = None
+    assert L.moe_forward_expert_choice(*a) == INV
+    a = list(f); a[16] = b.value - 1
+    assert L.moe_forward_expert_choice(*a) == WS
+    a = list(f); a[12] = A[0]          # y overlapping x
+    assert L.moe_forward_expert_choice(*a) == INV
+    a = list(f); a[0] = 0
+    assert L.moe_forward_expert_choice(*a) == OK
