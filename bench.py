@@ -16,7 +16,9 @@ do not read from cache; it gives each stage's duration and the roofline
 figures. The CPU oracle is timed on a bounded sample of the same workload.
 --gating / --fill select a gate rule and a capacity fill order (Batch
 Priority Routing); the step is then moe_forward_ex, and the permute stage
-includes the priority sort.
+includes the priority sort. --routing expert_choice times
+moe_forward_expert_choice instead (each expert takes C = capacity tokens);
+its stages are route (scores and selection), gather, ffn and combine.
 Prints one JSON line on stdout (progress goes to stderr).
 """
 import argparse
@@ -97,6 +99,7 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--gating", default="topk_softmax", choices=["topk_softmax", "softmax_topk", "softmax_topk_scaled"])
     ap.add_argument("--fill", default="token", choices=["token", "priority"])
+    ap.add_argument("--routing", default="token_choice", choices=["token_choice", "expert_choice"])
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run K device-to-device copies of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -134,6 +137,9 @@ def main():
     g = {n: v.cuda() for n, v in a.items() if v is not None and n != "token_ids"}
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    if args.routing == "expert_choice":
+        print(json.dumps(bench_expert_choice(args, w, a, g, moe, stream)), flush=True)
+        return
 
     # ---- headline: K x moe_forward ----
     y = torch.empty_like(g["x"])
@@ -256,6 +262,98 @@ def main():
         "stage_path_equals_forward": same_as_forward,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_expert_choice(args, w, a, g, moe, stream):
+    """Expert-choice layer: K timed moe_forward_expert_choice steps, then a stage pass."""
+    import numpy as np
+    import torch
+
+    T, d, E, k, F, cf = w.T, w.d, w.E, w.k, w.F, w.cf
+    s = 2 if w.dtype == "bf16" else 4
+    K, W = args.steps, args.warmup
+    C = moe.moe_capacity(T, E, k, cf)
+    R = E * C
+    y = torch.empty_like(g["x"])
+    ws = torch.empty(max(moe._size_query("moe_forward_expert_choice_workspace_bytes", T, d, E, k, cf, F,
+                                             moe._dt(g["x"])), 16), dtype=torch.uint8, device="cuda")
+
+    def forward():
+        moe.moe_forward_expert_choice(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], k, cf, y=y, ws=ws)
+
+    for _ in range(W):
+        forward()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        forward()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    log(f"moe_forward_expert_choice: {ms_step:.3f} ms/step (C = {C}, {R} rows)")
+
+    names = ["route", "gather", "ffn", "combine"]
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    samples = {n: [] for n in names}
+    evs = []
+    y2 = torch.empty_like(g["x"])
+    for it in range(W + K):
+        if flush is not None:
+            flush.fill_(it & 0xFF)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev[0].record(stream)
+        r = moe.moe_route_expert_choice(g["x"], g["w_router"], k, cf, stream=stream)
+        ev[1].record(stream)
+        xp = moe.moe_gather_rows(g["x"], r["expert_tokens"], R, stream=stream)
+        ev[2].record(stream)
+        _, o = moe.moe_grouped_ffn_rows(xp, r["expert_offsets"], g["w_gate"], g["w_up"], g["w_down"], R, stream=stream)
+        ev[3].record(stream)
+        moe.moe_combine_expert_choice(o, r["slot"], r["scores"], k, cf, y=y2, stream=stream)
+        ev[4].record(stream)
+        if it >= W:
+            evs.append(ev)
+    torch.cuda.synchronize()
+    for ev in evs:
+        for i, n in enumerate(names):
+            samples[n].append(ev[i].elapsed_time(ev[i + 1]))
+    st_ms = {n: float(np.mean(v)) for n, v in samples.items()}
+    active = E
+    alg = {
+        "route": dict(bytes=T * d * s + E * d * s + T * E * 4 * 3 + R * 4 + T * E * 4, flops=2 * T * d * E),
+        "gather": dict(bytes=2 * R * d * s + R * 4, flops=0),
+        "ffn": dict(bytes=active * 3 * F * d * s + 2 * R * d * s + 2 * R * F * s, flops=6 * d * F * R),
+        "combine": dict(bytes=R * d * s + T * E * 8 + T * d * s, flops=2 * R * d),
+    }
+    stages = {}
+    for n in names:
+        t = st_ms[n] * 1e-3
+        stages[n] = {"us": st_ms[n] * 1e3, "GB/s": alg[n]["bytes"] / t / 1e9, "TFLOP/s": alg[n]["flops"] / t / 1e12,
+                     "hbm_frac": alg[n]["bytes"] / t / 1e9 / PEAK["hbm_gbs"]}
+        log(f"  {n:8s} {st_ms[n] * 1e3:9.1f} us  {stages[n]['GB/s']:8.0f} GB/s  {stages[n]['TFLOP/s']:8.1f} TFLOP/s")
+    peak_mm = PEAK["bf16_tflops"] if w.dtype == "bf16" else PEAK["f32_tflops"]
+    achieved = alg["ffn"]["flops"] / (st_ms["ffn"] * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        from oracle import moe_oracle as orc
+        t0 = time.perf_counter()
+        S = min(T, 1024)
+        orc.expert_choice_forward(a["x"][:S], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], k, cf, w.dtype)
+        t = time.perf_counter() - t0
+        cpu = {"value": S / t, "unit": "tokens/s", "cores": None, "kind": "oracle",
+               "sample": f"expert-choice layer on the first {S} of {T} tokens (selection recomputed for them), {t:.1f} s"}
+    return {
+        "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "routing": "expert_choice", "T": T, "d": d, "E": E, "k": k, "F": F, "cf": cf,
+                   "tokens_per_expert": C, "rows": R, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "grouped SwiGLU FFN over the selected rows (both GEMMs)",
+                     "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s", "frac": achieved / peak_mm,
+                     "traffic": None, "alg_flops_per_launch": alg["ffn"]["flops"], "avg_launch_us": st_ms["ffn"] * 1e3},
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "stage_path_equals_forward": bool(torch.equal(y, y2)),
+    }
 
 
 if __name__ == "__main__":

@@ -165,7 +165,10 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(int64_t T, int64_t R, 
 }
 
 // y[t] = store(sum over experts e ascending with 0 <= slot[t, e] < R of
-//              score[t, e] * out_perm[slot[t, e]]), fp32 from +0; one wavefront per token.
+//              score[t, e] * out_perm[slot[t, e]]), fp32 from +0; one wavefront per
+// token. Lane l loads slot[t, e0 + l] and score[t, e0 + l] for a group of 64
+// experts; a ballot of the chosen ones is walked from the lowest set bit, so
+// only chosen experts are visited, in ascending order.
 template <typename S>
 __global__ __launch_bounds__(256) void ec_combine_kernel(int64_t T, int d, int E, int64_t R,
                                                          const typename S::elem* __restrict__ o,
@@ -173,26 +176,47 @@ __global__ __launch_bounds__(256) void ec_combine_kernel(int64_t T, int d, int E
                                                          const float* __restrict__ scores,
                                                          typename S::elem* __restrict__ y) {
   constexpr int V = S::kVec;
+  constexpr int MAXC = 8;   // row chunks of 64 lanes x V elements held in registers
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const char* ob = reinterpret_cast<const char*>(o);
   char* yb = reinterpret_cast<char*>(y) + (size_t)t * d * sizeof(typename S::elem);
   const size_t rb = (size_t)d * sizeof(typename S::elem);
-  for (int c = lane * V; c < d; c += 64 * V) {
-    float acc[V];
+  for (int c0 = 0; c0 < d; c0 += 64 * V * MAXC) {
+    float acc[MAXC][V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
-    for (int e = 0; e < E; ++e) {
-      const int r = slot[t * E + e];
-      if (r < 0 || r >= R) continue;
-      const float g = scores[t * E + e];
-      float f[V];
-      unpack16(S(), ld16(ob + (size_t)r * rb + (size_t)c * sizeof(typename S::elem)), f);
+    for (int q = 0; q < MAXC; ++q)
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = fmaf(g, f[i], acc[i]);
+      for (int i = 0; i < V; ++i) acc[q][i] = 0.f;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const int r_l = e < E ? slot[t * E + e] : -1;
+      const float g_l = e < E ? scores[t * E + e] : 0.f;
+      uint64_t m = __ballot(r_l >= 0 && r_l < R);
+      while (m) {
+        const int src = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        const int r = __shfl(r_l, src);
+        const float g = __shfl(g_l, src);
+        const char* orow = ob + (size_t)r * rb;
+#pragma unroll
+        for (int q = 0; q < MAXC; ++q) {
+          const int c = c0 + (q * 64 + lane) * V;
+          if (c < d) {
+            float f[V];
+            unpack16(S(), ld16(orow + (size_t)c * sizeof(typename S::elem)), f);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[q][i] = fmaf(g, f[i], acc[q][i]);
+          }
+        }
+      }
     }
-    st16(yb + (size_t)c * sizeof(typename S::elem), pack16(S(), acc));
+#pragma unroll
+    for (int q = 0; q < MAXC; ++q) {
+      const int c = c0 + (q * 64 + lane) * V;
+      if (c < d) st16(yb + (size_t)c * sizeof(typename S::elem), pack16(S(), acc[q]));
+    }
   }
 }
 
