@@ -64,6 +64,15 @@ Readings where the pages are silent (each is listed in the design notes):
     float32, ties to the lower token index; its rows list them in ascending
     token order; the gate of (t, e) is score[t, e] (not renormalised) and
     y[t] sums over the experts that chose t, in ascending expert order;
+  * backward pass ([TALK]: the permutation is recomputed in the backward
+    pass instead of being stored): routing, permutation, a = x W_gate^T,
+    b = x W_up^T, h and o are recomputed from the inputs; the gradient
+    follows the chain rule of the forward definition with these storage
+    rounding points: a, b (recomputed, held in the storage type), the
+    expert-output gradient d_o = g * dy, the SwiGLU input gradients da, db,
+    the permuted input gradient dx_perm, and every returned gradient. The
+    router gradient includes dropped slots (their gates still enter the
+    softmax of the chosen logits);
   * "storage" rounding: the layer stores h, o and y in its storage type. In
     "bf16" mode the float64 value is rounded to float32 and then to bfloat16
     (round to nearest even); in "f32" mode to float32; in "f64" mode not at
@@ -461,3 +470,100 @@ def forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, storage: str,
                 near_tie=near_tie_tokens(logits, k), demand=demand, offsets=offsets,
                 slot_row=slot_row, row_slot=row_slot, cap=cap, y=y,
                 o_rows=o_rows, h_rows=h_rows)
+
+
+# ---------------------------------------------------------------------------
+# backward pass  [TALK] (recomputed permutation); chain rule of the forward
+# ---------------------------------------------------------------------------
+
+def silu_grad(a: np.ndarray) -> np.ndarray:
+    """d silu / da = sigma(a) * (1 + a * (1 - sigma(a)))."""
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-a))
+    return sig * (1.0 + a * (1.0 - sig))
+
+
+def topk_softmax_grad(gates: np.ndarray, dg: np.ndarray) -> np.ndarray:
+    """Gradient through g = softmax(l_S) over the k chosen logits:
+    dl_j = g_j (dg_j - sum_j' g_j' dg_j')."""
+    return gates * (dg - (gates * dg).sum(axis=1, keepdims=True))
+
+
+def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: str) -> dict:
+    """Gradients of L = <dy, y> for the token-choice layer with Softmax(TopK)
+    gates and token-order capacity, with respect to x and every weight.
+
+    Forward (as `forward`): l = x W_g^T; S = TopK(l); g = softmax(l_S);
+    a = x_perm W_gate^T, b = x_perm W_up^T; h = st(silu(a) b); o = st(h W_down^T);
+    y = st(sum_j g_j o_j).  Backward, per kept row r = slot (t, j) of expert e:
+      d_o[r]   = st(g_j dy[t])
+      dg[t,j]  = <dy[t], o[r]>                  (0 for a dropped slot)
+      dl[t,S_j]= g_j (dg_j - sum_j' g_j' dg_j')  (softmax over the chosen k)
+      dh[r]    = d_o[r] W_down[e]
+      da[r]    = st(dh * b_st * silu'(a_st)),  db[r] = st(dh * silu(a_st))
+                 with a_st = st(a), b_st = st(b)
+      dx_perm  = st(da W_gate[e] + db W_up[e])
+      dW_gate[e] = st(sum_r da[r]^T x_perm[r]),  dW_up[e] = st(sum_r db[r]^T x_perm[r])
+      dW_down[e] = st(sum_r d_o[r]^T h[r])
+      dW_g[e]  = st(sum over (t, j) with S_j = e of dl[t, j] x[t])
+      dx[t]    = st(sum_j dl[t, j] W_g[S_j] + sum over kept j of dx_perm[slot (t, j)])
+    """
+    x64 = as_f64(x)
+    T, d = x64.shape
+    E = w_router.shape[0]
+    F = w_gate.shape[1]
+    wr = as_f64(w_router)
+    r = forward(x, w_router, w_gate, w_up, w_down, k, cf, storage)
+    idx, gates, slot_row, offsets, row_slot = r["topk_idx"], r["topk_gate"], r["slot_row"], r["offsets"], r["row_slot"]
+    R = int(offsets[E])
+    dy64 = as_f64(dy)
+    tok = row_slot // k
+    jj = row_slot % k
+    a_st = np.empty((R, F))
+    b_st = np.empty((R, F))
+    h = np.empty((R, F))
+    o = np.empty((R, d))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        xr = x64[tok[lo:hi]]
+        a = xr @ as_f64(w_gate[e]).T
+        b = xr @ as_f64(w_up[e]).T
+        a_st[lo:hi] = store(a, storage)
+        b_st[lo:hi] = store(b, storage)
+        h[lo:hi] = store(silu(a) * b, storage)
+        o[lo:hi] = store(h[lo:hi] @ as_f64(w_down[e]).T, storage)
+    d_o = store(gates[tok, jj][:, None] * dy64[tok], storage)
+    dg = np.zeros((T, k))
+    kept = slot_row >= 0
+    tt, kk = np.nonzero(kept)
+    dg[tt, kk] = np.einsum("ij,ij->i", dy64[tt], o[slot_row[tt, kk]])
+    dl = topk_softmax_grad(gates, dg)
+    dx_perm = np.empty((R, d))
+    dW_gate = np.zeros((E, F, d))
+    dW_up = np.zeros((E, F, d))
+    dW_down = np.zeros((E, d, F))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        dh = d_o[lo:hi] @ as_f64(w_down[e])
+        sa = silu(a_st[lo:hi])
+        da = store(dh * b_st[lo:hi] * silu_grad(a_st[lo:hi]), storage)
+        db = store(dh * sa, storage)
+        dx_perm[lo:hi] = store(da @ as_f64(w_gate[e]) + db @ as_f64(w_up[e]), storage)
+        xr = x64[tok[lo:hi]]
+        dW_gate[e] = da.T @ xr
+        dW_up[e] = db.T @ xr
+        dW_down[e] = d_o[lo:hi].T @ h[lo:hi]
+    dW_g = np.zeros((E, d))
+    for j in range(k):
+        np.add.at(dW_g, idx[:, j].astype(np.int64), dl[:, j][:, None] * x64)
+    dx = np.einsum("tj,tjd->td", dl, wr[idx.astype(np.int64)])
+    for j in range(k):
+        m = slot_row[:, j] >= 0
+        dx[m] += dx_perm[slot_row[m, j]]
+    return dict(forward=r, dx=store(dx, storage), dW_g=store(dW_g, storage), dW_gate=store(dW_gate, storage),
+                dW_up=store(dW_up, storage), dW_down=store(dW_down, storage), dl=dl, dg=dg, d_o=d_o,
+                a_st=a_st, b_st=b_st, dx_perm=dx_perm)

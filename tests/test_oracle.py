@@ -553,6 +553,85 @@ def check_ec_float32_decision():
     assert tok[:, 0].tolist() == [0, 2]
 
 
+# ---------------------------------------------------------------------------
+# backward pass
+# ---------------------------------------------------------------------------
+
+def _loss(x, wr, wg, wu, wd, dy, k, cf):
+    return float((orc.forward(x, wr, wg, wu, wd, k, cf, "f64")["y"] * dy).sum())
+
+
+def check_backward_finite_differences():
+    """Every gradient entry of a tiny layer (with and without drops) against a
+    central difference of L = <dy, y> through the forward oracle (float64, no
+    rounding). The step is far below every routing gap, so the routing and the
+    drops stay fixed."""
+    for (T, d, E, k, F, cf, seed) in [(12, 6, 4, 2, 5, 0.75, 1), (9, 4, 3, 3, 4, 0.0, 2), (10, 5, 4, 1, 6, 0.5, 3)]:
+        rng = np.random.default_rng(seed)
+        x = rng.standard_normal((T, d))
+        wr = rng.standard_normal((E, d))
+        wg = rng.standard_normal((E, F, d)) / math.sqrt(d)
+        wu = rng.standard_normal((E, F, d)) / math.sqrt(d)
+        wd = rng.standard_normal((E, d, F)) / math.sqrt(F)
+        dy = rng.standard_normal((T, d))
+        g = orc.backward(x, wr, wg, wu, wd, dy, k, cf, "f64")
+        if cf > 0:
+            assert (g["forward"]["slot_row"] < 0).any()
+        params = {"dx": x, "dW_g": wr, "dW_gate": wg, "dW_up": wu, "dW_down": wd}
+        eps = 1e-6
+        for name, arr in params.items():
+            flat = arr.reshape(-1)
+            num = np.empty(flat.size)
+            for i in range(flat.size):
+                keep = flat[i]
+                flat[i] = keep + eps
+                lp = _loss(x, wr, wg, wu, wd, dy, k, cf)
+                flat[i] = keep - eps
+                lm = _loss(x, wr, wg, wu, wd, dy, k, cf)
+                flat[i] = keep
+                num[i] = (lp - lm) / (2 * eps)
+            assert np.allclose(g[name].reshape(-1), num, rtol=1e-6, atol=1e-7), name
+
+
+def check_backward_autograd():
+    """torch.autograd through a dense evaluation with the oracle's routing and
+    drop decisions held fixed (every expert on every token, masked by the
+    kept slots; gates = softmax of the chosen logits): the same five gradients."""
+    for (T, E, k, cf) in [(30, 5, 2, 0.75), (25, 4, 1, 0.0), (20, 6, 3, 1.0)]:
+        x, wr, wg, wu, wd = small_layer(T=T, E=E, k=k)
+        dy = np.random.default_rng(4).standard_normal(x.shape)
+        g = orc.backward(x, wr, wg, wu, wd, dy, k, cf, "f64")
+        fw = g["forward"]
+        idx = torch.from_numpy(fw["topk_idx"].astype(np.int64))
+        kept = torch.from_numpy(fw["slot_row"] >= 0)
+        tx, twr, twg, twu, twd = (torch.tensor(a, requires_grad=True) for a in (x, wr, wg, wu, wd))
+        l = tx @ twr.T
+        gate = torch.softmax(torch.gather(l, 1, idx), dim=1)
+        y = torch.zeros_like(tx)
+        for e in range(E):
+            h = torch.nn.functional.silu(tx @ twg[e].T) * (tx @ twu[e].T)
+            oe = h @ twd[e].T
+            w = ((idx == e) & kept).double() * gate
+            y = y + w.sum(1, keepdim=True) * oe
+        (y * torch.from_numpy(dy)).sum().backward()
+        for name, t in [("dx", tx), ("dW_g", twr), ("dW_gate", twg), ("dW_up", twu), ("dW_down", twd)]:
+            assert np.allclose(g[name], t.grad.numpy(), rtol=1e-10, atol=1e-12), name
+
+
+def check_backward_storage_rounding():
+    """bf16 storage: the returned gradients are bf16 values, and they match the
+    float64 gradients to bf16 precision (the rounding points only perturb)."""
+    x, wr, wg, wu, wd = small_layer(T=30, E=4, k=2, dtype="bf16")
+    dy = torch.from_numpy(np.random.default_rng(5).standard_normal(x.shape)).to(torch.bfloat16).double().numpy()
+    gb = orc.backward(x, wr, wg, wu, wd, dy, 2, 1.0, "bf16")
+    g64 = orc.backward(x, wr, wg, wu, wd, dy, 2, 1.0, "f64")
+    for name in ("dx", "dW_g", "dW_gate", "dW_up", "dW_down"):
+        v = gb[name]
+        assert np.array_equal(orc.round_to_bf16(v.astype(np.float32)).astype(np.float64), v), name
+        scale = np.abs(g64[name]).max()
+        assert np.abs(v - g64[name]).max() <= 0.05 * scale, name
+
+
 ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
             check_zero_router_closed_form, check_gate_invariants, check_k_equals_E_is_softmax,
             check_printed_gates, check_capacity_values, check_permutation_bruteforce,
@@ -561,7 +640,8 @@ ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
             check_switch_scaled_zero_router_is_dense, check_bpr_bruteforce,
             check_bpr_reduces_to_token_order, check_bpr_float32_decision,
             check_bpr_forward_keeps_high_gates, check_ec_bruteforce, check_ec_selects_by_score_not_logit,
-            check_ec_full_capacity_is_dense_gating, check_ec_zero_router, check_ec_float32_decision]
+            check_ec_full_capacity_is_dense_gating, check_ec_zero_router, check_ec_float32_decision,
+            check_backward_finite_differences, check_backward_autograd, check_backward_storage_rounding]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -657,6 +737,10 @@ MUTANTS["ec_ties_to_later_token"] = ("expert_choice_select", lambda S, C, _o=orc
                                      _ec_reversed(S, C, _o), [check_ec_zero_router])
 MUTANTS["ec_rows_in_score_order"] = ("expert_choice_select", lambda S, C: _ec_score_order(S, C),
                                      [check_ec_bruteforce])
+MUTANTS["silu_grad_is_sigmoid"] = ("silu_grad", lambda a: 1.0 / (1.0 + np.exp(-a)),
+                                   [check_backward_autograd])
+MUTANTS["softmax_grad_without_the_mean"] = ("topk_softmax_grad", lambda gates, dg: gates * dg,
+                                            [check_backward_autograd])
 MUTANTS["bpr_score_as_float64"] = ("priority_order", lambda score: np.argsort(
     -np.asarray(score, np.float64), kind="stable"), [check_bpr_float32_decision])
 
