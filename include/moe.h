@@ -325,6 +325,36 @@ int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float 
                               float* scores_opt, int32_t* slot_opt,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Backward pass of the token-choice layer (Softmax(TopK) gates, token-order
+ * capacity), bf16 only (MOE_ERR_UNSUPPORTED for MOE_F32).
+ * Gradients of L = <dy, y> by the chain rule of the forward definition. The
+ * routing, the permutation and the expert activations are recomputed from
+ * the inputs (the upcycling talk's walkthrough recomputes the permutation in
+ * the backward pass), then, per kept row r = slot (t, j) of expert e:
+ *   d_o[r] = bf16(g_j dy[t]);  dg_j = <dy[t], o[r]> (0 for a dropped slot)
+ *   dl_j   = g_j (dg_j - sum_j' g_j' dg_j')     (all k slots, dropped ones too)
+ *   da[r]  = bf16(dh b silu'(a)), db[r] = bf16(dh silu(a)), dh = d_o[r] W_down[e],
+ *            with a = bf16(x_perm W_gate^T), b = bf16(x_perm W_up^T) recomputed
+ *   dx_perm[r] = bf16(da W_gate[e] + db W_up[e])
+ *   dw_gate[e] = bf16(sum_r da^T x_perm), dw_up[e] = bf16(sum_r db^T x_perm),
+ *   dw_down[e] = bf16(sum_r d_o^T h)   (an expert with no rows gets 0)
+ *   dw_router[e] = bf16(sum over (t, j) with S_j = e of dl_j x[t])
+ *   dx[t] = bf16(sum_j dl_j W_g[S_j] + sum over kept j of dx_perm[slot (t, j)])
+ * All accumulation is fp32. Layouts: dx [T, d], dw_router [E, d],
+ * dw_gate / dw_up [E, F, d], dw_down [E, d, F] (as the weights).
+ * ws, ws_bytes: scratch of moe_backward_workspace_bytes (recomputed
+ * activations, transposed weights and activations for the K-contiguous
+ * gradient GEMMs, fp32 partial sums of the router gradient).
+ * ------------------------------------------------------------------------- */
+int moe_backward_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
+                                 moe_dtype dt, size_t* bytes);
+int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+                 const void* x, const void* w_router, const void* w_gate, const void* w_up,
+                 const void* w_down, const void* dy,
+                 void* dx, void* dw_router, void* dw_gate, void* dw_up, void* dw_down,
+                 void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* moe_status_string(int status);
 

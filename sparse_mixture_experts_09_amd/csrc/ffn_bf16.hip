@@ -245,11 +245,25 @@ __device__ __forceinline__ void dma16(const void* g, char* lds) {
 #endif
 }
 
-template <int BN, bool SWIGLU>
+// Epilogues: EPI_PLAIN C = bf16(acc); EPI_SWIGLU C = bf16(silu(gate) * up);
+// EPI_SWIGLU_AB the same plus C2 = bf16(gate), C3 = bf16(up) (the backward
+// pass's recomputation); EPI_SWIGLU_BWD (plain tile, acc = dh): with a = X0,
+// b = X1 at the same element, C = bf16(dh * b * silu'(a)), C2 = bf16(dh * silu(a)).
+// ldc / ldx: row strides (elements) of the outputs / of X0 and X1.
+constexpr int EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_SWIGLU_AB = 2, EPI_SWIGLU_BWD = 3;
+
+__device__ __forceinline__ float silu_grad(float a) {
+  const float sg = 1.0f / (1.0f + __expf(-a));
+  return sg * (1.0f + a * (1.0f - sg));
+}
+
+template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN)>
 __global__ __launch_bounds__(512) void ffn_bf16_dma_kernel(
     int E, const int32_t* __restrict__ offsets, int N, int K, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT,
-    int P, int max_split, float* __restrict__ partials) {
+    int P, int max_split, float* __restrict__ partials, int ldc, uint16_t* __restrict__ C2,
+    uint16_t* __restrict__ C3, const uint16_t* __restrict__ X0, const uint16_t* __restrict__ X1, int ldx) {
+  static_assert(SWIGLU == (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_AB), "tile layout and epilogue");
   constexpr int BM = 256, NWM = 2, NWN = 4, NW = NWM * NWN;
   constexpr int BROWS = SWIGLU ? 2 * BN : BN;
   constexpr int WM = BM / NWM, WN = BN / NWN;
@@ -403,23 +417,57 @@ __global__ __launch_bounds__(512) void ffn_bf16_dma_kernel(
   for (int mb = 0; mb < MB; ++mb) {
     const int rloc = tc.m0 + wm * WM + mb * 32 + (lane & 31);
     if (rloc >= tc.seg_rows) continue;
-    uint16_t* crow = C + (size_t)(tc.seg_start + rloc) * (size_t)N;
+    const size_t grow = (size_t)(tc.seg_start + rloc);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = n0 + wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
         if (col >= N) continue;
+        const size_t at = grow * (size_t)ldc + col;
         float v[4];
+        if (EPI == EPI_PLAIN) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = acc[mb * NB + nb][4 * g + i];
-          v[i] = SWIGLU ? silu(a) * acc[MB * NB + mb * NB + nb][4 * g + i] : a;
+          for (int i = 0; i < 4; ++i) v[i] = acc[mb * NB + nb][4 * g + i];
+        } else if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_AB) {
+          float ga[4], up[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ga[i] = acc[mb * NB + nb][4 * g + i];
+            up[i] = acc[MB * NB + mb * NB + nb][4 * g + i];
+            v[i] = silu(ga[i]) * up[i];
+          }
+          if (EPI == EPI_SWIGLU_AB) {
+            uint2 wa, wb;
+            wa.x = pack_bf16x2(ga[0], ga[1]);
+            wa.y = pack_bf16x2(ga[2], ga[3]);
+            wb.x = pack_bf16x2(up[0], up[1]);
+            wb.y = pack_bf16x2(up[2], up[3]);
+            *reinterpret_cast<uint2*>(C2 + at) = wa;
+            *reinterpret_cast<uint2*>(C3 + at) = wb;
+          }
+        } else {   // EPI_SWIGLU_BWD
+          const size_t xa = grow * (size_t)ldx + col;
+          const uint2 ra = *reinterpret_cast<const uint2*>(X0 + xa);
+          const uint2 rb = *reinterpret_cast<const uint2*>(X1 + xa);
+          const float av[4] = {bf16_lo(ra.x), bf16_hi(ra.x), bf16_lo(ra.y), bf16_hi(ra.y)};
+          const float bv[4] = {bf16_lo(rb.x), bf16_hi(rb.x), bf16_lo(rb.y), bf16_hi(rb.y)};
+          float db[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float dh = acc[mb * NB + nb][4 * g + i];
+            v[i] = dh * bv[i] * silu_grad(av[i]);
+            db[i] = dh * silu(av[i]);
+          }
+          uint2 wdb;
+          wdb.x = pack_bf16x2(db[0], db[1]);
+          wdb.y = pack_bf16x2(db[2], db[3]);
+          *reinterpret_cast<uint2*>(C2 + at) = wdb;
         }
         uint2 w;
         w.x = pack_bf16x2(v[0], v[1]);
         w.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(crow + col) = w;
+        *reinterpret_cast<uint2*>(C + at) = w;
       }
     }
   }
@@ -457,25 +505,164 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(int E, const int32_t*
   }
 }
 
-template <int BN, bool SWIGLU>
+// ---------------------------------------------------------------------------
+// Weight gradients: per expert e, C_e[m][n] = sum over k in [koff[e], koff[e+1])
+// of A[m][k] * B[n][k], with A [M, ldk] and B [N, ldk] K-contiguous (the
+// transposed activations, each expert's rows padded to a multiple of 64 with
+// zeros, so every K range is whole 64-deep steps). Rows m < M1 go to
+// C0[e][m][n], rows m >= M1 to C1[e][m - M1][n] (gate and up gradients from one
+// launch). Same DMA main loop and fragment layout as ffn_bf16_dma_kernel; tiles
+// run expert by expert with m-tiles fastest, and each XCD gets a contiguous
+// run of tiles. An expert with no rows gets a zero gradient.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void wgrad_dma_kernel(int E, const int32_t* __restrict__ koff, int M, int M1,
+                                                        int N, int64_t ldk, const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ B, uint16_t* __restrict__ C0,
+                                                        uint16_t* __restrict__ C1) {
+  constexpr int BM = 256, BN = 256, NWM = 2, NWN = 4, NW = NWM * NWN;
+  constexpr int WM = BM / NWM, WN = BN / NWN;
+  constexpr int MB = WM / 32, NB = WN / 32, NACC = MB * NB;
+  constexpr int A_PW = BM / 8 / NW, B_PW = BN / 8 / NW;
+  constexpr int LOADS = A_PW + B_PW;
+  constexpr int STAGE = (BM + BN) * kRowB;
+  extern __shared__ __align__(16) char smem[];
+
+  const int MT = (M + BM - 1) / BM, NTn = (N + BN - 1) / BN;
+  const int tiles = E * MT * NTn;
+  const int x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
+  const int q = tiles / kXcds, rr = tiles % kXcds;
+  if (l >= q + (x < rr ? 1 : 0)) return;
+  const int tile = x * q + min(x, rr) + l;
+  const int e = tile / (MT * NTn), rem = tile % (MT * NTn);
+  const int m0 = (rem % MT) * BM, n0 = (rem / MT) * BN;
+  const int k0 = koff[e];
+  const int KT = (koff[e + 1] - k0) / kBK;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+
+  f32x16 acc[NACC];
+#pragma unroll
+  for (int i = 0; i < NACC; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  if (KT > 0) {
+    const char* Ab = reinterpret_cast<const char*>(A);
+    const char* Bb = reinterpret_cast<const char*>(B);
+    size_t a_off[A_PW], b_off[B_PW];
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) {
+      const int row = (wave * A_PW + i) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ dswz(row);
+      a_off[i] = (size_t)min(m0 + row, M - 1) * (size_t)ldk * 2 + (size_t)k0 * 2 + c * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i) {
+      const int row = (wave * B_PW + i) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ dswz(row);
+      b_off[i] = (size_t)min(n0 + row, N - 1) * (size_t)ldk * 2 + (size_t)k0 * 2 + c * 16;
+    }
+    auto dma = [&](int kt) {
+      const size_t ko = (size_t)(kt < KT ? kt : KT - 1) * kRowB;
+      char* st = smem + (kt & 1) * STAGE;
+#pragma unroll
+      for (int i = 0; i < A_PW; ++i) dma16(Ab + a_off[i] + ko, st + (wave * A_PW + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < B_PW; ++i) dma16(Bb + b_off[i] + ko, st + BM * kRowB + (wave * B_PW + i) * 1024);
+    };
+    bf16x8 fa[2][MB], fb[2][NB];
+    auto read_frags = [&](int stage, int sub, bf16x8(&A_)[MB], bf16x8(&B_)[NB]) {
+      const char* buf = smem + stage * STAGE;
+      const int chunk = 2 * sub + (lane >> 5);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        A_[mb] = __builtin_bit_cast(bf16x8, ld16(buf + daddr(wm * WM + mb * 32 + (lane & 31), chunk)));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        B_[nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(wn * WN + nb * 32 + (lane & 31), chunk)));
+    };
+    auto mma = [&](const bf16x8(&A_)[MB], const bf16x8(&B_)[NB]) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb * NB + nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B_[nb], A_[mb], acc[mb * NB + nb], 0, 0, 0);
+    };
+    dma(0);
+    dma(1);
+    wait_vmcnt<LOADS>();
+    __builtin_amdgcn_s_barrier();
+    read_frags(0, 0, fa[0], fb[0]);
+    for (int kt = 0; kt < KT - 1; ++kt) {
+      const int cur = kt & 1;
+      read_frags(cur, 1, fa[1], fb[1]);
+      mma(fa[0], fb[0]);
+      read_frags(cur, 2, fa[0], fb[0]);
+      mma(fa[1], fb[1]);
+      read_frags(cur, 3, fa[1], fb[1]);
+      mma(fa[0], fb[0]);
+      wait_lgkm0();
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      dma(kt + 2);
+      read_frags(cur ^ 1, 0, fa[0], fb[0]);
+      mma(fa[1], fb[1]);
+    }
+    {
+      const int cur = (KT - 1) & 1;
+      read_frags(cur, 1, fa[1], fb[1]);
+      mma(fa[0], fb[0]);
+      read_frags(cur, 2, fa[0], fb[0]);
+      mma(fa[1], fb[1]);
+      read_frags(cur, 3, fa[1], fb[1]);
+      mma(fa[0], fb[0]);
+      mma(fa[1], fb[1]);
+    }
+    wait_vmcnt<0>();
+  }
+  // lane holds row m (the A operand's row, lane & 31) and columns n = 8g + 4(lane >> 5) + 0..3
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = m0 + wm * WM + mb * 32 + (lane & 31);
+    if (m >= M) continue;
+    uint16_t* crow = m < M1 ? C0 + ((size_t)e * M1 + m) * (size_t)N
+                            : C1 + ((size_t)e * (M - M1) + (m - M1)) * (size_t)N;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
+        if (n >= N) continue;
+        uint2 w;
+        w.x = pack_bf16x2(acc[mb * NB + nb][4 * g], acc[mb * NB + nb][4 * g + 1]);
+        w.y = pack_bf16x2(acc[mb * NB + nb][4 * g + 2], acc[mb * NB + nb][4 * g + 3]);
+        *reinterpret_cast<uint2*>(crow + n) = w;
+      }
+  }
+}
+
+template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN)>
 hipError_t launch_dma(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A,
-                      const void* B0, const void* B1, void* C, float* partials, int P, hipStream_t s) {
+                      const void* B0, const void* B1, void* C, float* partials, int P, hipStream_t s,
+                      int ldc = 0, void* C2 = nullptr, void* C3 = nullptr, const void* X0 = nullptr,
+                      const void* X1 = nullptr, int ldx = 0) {
   constexpr int BM = 256;
   constexpr int BROWS = SWIGLU ? 2 * BN : BN;
   constexpr size_t kLds = 2 * (size_t)(BM + BROWS) * kRowB;
-  auto kern = &ffn_bf16_dma_kernel<BN, SWIGLU>;
+  auto kern = &ffn_bf16_dma_kernel<BN, SWIGLU, EPI>;
   // opt in to more than 64 KiB of dynamic LDS once per instantiation
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
   const int NT = (N + BN - 1) / BN;
   const int64_t tiles_ub = ((R_max + BM - 1) / BM + E) * NT;
-  const bool split = !SWIGLU && partials != nullptr && P > 0;
+  const bool split = EPI == EPI_PLAIN && partials != nullptr && P > 0 && (ldc == 0 || ldc == N);
   const int max_split = split ? kMaxSplit : 1;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid_blocks(tiles_ub, P, split)), dim3(512), kLds, s, E, offsets, N, K,
                      reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B0),
                      reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C), NT, P, max_split,
-                     partials);
+                     partials, ldc ? ldc : N, reinterpret_cast<uint16_t*>(C2), reinterpret_cast<uint16_t*>(C3),
+                     reinterpret_cast<const uint16_t*>(X0), reinterpret_cast<const uint16_t*>(X1), ldx);
   if (split)
     hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(P * (BM / 16))), dim3(256), 0, s, E, offsets, N, K, NT,
                        P, max_split, partials, reinterpret_cast<uint16_t*>(C));
@@ -543,6 +730,45 @@ hipError_t launch_ffn_bf16(int64_t R_max, int d, int E, int F, const void* x_per
   hipError_t err = launch_gemm_bf16(1, R_max, d, E, F, x_perm, offsets, wg, wu, h, nullptr, s);
   if (err != hipSuccess) return err;
   return launch_gemm_bf16(2, R_max, d, E, F, h, offsets, wd, nullptr, out, ws, s);
+}
+
+// ---------------------------------------------------------------------------
+// backward GEMMs (bf16)
+// ---------------------------------------------------------------------------
+
+hipError_t launch_bwd_recompute_gate_up(int64_t R_max, int d, int E, int F, const void* x_perm,
+                                        const int32_t* offsets, const void* wg, const void* wu, void* h,
+                                        void* a_st, void* b_st, hipStream_t s) {
+  return launch_dma<128, true, EPI_SWIGLU_AB>(R_max, E, offsets, F, d, x_perm, wg, wu, h, nullptr, 0, s, F, a_st,
+                                              b_st);
+}
+
+hipError_t launch_bwd_dh(int64_t R_max, int d, int E, int F, const void* d_o, const int32_t* offsets,
+                         const void* w_down_t, const void* a_st, const void* b_st, void* dab, hipStream_t s) {
+  // dab [R, 2F]: da in columns 0..F-1, db in F..2F-1
+  return launch_dma<256, false, EPI_SWIGLU_BWD>(R_max, E, offsets, F, d, d_o, w_down_t, nullptr, dab, nullptr, 0,
+                                                s, 2 * F, reinterpret_cast<uint16_t*>(dab) + F, nullptr, a_st,
+                                                b_st, F);
+}
+
+hipError_t launch_bwd_dx_perm(int64_t R_max, int d, int E, int F, const void* dab, const int32_t* offsets,
+                              const void* w_gu_t, void* dx_perm, void* ws, hipStream_t s) {
+  return launch_dma<256, false>(R_max, E, offsets, d, 2 * F, dab, w_gu_t, nullptr, dx_perm,
+                                reinterpret_cast<float*>(ws), ws ? compute_units() : 0, s);
+}
+
+hipError_t launch_wgrad(int E, const int32_t* koff, int M, int M1, int N, int64_t ldk, const void* A, const void* B,
+                        void* C0, void* C1, hipStream_t s) {
+  constexpr size_t kLds = 2 * (size_t)(256 + 256) * kRowB;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_dma_kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (attr != hipSuccess) return attr;
+  const int64_t tiles = (int64_t)E * ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL(wgrad_dma_kernel, dim3((unsigned)grid), dim3(512), kLds, s, E, koff, M, M1, N, ldk,
+                     reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B),
+                     reinterpret_cast<uint16_t*>(C0), reinterpret_cast<uint16_t*>(C1));
+  return hipGetLastError();
 }
 
 }  // namespace moe

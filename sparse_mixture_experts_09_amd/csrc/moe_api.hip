@@ -590,6 +590,139 @@ int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float 
   return hip_status(e);
 }
 
+// ---------------------------------------------------------------------------
+// backward pass
+// ---------------------------------------------------------------------------
+
+struct BwdLayout {
+  size_t idx, gate, slot_row, row_slot, counts, offsets, chunks, koff, dl, x_perm, a_st, b_st, h, o, d_o, dab,
+      dx_perm, w_down_t, w_gu_t, xp_t, d_o_t, h_t, dab_t, router_part, ffn, total;
+};
+
+static BwdLayout bwd_layout(int64_t T, int d, int E, int k, int64_t R_max, int F) {
+  BwdLayout L;
+  const int64_t Rp = moe::padded_rows_max(R_max, E);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round_up(bytes);
+    return at;
+  };
+  L.idx = take((size_t)T * k * 4);
+  L.gate = take((size_t)T * k * 4);
+  L.slot_row = take((size_t)T * k * 4);
+  L.row_slot = take((size_t)R_max * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.chunks = take((size_t)moe::permute_chunks(T) * E * 4);
+  L.koff = take((size_t)(E + 1) * 4);
+  L.dl = take((size_t)T * k * 4);
+  L.x_perm = take((size_t)R_max * d * 2);
+  L.a_st = take((size_t)R_max * F * 2);
+  L.b_st = take((size_t)R_max * F * 2);
+  L.h = take((size_t)R_max * F * 2);
+  L.o = take((size_t)R_max * d * 2);
+  L.d_o = take((size_t)R_max * d * 2);
+  L.dab = take((size_t)R_max * 2 * F * 2);
+  L.dx_perm = take((size_t)R_max * d * 2);
+  L.w_down_t = take((size_t)E * F * d * 2);
+  L.w_gu_t = take((size_t)E * d * 2 * F * 2);
+  L.xp_t = take((size_t)d * Rp * 2);
+  L.d_o_t = take((size_t)d * Rp * 2);
+  L.h_t = take((size_t)F * Rp * 2);
+  L.dab_t = take((size_t)2 * F * Rp * 2);
+  L.router_part = take(moe::router_wgrad_partial_bytes(T, d, E));
+  L.ffn = take(ffn_ws_bytes(R_max, E, MOE_BF16));
+  L.total = o;
+  return L;
+}
+
+int moe_backward_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+                                 size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  int st = check_scalars(T, d, E, k, cf, F, dt, true);
+  if (st != MOE_OK) return st;
+  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  *bytes = bwd_layout(T, d, E, k, rows_max_of(T, E, k, capacity_of(T, E, k, cf)), F).total;
+  return MOE_OK;
+}
+
+int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt, const void* x,
+                 const void* w_router, const void* w_gate, const void* w_up, const void* w_down, const void* dy,
+                 void* dx, void* dw_router, void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  int st = check_scalars(T, d, E, k, cf, F, dt, true);
+  if (st != MOE_OK) return st;
+  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !dy || !dx || !dw_router || !dw_gate || !dw_up ||
+      !dw_down || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(dy) || !aligned16(dx) || !aligned16(dw_router) || !aligned16(dw_gate) || !aligned16(dw_up) ||
+      !aligned16(dw_down) || !aligned16(ws))
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t cap = capacity_of(T, E, k, cf);
+  const int64_t R_max = rows_max_of(T, E, k, cap);
+  const int64_t Rp = moe::padded_rows_max(R_max, E);
+  if (Rp >= ((int64_t)1 << 31) || (int64_t)E * F * d >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  const BwdLayout L = bwd_layout(T, d, E, k, R_max, F);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const size_t wbytes = (size_t)E * F * d * 2;
+  const Range all[] = {{dx, (size_t)T * d * 2},    {dw_router, (size_t)E * d * 2}, {dw_gate, wbytes},
+                       {dw_up, wbytes},            {dw_down, wbytes},              {ws, L.total},
+                       {x, (size_t)T * d * 2},     {w_router, (size_t)E * d * 2},  {w_gate, wbytes},
+                       {w_up, wbytes},             {w_down, wbytes},               {dy, (size_t)T * d * 2}};
+  if (any_overlap(all, 6, 12)) return MOE_ERR_INVALID_ARG;
+
+  char* w = reinterpret_cast<char*>(ws);
+  auto I32 = [&](size_t at) { return reinterpret_cast<int32_t*>(w + at); };
+  int32_t* idx = I32(L.idx);
+  float* gate = reinterpret_cast<float*>(w + L.gate);
+  int32_t* srow = I32(L.slot_row);
+  int32_t* offsets = I32(L.offsets);
+  int32_t* koff = I32(L.koff);
+  float* dl = reinterpret_cast<float*>(w + L.dl);
+  void* ffn_ws = ffn_ws_bytes(R_max, E, MOE_BF16) ? w + L.ffn : nullptr;
+
+  // recompute: routing, permutation, a, b, h and o
+  hipError_t e = moe::launch_router(true, T, d, E, k, 0, x, w_router, idx, gate, nullptr, stream);
+  if (e == hipSuccess)
+    e = moe::launch_permute(true, T, d, E, k, cap, x, idx, nullptr, I32(L.counts), offsets, srow, I32(L.row_slot),
+                            w + L.x_perm, I32(L.chunks), stream);
+  if (e == hipSuccess)
+    e = moe::launch_bwd_recompute_gate_up(R_max, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w + L.h, w + L.a_st,
+                                          w + L.b_st, stream);
+  if (e == hipSuccess)
+    e = moe::launch_gemm_bf16(2, R_max, d, E, F, w + L.h, offsets, w_down, nullptr, w + L.o, ffn_ws, stream);
+  // combine and gate backward: d_o rows, dl
+  if (e == hipSuccess) e = moe::launch_gate_bwd(T, d, k, dy, w + L.o, srow, gate, w + L.d_o, dl, stream);
+  // data gradients through the experts
+  if (e == hipSuccess) e = moe::launch_batch_transpose(E, d, F, d, 0, w_down, w + L.w_down_t, stream);
+  if (e == hipSuccess)
+    e = moe::launch_bwd_dh(R_max, d, E, F, w + L.d_o, offsets, w + L.w_down_t, w + L.a_st, w + L.b_st, w + L.dab,
+                           stream);
+  if (e == hipSuccess) e = moe::launch_batch_transpose(E, F, d, 2 * F, 0, w_gate, w + L.w_gu_t, stream);
+  if (e == hipSuccess) e = moe::launch_batch_transpose(E, F, d, 2 * F, F, w_up, w + L.w_gu_t, stream);
+  if (e == hipSuccess)
+    e = moe::launch_bwd_dx_perm(R_max, d, E, F, w + L.dab, offsets, w + L.w_gu_t, w + L.dx_perm, ffn_ws, stream);
+  // weight gradients: transposed activations, expert rows padded to 64
+  if (e == hipSuccess) e = moe::launch_pad_offsets(E, offsets, koff, stream);
+  if (e == hipSuccess) e = moe::launch_seg_transpose(E, Rp, d, Rp, offsets, koff, w + L.x_perm, w + L.xp_t, stream);
+  if (e == hipSuccess) e = moe::launch_seg_transpose(E, Rp, 2 * F, Rp, offsets, koff, w + L.dab, w + L.dab_t, stream);
+  if (e == hipSuccess) e = moe::launch_seg_transpose(E, Rp, d, Rp, offsets, koff, w + L.d_o, w + L.d_o_t, stream);
+  if (e == hipSuccess) e = moe::launch_seg_transpose(E, Rp, F, Rp, offsets, koff, w + L.h, w + L.h_t, stream);
+  if (e == hipSuccess)
+    e = moe::launch_wgrad(E, koff, 2 * F, F, d, Rp, w + L.dab_t, w + L.xp_t, dw_gate, dw_up, stream);
+  if (e == hipSuccess) e = moe::launch_wgrad(E, koff, d, d, F, Rp, w + L.d_o_t, w + L.h_t, dw_down, nullptr, stream);
+  // router weight and input gradients
+  if (e == hipSuccess)
+    e = moe::launch_router_wgrad(T, d, E, k, x, idx, dl, reinterpret_cast<float*>(w + L.router_part), dw_router,
+                                 stream);
+  if (e == hipSuccess) e = moe::launch_dx_final(T, d, k, dl, idx, w_router, w + L.dx_perm, srow, dx, stream);
+  return hip_status(e);
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -65,6 +65,10 @@ _SIGS = {
                                                                  ctypes.c_int, ctypes.POINTER(_sz)]),
     "moe_forward_expert_choice": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp,
                                                  _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_backward_workspace_bytes": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int,
+                                                    ctypes.POINTER(_sz)]),
+    "moe_backward": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -400,3 +404,24 @@ def moe_forward_expert_choice(x, w_router, w_gate, w_up, w_down, k: int, cf: flo
                                          ws.numel(), _stream(stream))
     _check("moe_forward_expert_choice", st)
     return y
+
+
+# ---------------------------------------------------------------------------
+# backward pass
+# ---------------------------------------------------------------------------
+
+def moe_backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, ws=None, stream=None):
+    """Gradients of <dy, y> for the token-choice layer (bf16). Returns dict(dx,
+    dw_router, dw_gate, dw_up, dw_down), shaped like x and the weights."""
+    T, d = x.shape
+    E, F, _ = w_gate.shape
+    out = dict(dx=torch.empty_like(x), dw_router=torch.empty_like(w_router), dw_gate=torch.empty_like(w_gate),
+               dw_up=torch.empty_like(w_up), dw_down=torch.empty_like(w_down))
+    if ws is None:
+        n = _size_query("moe_backward_workspace_bytes", T, d, E, k, cf, F, _dt(x))
+        ws = torch.empty(max(n, 16), dtype=torch.uint8, device=x.device)
+    st = lib().moe_backward(T, d, E, k, cf, F, _dt(x), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
+                            _ptr(w_down), _ptr(dy), _ptr(out["dx"]), _ptr(out["dw_router"]), _ptr(out["dw_gate"]),
+                            _ptr(out["dw_up"]), _ptr(out["dw_down"]), _ptr(ws), ws.numel(), _stream(stream))
+    _check("moe_backward", st)
+    return out

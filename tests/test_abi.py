@@ -27,7 +27,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 25
+    assert len(names) == 27
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -89,7 +89,8 @@ def _no_fake_pointers_on_a_gpu(request):
     if "fake" in request.node.name or request.node.name.startswith(("test_forward_validation",
                                                                    "test_stage_entry_points",
                                                                    "test_gating_and_priority",
-                                                                   "test_expert_choice_entry")):
+                                                                   "test_expert_choice_entry",
+                                                                   "test_backward_entry")):
         if torch.cuda.device_count() > 0:
             pytest.skip("fake device pointers are only passed where no GPU is visible")
 
@@ -231,3 +232,27 @@ def test_expert_choice_entry_points_validate():
     assert L.moe_forward_expert_choice(*a) == INV
     a = list(f); a[0] = 0
     assert L.moe_forward_expert_choice(*a) == OK
+
+
+def test_backward_entry_points_validate():
+    L = moe.lib()
+    b = ctypes.c_size_t()
+    assert L.moe_backward_workspace_bytes(64, 64, 4, 2, 1.0, 128, F32, ctypes.byref(b)) == UNS
+    assert L.moe_backward_workspace_bytes(64, 64, 4, 2, 1.0, 128, BF16, ctypes.byref(b)) == OK
+    need = b.value
+    bw = [64, 64, 4, 2, 1.0, 128, BF16, A[0], A[1], A[2], A[3], A[4], A[5], A[6], A[7], A[8], A[9], A[10], A[11],
+          1 << 40, None]
+    a = list(bw); a[6] = F32
+    assert L.moe_backward(*a) == UNS
+    a = list(bw); a[12] = None                  # dy
+    assert L.moe_backward(*a) == INV
+    a = list(bw); a[19] = need - 1
+    assert L.moe_backward(*a) == WS
+    a = list(bw); a[13] = A[0]                  # dx overlapping x
+    assert L.moe_backward(*a) == INV
+    a = list(bw); a[16] = A[10]                 # dw_up overlapping dw_down
+    assert L.moe_backward(*a) == INV
+    a = list(bw); a[5] = 72                     # F not a multiple of 64
+    assert L.moe_backward(*a) == UNS
+    a = list(bw); a[0] = 0
+    assert L.moe_backward(*a) == OK

@@ -1,0 +1,106 @@
+"""GPU parity for the backward pass of the token-choice layer (bf16) against
+the CPU oracle's chain-rule gradients (same storage rounding points), through
+the C interface: dx, dW_g, dW_gate, dW_up and dW_down."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import sparse_mixture_experts_09_amd as moe
+from oracle import moe_oracle as orc
+from parity import compare_routing, host
+from test_gpu_parity import SMALL, case_id, dev, device_inputs, workload
+
+pytestmark = pytest.mark.gpu
+
+BF16_CASES = [c for c in SMALL if c[6] == "bf16"]
+
+
+def make_dy(w, seed):
+    rng = np.random.default_rng(1000 + seed)
+    return torch.from_numpy(rng.standard_normal((w.T, w.d)).astype(np.float32)).to(torch.bfloat16)
+
+
+def check_grad(name, got, ref):
+    """Row-wise: max |err| / max |ref| <= 2e-2 per row of the last dimension,
+    and mean |err| <= 1e-2 * mean |ref| over the tensor; rows whose reference
+    is exactly zero must be zero."""
+    g = np.asarray(got, np.float64).reshape(-1, got.shape[-1])
+    r = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    assert np.all(np.isfinite(g)), name
+    err = np.abs(g - r)
+    rmax = np.abs(r).max(axis=1)
+    zero = rmax == 0
+    assert np.all(g[zero] == 0.0), f"{name}: rows with a zero reference are not zero"
+    rel = (err.max(axis=1)[~zero] / rmax[~zero]).max(initial=0.0)
+    mae = err.mean() / max(np.abs(r).mean(), 1e-30)
+    assert rel <= 2e-2, f"{name}: row max-rel {rel:.3g}"
+    assert mae <= 1e-2, f"{name}: relative MAE {mae:.3g}"
+    return rel, mae
+
+
+def run_and_check(w, a, g, dy, seed_label):
+    ref = orc.backward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy.double().numpy(), w.k, w.cf,
+                       "bf16")
+    fw = ref["forward"]
+    # routing decisions must match (no near ties in these seeds)
+    idx, gate, _ = moe.moe_route(g["x"], g["w_router"], w.k)
+    torch.cuda.synchronize()
+    assert compare_routing(host(idx), host(gate), fw) == 0
+    out = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dev(dy), w.k, w.cf)
+    torch.cuda.synchronize()
+    res = {}
+    for key, rk in [("dx", "dx"), ("dw_router", "dW_g"), ("dw_gate", "dW_gate"), ("dw_up", "dW_up"),
+                    ("dw_down", "dW_down")]:
+        res[key] = check_grad(key, host(out[key]), ref[rk])
+    print(f"{seed_label}: " + ", ".join(f"{k_} rel {v[0]:.3g} mae {v[1]:.3g}" for k_, v in res.items()))
+    return out
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=case_id)
+def test_backward(case):
+    w, a = workload(case)
+    g = device_inputs(case)
+    run_and_check(w, a, g, make_dy(w, case[7]), case_id(case))
+
+
+def test_backward_mid_size():
+    """Several 256-row tiles per expert, drops, K ranges of many 64-deep steps."""
+    w, a = mi.random_small(2048, 1024, 8, 2, 2048, 1.0, "bf16", 70)
+    g = {k_: dev(v) for k_, v in a.items() if v is not None}
+    run_and_check(w, a, g, make_dy(w, 70), "T2048_d1024_E8_k2_F2048_cf1.0")
+
+
+def test_backward_empty_expert_has_zero_weight_gradients():
+    """Every token has a large first feature and W_g[e, 0] = e, so the top-2 is
+    always experts 3 and 2: experts 0 and 1 get no rows and their weight
+    gradients must be exactly zero."""
+    w, a = mi.random_small(256, 128, 4, 2, 128, 0.0, "bf16", 71)
+    a = dict(a)
+    x = a["x"].float() * 0.1
+    x[:, 0] = 4.0
+    wr = a["w_router"].float() * 0.01
+    wr[:, 0] = torch.arange(4, dtype=torch.float32)
+    a["x"], a["w_router"] = x.to(torch.bfloat16), wr.to(torch.bfloat16)
+    fw = orc.forward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], w.k, w.cf, "bf16")
+    assert fw["demand"][0] == 0 and fw["demand"][1] == 0
+    g = {k_: dev(v) for k_, v in a.items() if v is not None}
+    out = run_and_check(w, a, g, make_dy(w, 71), "experts 0 and 1 unused")
+    for e in (0, 1):
+        assert torch.all(out["dw_gate"][e] == 0) and torch.all(out["dw_up"][e] == 0)
+        assert torch.all(out["dw_down"][e] == 0)
+    assert torch.any(out["dw_gate"][3] != 0)
+
+
+def test_backward_is_deterministic():
+    case = BF16_CASES[0]
+    w, _ = workload(case)
+    g = device_inputs(case)
+    dy = dev(make_dy(w, 1))
+    first = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, w.k, w.cf)
+    for _ in range(3):
+        again = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, w.k, w.cf)
+        for key in first:
+            assert torch.equal(first[key], again[key]), key
