@@ -19,6 +19,8 @@ Priority Routing); the step is then moe_forward_ex, and the permute stage
 includes the priority sort. --routing expert_choice times
 moe_forward_expert_choice instead (each expert takes C = capacity tokens);
 its stages are route (scores and selection), gather, ffn and combine.
+--pass backward times moe_backward (gradients of <dy, y> for x and all
+weights, with the forward recomputed inside) instead of the forward.
 Prints one JSON line on stdout (progress goes to stderr).
 """
 import argparse
@@ -100,6 +102,7 @@ def main():
     ap.add_argument("--gating", default="topk_softmax", choices=["topk_softmax", "softmax_topk", "softmax_topk_scaled"])
     ap.add_argument("--fill", default="token", choices=["token", "priority"])
     ap.add_argument("--routing", default="token_choice", choices=["token_choice", "expert_choice"])
+    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"])
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run K device-to-device copies of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -139,6 +142,9 @@ def main():
     stream = torch.cuda.current_stream()
     if args.routing == "expert_choice":
         print(json.dumps(bench_expert_choice(args, w, a, g, moe, stream)), flush=True)
+        return
+    if args.which == "backward":
+        print(json.dumps(bench_backward(args, w, a, g, moe, stream)), flush=True)
         return
 
     # ---- headline: K x moe_forward ----
@@ -262,6 +268,49 @@ def main():
         "stage_path_equals_forward": same_as_forward,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_backward(args, w, a, g, moe, stream):
+    """Backward pass: K timed moe_backward steps (forward recomputed inside)."""
+    import numpy as np
+    import torch
+
+    T, d, E, k, F, cf = w.T, w.d, w.E, w.k, w.F, w.cf
+    K, W = args.steps, args.warmup
+    dy = torch.from_numpy(np.random.default_rng(0).standard_normal((T, d)).astype(np.float32)).to(g["x"].dtype).cuda()
+    n = moe._size_query("moe_backward_workspace_bytes", T, d, E, k, cf, F, moe._dt(g["x"]))
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
+    out = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, k, cf, ws=ws)
+
+    def step():
+        moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, k, cf, ws=ws)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    idx, gate, _ = moe.moe_route(g["x"], g["w_router"], k)
+    perm = moe.moe_permute(g["x"], idx, E, cf)
+    R = int(perm["expert_offsets"][-1].item())
+    flops = 18 * d * F * R + 4 * T * d * E
+    peak = PEAK["bf16_tflops"]
+    achieved = flops / (ms_step * 1e-3) / 1e12
+    log(f"moe_backward: {ms_step:.3f} ms/step, {achieved:.0f} TFLOP/s over the layer ({R} rows), workspace {n / 2**30:.2f} GiB")
+    return {
+        "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "pass": "backward", "T": T, "d": d, "E": E, "k": k, "F": F, "cf": cf,
+                   "kept_rows": R, "workspace_bytes": n, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "whole backward (recompute + data and weight gradient GEMMs)",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "alg_flops_per_launch": flops, "avg_launch_us": ms_step * 1e3},
+        "cpu_baseline": None,
+    }
 
 
 def bench_expert_choice(args, w, a, g, moe, stream):
