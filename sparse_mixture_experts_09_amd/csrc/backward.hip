@@ -36,13 +36,46 @@ __global__ void pad_offsets_kernel(int E, const int32_t* __restrict__ offsets, i
   koff[E] = run;
 }
 
+// 64 x 64 bf16 tile transposes. A thread moves 16-byte pieces: it loads 8
+// consecutive columns of an input row into LDS with one 16-byte write, and
+// gathers 8 consecutive rows of one column for one 16-byte output store.
+constexpr int kTP = 72;   // LDS row pitch in elements (64 + 8 keeps 16-byte alignment)
+
+// in_row(i) = pointer to input row i of the tile or nullptr (zero row);
+// out_row(j) = pointer to output row j of the tile (64 elements) or nullptr.
+template <typename InRow, typename OutRow>
+__device__ __forceinline__ void transpose_tile64(InRow in_row, int in_cols_valid, OutRow out_row,
+                                                 uint16_t (*tile)[kTP]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int i = pass * 32 + (t >> 3), ch = t & 7;
+    const uint16_t* src = in_row(i);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (src != nullptr && ch * 8 < in_cols_valid) v = ld16(src + ch * 8);
+    *reinterpret_cast<u32x4*>(&tile[i][ch * 8]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int j = pass * 32 + (t >> 3), ch = t & 7;
+    uint16_t* dst = out_row(j);
+    if (dst == nullptr) continue;
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = (uint32_t)tile[ch * 8 + 2 * q][j] | ((uint32_t)tile[ch * 8 + 2 * q + 1][j] << 16);
+    st16(dst + ch * 8, v);
+  }
+}
+
 // Block (cb, pb): 64 columns c0 = 64 cb of the input and 64 padded positions
 // p0 = 64 pb of the output. A 64-aligned block of positions lies inside one
-// expert, since every expert's range is a multiple of 64.
+// expert, since every expert's range is a multiple of 64. C is a multiple of 8.
 __global__ __launch_bounds__(256) void seg_transpose_kernel(int E, int C, int64_t ldo, const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ koff,
                                                             const uint16_t* __restrict__ in, uint16_t* __restrict__ out) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ __align__(16) uint16_t tile[64][kTP];
   const int c0 = blockIdx.x * 64;
   const int p0 = blockIdx.y * 64;
   if (p0 >= koff[E]) return;
@@ -50,38 +83,23 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(int E, int C, int64_
   while (e + 1 < E && koff[e + 1] <= p0) ++e;
   const int cnt = offsets[e + 1] - offsets[e];
   const int i0 = p0 - koff[e];                 // first row of the block inside expert e
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {           // read: rows of the input, coalesced along columns
-    const int c = c0 + tx;
-    uint16_t v = 0;
-    if (i0 + i < cnt && c < C) v = in[(size_t)(offsets[e] + i0 + i) * C + c];
-    tile[i][tx] = v;
-  }
-  __syncthreads();
-  for (int j = ty; j < 64; j += 4) {           // write: rows of the output, coalesced along positions
-    const int c = c0 + j;
-    if (c < C) out[(size_t)c * ldo + p0 + tx] = tile[tx][j];
-  }
+  const int64_t base = offsets[e] + i0;
+  transpose_tile64(
+      [&](int i) -> const uint16_t* { return i0 + i < cnt ? in + (size_t)(base + i) * C + c0 : nullptr; },
+      C - c0, [&](int j) -> uint16_t* { return c0 + j < C ? out + (size_t)(c0 + j) * ldo + p0 : nullptr; }, tile);
 }
 
+// [B][rows][cols] -> [B][cols][ldo] at column col_off; rows and cols are multiples of 64.
 __global__ __launch_bounds__(256) void batch_transpose_kernel(int rows, int cols, int64_t ldo, int col_off,
                                                               const uint16_t* __restrict__ in,
                                                               uint16_t* __restrict__ out) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ __align__(16) uint16_t tile[64][kTP];
   const int b = blockIdx.z;
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
   const uint16_t* ib = in + (size_t)b * rows * cols;
   uint16_t* ob = out + (size_t)b * cols * ldo;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < rows && c < cols) ? ib[(size_t)r * cols + c] : (uint16_t)0;
-  }
-  __syncthreads();
-  for (int j = ty; j < 64; j += 4) {
-    const int c = c0 + j, r = r0 + tx;
-    if (c < cols && r < rows) ob[(size_t)c * ldo + col_off + r] = tile[tx][j];
-  }
+  transpose_tile64([&](int i) -> const uint16_t* { return ib + (size_t)(r0 + i) * cols + c0; }, 64,
+                   [&](int j) -> uint16_t* { return ob + (size_t)(c0 + j) * ldo + col_off + r0; }, tile);
 }
 
 // One wavefront per token; lane l covers the 8-element pieces l, l + 64, ... of a row.
