@@ -506,6 +506,219 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(int E, const int32_t*
 }
 
 // ---------------------------------------------------------------------------
+// Forward main path: the same 256 x BN tiles, wavefront split (2 x 4), LDS
+// layout and epilogues as ffn_bf16_dma_kernel, with register-staged loads:
+// each thread fetches four 16-byte pieces of each operand per K step with
+// buffer loads (whole 128-byte rows across 8 lanes; the descriptors' record
+// counts end at the expert's last row and at the weight's last row, so
+// loads past them return zeros), and writes them to the other LDS stage
+// with the bank swizzle applied on the LDS side. One K step:
+//   read fragments of substeps 0 and 1; substep 0 MFMAs interleaved with the
+//   LDS writes of tile kt+1 (loaded one step earlier); substep 1 MFMAs
+//   interleaved with the buffer loads of tile kt+2; substeps 2 and 3 with
+//   their fragment reads; one barrier.
+// The interleave is pinned with sched_group_barrier so the matrix pipe has
+// work while the stores and loads issue; the last K step is peeled and the
+// body has no branches (the load past the last tile reloads the last one).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+template <int BN, bool SWIGLU>
+__global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
+    int E, const int32_t* __restrict__ offsets, int N, int K, const uint16_t* __restrict__ A,
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT,
+    int P, int max_split, float* __restrict__ partials) {
+  constexpr int BM = 256, NWM = 2, NWN = 4, NT_ = 512;
+  constexpr int BROWS = SWIGLU ? 2 * BN : BN;
+  static_assert(BROWS == 256, "both operands are 256-row tiles");
+  constexpr int WM = BM / NWM, WN = BN / NWN;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int NBF = (SWIGLU ? 2 : 1) * NB;
+  constexpr int NACC = MB * NBF;
+  constexpr int PT = 2048 / NT_;                 // 16-byte pieces per thread per operand per K step
+  constexpr int RSTEP = NT_ / 8;                 // rows between a thread's pieces
+  constexpr int STAGE = (BM + BROWS) * kRowB;
+  constexpr int NM = MB * NBF, NR = MB + NBF;    // MFMAs and fragment reads per substep
+  extern __shared__ __align__(16) char smem[];
+
+  const int KTall = K / kBK;
+  WorkItem w;
+  if (!find_item(offsets, E, BM, NT, P, max_split, KTall, blockIdx.x, w)) return;
+  const TileCoord tc = w.tc;
+  int kb = 0, KT = KTall;
+  if (w.split >= 0) {
+    const int ns = make_plan(offsets, E, BM, NT, P, max_split, KTall).s;
+    kb = w.slice * KTall / ns;
+    KT = (w.slice + 1) * KTall / ns - kb;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int n0 = tc.n_tile * BN;
+
+  const size_t rowb = (size_t)K * 2;
+  const int a_rows = min(BM, tc.seg_rows - tc.m0);
+  const int b_rows = min(BN, N - n0);
+  const auto ra = make_rsrc(A + (size_t)(tc.seg_start + tc.m0) * K, (uint32_t)(a_rows * rowb));
+  const size_t wrow0 = (size_t)tc.e * N + n0;
+  const auto rb0 = make_rsrc(B0 + wrow0 * K, (uint32_t)(b_rows * rowb));
+  const auto rb1 = make_rsrc((SWIGLU ? B1 : B0) + wrow0 * K, (uint32_t)(b_rows * rowb));
+  const int row0 = tid >> 3, ch = tid & 7;
+  const uint32_t voff = (uint32_t)(row0 * rowb) + ch * 16 + (uint32_t)kb * kRowB;
+  const uint32_t rstep = (uint32_t)(RSTEP * rowb);
+  const int wofs = row0 * kRowB + ((ch ^ dswz(row0)) << 4);   // RSTEP is a multiple of 16: same swizzle
+
+  u32x4 stg[2 * PT];
+  auto gload = [&](int kt) {
+    const uint32_t ko = (uint32_t)(kt < KT ? kt : KT - 1) * kRowB;
+#pragma unroll
+    for (int i = 0; i < PT; ++i) stg[i] = bload16(ra, voff + i * rstep + ko);
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      // weight rows 0 .. BROWS-1: plain tiles read B0; SwiGLU tiles read BN gate rows, then BN up rows
+      const bool up = SWIGLU && i * RSTEP >= BN;
+      stg[PT + i] = bload16(up ? rb1 : rb0, voff + (up ? i * rstep - BN * (uint32_t)rowb : i * rstep) + ko);
+    }
+  };
+  auto swrite = [&](int stage) {
+    char* b = smem + stage * STAGE + wofs;
+#pragma unroll
+    for (int i = 0; i < PT; ++i) st16(b + i * RSTEP * kRowB, stg[i]);
+#pragma unroll
+    for (int i = 0; i < PT; ++i) st16(b + BM * kRowB + i * RSTEP * kRowB, stg[PT + i]);
+  };
+
+  f32x16 acc[NACC];
+#pragma unroll
+  for (int i = 0; i < NACC; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  bf16x8 fa[2][MB], fb[2][NBF];
+  auto read_frags = [&](int stage, int sub, bf16x8(&A_)[MB], bf16x8(&B_)[NBF]) {
+    const char* buf = smem + stage * STAGE;
+    const int chunk = 2 * sub + (lane >> 5);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      A_[mb] = __builtin_bit_cast(bf16x8, ld16(buf + daddr(wm * WM + mb * 32 + (lane & 31), chunk)));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int row = wn * WN + nb * 32 + (lane & 31);
+      B_[nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(row, chunk)));
+      if (SWIGLU) B_[NB + nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(BN + row, chunk)));
+    }
+  };
+  auto mma = [&](const bf16x8(&A_)[MB], const bf16x8(&B_)[NBF]) {
+#pragma unroll
+    for (int nb = 0; nb < NBF; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int a = (nb / NB) * MB * NB + mb * NB + (nb % NB);
+        acc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B_[nb], A_[mb], acc[a], 0, 0, 0);
+      }
+  };
+
+  gload(0);
+  wait_vmcnt<0>();
+  swrite(0);
+  gload(1);
+  wait_lgkm0();
+  __syncthreads();
+  for (int kt = 0; kt < KT - 1; ++kt) {
+    const int cur = kt & 1;
+    read_frags(cur, 0, fa[0], fb[0]);
+    read_frags(cur, 1, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    wait_vmcnt<0>();               // tile kt+1 is in the staging registers
+    swrite(cur ^ 1);
+    gload(kt + 2);
+    read_frags(cur, 2, fa[0], fb[0]);
+    mma(fa[1], fb[1]);
+    read_frags(cur, 3, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    mma(fa[1], fb[1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);   // fragments of substeps 0 and 1
+#pragma unroll
+    for (int i = 0; i < 2 * PT; ++i) {                          // substep 0 MFMAs with the LDS writes
+      __builtin_amdgcn_sched_group_barrier(0x008, NM / (2 * PT) > 0 ? NM / (2 * PT) : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * PT; ++i) {                          // substep 1 MFMAs with the buffer loads
+      __builtin_amdgcn_sched_group_barrier(0x008, NM / (2 * PT) > 0 ? NM / (2 * PT) : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * NR; ++i) {                          // substeps 2, 3 fragments among MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 64, 0);
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+  }
+  {
+    const int cur = (KT - 1) & 1;
+    read_frags(cur, 0, fa[0], fb[0]);
+    read_frags(cur, 1, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    read_frags(cur, 2, fa[0], fb[0]);
+    mma(fa[1], fb[1]);
+    read_frags(cur, 3, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    mma(fa[1], fb[1]);
+  }
+  wait_vmcnt<0>();   // the reload past the last tile
+
+  if (!SWIGLU && w.split >= 0) {
+    const int ns = make_plan(offsets, E, BM, NT, P, max_split, KTall).s;
+    float* pt = partials + (size_t)(w.split * ns + w.slice) * BM * BN;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = wm * WM + mb * 32 + (lane & 31);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[mb * NB + nb][4 * g + i];
+          *reinterpret_cast<f32x4*>(pt + (size_t)row * BN + col) = v;
+        }
+    }
+    return;
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int rloc = tc.m0 + wm * WM + mb * 32 + (lane & 31);
+    if (rloc >= tc.seg_rows) continue;
+    uint16_t* crow = C + (size_t)(tc.seg_start + rloc) * (size_t)N;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = n0 + wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
+        if (col >= N) continue;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = acc[mb * NB + nb][4 * g + i];
+          v[i] = SWIGLU ? silu(a) * acc[MB * NB + mb * NB + nb][4 * g + i] : a;
+        }
+        uint2 o;
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(crow + col) = o;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Weight gradients: per expert e, C_e[m][n] = sum over k in [koff[e], koff[e+1])
 // of A[m][k] * B[n][k], with A [M, ldk] and B [N, ldk] K-contiguous (the
 // transposed activations, each expert's rows padded to a multiple of 64 with
@@ -641,6 +854,29 @@ __global__ __launch_bounds__(512) void wgrad_dma_kernel(int E, const int32_t* __
   }
 }
 
+template <int BN, bool SWIGLU>
+hipError_t launch_reg(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A, const void* B0,
+                      const void* B1, void* C, float* partials, int P, hipStream_t s) {
+  constexpr int BM = 256;
+  constexpr size_t kLds = 2 * (size_t)(BM + 256) * kRowB;
+  auto kern = &ffn_bf16_reg_kernel<BN, SWIGLU>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (attr != hipSuccess) return attr;
+  const int NT = (N + BN - 1) / BN;
+  const int64_t tiles_ub = ((R_max + BM - 1) / BM + E) * NT;
+  const bool split = !SWIGLU && partials != nullptr && P > 0;
+  const int max_split = split ? kMaxSplit : 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid_blocks(tiles_ub, P, split)), dim3(512), kLds, s, E, offsets, N, K,
+                     reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B0),
+                     reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C), NT, P, max_split,
+                     partials);
+  if (split)
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(P * (BM / 16))), dim3(256), 0, s, E, offsets, N, K, NT,
+                       P, max_split, partials, reinterpret_cast<uint16_t*>(C));
+  return hipGetLastError();
+}
+
 template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN)>
 hipError_t launch_dma(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A,
                       const void* B0, const void* B1, void* C, float* partials, int P, hipStream_t s,
@@ -716,8 +952,8 @@ hipError_t launch_gemm_bf16(int which, int64_t R_max, int d, int E, int F, const
   // 256-row DMA tiles once experts average at least 128 rows; below that the
   // 128-row tiles waste less work on the ragged last tile of each expert.
   if (ffn_bf16_big_tiles(R_max, E)) {
-    if (which == 1) return launch_dma<128, true>(R_max, E, offsets, F, d, in, w0, w1, out, nullptr, 0, s);
-    return launch_dma<256, false>(R_max, E, offsets, d, F, in, w0, nullptr, out, reinterpret_cast<float*>(ws),
+    if (which == 1) return launch_reg<128, true>(R_max, E, offsets, F, d, in, w0, w1, out, nullptr, 0, s);
+    return launch_reg<256, false>(R_max, E, offsets, d, F, in, w0, nullptr, out, reinterpret_cast<float*>(ws),
                                   ws ? compute_units() : 0, s);
   }
   if (which == 1) return launch_gemm<128, 64, true>(R_max, E, offsets, F, d, in, w0, w1, out, s);
