@@ -719,6 +719,166 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Few rows per expert (decode): the grouped GEMMs read every weight once and
+// the token rows are few, so the time is the weight stream from HBM.
+//
+// A block computes one 32-row weight tile (GEMM1: 16 gate rows then the 16
+// up rows of the same features; GEMM2: 32 rows of W_down) against all rows
+// of one expert (MT tiles of 32; rows past the expert's last read as zeros).
+// Its NW wavefronts split the 64-deep K steps round-robin and never wait for
+// each other inside the K loop: each wavefront streams its steps through D
+// stages of its own LDS with buffer -> LDS DMA (8 lanes fetch one whole
+// 128-byte row piece, so every load instruction covers 8 full lines) and
+// reads the MFMA fragments back with the bank swizzle of the tiled kernels.
+// At the end the partial tiles are added in wavefront order through LDS.
+// The DMA past the last K step uses offsets above every record count, so it
+// fetches nothing and the wait counts stay the same on every step.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, char* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voff, 0, 0, 0);
+#endif
+}
+
+template <bool SWIGLU, int MT, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void ffn_bf16_skinny_kernel(int E, const int32_t* __restrict__ offsets, int N,
+                                                                  int K, const uint16_t* __restrict__ A,
+                                                                  const uint16_t* __restrict__ B0,
+                                                                  const uint16_t* __restrict__ B1,
+                                                                  uint16_t* __restrict__ C) {
+  constexpr int TF = SWIGLU ? 16 : 32;          // output features per block
+  constexpr int ROWS = 32 * (1 + MT);           // LDS rows per stage: weight tile, then token rows
+  constexpr int L = ROWS / 8;                   // DMA instructions per stage
+  constexpr int STAGE = ROWS * kRowB;
+  extern __shared__ __align__(16) char lds[];   // NW * D * STAGE
+  const int NTb = N / TF;
+  const int e = blockIdx.x / NTb, f0 = (blockIdx.x % NTb) * TF;
+  const int lo = offsets[e], cnt = offsets[e + 1] - lo;
+  if (cnt <= 0) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 31, g = lane >> 5;
+  const uint32_t rowb = (uint32_t)K * 2;
+  char* my = lds + wave * D * STAGE;
+  const auto rw0 = make_rsrc(B0 + (size_t)e * N * K, (uint32_t)N * rowb);
+  const auto rw1 = make_rsrc((SWIGLU ? B1 : B0) + (size_t)e * N * K, (uint32_t)N * rowb);
+  const auto rx = make_rsrc(A + (size_t)lo * K, (uint32_t)min(cnt, 32 * MT) * rowb);
+  // DMA instruction i fills LDS rows 8i..8i+7 of a stage; lane l brings the
+  // 16-byte piece that belongs at slot l % 8 of row 8i + l / 8.
+  const int lr = lane >> 3, lc = lane & 7;
+  uint32_t src[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int row = 8 * i + lr;
+    const uint32_t c = (uint32_t)(lc ^ dswz(row));
+    const int srow = i < 4 ? (SWIGLU ? f0 + 8 * (i & 1) + lr : f0 + row) : row - 32;
+    src[i] = (uint32_t)srow * rowb + c * 16;
+  }
+  const int KT = K / kBK;
+  auto issue = [&](int stage, int kt) {
+    char* st = my + stage * STAGE;
+    const uint32_t ko = kt < KT ? (uint32_t)kt * kRowB : 0x80000000u;
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      bdma16(i < 4 ? ((SWIGLU && i >= 2) ? rw1 : rw0) : rx, src[i] + ko, st + i * 1024);
+  };
+  f32x16 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[m][q] = 0.f;
+  const int S = wave < KT ? (KT - wave + NW - 1) / NW : 0;   // K steps of this wavefront
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) issue(j, wave + NW * j);
+  int rs = 0, ws = D - 1;
+  for (int j = 0; j < S; ++j) {
+    issue(ws, wave + NW * (j + D - 1));   // into the stage read one step ago
+    wait_vmcnt<(D - 1) * L>();            // stage rs has landed
+    const char* st = my + rs * STAGE;
+    bf16x8 wf[4], xf[4][MT];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = 2 * s + g;
+      wf[s] = __builtin_bit_cast(bf16x8, ld16(st + daddr(r, c)));
+#pragma unroll
+      for (int m = 0; m < MT; ++m) xf[s][m] = __builtin_bit_cast(bf16x8, ld16(st + daddr(32 * (1 + m) + r, c)));
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], xf[s][m], acc[m], 0, 0, 0);
+    wait_lgkm0();                         // reads of stage rs done before it is refilled
+    rs = rs + 1 == D ? 0 : rs + 1;
+    ws = ws + 1 == D ? 0 : ws + 1;
+  }
+  wait_vmcnt<0>();   // the empty DMAs past the end, before the stage memory is reused
+  float* red = reinterpret_cast<float*>(my);
+  if (wave > 0) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) red[(m * 16 + q) * 64 + lane] = acc[m][q];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w2 = 1; w2 < NW; ++w2) {
+    const float* rw = reinterpret_cast<const float*>(lds + w2 * D * STAGE);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[m][q] += rw[(m * 16 + q) * 64 + lane];
+  }
+  // lane: row m*32 + r; GEMM1 features f0 + 8 q4 + 4 g + i from gate acc[4 q4 + i]
+  // and up acc[8 + 4 q4 + i] (tile rows 16.. are the up rows); GEMM2 features
+  // f0 + 8 q4 + 4 g + i from acc[4 q4 + i]
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int row = m * 32 + r;
+    if (row >= cnt) continue;
+    uint16_t* crow = C + (size_t)(lo + row) * N;
+#pragma unroll
+    for (int q4 = 0; q4 < (SWIGLU ? 2 : 4); ++q4) {
+      const int col = f0 + 8 * q4 + 4 * g;
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[i] = SWIGLU ? silu(acc[m][4 * q4 + i]) * acc[m][8 + 4 * q4 + i] : acc[m][4 * q4 + i];
+      uint2 o;
+      o.x = pack_bf16x2(v[0], v[1]);
+      o.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(crow + col) = o;
+    }
+  }
+}
+
+template <bool SWIGLU, int MT, int D, int NW>
+hipError_t launch_skinny_cfg(int E, const int32_t* offsets, int N, int K, const void* A, const void* B0,
+                             const void* B1, void* C, hipStream_t s) {
+  constexpr int kLds = NW * D * 32 * (1 + MT) * kRowB;
+  static_assert(kLds <= 160 * 1024, "LDS per block");
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_skinny_kernel<SWIGLU, MT, D, NW>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (attr != hipSuccess) return attr;
+  const int64_t blocks = (int64_t)E * (N / (SWIGLU ? 16 : 32));
+  hipLaunchKernelGGL((ffn_bf16_skinny_kernel<SWIGLU, MT, D, NW>), dim3((unsigned)blocks), dim3(64 * NW), kLds, s, E,
+                     offsets, N, K, reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B0),
+                     reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C));
+  return hipGetLastError();
+}
+
+// seg_max rows per expert at most (<= 64); N a multiple of 32, N * K * 2 < 2^31.
+template <bool SWIGLU>
+hipError_t launch_skinny(int64_t seg_max, int E, const int32_t* offsets, int N, int K, const void* A,
+                         const void* B0, const void* B1, void* C, hipStream_t s) {
+  if (SWIGLU)
+    return seg_max <= 32 ? launch_skinny_cfg<true, 1, 3, 2>(E, offsets, N, K, A, B0, B1, C, s)
+                         : launch_skinny_cfg<true, 2, 3, 2>(E, offsets, N, K, A, B0, B1, C, s);
+  return seg_max <= 32 ? launch_skinny_cfg<false, 1, 2, 8>(E, offsets, N, K, A, B0, B1, C, s)
+                       : launch_skinny_cfg<false, 2, 2, 4>(E, offsets, N, K, A, B0, B1, C, s);
+}
+
+// ---------------------------------------------------------------------------
 // Weight gradients: per expert e, C_e[m][n] = sum over k in [koff[e], koff[e+1])
 // of A[m][k] * B[n][k], with A [M, ldk] and B [N, ldk] K-contiguous (the
 // transposed activations, each expert's rows padded to a multiple of 64 with
@@ -946,9 +1106,18 @@ size_t ffn_bf16_workspace_bytes(int64_t R_max, int E) {
   return (size_t)compute_units() * 256 * 256 * sizeof(float);
 }
 
-hipError_t launch_gemm_bf16(int which, int64_t R_max, int d, int E, int F, const void* in,
+bool ffn_bf16_skinny(int64_t seg_max, int d, int F) {
+  return seg_max <= 64 && (int64_t)d * F * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_bf16(int which, int64_t R_max, int64_t seg_max, int d, int E, int F, const void* in,
                             const int32_t* offsets, const void* w0, const void* w1, void* out,
                             void* ws, hipStream_t s) {
+  // At most 64 rows per expert: stream the weights, no row tiles.
+  if (ffn_bf16_skinny(seg_max, d, F)) {
+    if (which == 1) return launch_skinny<true>(seg_max, E, offsets, F, d, in, w0, w1, out, s);
+    return launch_skinny<false>(seg_max, E, offsets, d, F, in, w0, nullptr, out, s);
+  }
   // 256-row DMA tiles once experts average at least 128 rows; below that the
   // 128-row tiles waste less work on the ragged last tile of each expert.
   if (ffn_bf16_big_tiles(R_max, E)) {
@@ -960,12 +1129,12 @@ hipError_t launch_gemm_bf16(int which, int64_t R_max, int d, int E, int F, const
   return launch_gemm<128, 128, false>(R_max, E, offsets, d, F, in, w0, nullptr, out, s);
 }
 
-hipError_t launch_ffn_bf16(int64_t R_max, int d, int E, int F, const void* x_perm,
+hipError_t launch_ffn_bf16(int64_t R_max, int64_t seg_max, int d, int E, int F, const void* x_perm,
                            const int32_t* offsets, const void* wg, const void* wu, const void* wd,
                            void* h, void* out, void* ws, hipStream_t s) {
-  hipError_t err = launch_gemm_bf16(1, R_max, d, E, F, x_perm, offsets, wg, wu, h, nullptr, s);
+  hipError_t err = launch_gemm_bf16(1, R_max, seg_max, d, E, F, x_perm, offsets, wg, wu, h, nullptr, s);
   if (err != hipSuccess) return err;
-  return launch_gemm_bf16(2, R_max, d, E, F, h, offsets, wd, nullptr, out, ws, s);
+  return launch_gemm_bf16(2, R_max, seg_max, d, E, F, h, offsets, wd, nullptr, out, ws, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -51,6 +51,10 @@ int64_t rows_max_of(int64_t T, int E, int k, int64_t cap) {
   return a < b ? a : b;
 }
 
+// Rows of any one expert: a token takes an expert at most once, and no expert
+// keeps more than its capacity (cap <= T).
+int64_t seg_max_of(int64_t cap, int64_t R_max) { return cap < R_max ? cap : R_max; }
+
 // Scalar checks shared by every entry point. F < 0 means "not used".
 int check_scalars(int64_t T, int d, int E, int k, float cf, int F, int dt, bool ffn) {
   if (T < 0 || d < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
@@ -274,8 +278,9 @@ int moe_grouped_ffn(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_
                        {w_gate, wbytes}, {w_up, wbytes}, {w_down, wbytes}};
   if (any_overlap(all, 3, 8)) return MOE_ERR_INVALID_ARG;
   hipError_t e = dt == MOE_BF16
-                     ? moe::launch_ffn_bf16(R_max, d, E, F, x_perm, expert_offsets, w_gate, w_up,
-                                            w_down, h_ws, out_perm, need ? ws : nullptr, stream)
+                     ? moe::launch_ffn_bf16(R_max, seg_max_of(capacity_of(T, E, k, cf), R_max), d, E, F, x_perm,
+                                            expert_offsets, w_gate, w_up, w_down, h_ws, out_perm,
+                                            need ? ws : nullptr, stream)
                      : moe::launch_ffn_f32(R_max, d, E, F, x_perm, expert_offsets, w_gate, w_up,
                                            w_down, h_ws, out_perm, stream);
   return hip_status(e);
@@ -301,7 +306,8 @@ static int expert_gemm(int which, int64_t T, int32_t d, int32_t E, int32_t k, fl
                        {expert_offsets, (size_t)(E + 1) * 4}, {w0, wbytes}, {w1, which == 1 ? wbytes : 0}};
   if (any_overlap(all, 2, 6)) return MOE_ERR_INVALID_ARG;
   hipError_t e = dt == MOE_BF16
-                     ? moe::launch_gemm_bf16(which, R_max, d, E, F, in, expert_offsets, w0, w1, out,
+                     ? moe::launch_gemm_bf16(which, R_max, seg_max_of(capacity_of(T, E, k, cf), R_max), d, E, F, in,
+                                             expert_offsets, w0, w1, out,
                                              need ? ws : nullptr, stream)
                      : moe::launch_gemm_f32(which, R_max, d, E, F, in, expert_offsets, w0, w1, out, stream);
   return hip_status(e);
@@ -386,8 +392,8 @@ int moe_forward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t
     e = moe::launch_permute(bf16, T, d, E, k, cap, x, idx, order, counts, offsets, srow, rslot, x_perm,
                             chunks, stream);
   if (e == hipSuccess)
-    e = bf16 ? moe::launch_ffn_bf16(R_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, h, out_perm,
-                                    ffn_ws_bytes(R_max, E, dt) ? ffn_ws : nullptr, stream)
+    e = bf16 ? moe::launch_ffn_bf16(R_max, seg_max_of(cap, R_max), d, E, F, x_perm, offsets, w_gate, w_up, w_down,
+                                    h, out_perm, ffn_ws_bytes(R_max, E, dt) ? ffn_ws : nullptr, stream)
              : moe::launch_ffn_f32(R_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, h, out_perm,
                                    stream);
   if (e == hipSuccess) e = moe::launch_combine(bf16, T, d, k, out_perm, srow, gate, y, stream);
@@ -489,7 +495,7 @@ int moe_grouped_ffn_rows(int64_t R_max, int32_t d, int32_t E, int32_t F, moe_dty
                        {w_gate, wbytes}, {w_up, wbytes}, {w_down, wbytes}};
   if (any_overlap(all, 3, 8)) return MOE_ERR_INVALID_ARG;
   hipError_t e = dt == MOE_BF16
-                     ? moe::launch_ffn_bf16(R_max, d, E, F, x_perm, expert_offsets, w_gate, w_up,
+                     ? moe::launch_ffn_bf16(R_max, R_max, d, E, F, x_perm, expert_offsets, w_gate, w_up,
                                             w_down, h_ws, out_perm, need ? ws : nullptr, stream)
                      : moe::launch_ffn_f32(R_max, d, E, F, x_perm, expert_offsets, w_gate, w_up,
                                            w_down, h_ws, out_perm, stream);
@@ -582,7 +588,7 @@ int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float 
   if (e == hipSuccess) e = moe::launch_ec_select(T, E, (int)C, scores, w + L.select, tokens, slot, offsets, stream);
   if (e == hipSuccess) e = moe::launch_gather_rows(bf16, T, R, d, x, tokens, w + L.x_perm, stream);
   if (e == hipSuccess)
-    e = bf16 ? moe::launch_ffn_bf16(R, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w_down, w + L.h,
+    e = bf16 ? moe::launch_ffn_bf16(R, C, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w_down, w + L.h,
                                     w + L.out_perm, ffn_ws_bytes(R, E, dt) ? w + L.ffn : nullptr, stream)
              : moe::launch_ffn_f32(R, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w_down, w + L.h,
                                    w + L.out_perm, stream);
@@ -694,7 +700,8 @@ int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F
     e = moe::launch_bwd_recompute_gate_up(R_max, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w + L.h, w + L.a_st,
                                           w + L.b_st, stream);
   if (e == hipSuccess)
-    e = moe::launch_gemm_bf16(2, R_max, d, E, F, w + L.h, offsets, w_down, nullptr, w + L.o, ffn_ws, stream);
+    e = moe::launch_gemm_bf16(2, R_max, seg_max_of(cap, R_max), d, E, F, w + L.h, offsets, w_down, nullptr, w + L.o,
+                              ffn_ws, stream);
   // combine and gate backward: d_o rows, dl
   if (e == hipSuccess) e = moe::launch_gate_bwd(T, d, k, dy, w + L.o, srow, gate, w + L.d_o, dl, stream);
   // data gradients through the experts

@@ -29,9 +29,10 @@ hipError_t launch_priority_order(int64_t T, const float* score, int64_t stride, 
                                  hipStream_t s);
 
 // The two grouped GEMMs (which = 1: gate/up with the SwiGLU epilogue, 2: down).
+// R_max bounds the rows in all, seg_max the rows of any one expert.
 // ws (bf16 down projection only, may be NULL): ffn_bf16_workspace_bytes() of
 // scratch for the partial tiles of its split tail.
-hipError_t launch_gemm_bf16(int which, int64_t R_max, int d, int E, int F, const void* in,
+hipError_t launch_gemm_bf16(int which, int64_t R_max, int64_t seg_max, int d, int E, int F, const void* in,
                             const int32_t* offsets, const void* w0, const void* w1, void* out,
                             void* ws, hipStream_t s);
 size_t ffn_bf16_workspace_bytes(int64_t R_max, int E);
@@ -40,7 +41,7 @@ hipError_t launch_gemm_f32(int which, int64_t R_max, int d, int E, int F, const 
                            const int32_t* offsets, const void* w0, const void* w1, void* out,
                            hipStream_t s);
 
-hipError_t launch_ffn_bf16(int64_t R_max, int d, int E, int F, const void* x_perm,
+hipError_t launch_ffn_bf16(int64_t R_max, int64_t seg_max, int d, int E, int F, const void* x_perm,
                            const int32_t* offsets, const void* wg, const void* wu, const void* wd,
                            void* h, void* out, void* ws, hipStream_t s);
 

@@ -26,6 +26,10 @@ SMALL = [
     (130, 64, 1, 1, 64, 0.0, "bf16", 15),        # one expert: the dense FFN
     (1, 128, 8, 2, 128, 0.0, "bf16", 17),        # a single token
     (333, 64, 4, 2, 64, 0.5, "bf16", 19),        # heavy dropping
+    (32, 512, 8, 2, 256, 0.0, "bf16", 21),       # decode-sized: 64 rows, weight-streaming GEMMs
+    (20, 64, 4, 3, 192, 0.0, "bf16", 22),        # 60 rows, one 64-deep K step in the gate/up GEMM
+    (64, 192, 1, 1, 128, 0.0, "bf16", 23),       # one expert with 64 rows: two full token tiles
+    (48, 128, 4, 1, 128, 0.5, "bf16", 24),       # decode-sized with drops
     (257, 64, 4, 1, 128, 1.25, "f32", 13),
     (200, 100, 5, 2, 72, 0.8, "f32", 14),        # fp32: d, F not multiples of the tiles
     (90, 32, 3, 3, 36, 0.0, "f32", 20),
