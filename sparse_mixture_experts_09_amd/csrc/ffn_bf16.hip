@@ -15,12 +15,16 @@
 // activations its second, so each lane's accumulator holds 4 consecutive output
 // features of one row, stored as one 8-byte write.
 //
-// Two kernels share the fragment layout and epilogue:
-//   ffn_bf16_dma_kernel  256-row tiles, 8 wavefronts (2 per SIMD), K step 64,
-//                        global -> LDS DMA into two stages (the main path);
-//   ffn_bf16_kernel      128-row tiles, 4 wavefronts, register-staged loads
-//                        (small problems, where big tiles waste work on the
-//                        ragged last tile of each expert).
+// Kernels (one fragment layout):
+//   ffn_bf16_reg_kernel     256-row tiles, 8 wavefronts (2 per SIMD), K step 64,
+//                           register-staged loads into two LDS stages (the main
+//                           path, forward and the backward data gradients);
+//   ffn_bf16_kernel         128-row tiles, 4 wavefronts (experts average fewer
+//                           than 128 rows: big tiles would waste work on the
+//                           ragged last tile of each expert);
+//   ffn_bf16_skinny_kernel  at most 64 rows per expert (decode): streams the
+//                           weights through per-wavefront LDS stages;
+//   wgrad_dma_kernel        weight gradients (grouped K), global -> LDS DMA.
 // In GEMM1 the weight tile holds BN gate rows followed by BN up rows, so the
 // two products for one h element sit in the same lane and register and the
 // SwiGLU epilogue needs no data exchange.
@@ -42,7 +46,11 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kRowBytes + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
 }
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+// sigmoid with the hardware reciprocal (1 ulp in fp32; every consumer rounds
+// to bf16): a large negative a gives exp(-a) = inf and sigmoid 0, so silu
+// is -0 there as with a true division
+__device__ __forceinline__ float sigmoid(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+__device__ __forceinline__ float silu(float a) { return a * sigmoid(a); }
 
 template <int BM, int BN, bool SWIGLU, int NWM, int NWN>
 __global__ __launch_bounds__(64 * NWM * NWN) void ffn_bf16_kernel(int E, const int32_t* __restrict__ offsets, int N,
@@ -199,9 +207,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) void ffn_bf16_kernel(int E, const i
 }
 
 // ---------------------------------------------------------------------------
-// Main kernel: operand tiles go straight from global memory into LDS with
-// global_load_lds_dwordx4 (no staging registers, no ds_write), K step 64, two
-// LDS stages of 256 + BROWS rows x 128 bytes.
+// DMA main loop (the weight-gradient kernel): operand tiles go straight from
+// global memory into LDS with global_load_lds_dwordx4 (no staging registers,
+// no ds_write), K step 64, two LDS stages of 256 + 256 rows x 128 bytes.
 //
 // One DMA instruction writes 1 KB of LDS contiguously (lane L at +16 L, i.e.
 // 8 rows of 128 bytes), so the bank swizzle is applied on the global side:
@@ -245,6 +253,23 @@ __device__ __forceinline__ void dma16(const void* g, char* lds) {
 #endif
 }
 
+// Raw buffer access: the record count ends the buffer, and a load past it
+// returns zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0));
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// a store past the record count is dropped
+__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)voff, 0, 0);
+}
+
 // Epilogues: EPI_PLAIN C = bf16(acc); EPI_SWIGLU C = bf16(silu(gate) * up);
 // EPI_SWIGLU_AB the same plus C2 = bf16(gate), C3 = bf16(up) (the backward
 // pass's recomputation); EPI_SWIGLU_BWD (plain tile, acc = dh): with a = X0,
@@ -252,167 +277,95 @@ __device__ __forceinline__ void dma16(const void* g, char* lds) {
 // ldc / ldx: row strides (elements) of the outputs / of X0 and X1.
 constexpr int EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_SWIGLU_AB = 2, EPI_SWIGLU_BWD = 3;
 
-__device__ __forceinline__ float silu_grad(float a) {
-  const float sg = 1.0f / (1.0f + __expf(-a));
-  return sg * (1.0f + a * (1.0f - sg));
+
+// Epilogues of the 256-row tiles (wavefront (wm, wn) owns rows wm*WM.. and
+// columns wn*WN.. of the tile; acc[mb*NB + nb] is the 32x32 block mb, nb, and
+// in SwiGLU tiles acc[MB*NB + ...] holds the matching up products). A lane
+// holds, for its row (lane & 31), columns 8*g + 4*(lane>>5) + 0..3.
+template <int BN, int MB, int NB, int WM, int WN>
+__device__ __forceinline__ void store_partials(const f32x16* acc, float* pt, int wm, int wn, int lane) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int row = wm * WM + mb * 32 + (lane & 31);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = acc[mb * NB + nb][4 * g + i];
+        *reinterpret_cast<f32x4*>(pt + (size_t)row * BN + col) = v;
+      }
+  }
 }
 
-template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN)>
-__global__ __launch_bounds__(512) void ffn_bf16_dma_kernel(
-    int E, const int32_t* __restrict__ offsets, int N, int K, const uint16_t* __restrict__ A,
-    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT,
-    int P, int max_split, float* __restrict__ partials, int ldc, uint16_t* __restrict__ C2,
-    uint16_t* __restrict__ C3, const uint16_t* __restrict__ X0, const uint16_t* __restrict__ X1, int ldx) {
-  static_assert(SWIGLU == (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_AB), "tile layout and epilogue");
-  constexpr int BM = 256, NWM = 2, NWN = 4, NW = NWM * NWN;
-  constexpr int BROWS = SWIGLU ? 2 * BN : BN;
-  constexpr int WM = BM / NWM, WN = BN / NWN;
-  constexpr int MB = WM / 32, NB = WN / 32;
-  constexpr int NBF = (SWIGLU ? 2 : 1) * NB;
-  constexpr int NACC = MB * NBF;
-  constexpr int A_PW = BM / 8 / NW, B_PW = BROWS / 8 / NW;   // 1 KB DMA pieces per wave per K step
-  constexpr int LOADS = A_PW + B_PW;
-  constexpr int STAGE = (BM + BROWS) * kRowB;
-  static_assert(BM % (8 * NW) == 0 && BROWS % (8 * NW) == 0 && WN % 32 == 0, "tile");
-  extern __shared__ __align__(16) char smem[];
-
-  const int KTall = K / kBK;
-  WorkItem w;
-  if (!find_item(offsets, E, BM, NT, P, max_split, KTall, blockIdx.x, w)) return;
-  const TileCoord tc = w.tc;
-  // K steps [kb, kb + KT) of this item (a slice of K for a split tail tile)
-  int kb = 0, KT = KTall;
-  if (w.split >= 0) {
-    const int ns = make_plan(offsets, E, BM, NT, P, max_split, KTall).s;
-    kb = w.slice * KTall / ns;
-    KT = (w.slice + 1) * KTall / ns - kb;
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / NWN, wn = wave % NWN;
-  const int n0 = tc.n_tile * BN;
-
-  // per-lane byte offsets of the 16-byte pieces this lane fetches (row clamped
-  // into the expert's segment / below N: duplicates feed no stored output)
-  const char* Ab = reinterpret_cast<const char*>(A);
-  const char* B0b = reinterpret_cast<const char*>(B0);
-  const char* B1b = reinterpret_cast<const char*>(B1);
-  const size_t wofs = (size_t)tc.e * (size_t)N * K * 2;
-  size_t a_off[A_PW], b_off[B_PW];
+template <int EPI, int BM, int MB, int NB, int WM, int WN>
+__device__ __forceinline__ void store_tile(const f32x16* acc, const TileCoord& tc, int wm, int wn, int n0, int N,
+                                           int ldc, uint16_t* __restrict__ C, uint16_t* __restrict__ C2,
+                                           uint16_t* __restrict__ C3, const uint16_t* __restrict__ X0,
+                                           const uint16_t* __restrict__ X1, int ldx, int lane) {
+  if constexpr (EPI == EPI_SWIGLU_BWD) {
+    // a and b come through buffer loads and da, db go out through buffer
+    // stores whose record counts end at the segment's last row (past it loads
+    // read zeros and stores are dropped); a column past N gets an offset
+    // beyond every record count. The loads for half of the row blocks are
+    // issued together before any of their stores (the compiler cannot move a
+    // buffer load above a buffer store), so the epilogue waits on memory
+    // twice per tile instead of once per 4 elements.
+    constexpr int MBH = MB / 2 > 0 ? MB / 2 : 1;
+    const int rows = min(BM, tc.seg_rows - tc.m0);
+    const size_t rb0 = (size_t)(tc.seg_start + tc.m0);
+    const auto r0 = make_rsrc(X0 + rb0 * ldx, (uint32_t)((size_t)rows * ldx * 2));
+    const auto r1 = make_rsrc(X1 + rb0 * ldx, (uint32_t)((size_t)rows * ldx * 2));
+    const auto wc = make_rsrc(C + rb0 * ldc, (uint32_t)((size_t)rows * ldc * 2));
+    const auto wc2 = make_rsrc(C2 + rb0 * ldc, (uint32_t)((size_t)rows * ldc * 2));
+    auto offs = [&](int mb, int nb, int g, int ld) {
+      const int rl = wm * WM + mb * 32 + (lane & 31);
+      const int col = n0 + wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
+      return col < N ? (uint32_t)(rl * ld + col) * 2u : 0x80000000u;
+    };
 #pragma unroll
-  for (int i = 0; i < A_PW; ++i) {
-    const int row = (wave * A_PW + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ dswz(row);
-    const int r = min(tc.m0 + row, tc.seg_rows - 1);
-    a_off[i] = (size_t)(tc.seg_start + r) * K * 2 + c * 16;
-  }
+    for (int h = 0; h < MB; h += MBH) {
+      uint2 ra[MBH][NB][4], rv[MBH][NB][4];
 #pragma unroll
-  for (int i = 0; i < B_PW; ++i) {
-    const int row = (wave * B_PW + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ dswz(row);
-    const int n = min(n0 + (SWIGLU && row >= BN ? row - BN : row), N - 1);
-    b_off[i] = wofs + (size_t)n * K * 2 + c * 16;
-  }
-  auto dma = [&](int kt) {
-    const int kc = kb + (kt < KT ? kt : KT - 1);
-    char* st = smem + (kt & 1) * STAGE;
-    const size_t koff = (size_t)kc * kRowB;
+      for (int m = 0; m < MBH; ++m)
 #pragma unroll
-    for (int i = 0; i < A_PW; ++i) dma16(Ab + a_off[i] + koff, st + (wave * A_PW + i) * 1024);
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int i = 0; i < B_PW; ++i) {
-      const int row = (wave * B_PW + i) * 8;   // first row of this piece (wave-uniform)
-      const char* base = (SWIGLU && row >= BN) ? B1b : B0b;
-      dma16(base + b_off[i] + koff, st + BM * kRowB + (wave * B_PW + i) * 1024);
-    }
-  };
-
-  f32x16 acc[NACC];
+          for (int g = 0; g < 4; ++g) {
+            ra[m][nb][g] = bload8(r0, offs(h + m, nb, g, ldx));
+            rv[m][nb][g] = bload8(r1, offs(h + m, nb, g, ldx));
+          }
 #pragma unroll
-  for (int i = 0; i < NACC; ++i)
+      for (int m = 0; m < MBH; ++m)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-
-  bf16x8 fa[2][MB], fb[2][NBF];
-  auto read_frags = [&](int stage, int s, bf16x8(&A_)[MB], bf16x8(&B_)[NBF]) {
-    const char* buf = smem + stage * STAGE;
-    const int chunk = 2 * s + (lane >> 5);
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      A_[mb] = __builtin_bit_cast(bf16x8, ld16(buf + daddr(wm * WM + mb * 32 + (lane & 31), chunk)));
+          for (int g = 0; g < 4; ++g) {
+            const uint2 a2 = ra[m][nb][g], b2 = rv[m][nb][g];
+            const float av[4] = {bf16_lo(a2.x), bf16_hi(a2.x), bf16_lo(a2.y), bf16_hi(a2.y)};
+            const float bv[4] = {bf16_lo(b2.x), bf16_hi(b2.x), bf16_lo(b2.y), bf16_hi(b2.y)};
+            float da[4], db[4];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int row = wn * WN + nb * 32 + (lane & 31);
-      B_[nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(row, chunk)));
-      if (SWIGLU) B_[NB + nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(BN + row, chunk)));
-    }
-  };
-  auto mma = [&](const bf16x8(&A_)[MB], const bf16x8(&B_)[NBF]) {
-#pragma unroll
-    for (int nb = 0; nb < NBF; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        // accumulator order: [gate | plain][mb][nb], then [up][mb][nb]
-        const int a = (nb / NB) * MB * NB + mb * NB + (nb % NB);
-        acc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B_[nb], A_[mb], acc[a], 0, 0, 0);
-      }
-  };
-
-  dma(0);
-  dma(1);
-  wait_vmcnt<LOADS>();          // tile 0 landed (tile 1 may be in flight)
-  __builtin_amdgcn_s_barrier();
-  read_frags(0, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < KT - 1; ++kt) {
-    const int cur = kt & 1;
-    read_frags(cur, 1, fa[1], fb[1]);
-    mma(fa[0], fb[0]);
-    read_frags(cur, 2, fa[0], fb[0]);
-    mma(fa[1], fb[1]);
-    read_frags(cur, 3, fa[1], fb[1]);
-    mma(fa[0], fb[0]);
-    wait_lgkm0();               // this wave's reads of stage cur are done
-    wait_vmcnt<0>();            // tile kt + 1 landed
-    __builtin_amdgcn_s_barrier();
-    dma(kt + 2);                // into stage cur
-    read_frags(cur ^ 1, 0, fa[0], fb[0]);
-    mma(fa[1], fb[1]);
-  }
-  {
-    const int cur = (KT - 1) & 1;
-    read_frags(cur, 1, fa[1], fb[1]);
-    mma(fa[0], fb[0]);
-    read_frags(cur, 2, fa[0], fb[0]);
-    mma(fa[1], fb[1]);
-    read_frags(cur, 3, fa[1], fb[1]);
-    mma(fa[0], fb[0]);
-    mma(fa[1], fb[1]);
-  }
-  // the redundant prefetch of tile KT may still be landing in a stage nobody reads;
-  // drain it so no DMA outlives the block's LDS allocation
-  wait_vmcnt<0>();
-
-  if (!SWIGLU && w.split >= 0) {
-    // K-slice of a split tail tile: the fp32 partial tile [BM][BN], reduced later
-    const int ns = make_plan(offsets, E, BM, NT, P, max_split, KTall).s;
-    float* pt = partials + (size_t)(w.split * ns + w.slice) * BM * BN;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int row = wm * WM + mb * 32 + (lane & 31);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
-          f32x4 v;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[mb * NB + nb][4 * g + i];
-          *reinterpret_cast<f32x4*>(pt + (size_t)row * BN + col) = v;
-        }
+            for (int i = 0; i < 4; ++i) {
+              // silu(a) = a sg and silu'(a) = sg (1 + a (1 - sg)), sg = sigmoid(a)
+              const float dh = acc[(h + m) * NB + nb][4 * g + i], sg = sigmoid(av[i]);
+              da[i] = dh * bv[i] * (sg * (1.0f + av[i] * (1.0f - sg)));
+              db[i] = dh * (av[i] * sg);
+            }
+            uint2 wa, wdb;
+            wa.x = pack_bf16x2(da[0], da[1]);
+            wa.y = pack_bf16x2(da[2], da[3]);
+            wdb.x = pack_bf16x2(db[0], db[1]);
+            wdb.y = pack_bf16x2(db[2], db[3]);
+            const uint32_t co = offs(h + m, nb, g, ldc);
+            bstore8(wc, co, wa);
+            bstore8(wc2, co, wdb);
+          }
     }
     return;
   }
-
-  // epilogue: lane holds, for its row (lane & 31), features 8*g + 4*(lane>>5) + 0..3
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int rloc = tc.m0 + wm * WM + mb * 32 + (lane & 31);
@@ -429,7 +382,7 @@ __global__ __launch_bounds__(512) void ffn_bf16_dma_kernel(
         if (EPI == EPI_PLAIN) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = acc[mb * NB + nb][4 * g + i];
-        } else if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_AB) {
+        } else {   // EPI_SWIGLU, EPI_SWIGLU_AB
           float ga[4], up[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -446,23 +399,6 @@ __global__ __launch_bounds__(512) void ffn_bf16_dma_kernel(
             *reinterpret_cast<uint2*>(C2 + at) = wa;
             *reinterpret_cast<uint2*>(C3 + at) = wb;
           }
-        } else {   // EPI_SWIGLU_BWD
-          const size_t xa = grow * (size_t)ldx + col;
-          const uint2 ra = *reinterpret_cast<const uint2*>(X0 + xa);
-          const uint2 rb = *reinterpret_cast<const uint2*>(X1 + xa);
-          const float av[4] = {bf16_lo(ra.x), bf16_hi(ra.x), bf16_lo(ra.y), bf16_hi(ra.y)};
-          const float bv[4] = {bf16_lo(rb.x), bf16_hi(rb.x), bf16_lo(rb.y), bf16_hi(rb.y)};
-          float db[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float dh = acc[mb * NB + nb][4 * g + i];
-            v[i] = dh * bv[i] * silu_grad(av[i]);
-            db[i] = dh * silu(av[i]);
-          }
-          uint2 wdb;
-          wdb.x = pack_bf16x2(db[0], db[1]);
-          wdb.y = pack_bf16x2(db[2], db[3]);
-          *reinterpret_cast<uint2*>(C2 + at) = wdb;
         }
         uint2 w;
         w.x = pack_bf16x2(v[0], v[1]);
@@ -506,8 +442,9 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(int E, const int32_t*
 }
 
 // ---------------------------------------------------------------------------
-// Forward main path: the same 256 x BN tiles, wavefront split (2 x 4), LDS
-// layout and epilogues as ffn_bf16_dma_kernel, with register-staged loads:
+// Main path: 256 x BN tiles (256 weight rows: BN gate + BN up rows in GEMM1),
+// wavefronts split 2 x 4, the LDS layout and bank swizzle of the DMA loop
+// above and the epilogues of store_tile, with register-staged loads:
 // each thread fetches four 16-byte pieces of each operand per K step with
 // buffer loads (whole 128-byte rows across 8 lanes; the descriptors' record
 // counts end at the expert's last row and at the weight's last row, so
@@ -521,18 +458,14 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(int E, const int32_t*
 // work while the stores and loads issue; the last K step is peeled and the
 // body has no branches (the load past the last tile reloads the last one).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
-}
 
-template <int BN, bool SWIGLU>
+template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN)>
 __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
     int E, const int32_t* __restrict__ offsets, int N, int K, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT,
-    int P, int max_split, float* __restrict__ partials) {
+    int P, int max_split, float* __restrict__ partials, int ldc, uint16_t* __restrict__ C2,
+    uint16_t* __restrict__ C3, const uint16_t* __restrict__ X0, const uint16_t* __restrict__ X1, int ldx) {
+  static_assert(SWIGLU == (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_AB), "tile layout and epilogue");
   constexpr int BM = 256, NWM = 2, NWN = 4, NT_ = 512;
   constexpr int BROWS = SWIGLU ? 2 * BN : BN;
   static_assert(BROWS == 256, "both operands are 256-row tiles");
@@ -675,47 +608,10 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
 
   if (!SWIGLU && w.split >= 0) {
     const int ns = make_plan(offsets, E, BM, NT, P, max_split, KTall).s;
-    float* pt = partials + (size_t)(w.split * ns + w.slice) * BM * BN;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int row = wm * WM + mb * 32 + (lane & 31);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
-          f32x4 v;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[mb * NB + nb][4 * g + i];
-          *reinterpret_cast<f32x4*>(pt + (size_t)row * BN + col) = v;
-        }
-    }
+    store_partials<BN, MB, NB, WM, WN>(acc, partials + (size_t)(w.split * ns + w.slice) * BM * BN, wm, wn, lane);
     return;
   }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int rloc = tc.m0 + wm * WM + mb * 32 + (lane & 31);
-    if (rloc >= tc.seg_rows) continue;
-    uint16_t* crow = C + (size_t)(tc.seg_start + rloc) * (size_t)N;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = n0 + wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
-        if (col >= N) continue;
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = acc[mb * NB + nb][4 * g + i];
-          v[i] = SWIGLU ? silu(a) * acc[MB * NB + mb * NB + nb][4 * g + i] : a;
-        }
-        uint2 o;
-        o.x = pack_bf16x2(v[0], v[1]);
-        o.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(crow + col) = o;
-      }
-    }
-  }
+  store_tile<EPI, BM, MB, NB, WM, WN>(acc, tc, wm, wn, n0, N, ldc, C, C2, C3, X0, X1, ldx, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -884,7 +780,7 @@ hipError_t launch_skinny(int64_t seg_max, int E, const int32_t* offsets, int N, 
 // transposed activations, each expert's rows padded to a multiple of 64 with
 // zeros, so every K range is whole 64-deep steps). Rows m < M1 go to
 // C0[e][m][n], rows m >= M1 to C1[e][m - M1][n] (gate and up gradients from one
-// launch). Same DMA main loop and fragment layout as ffn_bf16_dma_kernel; tiles
+// launch). The DMA main loop above, with the common fragment layout; tiles
 // run expert by expert with m-tiles fastest, and each XCD gets a contiguous
 // run of tiles. An expert with no rows gets a zero gradient.
 // ---------------------------------------------------------------------------
@@ -1014,39 +910,14 @@ __global__ __launch_bounds__(512) void wgrad_dma_kernel(int E, const int32_t* __
   }
 }
 
-template <int BN, bool SWIGLU>
+template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN)>
 hipError_t launch_reg(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A, const void* B0,
-                      const void* B1, void* C, float* partials, int P, hipStream_t s) {
+                      const void* B1, void* C, float* partials, int P, hipStream_t s, int ldc = 0,
+                      void* C2 = nullptr, void* C3 = nullptr, const void* X0 = nullptr, const void* X1 = nullptr,
+                      int ldx = 0) {
   constexpr int BM = 256;
   constexpr size_t kLds = 2 * (size_t)(BM + 256) * kRowB;
-  auto kern = &ffn_bf16_reg_kernel<BN, SWIGLU>;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-  if (attr != hipSuccess) return attr;
-  const int NT = (N + BN - 1) / BN;
-  const int64_t tiles_ub = ((R_max + BM - 1) / BM + E) * NT;
-  const bool split = !SWIGLU && partials != nullptr && P > 0;
-  const int max_split = split ? kMaxSplit : 1;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid_blocks(tiles_ub, P, split)), dim3(512), kLds, s, E, offsets, N, K,
-                     reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B0),
-                     reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C), NT, P, max_split,
-                     partials);
-  if (split)
-    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(P * (BM / 16))), dim3(256), 0, s, E, offsets, N, K, NT,
-                       P, max_split, partials, reinterpret_cast<uint16_t*>(C));
-  return hipGetLastError();
-}
-
-template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN)>
-hipError_t launch_dma(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A,
-                      const void* B0, const void* B1, void* C, float* partials, int P, hipStream_t s,
-                      int ldc = 0, void* C2 = nullptr, void* C3 = nullptr, const void* X0 = nullptr,
-                      const void* X1 = nullptr, int ldx = 0) {
-  constexpr int BM = 256;
-  constexpr int BROWS = SWIGLU ? 2 * BN : BN;
-  constexpr size_t kLds = 2 * (size_t)(BM + BROWS) * kRowB;
-  auto kern = &ffn_bf16_dma_kernel<BN, SWIGLU, EPI>;
-  // opt in to more than 64 KiB of dynamic LDS once per instantiation
+  auto kern = &ffn_bf16_reg_kernel<BN, SWIGLU, EPI>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
@@ -1118,7 +989,7 @@ hipError_t launch_gemm_bf16(int which, int64_t R_max, int64_t seg_max, int d, in
     if (which == 1) return launch_skinny<true>(seg_max, E, offsets, F, d, in, w0, w1, out, s);
     return launch_skinny<false>(seg_max, E, offsets, d, F, in, w0, nullptr, out, s);
   }
-  // 256-row DMA tiles once experts average at least 128 rows; below that the
+  // 256-row tiles once experts average at least 128 rows; below that the
   // 128-row tiles waste less work on the ragged last tile of each expert.
   if (ffn_bf16_big_tiles(R_max, E)) {
     if (which == 1) return launch_reg<128, true>(R_max, E, offsets, F, d, in, w0, w1, out, nullptr, 0, s);
@@ -1144,21 +1015,23 @@ hipError_t launch_ffn_bf16(int64_t R_max, int64_t seg_max, int d, int E, int F, 
 hipError_t launch_bwd_recompute_gate_up(int64_t R_max, int d, int E, int F, const void* x_perm,
                                         const int32_t* offsets, const void* wg, const void* wu, void* h,
                                         void* a_st, void* b_st, hipStream_t s) {
-  return launch_dma<128, true, EPI_SWIGLU_AB>(R_max, E, offsets, F, d, x_perm, wg, wu, h, nullptr, 0, s, F, a_st,
+  return launch_reg<128, true, EPI_SWIGLU_AB>(R_max, E, offsets, F, d, x_perm, wg, wu, h, nullptr, 0, s, F, a_st,
                                               b_st);
 }
 
 hipError_t launch_bwd_dh(int64_t R_max, int d, int E, int F, const void* d_o, const int32_t* offsets,
                          const void* w_down_t, const void* a_st, const void* b_st, void* dab, hipStream_t s) {
-  // dab [R, 2F]: da in columns 0..F-1, db in F..2F-1
-  return launch_dma<256, false, EPI_SWIGLU_BWD>(R_max, E, offsets, F, d, d_o, w_down_t, nullptr, dab, nullptr, 0,
+  // dab [R, 2F]: da in columns 0..F-1, db in F..2F-1; the epilogue's buffer
+  // offsets within a 256-row tile of dab must stay below 2^31
+  if ((int64_t)256 * 2 * F * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  return launch_reg<256, false, EPI_SWIGLU_BWD>(R_max, E, offsets, F, d, d_o, w_down_t, nullptr, dab, nullptr, 0,
                                                 s, 2 * F, reinterpret_cast<uint16_t*>(dab) + F, nullptr, a_st,
                                                 b_st, F);
 }
 
 hipError_t launch_bwd_dx_perm(int64_t R_max, int d, int E, int F, const void* dab, const int32_t* offsets,
                               const void* w_gu_t, void* dx_perm, void* ws, hipStream_t s) {
-  return launch_dma<256, false>(R_max, E, offsets, d, 2 * F, dab, w_gu_t, nullptr, dx_perm,
+  return launch_reg<256, false>(R_max, E, offsets, d, 2 * F, dab, w_gu_t, nullptr, dx_perm,
                                 reinterpret_cast<float*>(ws), ws ? compute_units() : 0, s);
 }
 
