@@ -188,7 +188,7 @@ def main():
     h = torch.empty((R_max, F), dtype=g["x"].dtype, device="cuda")
     o = torch.empty((R_max, d), dtype=g["x"].dtype, device="cuda")
     y2 = torch.empty_like(g["x"])
-    flush = None if args.no_flush else torch.zeros(128 << 20, dtype=torch.int32, device="cuda")
+    flush = None if args.no_flush else torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
     names = ["route", "permute", "gate_up", "down", "combine"]
     samples = {n: [] for n in names}
     for it in range(W + K):
@@ -350,7 +350,7 @@ def bench_expert_choice(args, w, a, g, moe, stream):
     log(f"moe_forward_expert_choice: {ms_step:.3f} ms/step (C = {C}, {R} rows)")
 
     names = ["route", "gather", "ffn", "combine"]
-    flush = None if args.no_flush else torch.zeros(128 << 20, dtype=torch.int32, device="cuda")
+    flush = None if args.no_flush else torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
     samples = {n: [] for n in names}
     evs = []
     y2 = torch.empty_like(g["x"])

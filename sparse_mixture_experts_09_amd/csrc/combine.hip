@@ -10,6 +10,10 @@
 // One wavefront per token: lane l handles the 16-byte slices l, l+64, ... of
 // the row; for each slice it reads the k expert-output rows (in slot order),
 // accumulates gate * value in fp32 from +0 and writes the rounded sum once.
+// Each slot reads through a buffer descriptor of its own (base at its row,
+// record count one row, or 0 for a dropped slot, whose gate is taken as 0),
+// so the k loads carry no branch and issue together; a dropped slot adds
+// 0 * 0 to a sum that started at +0, which leaves every bit of it unchanged.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -17,7 +21,7 @@ namespace moe {
 
 namespace {
 
-template <typename S>
+template <typename S, int KM>
 __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int d, int k,
                                                       const char* __restrict__ out_perm,
                                                       const int32_t* __restrict__ slot_row,
@@ -27,47 +31,59 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int d, int k,
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  int rows[8];
-  float g[8];
+  const uint32_t row_bytes = (uint32_t)d * sizeof(typename S::elem);
+  __amdgpu_buffer_rsrc_t src[KM];   // KM: k rounded up to 1, 2, 4 or 8
+  float g[KM];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    rows[j] = j < k ? slot_row[t * k + j] : -1;
-    g[j] = j < k ? gate[t * k + j] : 0.f;
+  for (int j = 0; j < KM; ++j) {
+    // the same for every lane (one token per wavefront)
+    const int r = __builtin_amdgcn_readfirstlane(j < k ? slot_row[t * k + j] : -1);
+    g[j] = r >= 0 ? gate[t * k + j] : 0.f;
+    src[j] = make_rsrc(out_perm + (size_t)(r >= 0 ? r : 0) * row_bytes, r >= 0 ? row_bytes : 0u);
   }
-  const size_t row_bytes = (size_t)d * sizeof(typename S::elem);
   char* dst = y + (size_t)t * row_bytes;
 #pragma unroll 2
-  for (size_t off = (size_t)lane * 16; off < row_bytes; off += 64 * 16) {
+  for (uint32_t off = (uint32_t)lane * 16; off < row_bytes; off += 64 * 16) {
+    u32x4 v[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) v[j] = bload16(src[j], off);
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (rows[j] >= 0) {
-        float f[V];
-        unpack16(S(), ld16(out_perm + (size_t)rows[j] * row_bytes + off), f);
+    for (int j = 0; j < KM; ++j) {
+      float f[V];
+      unpack16(S(), v[j], f);
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] = fmaf(g[j], f[i], acc[i]);
-      }
+      for (int i = 0; i < V; ++i) acc[i] = fmaf(g[j], f[i], acc[i]);
     }
     st16(dst + off, pack16(S(), acc));
   }
+}
+
+template <typename S, int KM>
+hipError_t launch_combine_k(int64_t T, int d, int k, const void* out_perm, const int32_t* slot_row, const float* gate,
+                            void* y, hipStream_t s) {
+  hipLaunchKernelGGL((combine_kernel<S, KM>), dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, T, d, k,
+                     reinterpret_cast<const char*>(out_perm), slot_row, gate, reinterpret_cast<char*>(y));
+  return hipGetLastError();
+}
+
+template <typename S>
+hipError_t launch_combine_s(int64_t T, int d, int k, const void* out_perm, const int32_t* slot_row,
+                            const float* gate, void* y, hipStream_t s) {
+  if (k <= 1) return launch_combine_k<S, 1>(T, d, k, out_perm, slot_row, gate, y, s);
+  if (k <= 2) return launch_combine_k<S, 2>(T, d, k, out_perm, slot_row, gate, y, s);
+  if (k <= 4) return launch_combine_k<S, 4>(T, d, k, out_perm, slot_row, gate, y, s);
+  return launch_combine_k<S, 8>(T, d, k, out_perm, slot_row, gate, y, s);
 }
 
 }  // namespace
 
 hipError_t launch_combine(bool bf16, int64_t T, int d, int k, const void* out_perm,
                           const int32_t* slot_row, const float* gate, void* y, hipStream_t s) {
-  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
-  if (bf16)
-    hipLaunchKernelGGL(combine_kernel<BF16>, grid, block, 0, s, T, d, k,
-                       reinterpret_cast<const char*>(out_perm), slot_row, gate,
-                       reinterpret_cast<char*>(y));
-  else
-    hipLaunchKernelGGL(combine_kernel<F32>, grid, block, 0, s, T, d, k,
-                       reinterpret_cast<const char*>(out_perm), slot_row, gate,
-                       reinterpret_cast<char*>(y));
-  return hipGetLastError();
+  return bf16 ? launch_combine_s<BF16>(T, d, k, out_perm, slot_row, gate, y, s)
+              : launch_combine_s<F32>(T, d, k, out_perm, slot_row, gate, y, s);
 }
 
 }  // namespace moe

@@ -253,23 +253,6 @@ __device__ __forceinline__ void dma16(const void* g, char* lds) {
 #endif
 }
 
-// Raw buffer access: the record count ends the buffer, and a load past it
-// returns zeros without touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
-}
-__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0));
-}
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-// a store past the record count is dropped
-__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)voff, 0, 0);
-}
-
 // Epilogues: EPI_PLAIN C = bf16(acc); EPI_SWIGLU C = bf16(silu(gate) * up);
 // EPI_SWIGLU_AB the same plus C2 = bf16(gate), C3 = bf16(up) (the backward
 // pass's recomputation); EPI_SWIGLU_BWD (plain tile, acc = dh): with a = X0,
@@ -472,7 +455,8 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
     int E, const int32_t* __restrict__ offsets, int N, int K, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT,
     int P, int max_split, float* __restrict__ partials, int ldc, uint16_t* __restrict__ C2,
-    uint16_t* __restrict__ C3, const uint16_t* __restrict__ X0, const uint16_t* __restrict__ X1, int ldx) {
+    uint16_t* __restrict__ C3, const uint16_t* __restrict__ X0, const uint16_t* __restrict__ X1, int ldx,
+    const int32_t* __restrict__ a_slot, int a_k, uint32_t a_records) {
   static_assert(SWIGLU == (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_AB), "tile layout and epilogue");
   constexpr int BM = 256, NWM = 2, NWN = 4, NT_ = 512;
   constexpr int BROWS = SWIGLU ? 2 * BN : BN;
@@ -504,13 +488,32 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
   const size_t rowb = (size_t)K * 2;
   const int a_rows = min(BM, tc.seg_rows - tc.m0);
   const int b_rows = min(BN, N - n0);
-  const auto ra = make_rsrc(A + (size_t)(tc.seg_start + tc.m0) * K, (uint32_t)(a_rows * rowb));
   const size_t wrow0 = (size_t)tc.e * N + n0;
   const auto rb0 = make_rsrc(B0 + wrow0 * K, (uint32_t)(b_rows * rowb));
   const auto rb1 = make_rsrc((SWIGLU ? B1 : B0) + wrow0 * K, (uint32_t)(b_rows * rowb));
   const int row0 = tid >> 3, ch = tid & 7;
   const uint32_t voff = (uint32_t)(row0 * rowb) + ch * 16 + (uint32_t)kb * kRowB;
   const uint32_t rstep = (uint32_t)(RSTEP * rowb);
+  // Token rows: the expert's segment of A, or (a_slot given) rows gathered
+  // from the unpermuted activations A [a_records / rowb rows]: permuted row r
+  // is token a_slot[r] / a_k; a tile row past the segment gets an offset at
+  // the record count, so it reads zeros.
+  __amdgpu_buffer_rsrc_t ra;
+  uint32_t aoff[PT];
+  if (a_slot != nullptr) {
+    ra = make_rsrc(A, a_records);
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int r = row0 + p * RSTEP;
+      aoff[p] = r < a_rows ? ((uint32_t)a_slot[tc.seg_start + tc.m0 + r] / (uint32_t)a_k) * (uint32_t)rowb + ch * 16 +
+                                 (uint32_t)kb * kRowB
+                           : a_records;
+    }
+  } else {
+    ra = make_rsrc(A + (size_t)(tc.seg_start + tc.m0) * K, (uint32_t)(a_rows * rowb));
+#pragma unroll
+    for (int p = 0; p < PT; ++p) aoff[p] = voff + p * rstep;
+  }
   const int wofs = row0 * kRowB + ((ch ^ dswz(row0)) << 4);   // RSTEP is a multiple of 16: same swizzle
 
   // A thread's pieces: p < PT are token rows row0 + p*RSTEP, p >= PT weight
@@ -521,7 +524,7 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
   auto gl = [&](int p, int kt) {
     const uint32_t ko = (uint32_t)(kt < KT ? kt : KT - 1) * kRowB;
     if (p < PT) {
-      stg[p] = bload16(ra, voff + p * rstep + ko);
+      stg[p] = bload16(ra, aoff[p] + ko);
     } else {
       const int i = p - PT;
       const bool up = SWIGLU && i * RSTEP >= BN;
@@ -956,7 +959,7 @@ template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN)>
 hipError_t launch_reg(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A, const void* B0,
                       const void* B1, void* C, float* partials, int P, hipStream_t s, int ldc = 0,
                       void* C2 = nullptr, void* C3 = nullptr, const void* X0 = nullptr, const void* X1 = nullptr,
-                      int ldx = 0) {
+                      int ldx = 0, const int32_t* a_slot = nullptr, int a_k = 1, uint32_t a_records = 0) {
   constexpr int BM = 256;
   constexpr size_t kLds = 2 * (size_t)(BM + 256) * kRowB;
   auto kern = &ffn_bf16_reg_kernel<BN, SWIGLU, EPI>;
@@ -971,7 +974,8 @@ hipError_t launch_reg(int64_t R_max, int E, const int32_t* offsets, int N, int K
                      reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B0),
                      reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C), NT, P, max_split,
                      partials, ldc ? ldc : N, reinterpret_cast<uint16_t*>(C2), reinterpret_cast<uint16_t*>(C3),
-                     reinterpret_cast<const uint16_t*>(X0), reinterpret_cast<const uint16_t*>(X1), ldx);
+                     reinterpret_cast<const uint16_t*>(X0), reinterpret_cast<const uint16_t*>(X1), ldx, a_slot, a_k,
+                     a_records);
   if (split)
     hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(P * (BM / 16))), dim3(256), 0, s, E, offsets, N, K, NT,
                        P, max_split, partials, reinterpret_cast<uint16_t*>(C));
@@ -1023,9 +1027,29 @@ bool ffn_bf16_skinny(int64_t seg_max, int d, int F) {
   return seg_max <= 64 && (int64_t)d * F * 2 < ((int64_t)1 << 31);
 }
 
+bool ffn_bf16_can_gather(int64_t R_max, int64_t seg_max, int d, int E, int F, int64_t T) {
+  return !ffn_bf16_skinny(seg_max, d, F) && ffn_bf16_big_tiles(R_max, E) &&
+         (T + 1) * (int64_t)d * 2 < ((int64_t)1 << 31);
+}
+
+// Gathering saves the scatter of R rows (up to k T) but puts one more memory
+// round trip (the row -> slot map) in front of every tile's first loads. On
+// MI355X that was a loss at k = 2 (Mixtral-shaped layer +40 us, scatter 17 us)
+// and a gain at k = 8 (fine-grained layer -50 us, scatter 53 us).
+bool ffn_bf16_gathers(int64_t R_max, int64_t seg_max, int d, int E, int F, int64_t T, int k) {
+  return k >= 4 && ffn_bf16_can_gather(R_max, seg_max, d, E, F, T);
+}
+
 hipError_t launch_gemm_bf16(int which, int64_t R_max, int64_t seg_max, int d, int E, int F, const void* in,
                             const int32_t* offsets, const void* w0, const void* w1, void* out,
-                            void* ws, hipStream_t s) {
+                            void* ws, hipStream_t s, const int32_t* gather_slot, int gather_k, int64_t gather_T) {
+  if (gather_slot != nullptr) {
+    // GEMM1 reading token rows straight from the unpermuted activations
+    if (which != 1 || !ffn_bf16_can_gather(R_max, seg_max, d, E, F, gather_T) || gather_k < 1)
+      return hipErrorInvalidValue;
+    return launch_reg<128, true>(R_max, E, offsets, F, d, in, w0, w1, out, nullptr, 0, s, 0, nullptr, nullptr,
+                                 nullptr, nullptr, 0, gather_slot, gather_k, (uint32_t)(gather_T * d * 2));
+  }
   // At most 64 rows per expert: stream the weights, no row tiles.
   if (ffn_bf16_skinny(seg_max, d, F)) {
     if (which == 1) return launch_skinny<true>(seg_max, E, offsets, F, d, in, w0, w1, out, s);
@@ -1044,8 +1068,10 @@ hipError_t launch_gemm_bf16(int which, int64_t R_max, int64_t seg_max, int d, in
 
 hipError_t launch_ffn_bf16(int64_t R_max, int64_t seg_max, int d, int E, int F, const void* x_perm,
                            const int32_t* offsets, const void* wg, const void* wu, const void* wd,
-                           void* h, void* out, void* ws, hipStream_t s) {
-  hipError_t err = launch_gemm_bf16(1, R_max, seg_max, d, E, F, x_perm, offsets, wg, wu, h, nullptr, s);
+                           void* h, void* out, void* ws, hipStream_t s, const int32_t* gather_slot, int gather_k,
+                           int64_t gather_T) {
+  hipError_t err = launch_gemm_bf16(1, R_max, seg_max, d, E, F, x_perm, offsets, wg, wu, h, nullptr, s, gather_slot,
+                                    gather_k, gather_T);
   if (err != hipSuccess) return err;
   return launch_gemm_bf16(2, R_max, seg_max, d, E, F, h, offsets, wd, nullptr, out, ws, s);
 }

@@ -385,15 +385,20 @@ int moe_forward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t
   void* ffn_ws = w + L.ffn;
   const bool bf16 = dt == MOE_BF16;
 
+  // bf16 with 256-row tiles and k >= 4: the gate/up GEMM reads the token
+  // rows of x through the row -> slot map, and the permutation writes no x_perm
+  const int64_t seg_max = seg_max_of(cap, R_max);
+  const bool gather = bf16 && moe::ffn_bf16_gathers(R_max, seg_max, d, E, F, T, k);
   hipError_t e = moe::launch_router(bf16, T, d, E, k, gating, x, w_router, idx, gate, nullptr, stream);
   // Batch Priority Routing: the importance score is each token's top-1 gate
   if (e == hipSuccess && order) e = moe::launch_priority_order(T, gate, k, order, w + L.sort, stream);
   if (e == hipSuccess)
-    e = moe::launch_permute(bf16, T, d, E, k, cap, x, idx, order, counts, offsets, srow, rslot, x_perm,
-                            chunks, stream);
+    e = moe::launch_permute(bf16, T, d, E, k, cap, x, idx, order, counts, offsets, srow, rslot,
+                            gather ? nullptr : x_perm, chunks, stream);
   if (e == hipSuccess)
-    e = bf16 ? moe::launch_ffn_bf16(R_max, seg_max_of(cap, R_max), d, E, F, x_perm, offsets, w_gate, w_up, w_down,
-                                    h, out_perm, ffn_ws_bytes(R_max, E, dt) ? ffn_ws : nullptr, stream)
+    e = bf16 ? moe::launch_ffn_bf16(R_max, seg_max, d, E, F, gather ? x : x_perm, offsets, w_gate, w_up, w_down, h,
+                                    out_perm, ffn_ws_bytes(R_max, E, dt) ? ffn_ws : nullptr, stream,
+                                    gather ? rslot : nullptr, k, T)
              : moe::launch_ffn_f32(R_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, h, out_perm,
                                    stream);
   if (e == hipSuccess) e = moe::launch_combine(bf16, T, d, k, out_perm, srow, gate, y, stream);

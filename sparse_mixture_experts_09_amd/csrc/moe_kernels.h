@@ -32,9 +32,16 @@ hipError_t launch_priority_order(int64_t T, const float* score, int64_t stride, 
 // R_max bounds the rows in all, seg_max the rows of any one expert.
 // ws (bf16 down projection only, may be NULL): ffn_bf16_workspace_bytes() of
 // scratch for the partial tiles of its split tail.
+// gather_slot (GEMM1 only, when ffn_bf16_can_gather): `in` is the unpermuted
+// activations [gather_T, d] and permuted row r reads token gather_slot[r] /
+// gather_k (the row -> slot map of the permutation), so no x_perm is needed.
 hipError_t launch_gemm_bf16(int which, int64_t R_max, int64_t seg_max, int d, int E, int F, const void* in,
                             const int32_t* offsets, const void* w0, const void* w1, void* out,
-                            void* ws, hipStream_t s);
+                            void* ws, hipStream_t s, const int32_t* gather_slot = nullptr, int gather_k = 0,
+                            int64_t gather_T = 0);
+bool ffn_bf16_can_gather(int64_t R_max, int64_t seg_max, int d, int E, int F, int64_t T);
+// whether moe_forward gathers (it does where that measured faster: k >= 4)
+bool ffn_bf16_gathers(int64_t R_max, int64_t seg_max, int d, int E, int F, int64_t T, int k);
 size_t ffn_bf16_workspace_bytes(int64_t R_max, int E);
 int compute_units();
 hipError_t launch_gemm_f32(int which, int64_t R_max, int d, int E, int F, const void* in,
@@ -43,7 +50,8 @@ hipError_t launch_gemm_f32(int which, int64_t R_max, int d, int E, int F, const 
 
 hipError_t launch_ffn_bf16(int64_t R_max, int64_t seg_max, int d, int E, int F, const void* x_perm,
                            const int32_t* offsets, const void* wg, const void* wu, const void* wd,
-                           void* h, void* out, void* ws, hipStream_t s);
+                           void* h, void* out, void* ws, hipStream_t s, const int32_t* gather_slot = nullptr,
+                           int gather_k = 0, int64_t gather_T = 0);
 
 hipError_t launch_ffn_f32(int64_t R_max, int d, int E, int F, const void* x_perm,
                           const int32_t* offsets, const void* wg, const void* wu, const void* wd,

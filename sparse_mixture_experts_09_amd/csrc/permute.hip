@@ -380,6 +380,7 @@ hipError_t launch_permute(bool bf16, int64_t T, int d, int E, int k, int64_t cap
                      expert_counts, expert_offsets);
   hipLaunchKernelGGL(perm_rank_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, E, k, cap, idx, order,
                      chunk_counts, expert_offsets, slot_row, row_slot);
+  if (x_perm == nullptr) return hipGetLastError();   // the layout only: the GEMM gathers the rows
   const size_t row_bytes = (size_t)d * (bf16 ? 2 : 4);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, T, k,
                      row_bytes, reinterpret_cast<const char*>(x), slot_row,

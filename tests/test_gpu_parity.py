@@ -406,3 +406,31 @@ def test_grouped_ffn_split_tail(case):
     assert_close_rows(host(h1[:R]), hh, "bf16", "h")
     assert_close_rows(host(o1[:R]), oo, "bf16", "o (split tail)")
     assert_close_rows(host(o3[:R]), oo, "bf16", "o (no split)")
+
+
+@pytest.mark.parametrize("fill", ["token", "priority"])
+@pytest.mark.parametrize("case", [
+    (3000, 1024, 6, 4, 512, 1.1, "bf16", 33),    # drops, ragged experts
+    (2048, 512, 16, 8, 256, 0.0, "bf16", 31),    # dropless, k = 8
+    (1000, 512, 16, 4, 256, 1.0, "bf16", 12),    # k = 4, 16 experts
+    (2048, 512, 8, 2, 1024, 0.0, "bf16", 34),    # k = 2: no gather, same check
+], ids=case_id)
+def test_forward_gather_equals_stage_path(case, fill):
+    """With 256-row tiles and k >= 4, moe_forward's gate/up GEMM reads the token
+    rows of x through the row -> slot map instead of a scattered x_perm; the
+    staged path (moe_permute's scatter, then moe_grouped_ffn) must give the
+    same bits, and both must match the oracle."""
+    w, a = workload(case)
+    assert moe.moe_rows_max(w.T, w.E, w.k, w.cf) >= 128 * w.E   # 256-row tiles
+    g = device_inputs(case)
+    y = moe.moe_forward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], w.k, w.cf, fill_order=fill)
+    idx, gate, _ = moe.moe_route(g["x"], g["w_router"], w.k)
+    perm = moe.moe_permute(g["x"], idx, w.E, w.cf, score=gate if fill == "priority" else None, score_stride=w.k)
+    h, o = moe.moe_grouped_ffn(perm["x_perm"], perm["expert_offsets"], g["w_gate"], g["w_up"], g["w_down"],
+                               w.T, w.k, w.cf)
+    y2 = moe.moe_unpermute_combine(o, perm["slot_row"], gate, w.E, w.cf)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    ref = orc.forward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], w.k, w.cf, w.dtype,
+                      bpr=fill == "priority")
+    assert_close_rows(host(y), ref["y"], w.dtype)
