@@ -30,6 +30,9 @@ SMALL = [
     (20, 64, 4, 3, 192, 0.0, "bf16", 22),        # 60 rows, one 64-deep K step in the gate/up GEMM
     (64, 192, 1, 1, 128, 0.0, "bf16", 23),       # one expert with 64 rows: two full token tiles
     (48, 128, 4, 1, 128, 0.5, "bf16", 24),       # decode-sized with drops
+    (600, 128, 256, 8, 64, 1.0, "bf16", 27),     # the most experts and slots: E = 256, k = 8
+    (40, 128, 256, 8, 64, 1.0, "bf16", 25),      # E = 256 with 78 empty experts, capacity 2
+    (200, 64, 8, 2, 64, 0.01, "bf16", 26),       # capacity 1: every expert keeps one token
     (257, 64, 4, 1, 128, 1.25, "f32", 13),
     (200, 100, 5, 2, 72, 0.8, "f32", 14),        # fp32: d, F not multiples of the tiles
     (90, 32, 3, 3, 36, 0.0, "f32", 20),
