@@ -283,6 +283,54 @@ __device__ __forceinline__ void store_partials(const f32x16* acc, float* pt, int
   }
 }
 
+// Plain and SwiGLU epilogues through LDS (the stage buffers, free once the K
+// loop is done): the wavefronts write their bf16 values into a [BM][W] tile
+// (row r at r * 2W bytes, 16-byte chunk c at position c ^ (r mod W/8)), then
+// every thread stores whole 16-byte pieces, W/8 lanes per output row, so
+// each store instruction covers whole 128-byte lines. Stored straight from
+// the MFMA layout, one 8-byte store spans 32 rows (32 partial lines), and
+// draining those stores cost ~9 us per 256 x 256 tile round. Rows at or past
+// the segment's end and columns at or past N are not stored; N is a multiple
+// of 8. The caller has passed a barrier after its last LDS read.
+template <int EPI, int BM, int MB, int NB, int WM, int WN, int W>
+__device__ __forceinline__ void store_tile_lds(const f32x16* acc, const TileCoord& tc, int wm, int wn, int n0, int N,
+                                               int ldc, uint16_t* __restrict__ C, char* lds, int tid) {
+  static_assert(EPI == EPI_PLAIN || EPI == EPI_SWIGLU, "plain or SwiGLU tile");
+  constexpr int CH = W / 8;                      // 16-byte chunks per tile row
+  constexpr int RB = W * 2;                      // bytes per tile row
+  const int lane = tid & 63;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int row = wm * WM + mb * 32 + (lane & 31);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = acc[mb * NB + nb][4 * g + i];
+          v[i] = EPI == EPI_SWIGLU ? silu(a) * acc[MB * NB + mb * NB + nb][4 * g + i] : a;
+        }
+        uint2 o;
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(lds + row * RB + (((col >> 3) ^ (row & (CH - 1))) << 4) + ((col >> 2) & 1) * 8) = o;
+      }
+  }
+  __syncthreads();
+  const int rows = min(BM, tc.seg_rows - tc.m0);
+  uint16_t* c0 = C + (size_t)(tc.seg_start + tc.m0) * ldc + n0;
+  constexpr int PER = BM * CH / 512;           // pieces per thread (512 threads)
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int cidx = tid + i * 512, row = cidx / CH, ch = cidx % CH;
+    const u32x4 v = ld16(lds + row * RB + ((ch ^ (row & (CH - 1))) << 4));
+    if (row < rows && n0 + ch * 8 < N) st16(c0 + (size_t)row * ldc + ch * 8, v);
+  }
+}
+
 template <int EPI, int BM, int MB, int NB, int WM, int WN>
 __device__ __forceinline__ void store_tile(const f32x16* acc, const TileCoord& tc, int wm, int wn, int n0, int N,
                                            int ldc, uint16_t* __restrict__ C, uint16_t* __restrict__ C2,
@@ -656,7 +704,12 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
     store_partials<BN, MB, NB, WM, WN>(acc, partials + (size_t)(w.split * ns + w.slice) * BM * BN, wm, wn, lane);
     return;
   }
-  store_tile<EPI, BM, MB, NB, WM, WN>(acc, tc, wm, wn, n0, N, ldc, C, C2, C3, X0, X1, ldx, lane);
+  if constexpr (EPI == EPI_PLAIN || EPI == EPI_SWIGLU) {
+    __syncthreads();   // every wavefront is done reading the stages
+    store_tile_lds<EPI, BM, MB, NB, WM, WN, BN>(acc, tc, wm, wn, n0, N, ldc, C, smem, tid);
+  } else {
+    store_tile<EPI, BM, MB, NB, WM, WN>(acc, tc, wm, wn, n0, N, ldc, C, C2, C3, X0, X1, ldx, lane);
+  }
 }
 
 // ---------------------------------------------------------------------------
