@@ -283,22 +283,17 @@ __device__ __forceinline__ void store_partials(const f32x16* acc, float* pt, int
   }
 }
 
-// Plain and SwiGLU epilogues through LDS (the stage buffers, free once the K
-// loop is done): the wavefronts write their bf16 values into a [BM][W] tile
-// (row r at r * 2W bytes, 16-byte chunk c at position c ^ (r mod W/8)), then
-// every thread stores whole 16-byte pieces, W/8 lanes per output row, so
-// each store instruction covers whole 128-byte lines. Stored straight from
-// the MFMA layout, one 8-byte store spans 32 rows (32 partial lines), and
-// draining those stores cost ~9 us per 256 x 256 tile round. Rows at or past
-// the segment's end and columns at or past N are not stored; N is a multiple
-// of 8. The caller has passed a barrier after its last LDS read.
-template <int EPI, int BM, int MB, int NB, int WM, int WN, int W>
-__device__ __forceinline__ void store_tile_lds(const f32x16* acc, const TileCoord& tc, int wm, int wn, int n0, int N,
-                                               int ldc, uint16_t* __restrict__ C, char* lds, int tid) {
-  static_assert(EPI == EPI_PLAIN || EPI == EPI_SWIGLU, "plain or SwiGLU tile");
-  constexpr int CH = W / 8;                      // 16-byte chunks per tile row
-  constexpr int RB = W * 2;                      // bytes per tile row
-  const int lane = tid & 63;
+// Output tiles through LDS (the stage buffers, free once the K loop is done):
+// the wavefronts write their bf16 values into a [BM][W] tile (row r at r * 2W
+// bytes, 16-byte chunk c at position c ^ (r mod W/8)), then every thread
+// stores whole 16-byte pieces, W/8 lanes per output row, so each store
+// instruction covers whole 128-byte lines. Stored straight from the MFMA
+// layout, one 8-byte store spans 32 rows (32 partial lines); draining those
+// cost ~9 us per 256 x 256 tile round. Callers pass a barrier after their
+// last LDS read before lds_put_tile.
+template <int MB, int NB, int WM, int WN, int W, class Val>
+__device__ __forceinline__ void lds_put_tile(char* lds, int wm, int wn, int lane, Val val) {
+  constexpr int CH = W / 8, RB = W * 2;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int row = wm * WM + mb * 32 + (lane & 31);
@@ -307,28 +302,45 @@ __device__ __forceinline__ void store_tile_lds(const f32x16* acc, const TileCoor
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = acc[mb * NB + nb][4 * g + i];
-          v[i] = EPI == EPI_SWIGLU ? silu(a) * acc[MB * NB + mb * NB + nb][4 * g + i] : a;
-        }
         uint2 o;
-        o.x = pack_bf16x2(v[0], v[1]);
-        o.y = pack_bf16x2(v[2], v[3]);
+        o.x = pack_bf16x2(val(mb, nb, g, 0), val(mb, nb, g, 1));
+        o.y = pack_bf16x2(val(mb, nb, g, 2), val(mb, nb, g, 3));
         *reinterpret_cast<uint2*>(lds + row * RB + (((col >> 3) ^ (row & (CH - 1))) << 4) + ((col >> 2) & 1) * 8) = o;
       }
   }
-  __syncthreads();
-  const int rows = min(BM, tc.seg_rows - tc.m0);
-  uint16_t* c0 = C + (size_t)(tc.seg_start + tc.m0) * ldc + n0;
+}
+// Then, after a barrier: tile row r goes to row_ptr(r) (nullptr: not stored),
+// its 16-byte piece c only if c < chunks.
+template <int BM, int W, class RowPtr>
+__device__ __forceinline__ void lds_store_rows(const char* lds, int tid, int chunks, RowPtr row_ptr) {
+  constexpr int CH = W / 8, RB = W * 2;
   constexpr int PER = BM * CH / 512;           // pieces per thread (512 threads)
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int cidx = tid + i * 512, row = cidx / CH, ch = cidx % CH;
     const u32x4 v = ld16(lds + row * RB + ((ch ^ (row & (CH - 1))) << 4));
-    if (row < rows && n0 + ch * 8 < N) st16(c0 + (size_t)row * ldc + ch * 8, v);
+    uint16_t* dst = row_ptr(row);
+    if (dst != nullptr && ch < chunks) st16(dst + ch * 8, v);
   }
+}
+
+// Plain and SwiGLU epilogues of the grouped GEMM tiles, through LDS: rows at
+// or past the segment's end and columns at or past N (a multiple of 8) are
+// not stored.
+template <int EPI, int BM, int MB, int NB, int WM, int WN, int W>
+__device__ __forceinline__ void store_tile_lds(const f32x16* acc, const TileCoord& tc, int wm, int wn, int n0, int N,
+                                               int ldc, uint16_t* __restrict__ C, char* lds, int tid) {
+  static_assert(EPI == EPI_PLAIN || EPI == EPI_SWIGLU, "plain or SwiGLU tile");
+  lds_put_tile<MB, NB, WM, WN, W>(lds, wm, wn, tid & 63, [&](int mb, int nb, int g, int i) {
+    const float a = acc[mb * NB + nb][4 * g + i];
+    return EPI == EPI_SWIGLU ? silu(a) * acc[MB * NB + mb * NB + nb][4 * g + i] : a;
+  });
+  __syncthreads();
+  const int rows = min(BM, tc.seg_rows - tc.m0);
+  uint16_t* c0 = C + (size_t)(tc.seg_start + tc.m0) * ldc + n0;
+  lds_store_rows<BM, W>(lds, tid, (N - n0) / 8, [&](int row) {
+    return row < rows ? c0 + (size_t)row * ldc : static_cast<uint16_t*>(nullptr);
+  });
 }
 
 template <int EPI, int BM, int MB, int NB, int WM, int WN>
@@ -987,25 +999,17 @@ __global__ __launch_bounds__(512) void wgrad_dma_kernel(int E, const int32_t* __
     }
     wait_vmcnt<0>();
   }
-  // lane holds row m (the A operand's row, lane & 31) and columns n = 8g + 4(lane >> 5) + 0..3
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = m0 + wm * WM + mb * 32 + (lane & 31);
-    if (m >= M) continue;
-    uint16_t* crow = m < M1 ? C0 + ((size_t)e * M1 + m) * (size_t)N
-                            : C1 + ((size_t)e * (M - M1) + (m - M1)) * (size_t)N;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
-        if (n >= N) continue;
-        uint2 w;
-        w.x = pack_bf16x2(acc[mb * NB + nb][4 * g], acc[mb * NB + nb][4 * g + 1]);
-        w.y = pack_bf16x2(acc[mb * NB + nb][4 * g + 2], acc[mb * NB + nb][4 * g + 3]);
-        *reinterpret_cast<uint2*>(crow + n) = w;
-      }
-  }
+  // the tile through LDS (every DMA has landed, so a barrier frees the stages):
+  // row m < M1 of expert e goes to C0[e][m], m >= M1 to C1[e][m - M1]
+  __syncthreads();
+  lds_put_tile<MB, NB, WM, WN, BN>(smem, wm, wn, lane,
+                                   [&](int mb, int nb, int g, int i) { return acc[mb * NB + nb][4 * g + i]; });
+  __syncthreads();
+  lds_store_rows<BM, BN>(smem, threadIdx.x, (N - n0) / 8, [&](int row) {
+    const int m = m0 + row;
+    if (m >= M) return static_cast<uint16_t*>(nullptr);
+    return (m < M1 ? C0 + ((size_t)e * M1 + m) * (size_t)N : C1 + ((size_t)e * (M - M1) + (m - M1)) * (size_t)N) + n0;
+  });
 }
 
 template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN)>
