@@ -260,7 +260,6 @@ __device__ __forceinline__ void dma16(const void* g, char* lds) {
 // ldc / ldx: row strides (elements) of the outputs / of X0 and X1.
 constexpr int EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_SWIGLU_AB = 2, EPI_SWIGLU_BWD = 3;
 
-
 // Epilogues of the 256-row tiles (wavefront (wm, wn) owns rows wm*WM.. and
 // columns wn*WN.. of the tile; acc[mb*NB + nb] is the 32x32 block mb, nb, and
 // in SwiGLU tiles acc[MB*NB + ...] holds the matching up products). A lane
@@ -291,9 +290,14 @@ __device__ __forceinline__ void store_partials(const f32x16* acc, float* pt, int
 // layout, one 8-byte store spans 32 rows (32 partial lines); draining those
 // cost ~9 us per 256 x 256 tile round. Callers pass a barrier after their
 // last LDS read before lds_put_tile.
+
+// byte offset of the 4 bf16 at (row, col), col a multiple of 4, in the tile
+template <int W>
+__device__ __forceinline__ int lds_tile_pos(int row, int col) {
+  return row * (W * 2) + (((col >> 3) ^ (row & (W / 8 - 1))) << 4) + ((col >> 2) & 1) * 8;
+}
 template <int MB, int NB, int WM, int WN, int W, class Val>
 __device__ __forceinline__ void lds_put_tile(char* lds, int wm, int wn, int lane, Val val) {
-  constexpr int CH = W / 8, RB = W * 2;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int row = wm * WM + mb * 32 + (lane & 31);
@@ -305,8 +309,24 @@ __device__ __forceinline__ void lds_put_tile(char* lds, int wm, int wn, int lane
         uint2 o;
         o.x = pack_bf16x2(val(mb, nb, g, 0), val(mb, nb, g, 1));
         o.y = pack_bf16x2(val(mb, nb, g, 2), val(mb, nb, g, 3));
-        *reinterpret_cast<uint2*>(lds + row * RB + (((col >> 3) ^ (row & (CH - 1))) << 4) + ((col >> 2) & 1) * 8) = o;
+        *reinterpret_cast<uint2*>(lds + lds_tile_pos<W>(row, col)) = o;
       }
+  }
+}
+// The reverse of lds_store_rows: tile row r from src + r * ld (a buffer whose
+// record count ends at the last valid row, so rows past it read zeros), its
+// 16-byte piece c only if c < chunks (else zeros).
+// Tile row j comes from source row row_of(j).
+template <int BM, int W, class RowOf>
+__device__ __forceinline__ void lds_load_rows(char* lds, int tid, int chunks, __amdgpu_buffer_rsrc_t src, int ld,
+                                              RowOf row_of) {
+  constexpr int CH = W / 8, RB = W * 2;
+  constexpr int PER = BM * CH / 512;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int cidx = tid + i * 512, row = cidx / CH, ch = cidx % CH;
+    const u32x4 v = bload16(src, ch < chunks ? (uint32_t)(row_of(row) * ld + ch * 8) * 2u : 0x80000000u);
+    st16(lds + row * RB + ((ch ^ (row & (CH - 1))) << 4), v);
   }
 }
 // Then, after a barrier: tile row r goes to row_ptr(r) (nullptr: not stored),
@@ -341,115 +361,6 @@ __device__ __forceinline__ void store_tile_lds(const f32x16* acc, const TileCoor
   lds_store_rows<BM, W>(lds, tid, (N - n0) / 8, [&](int row) {
     return row < rows ? c0 + (size_t)row * ldc : static_cast<uint16_t*>(nullptr);
   });
-}
-
-template <int EPI, int BM, int MB, int NB, int WM, int WN>
-__device__ __forceinline__ void store_tile(const f32x16* acc, const TileCoord& tc, int wm, int wn, int n0, int N,
-                                           int ldc, uint16_t* __restrict__ C, uint16_t* __restrict__ C2,
-                                           uint16_t* __restrict__ C3, const uint16_t* __restrict__ X0,
-                                           const uint16_t* __restrict__ X1, int ldx, int lane) {
-  if constexpr (EPI == EPI_SWIGLU_BWD) {
-    // a and b come through buffer loads and da, db go out through buffer
-    // stores whose record counts end at the segment's last row (past it loads
-    // read zeros and stores are dropped); a column past N gets an offset
-    // beyond every record count. The loads for half of the row blocks are
-    // issued together before any of their stores (the compiler cannot move a
-    // buffer load above a buffer store), so the epilogue waits on memory
-    // twice per tile instead of once per 4 elements.
-    constexpr int MBH = MB / 2 > 0 ? MB / 2 : 1;
-    const int rows = min(BM, tc.seg_rows - tc.m0);
-    const size_t rb0 = (size_t)(tc.seg_start + tc.m0);
-    const auto r0 = make_rsrc(X0 + rb0 * ldx, (uint32_t)((size_t)rows * ldx * 2));
-    const auto r1 = make_rsrc(X1 + rb0 * ldx, (uint32_t)((size_t)rows * ldx * 2));
-    const auto wc = make_rsrc(C + rb0 * ldc, (uint32_t)((size_t)rows * ldc * 2));
-    const auto wc2 = make_rsrc(C2 + rb0 * ldc, (uint32_t)((size_t)rows * ldc * 2));
-    auto offs = [&](int mb, int nb, int g, int ld) {
-      const int rl = wm * WM + mb * 32 + (lane & 31);
-      const int col = n0 + wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
-      return col < N ? (uint32_t)(rl * ld + col) * 2u : 0x80000000u;
-    };
-#pragma unroll
-    for (int h = 0; h < MB; h += MBH) {
-      uint2 ra[MBH][NB][4], rv[MBH][NB][4];
-#pragma unroll
-      for (int m = 0; m < MBH; ++m)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            ra[m][nb][g] = bload8(r0, offs(h + m, nb, g, ldx));
-            rv[m][nb][g] = bload8(r1, offs(h + m, nb, g, ldx));
-          }
-#pragma unroll
-      for (int m = 0; m < MBH; ++m)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const uint2 a2 = ra[m][nb][g], b2 = rv[m][nb][g];
-            const float av[4] = {bf16_lo(a2.x), bf16_hi(a2.x), bf16_lo(a2.y), bf16_hi(a2.y)};
-            const float bv[4] = {bf16_lo(b2.x), bf16_hi(b2.x), bf16_lo(b2.y), bf16_hi(b2.y)};
-            float da[4], db[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              // silu(a) = a sg and silu'(a) = sg (1 + a (1 - sg)), sg = sigmoid(a)
-              const float dh = acc[(h + m) * NB + nb][4 * g + i], sg = sigmoid(av[i]);
-              da[i] = dh * bv[i] * (sg * (1.0f + av[i] * (1.0f - sg)));
-              db[i] = dh * (av[i] * sg);
-            }
-            uint2 wa, wdb;
-            wa.x = pack_bf16x2(da[0], da[1]);
-            wa.y = pack_bf16x2(da[2], da[3]);
-            wdb.x = pack_bf16x2(db[0], db[1]);
-            wdb.y = pack_bf16x2(db[2], db[3]);
-            const uint32_t co = offs(h + m, nb, g, ldc);
-            bstore8(wc, co, wa);
-            bstore8(wc2, co, wdb);
-          }
-    }
-    return;
-  }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int rloc = tc.m0 + wm * WM + mb * 32 + (lane & 31);
-    if (rloc >= tc.seg_rows) continue;
-    const size_t grow = (size_t)(tc.seg_start + rloc);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = n0 + wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5);
-        if (col >= N) continue;
-        const size_t at = grow * (size_t)ldc + col;
-        float v[4];
-        if (EPI == EPI_PLAIN) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[mb * NB + nb][4 * g + i];
-        } else {   // EPI_SWIGLU, EPI_SWIGLU_AB
-          float ga[4], up[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            ga[i] = acc[mb * NB + nb][4 * g + i];
-            up[i] = acc[MB * NB + mb * NB + nb][4 * g + i];
-            v[i] = silu(ga[i]) * up[i];
-          }
-          if (EPI == EPI_SWIGLU_AB) {
-            uint2 wa, wb;
-            wa.x = pack_bf16x2(ga[0], ga[1]);
-            wa.y = pack_bf16x2(ga[2], ga[3]);
-            wb.x = pack_bf16x2(up[0], up[1]);
-            wb.y = pack_bf16x2(up[2], up[3]);
-            *reinterpret_cast<uint2*>(C2 + at) = wa;
-            *reinterpret_cast<uint2*>(C3 + at) = wb;
-          }
-        }
-        uint2 w;
-        w.x = pack_bf16x2(v[0], v[1]);
-        w.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(C + at) = w;
-      }
-    }
-  }
 }
 
 // Sum the K-slice partials of each split tail tile in slice order and store
@@ -487,7 +398,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(int E, const int32_t*
 // ---------------------------------------------------------------------------
 // Main path: 256 x BN tiles (256 weight rows: BN gate + BN up rows in GEMM1),
 // wavefronts split 2 x 4, the LDS layout and bank swizzle of the DMA loop
-// above and the epilogues of store_tile, with register-staged loads:
+// above and the LDS-staged epilogues, with register-staged loads:
 // each thread fetches four 16-byte pieces of each operand per K step with
 // buffer loads (whole 128-byte rows across 8 lanes; the descriptors' record
 // counts end at the expert's last row and at the weight's last row, so
@@ -719,8 +630,93 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
   if constexpr (EPI == EPI_PLAIN || EPI == EPI_SWIGLU) {
     __syncthreads();   // every wavefront is done reading the stages
     store_tile_lds<EPI, BM, MB, NB, WM, WN, BN>(acc, tc, wm, wn, n0, N, ldc, C, smem, tid);
-  } else {
-    store_tile<EPI, BM, MB, NB, WM, WN>(acc, tc, wm, wn, n0, N, ldc, C, C2, C3, X0, X1, ldx, lane);
+  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+    // a and b come in and da, db go out as whole-row 16-byte pieces through
+    // LDS, in two passes over half of every wavefront's row blocks (128 tile
+    // rows: wm * 128 + 64 h + 0..63 for pass h). A pass loads those rows of a
+    // and b into the two LDS halves (lds rows j = 64 wm + 0..63), turns b into
+    // da and a into db in place, and stores both. Stored straight from the
+    // MFMA layout each 8-byte access spanned 32 rows (32 partial lines).
+    static_assert(2 * (BM / 2) * BN * 2 <= 2 * STAGE && MB % 2 == 0, "two [BM/2][BN] bf16 tiles in LDS");
+    constexpr int HR = BM / 2, HALF = HR * BN * 2;
+    const int rows = min(BM, tc.seg_rows - tc.m0);
+    const int chunks = (N - n0) / 8;
+    const size_t xr0 = (size_t)(tc.seg_start + tc.m0) * ldx + n0;
+    const size_t cr0 = (size_t)(tc.seg_start + tc.m0) * ldc + n0;
+    const uint32_t xbytes = (uint32_t)((size_t)rows * ldx * 2);
+    const auto ra = make_rsrc(X0 + xr0, xbytes), rbv = make_rsrc(X1 + xr0, xbytes);
+    char* la = smem;
+    char* lb = smem + HALF;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      auto row_of = [&](int jr) { return (jr >> 6) * 128 + 64 * h + (jr & 63); };   // lds row -> tile row
+      __syncthreads();
+      lds_load_rows<HR, BN>(la, tid, chunks, ra, ldx, row_of);
+      lds_load_rows<HR, BN>(lb, tid, chunks, rbv, ldx, row_of);
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < MB / 2; ++m)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int jr = wm * 64 + m * 32 + (lane & 31);
+            const int pos = lds_tile_pos<BN>(jr, wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5));
+            uint2* pa = reinterpret_cast<uint2*>(la + pos);
+            uint2* pb = reinterpret_cast<uint2*>(lb + pos);
+            const uint2 a2 = *pa, b2 = *pb;
+            const float av[4] = {bf16_lo(a2.x), bf16_hi(a2.x), bf16_lo(a2.y), bf16_hi(a2.y)};
+            const float bv[4] = {bf16_lo(b2.x), bf16_hi(b2.x), bf16_lo(b2.y), bf16_hi(b2.y)};
+            float da[4], db[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              // silu(a) = a sg and silu'(a) = sg (1 + a (1 - sg)), sg = sigmoid(a)
+              const float dh = acc[(MB / 2 * h + m) * NB + nb][4 * g + i], sg = sigmoid(av[i]);
+              da[i] = dh * bv[i] * (sg * (1.0f + av[i] * (1.0f - sg)));
+              db[i] = dh * (av[i] * sg);
+            }
+            uint2 wa, wb;
+            wa.x = pack_bf16x2(da[0], da[1]);
+            wa.y = pack_bf16x2(da[2], da[3]);
+            wb.x = pack_bf16x2(db[0], db[1]);
+            wb.y = pack_bf16x2(db[2], db[3]);
+            *pb = wa;
+            *pa = wb;
+          }
+      __syncthreads();
+      lds_store_rows<HR, BN>(lb, tid, chunks, [&](int jr) {
+        const int r = row_of(jr);
+        return r < rows ? C + cr0 + (size_t)r * ldc : static_cast<uint16_t*>(nullptr);
+      });
+      lds_store_rows<HR, BN>(la, tid, chunks, [&](int jr) {
+        const int r = row_of(jr);
+        return r < rows ? C2 + cr0 + (size_t)r * ldc : static_cast<uint16_t*>(nullptr);
+      });
+    }
+  } else if constexpr (EPI == EPI_SWIGLU_AB) {
+    // h and a (gate) through the two halves of LDS, then b (up)
+    static_assert(BN * BM * 2 * 2 <= 2 * STAGE, "two [BM][BN] bf16 tiles in LDS");
+    constexpr int HALF = BM * BN * 2;
+    const int rows = min(BM, tc.seg_rows - tc.m0);
+    const size_t r0 = (size_t)(tc.seg_start + tc.m0) * ldc + n0;
+    auto rows_of = [&](uint16_t* base) {
+      return [=](int row) { return row < rows ? base + r0 + (size_t)row * ldc : static_cast<uint16_t*>(nullptr); };
+    };
+    __syncthreads();
+    lds_put_tile<MB, NB, WM, WN, BN>(smem, wm, wn, lane, [&](int mb, int nb, int g, int i) {
+      return silu(acc[mb * NB + nb][4 * g + i]) * acc[MB * NB + mb * NB + nb][4 * g + i];
+    });
+    lds_put_tile<MB, NB, WM, WN, BN>(smem + HALF, wm, wn, lane,
+                                     [&](int mb, int nb, int g, int i) { return acc[mb * NB + nb][4 * g + i]; });
+    __syncthreads();
+    lds_store_rows<BM, BN>(smem, tid, (N - n0) / 8, rows_of(C));
+    lds_store_rows<BM, BN>(smem + HALF, tid, (N - n0) / 8, rows_of(C2));
+    __syncthreads();
+    lds_put_tile<MB, NB, WM, WN, BN>(smem, wm, wn, lane, [&](int mb, int nb, int g, int i) {
+      return acc[MB * NB + mb * NB + nb][4 * g + i];
+    });
+    __syncthreads();
+    lds_store_rows<BM, BN>(smem, tid, (N - n0) / 8, rows_of(C3));
   }
 }
 

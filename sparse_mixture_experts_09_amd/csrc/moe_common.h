@@ -66,21 +66,14 @@ __device__ __forceinline__ u32x4 pack16(F32, const float* f) {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// Raw buffer access: the record count ends the buffer; a load past it returns
-// zeros without touching memory and a store past it is dropped. The base and
-// the count must be wave-uniform.
+// Raw buffer access: the record count ends the buffer, and a load past it
+// returns zeros without touching memory. The base and the count must be
+// wave-uniform.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
-}
-__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0));
-}
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)voff, 0, 0);
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
