@@ -11,8 +11,6 @@
 //                    up to 64 (the K ranges of the weight-gradient GEMMs);
 //   seg_transpose    [R, C] expert-major rows -> [C, ldo] with expert e's rows
 //                    at columns koff[e] .. (zero padding up to a multiple of 64);
-//   batch_transpose  [B][rows][cols] -> [B][cols][ldo] at a column offset
-//                    (weights, so the data-gradient GEMMs are K-contiguous too);
 //   gate_bwd         per token: dg_j = <dy, o_j>, d_o rows = bf16(g_j dy),
 //                    dl = g (dg - sum g dg) (softmax over the chosen logits);
 //   router_wgrad     dW_g[e] = sum over (t, j) with S_j = e of dl[t, j] x[t]
@@ -87,19 +85,6 @@ __global__ __launch_bounds__(256) void seg_transpose_kernel(int E, int C, int64_
   transpose_tile64(
       [&](int i) -> const uint16_t* { return i0 + i < cnt ? in + (size_t)(base + i) * C + c0 : nullptr; },
       C - c0, [&](int j) -> uint16_t* { return c0 + j < C ? out + (size_t)(c0 + j) * ldo + p0 : nullptr; }, tile);
-}
-
-// [B][rows][cols] -> [B][cols][ldo] at column col_off; rows and cols are multiples of 64.
-__global__ __launch_bounds__(256) void batch_transpose_kernel(int rows, int cols, int64_t ldo, int col_off,
-                                                              const uint16_t* __restrict__ in,
-                                                              uint16_t* __restrict__ out) {
-  __shared__ __align__(16) uint16_t tile[64][kTP];
-  const int b = blockIdx.z;
-  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-  const uint16_t* ib = in + (size_t)b * rows * cols;
-  uint16_t* ob = out + (size_t)b * cols * ldo;
-  transpose_tile64([&](int i) -> const uint16_t* { return ib + (size_t)(r0 + i) * cols + c0; }, 64,
-                   [&](int j) -> uint16_t* { return ob + (size_t)(c0 + j) * ldo + col_off + r0; }, tile);
 }
 
 // One wavefront per token; lane l covers the 8-element pieces l, l + 64, ... of a row.
@@ -239,14 +224,6 @@ hipError_t launch_seg_transpose(int E, int64_t rows_pad_max, int C, int64_t ldo,
                                 const int32_t* koff, const void* in, void* out, hipStream_t s) {
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((rows_pad_max + 63) / 64));
   hipLaunchKernelGGL(seg_transpose_kernel, grid, dim3(256), 0, s, E, C, ldo, offsets, koff,
-                     reinterpret_cast<const uint16_t*>(in), reinterpret_cast<uint16_t*>(out));
-  return hipGetLastError();
-}
-
-hipError_t launch_batch_transpose(int B, int rows, int cols, int64_t ldo, int col_off, const void* in, void* out,
-                                  hipStream_t s) {
-  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64), (unsigned)B);
-  hipLaunchKernelGGL(batch_transpose_kernel, grid, dim3(256), 0, s, rows, cols, ldo, col_off,
                      reinterpret_cast<const uint16_t*>(in), reinterpret_cast<uint16_t*>(out));
   return hipGetLastError();
 }

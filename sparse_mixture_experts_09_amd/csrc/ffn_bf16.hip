@@ -242,6 +242,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // One 16-byte-per-lane global -> LDS DMA (global_load_lds_dwordx4). The LDS
 // address must be wave-uniform; lane L lands at lds + 16 L. The builtin only
@@ -421,14 +423,15 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(int E, const int32_t*
 // last tile reloads the last one).
 // ---------------------------------------------------------------------------
 
-template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN)>
+template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN), bool BT = false>
 __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
     int E, const int32_t* __restrict__ offsets, int N, int K, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT,
     int P, int max_split, float* __restrict__ partials, int ldc, uint16_t* __restrict__ C2,
     uint16_t* __restrict__ C3, const uint16_t* __restrict__ X0, const uint16_t* __restrict__ X1, int ldx,
-    const int32_t* __restrict__ a_slot, int a_k, uint32_t a_records) {
+    const int32_t* __restrict__ a_slot, int a_k, uint32_t a_records, int ldb, int ksplit) {
   static_assert(SWIGLU == (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_AB), "tile layout and epilogue");
+  static_assert(!BT || !SWIGLU, "K-major weights: plain tiles only");
   constexpr int BM = 256, NWM = 2, NWN = 4, NT_ = 512;
   constexpr int BROWS = SWIGLU ? 2 * BN : BN;
   static_assert(BROWS == 256, "both operands are 256-row tiles");
@@ -439,7 +442,8 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
   constexpr int PT = 2048 / NT_;                 // 16-byte pieces per thread per operand per K step
   constexpr int RSTEP = NT_ / 8;                 // rows between a thread's pieces
   constexpr int STAGE = (BM + BROWS) * kRowB;
-  constexpr int NM = MB * NBF, NR = MB + NBF;    // MFMAs and fragment reads per substep
+  // MFMAs and fragment reads per substep (a K-major weight fragment takes two transposing reads)
+  constexpr int NM = MB * NBF, NR = MB + (BT ? 2 : 1) * NBF;
   extern __shared__ __align__(16) char smem[];
 
   const int KTall = K / kBK;
@@ -460,8 +464,20 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
   const int a_rows = min(BM, tc.seg_rows - tc.m0);
   const int b_rows = min(BN, N - n0);
   const size_t wrow0 = (size_t)tc.e * N + n0;
-  const auto rb0 = make_rsrc(B0 + wrow0 * K, (uint32_t)(b_rows * rowb));
-  const auto rb1 = make_rsrc((SWIGLU ? B1 : B0) + wrow0 * K, (uint32_t)(b_rows * rowb));
+  // K-major weights (BT): expert e's rows k < ksplit are B0[e] [ksplit][ldb],
+  // rows k >= ksplit are B1[e] [K - ksplit][ldb]; the descriptors start at
+  // column n0 (columns past N read the next row and are never stored)
+  const auto rb0 = BT ? make_rsrc(B0 + (size_t)tc.e * ksplit * ldb + n0, (uint32_t)(((size_t)ksplit * ldb - n0) * 2))
+                      : make_rsrc(B0 + wrow0 * K, (uint32_t)(b_rows * rowb));
+  const auto rb1 = BT ? make_rsrc((K > ksplit ? B1 : B0) + (size_t)tc.e * (K - ksplit) * ldb + n0,
+                                  (uint32_t)(((size_t)(K - ksplit) * ldb - n0) * 2))
+                      : make_rsrc((SWIGLU ? B1 : B0) + wrow0 * K, (uint32_t)(b_rows * rowb));
+  // BT staging: piece i of a thread is k-row (tid >> 5) + 16 i, 16-byte chunk tid & 31 of the
+  // 256 columns; in LDS the [64][256] tile has 512-byte rows with chunk c of row r at
+  // position c ^ ((r & 3) << 2), which keeps the transposing fragment reads conflict-free
+  const int bk0 = tid >> 5, bch = tid & 31;
+  const uint32_t bt_off = (uint32_t)(bk0 * ldb + bch * 8) * 2u;
+  const int bt_wofs = BM * kRowB + bk0 * 512 + ((bch ^ ((bk0 & 3) << 2)) << 4);
   const int row0 = tid >> 3, ch = tid & 7;
   const uint32_t voff = (uint32_t)(row0 * rowb) + ch * 16 + (uint32_t)kb * kRowB;
   const uint32_t rstep = (uint32_t)(RSTEP * rowb);
@@ -496,6 +512,11 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
     const uint32_t ko = (uint32_t)(kt < KT ? kt : KT - 1) * kRowB;
     if (p < PT) {
       stg[p] = bload16(ra, aoff[p] + ko);
+    } else if constexpr (BT) {
+      const int k = ((kt < KT ? kt : KT - 1) + kb) * kBK;   // first k-row of the step (whole in B0 or in B1)
+      const int i = p - PT;
+      stg[p] = k < ksplit ? bload16(rb0, bt_off + (uint32_t)((k + 16 * i) * ldb) * 2u)
+                          : bload16(rb1, bt_off + (uint32_t)((k - ksplit + 16 * i) * ldb) * 2u);
     } else {
       const int i = p - PT;
       const bool up = SWIGLU && i * RSTEP >= BN;
@@ -503,8 +524,11 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
     }
   };
   auto sw = [&](int p, int stage) {
-    char* b = smem + stage * STAGE + wofs;
-    st16(p < PT ? b + p * RSTEP * kRowB : b + BM * kRowB + (p - PT) * RSTEP * kRowB, stg[p]);
+    char* b = smem + stage * STAGE;
+    if (BT && p >= PT)   // k-row bk0 + 16 i: (r & 3) is the same for every i
+      st16(b + bt_wofs + (p - PT) * 16 * 512, stg[p]);
+    else
+      st16(p < PT ? b + wofs + p * RSTEP * kRowB : b + wofs + BM * kRowB + (p - PT) * RSTEP * kRowB, stg[p]);
   };
 
   f32x16 acc[NACC];
@@ -513,6 +537,13 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
   bf16x8 fa[2][MB], fb[2][NBF];
+  // BT fragment reads: ds_read_b64_tr_b16 gives lane i of a 16-lane group
+  // element i & 3 of the 4-element vectors read by lanes (i >> 2) + 4 j,
+  // j = 0..3. Lane s of group q reads k-row k0 + (s >> 2), columns
+  // n0 + 4 (s & 3) .. +3 (k0 = 16 sub + 8 (q >> 1), n0 = the block's first
+  // column + 16 (q & 1)), so lane i receives rows k0..k0+3 of column n0 + i;
+  // a second read at k0 + 4 completes the 8 k of the MFMA operand.
+  const int tq = lane >> 4, ts = lane & 15;
   auto read_frags = [&](int stage, int sub, bf16x8(&A_)[MB], bf16x8(&B_)[NBF]) {
     const char* buf = smem + stage * STAGE;
     const int chunk = 2 * sub + (lane >> 5);
@@ -521,9 +552,19 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
       A_[mb] = __builtin_bit_cast(bf16x8, ld16(buf + daddr(wm * WM + mb * 32 + (lane & 31), chunk)));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int row = wn * WN + nb * 32 + (lane & 31);
-      B_[nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(row, chunk)));
-      if (SWIGLU) B_[NB + nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(BN + row, chunk)));
+      if constexpr (BT) {
+        const int k = 16 * sub + 8 * (tq >> 1) + (ts >> 2);
+        const int n = wn * WN + nb * 32 + 16 * (tq & 1) + 4 * (ts & 3);
+        const char* at = buf + BM * kRowB + k * 512 + (((n >> 3) ^ ((k & 3) << 2)) << 4) + (n & 4) * 2;
+        const uint2 lo = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)at));
+        const uint2 hi = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(at + 4 * 512)));
+        const u32x4 v = {lo.x, lo.y, hi.x, hi.y};
+        B_[nb] = __builtin_bit_cast(bf16x8, v);
+      } else {
+        const int row = wn * WN + nb * 32 + (lane & 31);
+        B_[nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(row, chunk)));
+        if (SWIGLU) B_[NB + nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(BN + row, chunk)));
+      }
     }
   };
   auto mma = [&](const bf16x8(&A_)[MB], const bf16x8(&B_)[NBF]) {
@@ -1008,14 +1049,15 @@ __global__ __launch_bounds__(512) void wgrad_dma_kernel(int E, const int32_t* __
   });
 }
 
-template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN)>
+template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN), bool BT = false>
 hipError_t launch_reg(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A, const void* B0,
                       const void* B1, void* C, float* partials, int P, hipStream_t s, int ldc = 0,
                       void* C2 = nullptr, void* C3 = nullptr, const void* X0 = nullptr, const void* X1 = nullptr,
-                      int ldx = 0, const int32_t* a_slot = nullptr, int a_k = 1, uint32_t a_records = 0) {
+                      int ldx = 0, const int32_t* a_slot = nullptr, int a_k = 1, uint32_t a_records = 0,
+                      int ldb = 0, int ksplit = 0) {
   constexpr int BM = 256;
   constexpr size_t kLds = 2 * (size_t)(BM + 256) * kRowB;
-  auto kern = &ffn_bf16_reg_kernel<BN, SWIGLU, EPI>;
+  auto kern = &ffn_bf16_reg_kernel<BN, SWIGLU, EPI, BT>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
@@ -1028,7 +1070,7 @@ hipError_t launch_reg(int64_t R_max, int E, const int32_t* offsets, int N, int K
                      reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C), NT, P, max_split,
                      partials, ldc ? ldc : N, reinterpret_cast<uint16_t*>(C2), reinterpret_cast<uint16_t*>(C3),
                      reinterpret_cast<const uint16_t*>(X0), reinterpret_cast<const uint16_t*>(X1), ldx, a_slot, a_k,
-                     a_records);
+                     a_records, ldb, ksplit);
   if (split)
     hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(P * (BM / 16))), dim3(256), 0, s, E, offsets, N, K, NT,
                        P, max_split, partials, reinterpret_cast<uint16_t*>(C));
@@ -1141,19 +1183,26 @@ hipError_t launch_bwd_recompute_gate_up(int64_t R_max, int d, int E, int F, cons
 }
 
 hipError_t launch_bwd_dh(int64_t R_max, int d, int E, int F, const void* d_o, const int32_t* offsets,
-                         const void* w_down_t, const void* a_st, const void* b_st, void* dab, hipStream_t s) {
+                         const void* w_down, const void* a_st, const void* b_st, void* dab, hipStream_t s) {
   // dab [R, 2F]: da in columns 0..F-1, db in F..2F-1; the epilogue's buffer
-  // offsets within a 256-row tile of dab must stay below 2^31
-  if ((int64_t)256 * 2 * F * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  return launch_reg<256, false, EPI_SWIGLU_BWD>(R_max, E, offsets, F, d, d_o, w_down_t, nullptr, dab, nullptr, 0,
-                                                s, 2 * F, reinterpret_cast<uint16_t*>(dab) + F, nullptr, a_st,
-                                                b_st, F);
+  // offsets within a 256-row tile of dab, and those within one expert's
+  // W_down [d][F], must stay below 2^31
+  if ((int64_t)256 * 2 * F * 2 >= ((int64_t)1 << 31) || (int64_t)d * F * 2 >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
+  // dh = d_o . W_down[e] (contraction over d): W_down[e] [d][F] is the K-major weight
+  return launch_reg<256, false, EPI_SWIGLU_BWD, true>(R_max, E, offsets, F, d, d_o, w_down, nullptr, dab, nullptr, 0,
+                                                      s, 2 * F, reinterpret_cast<uint16_t*>(dab) + F, nullptr, a_st,
+                                                      b_st, F, nullptr, 1, 0, F, d);
 }
 
 hipError_t launch_bwd_dx_perm(int64_t R_max, int d, int E, int F, const void* dab, const int32_t* offsets,
-                              const void* w_gu_t, void* dx_perm, void* ws, hipStream_t s) {
-  return launch_reg<256, false>(R_max, E, offsets, d, 2 * F, dab, w_gu_t, nullptr, dx_perm,
-                                reinterpret_cast<float*>(ws), ws ? compute_units() : 0, s);
+                              const void* w_gate, const void* w_up, void* dx_perm, void* ws, hipStream_t s) {
+  if ((int64_t)d * F * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  // dx_perm = [da, db] . [W_gate[e]; W_up[e]] (contraction over 2F): K-major
+  // weight rows 0..F-1 from W_gate[e] [F][d], F..2F-1 from W_up[e]
+  return launch_reg<256, false, EPI_PLAIN, true>(R_max, E, offsets, d, 2 * F, dab, w_gate, w_up, dx_perm,
+                                                 reinterpret_cast<float*>(ws), ws ? compute_units() : 0, s, 0,
+                                                 nullptr, nullptr, nullptr, nullptr, 0, nullptr, 1, 0, d, F);
 }
 
 hipError_t launch_wgrad(int E, const int32_t* koff, int M, int M1, int N, int64_t ldk, const void* A, const void* B,

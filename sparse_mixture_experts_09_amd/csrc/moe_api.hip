@@ -607,7 +607,7 @@ int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float 
 
 struct BwdLayout {
   size_t idx, gate, slot_row, row_slot, counts, offsets, chunks, koff, dl, x_perm, a_st, b_st, h, o, d_o, dab,
-      dx_perm, w_down_t, w_gu_t, xp_t, d_o_t, h_t, dab_t, router_part, ffn, total;
+      dx_perm, xp_t, d_o_t, h_t, dab_t, router_part, ffn, total;
 };
 
 static BwdLayout bwd_layout(int64_t T, int d, int E, int k, int64_t R_max, int F) {
@@ -636,8 +636,6 @@ static BwdLayout bwd_layout(int64_t T, int d, int E, int k, int64_t R_max, int F
   L.d_o = take((size_t)R_max * d * 2);
   L.dab = take((size_t)R_max * 2 * F * 2);
   L.dx_perm = take((size_t)R_max * d * 2);
-  L.w_down_t = take((size_t)E * F * d * 2);
-  L.w_gu_t = take((size_t)E * d * 2 * F * 2);
   L.xp_t = take((size_t)d * Rp * 2);
   L.d_o_t = take((size_t)d * Rp * 2);
   L.h_t = take((size_t)F * Rp * 2);
@@ -709,15 +707,11 @@ int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F
                               ffn_ws, stream);
   // combine and gate backward: d_o rows, dl
   if (e == hipSuccess) e = moe::launch_gate_bwd(T, d, k, dy, w + L.o, srow, gate, w + L.d_o, dl, stream);
-  // data gradients through the experts
-  if (e == hipSuccess) e = moe::launch_batch_transpose(E, d, F, d, 0, w_down, w + L.w_down_t, stream);
+  // data gradients through the experts (the weights read as stored)
   if (e == hipSuccess)
-    e = moe::launch_bwd_dh(R_max, d, E, F, w + L.d_o, offsets, w + L.w_down_t, w + L.a_st, w + L.b_st, w + L.dab,
-                           stream);
-  if (e == hipSuccess) e = moe::launch_batch_transpose(E, F, d, 2 * F, 0, w_gate, w + L.w_gu_t, stream);
-  if (e == hipSuccess) e = moe::launch_batch_transpose(E, F, d, 2 * F, F, w_up, w + L.w_gu_t, stream);
+    e = moe::launch_bwd_dh(R_max, d, E, F, w + L.d_o, offsets, w_down, w + L.a_st, w + L.b_st, w + L.dab, stream);
   if (e == hipSuccess)
-    e = moe::launch_bwd_dx_perm(R_max, d, E, F, w + L.dab, offsets, w + L.w_gu_t, w + L.dx_perm, ffn_ws, stream);
+    e = moe::launch_bwd_dx_perm(R_max, d, E, F, w + L.dab, offsets, w_gate, w_up, w + L.dx_perm, ffn_ws, stream);
   // weight gradients: transposed activations, expert rows padded to 64
   if (e == hipSuccess) e = moe::launch_pad_offsets(E, offsets, koff, stream);
   if (e == hipSuccess) e = moe::launch_seg_transpose(E, Rp, d, Rp, offsets, koff, w + L.x_perm, w + L.xp_t, stream);

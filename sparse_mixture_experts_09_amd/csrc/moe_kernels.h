@@ -75,10 +75,12 @@ hipError_t launch_ec_combine(bool bf16, int64_t T, int d, int E, int64_t R, cons
 hipError_t launch_bwd_recompute_gate_up(int64_t R_max, int d, int E, int F, const void* x_perm,
                                         const int32_t* offsets, const void* wg, const void* wu, void* h,
                                         void* a_st, void* b_st, hipStream_t s);
+// dh and dx_perm read the weights as stored ([E, d, F] and [E, F, d]), with
+// transposing LDS reads
 hipError_t launch_bwd_dh(int64_t R_max, int d, int E, int F, const void* d_o, const int32_t* offsets,
-                         const void* w_down_t, const void* a_st, const void* b_st, void* dab, hipStream_t s);
+                         const void* w_down, const void* a_st, const void* b_st, void* dab, hipStream_t s);
 hipError_t launch_bwd_dx_perm(int64_t R_max, int d, int E, int F, const void* dab, const int32_t* offsets,
-                              const void* w_gu_t, void* dx_perm, void* ws, hipStream_t s);
+                              const void* w_gate, const void* w_up, void* dx_perm, void* ws, hipStream_t s);
 hipError_t launch_wgrad(int E, const int32_t* koff, int M, int M1, int N, int64_t ldk, const void* A, const void* B,
                         void* C0, void* C1, hipStream_t s);
 int64_t padded_rows_max(int64_t R_max, int E);
@@ -86,8 +88,6 @@ size_t router_wgrad_partial_bytes(int64_t T, int d, int E);
 hipError_t launch_pad_offsets(int E, const int32_t* offsets, int32_t* koff, hipStream_t s);
 hipError_t launch_seg_transpose(int E, int64_t rows_pad_max, int C, int64_t ldo, const int32_t* offsets,
                                 const int32_t* koff, const void* in, void* out, hipStream_t s);
-hipError_t launch_batch_transpose(int B, int rows, int cols, int64_t ldo, int col_off, const void* in, void* out,
-                                  hipStream_t s);
 hipError_t launch_gate_bwd(int64_t T, int d, int k, const void* dy, const void* o, const int32_t* slot_row,
                            const float* gate, void* d_o, float* dl, hipStream_t s);
 hipError_t launch_router_wgrad(int64_t T, int d, int E, int k, const void* x, const int32_t* idx, const float* dl,
