@@ -7,10 +7,6 @@
 // MoEs": y = sum_j g_j E_j(x), g = Softmax(TopK(x.W_g)); SwiGLU experts).
 //
 // Kernels here:
-//   pad_offsets      koff[e] = sum over e' < e of the expert's rows rounded
-//                    up to 64 (the K ranges of the weight-gradient GEMMs);
-//   seg_transpose    [R, C] expert-major rows -> [C, ldo] with expert e's rows
-//                    at columns koff[e] .. (zero padding up to a multiple of 64);
 //   gate_bwd         per token: dg_j = <dy, o_j>, d_o rows = bf16(g_j dy),
 //                    dl = g (dg - sum g dg) (softmax over the chosen logits);
 //   router_wgrad     dW_g[e] = sum over (t, j) with S_j = e of dl[t, j] x[t]
@@ -22,70 +18,6 @@
 namespace moe {
 
 namespace {
-
-__global__ void pad_offsets_kernel(int E, const int32_t* __restrict__ offsets, int32_t* __restrict__ koff) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int run = 0;
-  for (int e = 0; e < E; ++e) {
-    koff[e] = run;
-    const int cnt = offsets[e + 1] - offsets[e];
-    run += (cnt + 63) / 64 * 64;
-  }
-  koff[E] = run;
-}
-
-// 64 x 64 bf16 tile transposes. A thread moves 16-byte pieces: it loads 8
-// consecutive columns of an input row into LDS with one 16-byte write, and
-// gathers 8 consecutive rows of one column for one 16-byte output store.
-constexpr int kTP = 72;   // LDS row pitch in elements (64 + 8 keeps 16-byte alignment)
-
-// in_row(i) = pointer to input row i of the tile or nullptr (zero row);
-// out_row(j) = pointer to output row j of the tile (64 elements) or nullptr.
-template <typename InRow, typename OutRow>
-__device__ __forceinline__ void transpose_tile64(InRow in_row, int in_cols_valid, OutRow out_row,
-                                                 uint16_t (*tile)[kTP]) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int i = pass * 32 + (t >> 3), ch = t & 7;
-    const uint16_t* src = in_row(i);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (src != nullptr && ch * 8 < in_cols_valid) v = ld16(src + ch * 8);
-    *reinterpret_cast<u32x4*>(&tile[i][ch * 8]) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int j = pass * 32 + (t >> 3), ch = t & 7;
-    uint16_t* dst = out_row(j);
-    if (dst == nullptr) continue;
-    u32x4 v;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      v[q] = (uint32_t)tile[ch * 8 + 2 * q][j] | ((uint32_t)tile[ch * 8 + 2 * q + 1][j] << 16);
-    st16(dst + ch * 8, v);
-  }
-}
-
-// Block (cb, pb): 64 columns c0 = 64 cb of the input and 64 padded positions
-// p0 = 64 pb of the output. A 64-aligned block of positions lies inside one
-// expert, since every expert's range is a multiple of 64. C is a multiple of 8.
-__global__ __launch_bounds__(256) void seg_transpose_kernel(int E, int C, int64_t ldo, const int32_t* __restrict__ offsets,
-                                                            const int32_t* __restrict__ koff,
-                                                            const uint16_t* __restrict__ in, uint16_t* __restrict__ out) {
-  __shared__ __align__(16) uint16_t tile[64][kTP];
-  const int c0 = blockIdx.x * 64;
-  const int p0 = blockIdx.y * 64;
-  if (p0 >= koff[E]) return;
-  int e = 0;
-  while (e + 1 < E && koff[e + 1] <= p0) ++e;
-  const int cnt = offsets[e + 1] - offsets[e];
-  const int i0 = p0 - koff[e];                 // first row of the block inside expert e
-  const int64_t base = offsets[e] + i0;
-  transpose_tile64(
-      [&](int i) -> const uint16_t* { return i0 + i < cnt ? in + (size_t)(base + i) * C + c0 : nullptr; },
-      C - c0, [&](int j) -> uint16_t* { return c0 + j < C ? out + (size_t)(c0 + j) * ldo + p0 : nullptr; }, tile);
-}
 
 // One wavefront per token; lane l covers the 8-element pieces l, l + 64, ... of a row.
 __global__ __launch_bounds__(256) void gate_bwd_kernel(int64_t T, int d, int k, const uint16_t* __restrict__ dy,
@@ -209,23 +141,8 @@ __global__ __launch_bounds__(256) void dx_final_kernel(int64_t T, int d, int k, 
 
 }  // namespace
 
-int64_t padded_rows_max(int64_t R_max, int E) { return R_max + 64 * (int64_t)E; }
-
 size_t router_wgrad_partial_bytes(int64_t T, int d, int E) {
   return (size_t)((T + kRouterChunk - 1) / kRouterChunk) * E * d * 4;
-}
-
-hipError_t launch_pad_offsets(int E, const int32_t* offsets, int32_t* koff, hipStream_t s) {
-  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(64), 0, s, E, offsets, koff);
-  return hipGetLastError();
-}
-
-hipError_t launch_seg_transpose(int E, int64_t rows_pad_max, int C, int64_t ldo, const int32_t* offsets,
-                                const int32_t* koff, const void* in, void* out, hipStream_t s) {
-  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((rows_pad_max + 63) / 64));
-  hipLaunchKernelGGL(seg_transpose_kernel, grid, dim3(256), 0, s, E, C, ldo, offsets, koff,
-                     reinterpret_cast<const uint16_t*>(in), reinterpret_cast<uint16_t*>(out));
-  return hipGetLastError();
 }
 
 hipError_t launch_gate_bwd(int64_t T, int d, int k, const void* dy, const void* o, const int32_t* slot_row,

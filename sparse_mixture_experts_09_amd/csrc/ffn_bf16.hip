@@ -24,7 +24,8 @@
 //                           ragged last tile of each expert);
 //   ffn_bf16_skinny_kernel  at most 64 rows per expert (decode): streams the
 //                           weights through per-wavefront LDS stages;
-//   wgrad_dma_kernel        weight gradients (grouped K), global -> LDS DMA.
+//   wgrad_kernel            weight gradients (grouped K over each expert's rows;
+//                           both operands K-major, transposing LDS reads).
 // In GEMM1 the weight tile holds BN gate rows followed by BN up rows, so the
 // two products for one h element sit in the same lane and register and the
 // SwiGLU epilogue needs no data exchange.
@@ -207,25 +208,12 @@ __global__ __launch_bounds__(64 * NWM * NWN) void ffn_bf16_kernel(int E, const i
 }
 
 // ---------------------------------------------------------------------------
-// DMA main loop (the weight-gradient kernel): operand tiles go straight from
-// global memory into LDS with global_load_lds_dwordx4 (no staging registers,
-// no ds_write), K step 64, two LDS stages of 256 + 256 rows x 128 bytes.
-//
-// One DMA instruction writes 1 KB of LDS contiguously (lane L at +16 L, i.e.
-// 8 rows of 128 bytes), so the bank swizzle is applied on the global side:
-// the lane that lands on chunk position p of tile row r fetches chunk
-// p ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1). Full 128-byte rows keep every
-// global request a whole cache line.
-//
-// Schedule of one K step (tile kt in stage kt & 1, tile kt + 1 in flight):
-//   substeps 0..2: read the next substep's fragments, then 16 MFMAs per wave
-//   wait for my LDS reads and for tile kt + 1's DMA, s_barrier
-//   DMA tile kt + 2 into stage kt & 1 (every wave is done reading it)
-//   read fragments of tile kt + 1, substep 0; MFMAs of substep 3
-// The barrier is a bare s_barrier: __syncthreads() would also wait for the
-// DMA just issued. The loop body has no branches (the prefetch past the last
-// tile reloads the last tile into a stage nobody reads); the last K step is
-// peeled.
+// Tiles of the grouped GEMMs: K step 64, so a K-contiguous operand row is one
+// 128-byte LDS row; 16-byte chunk c of row r sits at position c ^ f(r),
+// f(r) = (r & 7) ^ ((r >> 3) & 1), which keeps both the row-wise 16-byte
+// writes and the fragment reads (rows r..r+15 of one chunk column) free of
+// bank conflicts, whether the LDS serves 8 lanes over 32 banks or 16 lanes
+// over 64 banks per cycle.
 // ---------------------------------------------------------------------------
 
 constexpr int kRowB = kBK * 2;                  // 128 bytes per LDS row
@@ -244,16 +232,6 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// One 16-byte-per-lane global -> LDS DMA (global_load_lds_dwordx4). The LDS
-// address must be wave-uniform; lane L lands at lds + 16 L. The builtin only
-// exists for the device, so the host pass sees an empty body (otherwise it
-// drops the host stubs of kernel templates that use it).
-__device__ __forceinline__ void dma16(const void* g, char* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
-#endif
-}
 
 // Epilogues: EPI_PLAIN C = bf16(acc); EPI_SWIGLU C = bf16(silu(gate) * up);
 // EPI_SWIGLU_AB the same plus C2 = bf16(gate), C3 = bf16(up) (the backward
@@ -399,8 +377,8 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(int E, const int32_t*
 
 // ---------------------------------------------------------------------------
 // Main path: 256 x BN tiles (256 weight rows: BN gate + BN up rows in GEMM1),
-// wavefronts split 2 x 4, the LDS layout and bank swizzle of the DMA loop
-// above and the LDS-staged epilogues, with register-staged loads:
+// wavefronts split 2 x 4, the LDS layout and bank swizzle above and the
+// LDS-staged epilogues, with register-staged loads:
 // each thread fetches four 16-byte pieces of each operand per K step with
 // buffer loads (whole 128-byte rows across 8 lanes; the descriptors' record
 // counts end at the expert's last row and at the weight's last row, so
@@ -922,25 +900,31 @@ hipError_t launch_skinny(int64_t seg_max, int E, const int32_t* offsets, int N, 
 }
 
 // ---------------------------------------------------------------------------
-// Weight gradients: per expert e, C_e[m][n] = sum over k in [koff[e], koff[e+1])
-// of A[m][k] * B[n][k], with A [M, ldk] and B [N, ldk] K-contiguous (the
-// transposed activations, each expert's rows padded to a multiple of 64 with
-// zeros, so every K range is whole 64-deep steps). Rows m < M1 go to
-// C0[e][m][n], rows m >= M1 to C1[e][m - M1][n] (gate and up gradients from one
-// launch). The DMA main loop above, with the common fragment layout; tiles
-// run expert by expert with m-tiles fastest, and each XCD gets a contiguous
-// run of tiles. An expert with no rows gets a zero gradient.
+// Weight gradients: per expert e, C_e[m][n] = sum over the expert's rows r in
+// [offsets[e], offsets[e+1]) of A[r][m] * B[r][n], with A [R, lda] and
+// B [R, ldb] the activations as stored (the token dimension is the
+// contraction, so both operands are K-major). Rows m < M1 go to C0[e][m][n],
+// rows m >= M1 to C1[e][m - M1][n] (gate and up gradients from one launch).
+// 256 x 256 tiles, 8 wavefronts, K step 64: both operands are staged as
+// [64 r][256 cols] tiles (32 lanes per 512-byte row) with the register-staged
+// spread schedule of the main path, and both MFMA fragments come from
+// transposing LDS reads (see ffn_bf16_reg_kernel with BT). The descriptors'
+// record counts end at the expert's last row, so the rows of the last step
+// past it read zeros. Tiles run expert by expert with m-tiles fastest, each
+// XCD a contiguous run of them; an expert with no rows gets a zero gradient.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void wgrad_dma_kernel(int E, const int32_t* __restrict__ koff, int M, int M1,
-                                                        int N, int64_t ldk, const uint16_t* __restrict__ A,
-                                                        const uint16_t* __restrict__ B, uint16_t* __restrict__ C0,
-                                                        uint16_t* __restrict__ C1) {
-  constexpr int BM = 256, BN = 256, NWM = 2, NWN = 4, NW = NWM * NWN;
+__global__ __launch_bounds__(512) void wgrad_kernel(int E, const int32_t* __restrict__ offsets, int M, int M1, int N,
+                                                    int lda, int ldb, const uint16_t* __restrict__ A,
+                                                    const uint16_t* __restrict__ B, uint16_t* __restrict__ C0,
+                                                    uint16_t* __restrict__ C1) {
+  constexpr int BM = 256, BN = 256, NWM = 2, NWN = 4, NT_ = 512;
   constexpr int WM = BM / NWM, WN = BN / NWN;
   constexpr int MB = WM / 32, NB = WN / 32, NACC = MB * NB;
-  constexpr int A_PW = BM / 8 / NW, B_PW = BN / 8 / NW;
-  constexpr int LOADS = A_PW + B_PW;
-  constexpr int STAGE = (BM + BN) * kRowB;
+  constexpr int PT = 4, NP = 2 * PT;               // 16-byte pieces per thread per operand per K step
+  constexpr int TILE = 64 * 512;                   // one operand's [64][256] bf16 tile
+  constexpr int STAGE = 2 * TILE;
+  constexpr int NM = MB * NB, NR = 2 * (MB + NB);  // MFMAs and transposing reads per substep
+  static_assert(NP == 8 && NM == 8, "two pieces and eight MFMAs per substep");
   extern __shared__ __align__(16) char smem[];
 
   const int MT = (M + BM - 1) / BM, NTn = (N + BN - 1) / BN;
@@ -951,9 +935,9 @@ __global__ __launch_bounds__(512) void wgrad_dma_kernel(int E, const int32_t* __
   const int tile = x * q + min(x, rr) + l;
   const int e = tile / (MT * NTn), rem = tile % (MT * NTn);
   const int m0 = (rem % MT) * BM, n0 = (rem / MT) * BN;
-  const int k0 = koff[e];
-  const int KT = (koff[e + 1] - k0) / kBK;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lo = offsets[e], cnt = offsets[e + 1] - lo;
+  const int KT = (cnt + kBK - 1) / kBK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / NWN, wn = wave % NWN;
 
   f32x16 acc[NACC];
@@ -963,39 +947,38 @@ __global__ __launch_bounds__(512) void wgrad_dma_kernel(int E, const int32_t* __
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
   if (KT > 0) {
-    const char* Ab = reinterpret_cast<const char*>(A);
-    const char* Bb = reinterpret_cast<const char*>(B);
-    size_t a_off[A_PW], b_off[B_PW];
-#pragma unroll
-    for (int i = 0; i < A_PW; ++i) {
-      const int row = (wave * A_PW + i) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ dswz(row);
-      a_off[i] = (size_t)min(m0 + row, M - 1) * (size_t)ldk * 2 + (size_t)k0 * 2 + c * 16;
-    }
-#pragma unroll
-    for (int i = 0; i < B_PW; ++i) {
-      const int row = (wave * B_PW + i) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ dswz(row);
-      b_off[i] = (size_t)min(n0 + row, N - 1) * (size_t)ldk * 2 + (size_t)k0 * 2 + c * 16;
-    }
-    auto dma = [&](int kt) {
-      const size_t ko = (size_t)(kt < KT ? kt : KT - 1) * kRowB;
-      char* st = smem + (kt & 1) * STAGE;
-#pragma unroll
-      for (int i = 0; i < A_PW; ++i) dma16(Ab + a_off[i] + ko, st + (wave * A_PW + i) * 1024);
-#pragma unroll
-      for (int i = 0; i < B_PW; ++i) dma16(Bb + b_off[i] + ko, st + BM * kRowB + (wave * B_PW + i) * 1024);
+    // columns past M (N) read the next row and are never stored
+    const auto ra = make_rsrc(A + (size_t)lo * lda + m0, (uint32_t)(((size_t)cnt * lda - m0) * 2));
+    const auto rb = make_rsrc(B + (size_t)lo * ldb + n0, (uint32_t)(((size_t)cnt * ldb - n0) * 2));
+    const int k0 = tid >> 5, c = tid & 31;
+    const uint32_t a_off = (uint32_t)(k0 * lda + c * 8) * 2u, b_off = (uint32_t)(k0 * ldb + c * 8) * 2u;
+    const int wofs = k0 * 512 + ((c ^ ((k0 & 3) << 2)) << 4);   // rows k0 + 16 i share (row & 3)
+    u32x4 stg[NP];
+    auto gl = [&](int p, int kt) {
+      const uint32_t k = (uint32_t)((kt < KT ? kt : KT - 1) * kBK + 16 * (p % PT));
+      stg[p] = p < PT ? bload16(ra, a_off + k * (uint32_t)lda * 2u) : bload16(rb, b_off + k * (uint32_t)ldb * 2u);
+    };
+    auto sw = [&](int p, int stage) {
+      st16(smem + stage * STAGE + (p < PT ? 0 : TILE) + wofs + (p % PT) * 16 * 512, stg[p]);
+    };
+    // lane i of 16-lane group tq gets rows k..k+3 of column (block base + 16 (tq & 1) + i)
+    const int tq = lane >> 4, ts = lane & 15;
+    auto frag = [&](const char* t, int sub, int col0) {
+      const int k = 16 * sub + 8 * (tq >> 1) + (ts >> 2);
+      const int n = col0 + 16 * (tq & 1) + 4 * (ts & 3);
+      const char* at = t + k * 512 + (((n >> 3) ^ ((k & 3) << 2)) << 4) + (n & 4) * 2;
+      const uint2 lo2 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)at));
+      const uint2 hi2 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(at + 4 * 512)));
+      const u32x4 v = {lo2.x, lo2.y, hi2.x, hi2.y};
+      return __builtin_bit_cast(bf16x8, v);
     };
     bf16x8 fa[2][MB], fb[2][NB];
     auto read_frags = [&](int stage, int sub, bf16x8(&A_)[MB], bf16x8(&B_)[NB]) {
       const char* buf = smem + stage * STAGE;
-      const int chunk = 2 * sub + (lane >> 5);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        A_[mb] = __builtin_bit_cast(bf16x8, ld16(buf + daddr(wm * WM + mb * 32 + (lane & 31), chunk)));
+      for (int mb = 0; mb < MB; ++mb) A_[mb] = frag(buf, sub, wm * WM + mb * 32);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        B_[nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(wn * WN + nb * 32 + (lane & 31), chunk)));
+      for (int nb = 0; nb < NB; ++nb) B_[nb] = frag(buf + TILE, sub, wn * WN + nb * 32);
     };
     auto mma = [&](const bf16x8(&A_)[MB], const bf16x8(&B_)[NB]) {
 #pragma unroll
@@ -1004,28 +987,44 @@ __global__ __launch_bounds__(512) void wgrad_dma_kernel(int E, const int32_t* __
         for (int mb = 0; mb < MB; ++mb)
           acc[mb * NB + nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B_[nb], A_[mb], acc[mb * NB + nb], 0, 0, 0);
     };
-    dma(0);
-    dma(1);
-    wait_vmcnt<LOADS>();
-    __builtin_amdgcn_s_barrier();
-    read_frags(0, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) gl(p, 0);
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int p = 0; p < NP; ++p) sw(p, 0);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) gl(p, 1);
+    wait_lgkm0();
+    __syncthreads();
     for (int kt = 0; kt < KT - 1; ++kt) {
       const int cur = kt & 1;
-      read_frags(cur, 1, fa[1], fb[1]);
-      mma(fa[0], fb[0]);
-      read_frags(cur, 2, fa[0], fb[0]);
-      mma(fa[1], fb[1]);
-      read_frags(cur, 3, fa[1], fb[1]);
-      mma(fa[0], fb[0]);
+      read_frags(cur, 0, fa[0], fb[0]);
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        if (sub < 3) read_frags(cur, sub + 1, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
+        mma(fa[sub & 1], fb[sub & 1]);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int p = 2 * sub + jj;
+          wait_vmcnt<NP - 1>();    // piece p of step kt+1 has landed (loaded one step ago)
+          sw(p, cur ^ 1);
+          gl(p, kt + 2);
+        }
+        if (sub < 3) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
       wait_lgkm0();
-      wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-      dma(kt + 2);
-      read_frags(cur ^ 1, 0, fa[0], fb[0]);
-      mma(fa[1], fb[1]);
     }
     {
       const int cur = (KT - 1) & 1;
+      read_frags(cur, 0, fa[0], fb[0]);
       read_frags(cur, 1, fa[1], fb[1]);
       mma(fa[0], fb[0]);
       read_frags(cur, 2, fa[0], fb[0]);
@@ -1034,15 +1033,14 @@ __global__ __launch_bounds__(512) void wgrad_dma_kernel(int E, const int32_t* __
       mma(fa[0], fb[0]);
       mma(fa[1], fb[1]);
     }
-    wait_vmcnt<0>();
+    wait_vmcnt<0>();   // the reload past the last step
   }
-  // the tile through LDS (every DMA has landed, so a barrier frees the stages):
-  // row m < M1 of expert e goes to C0[e][m], m >= M1 to C1[e][m - M1]
+  // the tile through LDS: row m < M1 of expert e goes to C0[e][m], m >= M1 to C1[e][m - M1]
   __syncthreads();
   lds_put_tile<MB, NB, WM, WN, BN>(smem, wm, wn, lane,
                                    [&](int mb, int nb, int g, int i) { return acc[mb * NB + nb][4 * g + i]; });
   __syncthreads();
-  lds_store_rows<BM, BN>(smem, threadIdx.x, (N - n0) / 8, [&](int row) {
+  lds_store_rows<BM, BN>(smem, tid, (N - n0) / 8, [&](int row) {
     const int m = m0 + row;
     if (m >= M) return static_cast<uint16_t*>(nullptr);
     return (m < M1 ? C0 + ((size_t)e * M1 + m) * (size_t)N : C1 + ((size_t)e * (M - M1) + (m - M1)) * (size_t)N) + n0;
@@ -1205,15 +1203,17 @@ hipError_t launch_bwd_dx_perm(int64_t R_max, int d, int E, int F, const void* da
                                                  nullptr, nullptr, nullptr, nullptr, 0, nullptr, 1, 0, d, F);
 }
 
-hipError_t launch_wgrad(int E, const int32_t* koff, int M, int M1, int N, int64_t ldk, const void* A, const void* B,
-                        void* C0, void* C1, hipStream_t s) {
-  constexpr size_t kLds = 2 * (size_t)(256 + 256) * kRowB;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_dma_kernel),
+hipError_t launch_wgrad(int E, const int32_t* offsets, int M, int M1, int N, int lda, int ldb, int64_t R,
+                        const void* A, const void* B, void* C0, void* C1, hipStream_t s) {
+  // buffer offsets within one expert's rows must stay below 2^31
+  if (R * (int64_t)(lda > ldb ? lda : ldb) * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  constexpr size_t kLds = 2 * (size_t)(2 * 64 * 512);
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_kernel),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
   const int64_t tiles = (int64_t)E * ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL(wgrad_dma_kernel, dim3((unsigned)grid), dim3(512), kLds, s, E, koff, M, M1, N, ldk,
+  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)grid), dim3(512), kLds, s, E, offsets, M, M1, N, lda, ldb,
                      reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B),
                      reinterpret_cast<uint16_t*>(C0), reinterpret_cast<uint16_t*>(C1));
   return hipGetLastError();

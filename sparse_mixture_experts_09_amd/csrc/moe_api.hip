@@ -606,13 +606,12 @@ int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float 
 // ---------------------------------------------------------------------------
 
 struct BwdLayout {
-  size_t idx, gate, slot_row, row_slot, counts, offsets, chunks, koff, dl, x_perm, a_st, b_st, h, o, d_o, dab,
-      dx_perm, xp_t, d_o_t, h_t, dab_t, router_part, ffn, total;
+  size_t idx, gate, slot_row, row_slot, counts, offsets, chunks, dl, x_perm, a_st, b_st, h, o, d_o, dab, dx_perm,
+      router_part, ffn, total;
 };
 
 static BwdLayout bwd_layout(int64_t T, int d, int E, int k, int64_t R_max, int F) {
   BwdLayout L;
-  const int64_t Rp = moe::padded_rows_max(R_max, E);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -626,7 +625,6 @@ static BwdLayout bwd_layout(int64_t T, int d, int E, int k, int64_t R_max, int F
   L.counts = take((size_t)E * 4);
   L.offsets = take((size_t)(E + 1) * 4);
   L.chunks = take((size_t)moe::permute_chunks(T) * E * 4);
-  L.koff = take((size_t)(E + 1) * 4);
   L.dl = take((size_t)T * k * 4);
   L.x_perm = take((size_t)R_max * d * 2);
   L.a_st = take((size_t)R_max * F * 2);
@@ -636,10 +634,6 @@ static BwdLayout bwd_layout(int64_t T, int d, int E, int k, int64_t R_max, int F
   L.d_o = take((size_t)R_max * d * 2);
   L.dab = take((size_t)R_max * 2 * F * 2);
   L.dx_perm = take((size_t)R_max * d * 2);
-  L.xp_t = take((size_t)d * Rp * 2);
-  L.d_o_t = take((size_t)d * Rp * 2);
-  L.h_t = take((size_t)F * Rp * 2);
-  L.dab_t = take((size_t)2 * F * Rp * 2);
   L.router_part = take(moe::router_wgrad_partial_bytes(T, d, E));
   L.ffn = take(ffn_ws_bytes(R_max, E, MOE_BF16));
   L.total = o;
@@ -673,8 +667,10 @@ int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F
     return MOE_ERR_UNSUPPORTED;
   const int64_t cap = capacity_of(T, E, k, cf);
   const int64_t R_max = rows_max_of(T, E, k, cap);
-  const int64_t Rp = moe::padded_rows_max(R_max, E);
-  if (Rp >= ((int64_t)1 << 31) || (int64_t)E * F * d >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  // the GEMMs address one expert's weights, and the kept rows of one activation, with 31-bit offsets
+  const int64_t widest = 2 * (int64_t)F > d ? 2 * (int64_t)F : d;
+  if (R_max * widest * 2 >= ((int64_t)1 << 31) || (int64_t)d * F * 2 >= ((int64_t)1 << 31))
+    return MOE_ERR_UNSUPPORTED;
   const BwdLayout L = bwd_layout(T, d, E, k, R_max, F);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   const size_t wbytes = (size_t)E * F * d * 2;
@@ -690,7 +686,6 @@ int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F
   float* gate = reinterpret_cast<float*>(w + L.gate);
   int32_t* srow = I32(L.slot_row);
   int32_t* offsets = I32(L.offsets);
-  int32_t* koff = I32(L.koff);
   float* dl = reinterpret_cast<float*>(w + L.dl);
   void* ffn_ws = ffn_ws_bytes(R_max, E, MOE_BF16) ? w + L.ffn : nullptr;
 
@@ -712,15 +707,11 @@ int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F
     e = moe::launch_bwd_dh(R_max, d, E, F, w + L.d_o, offsets, w_down, w + L.a_st, w + L.b_st, w + L.dab, stream);
   if (e == hipSuccess)
     e = moe::launch_bwd_dx_perm(R_max, d, E, F, w + L.dab, offsets, w_gate, w_up, w + L.dx_perm, ffn_ws, stream);
-  // weight gradients: transposed activations, expert rows padded to 64
-  if (e == hipSuccess) e = moe::launch_pad_offsets(E, offsets, koff, stream);
-  if (e == hipSuccess) e = moe::launch_seg_transpose(E, Rp, d, Rp, offsets, koff, w + L.x_perm, w + L.xp_t, stream);
-  if (e == hipSuccess) e = moe::launch_seg_transpose(E, Rp, 2 * F, Rp, offsets, koff, w + L.dab, w + L.dab_t, stream);
-  if (e == hipSuccess) e = moe::launch_seg_transpose(E, Rp, d, Rp, offsets, koff, w + L.d_o, w + L.d_o_t, stream);
-  if (e == hipSuccess) e = moe::launch_seg_transpose(E, Rp, F, Rp, offsets, koff, w + L.h, w + L.h_t, stream);
+  // weight gradients over each expert's rows (the activations as stored)
   if (e == hipSuccess)
-    e = moe::launch_wgrad(E, koff, 2 * F, F, d, Rp, w + L.dab_t, w + L.xp_t, dw_gate, dw_up, stream);
-  if (e == hipSuccess) e = moe::launch_wgrad(E, koff, d, d, F, Rp, w + L.d_o_t, w + L.h_t, dw_down, nullptr, stream);
+    e = moe::launch_wgrad(E, offsets, 2 * F, F, d, 2 * F, d, R_max, w + L.dab, w + L.x_perm, dw_gate, dw_up, stream);
+  if (e == hipSuccess)
+    e = moe::launch_wgrad(E, offsets, d, d, F, d, F, R_max, w + L.d_o, w + L.h, dw_down, nullptr, stream);
   // router weight and input gradients
   if (e == hipSuccess)
     e = moe::launch_router_wgrad(T, d, E, k, x, idx, dl, reinterpret_cast<float*>(w + L.router_part), dw_router,

@@ -81,13 +81,10 @@ hipError_t launch_bwd_dh(int64_t R_max, int d, int E, int F, const void* d_o, co
                          const void* w_down, const void* a_st, const void* b_st, void* dab, hipStream_t s);
 hipError_t launch_bwd_dx_perm(int64_t R_max, int d, int E, int F, const void* dab, const int32_t* offsets,
                               const void* w_gate, const void* w_up, void* dx_perm, void* ws, hipStream_t s);
-hipError_t launch_wgrad(int E, const int32_t* koff, int M, int M1, int N, int64_t ldk, const void* A, const void* B,
-                        void* C0, void* C1, hipStream_t s);
-int64_t padded_rows_max(int64_t R_max, int E);
+// weight gradients over each expert's rows of A [R, lda] and B [R, ldb] (as stored)
+hipError_t launch_wgrad(int E, const int32_t* offsets, int M, int M1, int N, int lda, int ldb, int64_t R,
+                        const void* A, const void* B, void* C0, void* C1, hipStream_t s);
 size_t router_wgrad_partial_bytes(int64_t T, int d, int E);
-hipError_t launch_pad_offsets(int E, const int32_t* offsets, int32_t* koff, hipStream_t s);
-hipError_t launch_seg_transpose(int E, int64_t rows_pad_max, int C, int64_t ldo, const int32_t* offsets,
-                                const int32_t* koff, const void* in, void* out, hipStream_t s);
 hipError_t launch_gate_bwd(int64_t T, int d, int k, const void* dy, const void* o, const int32_t* slot_row,
                            const float* gate, void* d_o, float* dl, hipStream_t s);
 hipError_t launch_router_wgrad(int64_t T, int d, int E, int k, const void* x, const int32_t* idx, const float* dl,
