@@ -28,6 +28,7 @@ namespace moe {
 namespace {
 
 constexpr int kSelThreads = 1024;
+constexpr int64_t kSelLdsKeys = 32768;   // up to this many tokens the select keys stay in LDS (128 KB)
 
 __device__ __forceinline__ uint32_t desc_score_key(float f) {
   uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
@@ -58,6 +59,8 @@ __device__ __forceinline__ int scan1024(int v, int* sh, int* total) {
   return v + before;
 }
 
+// KL: the keys live in LDS (T <= kSelLdsKeys), else in the global scratch row.
+template <bool KL>
 __global__ __launch_bounds__(kSelThreads) void ec_select_kernel(int64_t T, int E, int C,
                                                                 const float* __restrict__ scores,
                                                                 uint32_t* __restrict__ keys_ws,
@@ -67,9 +70,10 @@ __global__ __launch_bounds__(kSelThreads) void ec_select_kernel(int64_t T, int E
   __shared__ int hist[256];
   __shared__ int sh[kSelThreads / 64];
   __shared__ int sel_digit, sel_before;
+  extern __shared__ uint32_t lkeys[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int e = blockIdx.x;
-  uint32_t* keys = keys_ws + (size_t)e * T;
+  uint32_t* keys = KL ? lkeys : keys_ws + (size_t)e * T;
   for (int64_t t = tid; t < T; t += kSelThreads) keys[t] = desc_score_key(scores[t * E + e]);
   __syncthreads();
 
@@ -195,19 +199,32 @@ __global__ __launch_bounds__(256) void ec_combine_kernel(int64_t T, int d, int E
       const float g_l = e < E ? scores[t * E + e] : 0.f;
       uint64_t m = __ballot(r_l >= 0 && r_l < R);
       while (m) {
-        const int src = __ffsll((unsigned long long)m) - 1;
-        m &= m - 1;
-        const int r = __shfl(r_l, src);
-        const float g = __shfl(g_l, src);
-        const char* orow = ob + (size_t)r * rb;
+        // up to 4 chosen experts at a time (ascending), each through its own
+        // descriptor (record count 0 and weight 0 for an empty place), so the
+        // loads issue together and the sum keeps the one-by-one order and bits
+        __amdgpu_buffer_rsrc_t src[4];
+        float g[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int sl = m ? __ffsll((unsigned long long)m) - 1 : -1;
+          m &= m - 1;
+          const int r = __builtin_amdgcn_readfirstlane(sl >= 0 ? __shfl(r_l, sl) : -1);
+          g[j] = sl >= 0 ? __shfl(g_l, sl) : 0.f;
+          src[j] = make_rsrc(ob + (size_t)(r >= 0 ? r : 0) * rb, r >= 0 ? (uint32_t)rb : 0u);
+        }
 #pragma unroll
         for (int q = 0; q < MAXC; ++q) {
           const int c = c0 + (q * 64 + lane) * V;
-          if (c < d) {
-            float f[V];
-            unpack16(S(), ld16(orow + (size_t)c * sizeof(typename S::elem)), f);
+          const uint32_t off = (uint32_t)c * sizeof(typename S::elem);
+          u32x4 v[4];
 #pragma unroll
-            for (int i = 0; i < V; ++i) acc[q][i] = fmaf(g, f[i], acc[q][i]);
+          for (int j = 0; j < 4; ++j) v[j] = bload16(src[j], c < d ? off : 0x80000000u);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float f[V];
+            unpack16(S(), v[j], f);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[q][i] = fmaf(g[j], f[i], acc[q][i]);
           }
         }
       }
@@ -226,8 +243,18 @@ size_t ec_select_bytes(int64_t T, int E) { return (size_t)E * T * 4; }
 
 hipError_t launch_ec_select(int64_t T, int E, int C, const float* scores, void* ws, int32_t* tokens,
                             int32_t* slot, int32_t* offsets, hipStream_t s) {
-  hipLaunchKernelGGL(ec_select_kernel, dim3((unsigned)E), dim3(kSelThreads), 0, s, T, E, C, scores,
-                     reinterpret_cast<uint32_t*>(ws), tokens, slot, offsets);
+  if (T <= kSelLdsKeys) {
+    const int bytes = (int)(T * 4);
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&ec_select_kernel<true>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       (int)(kSelLdsKeys * 4));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(ec_select_kernel<true>, dim3((unsigned)E), dim3(kSelThreads), bytes, s, T, E, C, scores,
+                       reinterpret_cast<uint32_t*>(ws), tokens, slot, offsets);
+  } else {
+    hipLaunchKernelGGL(ec_select_kernel<false>, dim3((unsigned)E), dim3(kSelThreads), 0, s, T, E, C, scores,
+                       reinterpret_cast<uint32_t*>(ws), tokens, slot, offsets);
+  }
   return hipGetLastError();
 }
 
