@@ -345,7 +345,36 @@ __device__ __forceinline__ void store_tile_lds(const f32x16* acc, const TileCoor
 
 // Sum the K-slice partials of each split tail tile in slice order and store
 // the bf16 result (rows inside the expert's segment, columns below N).
-// One block per (split tile, 16-row group); a thread owns 16 columns.
+// One block per (split tile, 16-row group); each wavefront sums four rows,
+// a lane four columns: every load instruction reads one whole 1 KB partial
+// row, and all S x 4 loads of a wavefront are in flight before the sums.
+template <int S>
+__device__ __forceinline__ void split_reduce_rows(const float* __restrict__ part, size_t slice_stride, int row0,
+                                                  int rows_left, int col, bool col_ok, uint16_t* __restrict__ crow0,
+                                                  size_t ldc) {
+  constexpr int BN = 256, RW = 4;
+  f32x4 v[RW][S];
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+      v[i][j] = (col_ok && i < rows_left)
+                    ? *reinterpret_cast<const f32x4*>(part + j * slice_stride + (size_t)(row0 + i) * BN + col)
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    f32x4 sum = v[i][0];
+#pragma unroll
+    for (int j = 1; j < S; ++j) sum += v[i][j];
+    if (col_ok && i < rows_left) {
+      uint2 w;
+      w.x = pack_bf16x2(sum[0], sum[1]);
+      w.y = pack_bf16x2(sum[2], sum[3]);
+      *reinterpret_cast<uint2*>(crow0 + (size_t)i * ldc + col) = w;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void split_reduce_kernel(int E, const int32_t* __restrict__ offsets, int N,
                                                            int K, int NT, int P, int max_split,
                                                            const float* __restrict__ partials,
@@ -356,22 +385,23 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(int E, const int32_t*
   if (t >= p.r) return;
   TileCoord tc;
   if (!locate_tile(offsets, E, BM, NT, p.full + t, tc)) return;
-  const int row = (blockIdx.x % (BM / 16)) * 16 + (threadIdx.x >> 4);
-  const int rloc = tc.m0 + row;
-  if (rloc >= tc.seg_rows) return;
-  const int c0 = (threadIdx.x & 15) * 16;
-  uint16_t* crow = C + (size_t)(tc.seg_start + rloc) * (size_t)N + (size_t)tc.n_tile * BN;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int col = c0 + 4 * q;
-    if (tc.n_tile * BN + col >= N) break;
-    f32x4 sum = *reinterpret_cast<const f32x4*>(partials + ((size_t)(t * p.s) * BM + row) * BN + col);
-    for (int j = 1; j < p.s; ++j)
-      sum += *reinterpret_cast<const f32x4*>(partials + ((size_t)(t * p.s + j) * BM + row) * BN + col);
-    uint2 w;
-    w.x = pack_bf16x2(sum[0], sum[1]);
-    w.y = pack_bf16x2(sum[2], sum[3]);
-    *reinterpret_cast<uint2*>(crow + col) = w;
+  const int lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x % (BM / 16)) * 16 + (threadIdx.x >> 6) * 4;
+  const int rows_left = tc.seg_rows - (tc.m0 + row0);
+  if (rows_left <= 0) return;
+  const int col = lane * 4;
+  const bool col_ok = tc.n_tile * BN + col < N;
+  const float* part = partials + (size_t)(t * p.s) * BM * BN;
+  const size_t ss = (size_t)BM * BN;
+  uint16_t* crow0 = C + (size_t)(tc.seg_start + tc.m0 + row0) * (size_t)N + (size_t)tc.n_tile * BN;
+  switch (p.s) {
+    case 2: split_reduce_rows<2>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+    case 3: split_reduce_rows<3>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+    case 4: split_reduce_rows<4>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+    case 5: split_reduce_rows<5>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+    case 6: split_reduce_rows<6>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+    case 7: split_reduce_rows<7>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+    default: split_reduce_rows<kMaxSplit>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
   }
 }
 

@@ -20,8 +20,13 @@
 //               lanes below give the in-wave rank; wave totals in LDS give
 //               the in-chunk rank; plus the chunk prefix from step 2. Writes
 //               slot_row (row or -1) and row_slot.
-//   4. scatter: one wavefront per token reads the x row once with 16-byte
-//               loads and writes it to each of its kept rows.
+//   4. scatter: one wavefront per token (per 1 KB piece of its row below
+//               2048 tokens) reads the row once with 16-byte loads and writes
+//               it to each of the token's kept rows.
+// Up to 1024 tokens, steps 1-3 run as one 1024-thread workgroup instead
+// (perm_layout_kernel): the same ballot ranks per wavefront, the per-expert
+// prefix over the wavefronts, the demand and the offsets, all in LDS, so the
+// layout costs one launch.
 //
 // Batch Priority Routing ("Scaling Vision with Sparse Mixture of Experts",
 // section "Priority Routing": tokens are taken by an importance score rather
@@ -153,12 +158,129 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(int64_t T, int E, int k,
   }
 }
 
-__global__ __launch_bounds__(256) void perm_scatter_kernel(int64_t T, int k, size_t row_bytes,
+// Steps 1-3 in one workgroup for T <= 1024: thread tid holds the token at
+// position tid of the arrival sequence. LDS: wcnt[wave * E + e] = the
+// wavefront's assignments to e, turned in place into their exclusive prefix
+// over the wavefronts; off[E]; the per-wavefront scan totals. (Several passes
+// of 1024 tokens in one workgroup measured slower than the chunked kernels at
+// 4096 tokens: one CU then walks every wavefront's ballots.)
+constexpr int kLayoutMaxT = 1024;
+
+__global__ __launch_bounds__(1024) void perm_layout_kernel(int T, int E, int k, int64_t cap,
+                                                           const int32_t* __restrict__ idx,
+                                                           const int32_t* __restrict__ order,
+                                                           int32_t* __restrict__ expert_counts,
+                                                           int32_t* __restrict__ expert_offsets,
+                                                           int32_t* __restrict__ slot_row,
+                                                           int32_t* __restrict__ row_slot) {
+  extern __shared__ int sh[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int* wcnt = sh;
+  int* off = sh + 16 * E;
+  int* wsum = off + E;
+  const int tok = tid < T ? (order ? order[tid] : tid) : -1;
+  int ex[8], rk[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int e = (tok >= 0 && j < k) ? idx[(int64_t)tok * k + j] : -1;
+    ex[j] = (e >= 0 && e < E) ? e : -1;
+    rk[j] = 0;
+  }
+  for (int i = tid; i < 16 * E; i += 1024) wcnt[i] = 0;
+  __syncthreads();
+  // in-wavefront ranks: one ballot per distinct expert present in the wavefront
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t pend = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pend |= (ex[j] >= 0 ? 1u : 0u) << j;
+  for (;;) {
+    const uint64_t busy = __ballot(pend != 0);
+    if (busy == 0) break;
+    int mine = -1;
+#pragma unroll
+    for (int j = 7; j >= 0; --j)
+      if ((pend >> j) & 1) mine = ex[j];
+    const int e = __builtin_amdgcn_readlane(mine, __ffsll((long long)busy) - 1);
+    bool has = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) has |= ((pend >> j) & 1) && ex[j] == e;
+    const uint64_t m = __ballot(has);
+    const int r = __popcll(m & below);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (((pend >> j) & 1) && ex[j] == e) {
+        rk[j] = r;
+        pend &= ~(1u << j);
+      }
+    if (lane == 0) wcnt[wave * E + e] = __popcll(m);
+  }
+  __syncthreads();
+  // per expert (one wavefront each, lane w for wavefront w's count): the
+  // exclusive prefix over the wavefronts in place, the demand into off[e]
+  for (int e = wave; e < E; e += 16) {
+    const int c = lane < 16 ? wcnt[lane * E + e] : 0;
+    int v = c;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int u = __shfl_up(v, o);
+      if (lane >= o) v += u;
+    }
+    if (lane < 16) wcnt[lane * E + e] = v - c;
+    if (lane == 15) off[e] = v;
+  }
+  __syncthreads();
+  int kept = 0;
+  if (tid < E) {
+    const int run = off[tid];
+    expert_counts[tid] = run;
+    kept = (int)min<int64_t>(run, cap);
+  }
+  // exclusive scan of kept over the experts (E <= 256: wavefronts 0-3)
+  int v = kept;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  if (tid < E) {
+    int add = 0;
+    for (int w = 0; w < wave; ++w) add += wsum[w];
+    const int excl = v + add - kept;
+    off[tid] = excl;
+    expert_offsets[tid] = excl;
+    if (tid == E - 1) expert_offsets[E] = excl + kept;
+  }
+  __syncthreads();
+  if (tok < 0) return;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    const int e = ex[j];
+    int row = -1;
+    if (e >= 0) {
+      const int rank = wcnt[wave * E + e] + rk[j];
+      if (rank < cap) {
+        row = off[e] + rank;
+        row_slot[row] = tok * k + j;
+      }
+    }
+    slot_row[(int64_t)tok * k + j] = row;
+  }
+}
+
+// Each wavefront copies `ppw` 1 KB pieces of one token's row (16 bytes a
+// lane per piece), reading each piece once and storing it to each kept row
+// of the token; a row has `pieces` pieces, split over pieces / ppw wavefronts.
+__global__ __launch_bounds__(256) void perm_scatter_kernel(int64_t T, int k, size_t row_bytes, int pieces, int ppw,
                                                            const char* __restrict__ x,
                                                            const int32_t* __restrict__ slot_row,
                                                            char* __restrict__ x_perm) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wpt = pieces / ppw;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t t = wpt == 1 ? gw : gw / wpt;
   if (t >= T) return;
   int rows[8];
   bool any = false;
@@ -169,8 +291,10 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(int64_t T, int k, siz
   }
   if (!any) return;
   const char* src = x + (size_t)t * row_bytes;
+  const size_t first = (size_t)(gw - t * wpt) * ppw * 1024 + (size_t)lane * 16;
+  const size_t end = min(row_bytes, first - (size_t)lane * 16 + (size_t)ppw * 1024);
 #pragma unroll 2
-  for (size_t off = (size_t)lane * 16; off < row_bytes; off += 64 * 16) {
+  for (size_t off = first; off < end; off += 1024) {
     const u32x4 v = ld16(src + off);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -373,18 +497,28 @@ hipError_t launch_permute(bool bf16, int64_t T, int d, int E, int k, int64_t cap
                           const int32_t* idx, const int32_t* order, int32_t* expert_counts,
                           int32_t* expert_offsets, int32_t* slot_row, int32_t* row_slot, void* x_perm,
                           int32_t* chunk_counts, hipStream_t s) {
-  const int64_t nchunks = permute_chunks(T);
-  hipLaunchKernelGGL(perm_hist_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, E, k, idx, order,
-                     chunk_counts);
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, s, (int)nchunks, E, cap, chunk_counts,
-                     expert_counts, expert_offsets);
-  hipLaunchKernelGGL(perm_rank_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, E, k, cap, idx, order,
-                     chunk_counts, expert_offsets, slot_row, row_slot);
+  if (T <= kLayoutMaxT) {
+    const size_t lds = (size_t)(17 * E + 16) * sizeof(int);
+    hipLaunchKernelGGL(perm_layout_kernel, dim3(1), dim3(1024), lds, s, (int)T, E, k, cap, idx, order,
+                       expert_counts, expert_offsets, slot_row, row_slot);
+  } else {
+    const int64_t nchunks = permute_chunks(T);
+    hipLaunchKernelGGL(perm_hist_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, E, k, idx, order,
+                       chunk_counts);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, s, (int)nchunks, E, cap, chunk_counts,
+                       expert_counts, expert_offsets);
+    hipLaunchKernelGGL(perm_rank_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, E, k, cap, idx, order,
+                       chunk_counts, expert_offsets, slot_row, row_slot);
+  }
   if (x_perm == nullptr) return hipGetLastError();   // the layout only: the GEMM gathers the rows
   const size_t row_bytes = (size_t)d * (bf16 ? 2 : 4);
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, T, k,
-                     row_bytes, reinterpret_cast<const char*>(x), slot_row,
-                     reinterpret_cast<char*>(x_perm));
+  const int pieces = (int)((row_bytes + 1023) / 1024);
+  // few tokens: a wavefront per piece, for parallelism; many: a wavefront per
+  // row (measured faster at 4096 tokens of 8 KB)
+  const int ppw = T < 2048 ? 1 : pieces;
+  const int64_t waves = T * (pieces / ppw);
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, T, k, row_bytes,
+                     pieces, ppw, reinterpret_cast<const char*>(x), slot_row, reinterpret_cast<char*>(x_perm));
   return hipGetLastError();
 }
 

@@ -144,6 +144,33 @@ def test_permute(case):
     assert torch.equal(xp, a["x"][torch.from_numpy(ref["row_slot"].astype(np.int64)) // w.k])
 
 
+# Token counts on both sides of the one-workgroup layout (up to 1024 tokens)
+# and of the scatter's switch from a wavefront per 1 KB piece to a wavefront
+# per row (2048 tokens); rows of 1200 bytes end inside their second piece.
+@pytest.mark.parametrize("T,d,E,k,cf,dtype,seed", [
+    (1024, 600, 256, 8, 1.0, "bf16", 60),   # the largest one-workgroup layout, E = 256
+    (1025, 600, 16, 2, 0.7, "bf16", 61),    # the smallest chunked layout
+    (2047, 300, 8, 2, 1.0, "f32", 62),
+    (2048, 600, 8, 3, 0.9, "bf16", 63),
+    (999, 64, 1, 1, 0.5, "bf16", 64),       # one expert, half the tokens dropped
+])
+def test_permute_layout_sizes(T, d, E, k, cf, dtype, seed):
+    w = mi.Workload("perm_sizes", T=T, d=d, E=E, k=k, F=8, cf=cf, dtype=dtype, seed=seed)
+    a = mi.generate(w, expert_weights=False)
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    cap = orc.capacity(T, E, k, cf)
+    demand, offsets, slot_row, row_slot = orc.fill_in_token_order(idx, E, cap)
+    out = moe.moe_permute(dev(a["x"]), dev(torch.from_numpy(idx)), E, cf)
+    torch.cuda.synchronize()
+    R = int(offsets[-1])
+    assert np.array_equal(host(out["expert_counts"]), demand)
+    assert np.array_equal(host(out["expert_offsets"]), offsets)
+    assert np.array_equal(host(out["slot_row"]), slot_row)
+    assert np.array_equal(host(out["row_slot"])[:R], row_slot)
+    assert torch.equal(out["x_perm"][:R].cpu(), a["x"][torch.from_numpy(row_slot.astype(np.int64)) // k])
+
+
 @pytest.mark.parametrize("case", SMALL + NAMED_SMALL, ids=case_id)
 def test_grouped_ffn(case):
     w, a = workload(case)

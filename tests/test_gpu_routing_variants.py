@@ -137,6 +137,8 @@ def test_permute_priority(case, stride_k):
     (1, 4, 2, 1.0, 53),
     (16384, 8, 2, 0.5, 54),      # largest single-workgroup sort
     (16385, 8, 2, 0.5, 55),      # smallest radix sort
+    (1024, 256, 8, 0.5, 56),     # the largest one-workgroup capacity layout
+    (1025, 32, 4, 0.7, 57),      # the smallest chunked layout
 ])
 def test_permute_priority_ties_and_sizes(T, E, k, cf, seed):
     """Many exact ties (a handful of score values, with -0 and +0 equal), the
