@@ -947,10 +947,10 @@ __global__ __launch_bounds__(512) void wgrad_kernel(int E, const int32_t* __rest
                                                     int lda, int ldb, const uint16_t* __restrict__ A,
                                                     const uint16_t* __restrict__ B, uint16_t* __restrict__ C0,
                                                     uint16_t* __restrict__ C1) {
-  constexpr int BM = 256, BN = 256, NWM = 2, NWN = 4, NT_ = 512;
+  constexpr int BM = 256, BN = 256, NWM = 2, NWN = 4;
   constexpr int WM = BM / NWM, WN = BN / NWN;
   constexpr int MB = WM / 32, NB = WN / 32, NACC = MB * NB;
-  constexpr int PT = 4, NP = 2 * PT;               // 16-byte pieces per thread per operand per K step
+  constexpr int PT = 4, NP = 2 * PT;               // 16-byte pieces per thread per operand per K step (512 threads)
   constexpr int TILE = 64 * 512;                   // one operand's [64][256] bf16 tile
   constexpr int STAGE = 2 * TILE;
   constexpr int NM = MB * NB, NR = 2 * (MB + NB);  // MFMAs and transposing reads per substep
