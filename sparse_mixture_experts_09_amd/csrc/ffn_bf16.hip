@@ -16,9 +16,13 @@
 // features of one row, stored as one 8-byte write.
 //
 // Kernels (one fragment layout):
-//   ffn_bf16_reg_kernel     256-row tiles, 8 wavefronts (2 per SIMD), K step 64,
-//                           register-staged loads into two LDS stages (the main
-//                           path, forward and the backward data gradients);
+//   ffn_bf16_w4_kernel      256-row tiles, 4 wavefronts (1 per SIMD) of 128 x 128,
+//                           K step 64, register-staged loads into two LDS
+//                           stages, fragments read a substep ahead (the forward
+//                           main path);
+//   ffn_bf16_reg_kernel     the same tiles with 8 wavefronts (2 per SIMD) of
+//                           128 x 64 (the backward pass's recomputation and data
+//                           gradients, with their epilogues and K-major weights);
 //   ffn_bf16_kernel         128-row tiles, 4 wavefronts (experts average fewer
 //                           than 128 rows: big tiles would waste work on the
 //                           ragged last tile of each expert);
@@ -276,10 +280,14 @@ template <int W>
 __device__ __forceinline__ int lds_tile_pos(int row, int col) {
   return row * (W * 2) + (((col >> 3) ^ (row & (W / 8 - 1))) << 4) + ((col >> 2) & 1) * 8;
 }
-template <int MB, int NB, int WM, int WN, int W, class Val>
+// SERIAL: one row block at a time (a scheduling fence after each), for
+// callers whose accumulators fill the register file: hoisting every
+// conversion ahead of the LDS writes would spill.
+template <int MB, int NB, int WM, int WN, int W, class Val, bool SERIAL = false>
 __device__ __forceinline__ void lds_put_tile(char* lds, int wm, int wn, int lane, Val val) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
+    if (SERIAL) __builtin_amdgcn_sched_barrier(0);
     const int row = wm * WM + mb * 32 + (lane & 31);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -311,13 +319,13 @@ __device__ __forceinline__ void lds_load_rows(char* lds, int tid, int chunks, __
 }
 // Then, after a barrier: tile row r goes to row_ptr(r) (nullptr: not stored),
 // its 16-byte piece c only if c < chunks.
-template <int BM, int W, class RowPtr>
+template <int BM, int W, class RowPtr, int NTHR = 512>
 __device__ __forceinline__ void lds_store_rows(const char* lds, int tid, int chunks, RowPtr row_ptr) {
   constexpr int CH = W / 8, RB = W * 2;
-  constexpr int PER = BM * CH / 512;           // pieces per thread (512 threads)
+  constexpr int PER = BM * CH / NTHR;          // pieces per thread (NTHR threads)
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int cidx = tid + i * 512, row = cidx / CH, ch = cidx % CH;
+    const int cidx = tid + i * NTHR, row = cidx / CH, ch = cidx % CH;
     const u32x4 v = ld16(lds + row * RB + ((ch ^ (row & (CH - 1))) << 4));
     uint16_t* dst = row_ptr(row);
     if (dst != nullptr && ch < chunks) st16(dst + ch * 8, v);
@@ -327,20 +335,82 @@ __device__ __forceinline__ void lds_store_rows(const char* lds, int tid, int chu
 // Plain and SwiGLU epilogues of the grouped GEMM tiles, through LDS: rows at
 // or past the segment's end and columns at or past N (a multiple of 8) are
 // not stored.
-template <int EPI, int BM, int MB, int NB, int WM, int WN, int W>
+template <int EPI, int BM, int MB, int NB, int WM, int WN, int W, int NTHR = 512>
 __device__ __forceinline__ void store_tile_lds(const f32x16* acc, const TileCoord& tc, int wm, int wn, int n0, int N,
                                                int ldc, uint16_t* __restrict__ C, char* lds, int tid) {
   static_assert(EPI == EPI_PLAIN || EPI == EPI_SWIGLU, "plain or SwiGLU tile");
-  lds_put_tile<MB, NB, WM, WN, W>(lds, wm, wn, tid & 63, [&](int mb, int nb, int g, int i) {
+  auto val = [&](int mb, int nb, int g, int i) {
     const float a = acc[mb * NB + nb][4 * g + i];
     return EPI == EPI_SWIGLU ? silu(a) * acc[MB * NB + mb * NB + nb][4 * g + i] : a;
-  });
+  };
+  lds_put_tile<MB, NB, WM, WN, W, decltype(val), NTHR == 256>(lds, wm, wn, tid & 63, val);
   __syncthreads();
   const int rows = min(BM, tc.seg_rows - tc.m0);
   uint16_t* c0 = C + (size_t)(tc.seg_start + tc.m0) * ldc + n0;
-  lds_store_rows<BM, W>(lds, tid, (N - n0) / 8, [&](int row) {
-    return row < rows ? c0 + (size_t)row * ldc : static_cast<uint16_t*>(nullptr);
-  });
+  auto row_ptr = [&](int row) { return row < rows ? c0 + (size_t)row * ldc : static_cast<uint16_t*>(nullptr); };
+  lds_store_rows<BM, W, decltype(row_ptr), NTHR>(lds, tid, (N - n0) / 8, row_ptr);
+}
+
+// Plain 256 x BN tiles whose wavefronts own 128 whole rows each (wavefront
+// row wm), through LDS as fp32 in two passes: pass h takes row blocks 2h and
+// 2h+1 of every wavefront (tile rows wm*128 + 64h + 0..63), so all four
+// wavefronts write in both passes; LDS row j ([128][BN] floats, 16-byte
+// chunk c of row r at position c ^ (r mod BN/4)) holds tile row
+// (j / 64) * 128 + 64h + j % 64. After a pass the threads store whole 16-byte
+// pieces: fp32 rows of the partial tile pt of a split tail slice ([256][BN],
+// row-major), or, with pt null, the bf16 tile (8 floats per piece; rows at or
+// past the segment's end and columns at or past N are not stored). Both cases
+// share the writes of the accumulators, so no accumulator is live across a
+// branch (with 256 of them a lane, a branch there made the register
+// allocator spill).
+template <int BN, int MB, int NB, int WN, int NTHR>
+__device__ __forceinline__ void store_plain_lds(const f32x16* acc, int wm, int wn, int lane, int tid, char* lds,
+                                                float* pt, const TileCoord& tc, int n0, int N, int ldc,
+                                                uint16_t* __restrict__ C) {
+  constexpr int CH = BN / 4, RB = BN * 4;
+  static_assert(MB == 4 && 128 * RB <= 2 * 65536, "two row blocks of each wavefront per pass fit in LDS");
+  const int rows = min(256, tc.seg_rows - tc.m0);
+  const int ncols = N - n0;
+  uint16_t* c0 = C + (size_t)(tc.seg_start + tc.m0) * ldc + n0;
+  auto at = [&](int row, int c) { return lds + row * RB + ((c ^ (row & (CH - 1))) << 4); };
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int mb = 2 * h + m, row = wm * 64 + m * 32 + (lane & 31);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[mb * NB + nb][4 * g + i];
+          *reinterpret_cast<f32x4*>(at(row, (wn * WN + nb * 32 + 8 * g + 4 * (lane >> 5)) >> 2)) = v;
+        }
+    }
+    __syncthreads();
+    auto trow = [&](int j) { return (j >> 6) * 128 + 64 * h + (j & 63); };
+    if (pt != nullptr) {
+#pragma unroll 4
+      for (int i = 0; i < 128 * CH / NTHR; ++i) {
+        const int cidx = tid + i * NTHR, row = cidx / CH, c = cidx % CH;
+        st16(pt + (size_t)trow(row) * BN + 4 * c, ld16(at(row, c)));
+      }
+    } else {
+#pragma unroll 4
+      for (int i = 0; i < 128 * (CH / 2) / NTHR; ++i) {
+        const int cidx = tid + i * NTHR, row = cidx / (CH / 2), c8 = cidx % (CH / 2);
+        const f32x4 lo = __builtin_bit_cast(f32x4, ld16(at(row, 2 * c8)));
+        const f32x4 hi = __builtin_bit_cast(f32x4, ld16(at(row, 2 * c8 + 1)));
+        const u32x4 o = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                         pack_bf16x2(hi[2], hi[3])};
+        const int tr = trow(row);
+        if (tr < rows && 8 * c8 < ncols) st16(c0 + (size_t)tr * ldc + 8 * c8, o);
+      }
+    }
+  }
 }
 
 // Sum the K-slice partials of each split tail tile in slice order and store
@@ -770,6 +840,215 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Forward tiles with 4 wavefronts (one per SIMD), each owning 128 token rows x
+// 128 weight rows of the 256 x 256 tile (256 fp32 accumulators a lane, held
+// in the accumulation registers), so a K step reads a third less from LDS
+// than with 8 wavefronts of 128 x 64. With one wavefront per SIMD nothing
+// hides a fragment read that an MFMA waits for, so the reads run one 16-deep
+// substep ahead of the MFMAs, across the K steps too: the 16 pieces a thread
+// stages per K step (8 token rows, 8 weight rows) are written to the other
+// LDS stage four per substep, each reloaded at once with the step after
+// (one K step to land); the last four are written early in substep 3, then
+// the step's one barrier, and the first fragments of the next step are read
+// while the remaining 8 MFMAs of substep 3 run. Stage reuse: a stage is
+// rewritten only after the barrier that follows every wavefront's last read
+// of it. Tile plan, gather, split tail and LDS-staged epilogue as in
+// ffn_bf16_reg_kernel. Measured against that kernel on a dense 1024 x 65536
+// GEMM: +3% at K = 4096, +5% at K = 14336.
+// ---------------------------------------------------------------------------
+template <int BN, bool SWIGLU>
+__global__ __launch_bounds__(256) void ffn_bf16_w4_kernel(
+    int E, const int32_t* __restrict__ offsets, int N, int K, const uint16_t* __restrict__ A,
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT, int P,
+    int max_split, float* __restrict__ partials, int ldc, const int32_t* __restrict__ a_slot, int a_k,
+    uint32_t a_records) {
+  constexpr int BM = 256, NWN = 2, NT_ = 256;
+  constexpr int BROWS = SWIGLU ? 2 * BN : BN;
+  static_assert(BROWS == 256, "both operands are 256-row tiles");
+  constexpr int WM = BM / 2, WN = BN / NWN;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int NBF = (SWIGLU ? 2 : 1) * NB;
+  constexpr int NACC = MB * NBF, NM = NACC, NR = MB + NBF;
+  constexpr int PT = 2048 / NT_;                 // 16-byte pieces per thread per operand per K step
+  constexpr int NP = 2 * PT, QS = NP / 4;        // pieces per thread per K step, per substep
+  constexpr int RSTEP = NT_ / 8;                 // rows between a thread's pieces
+  constexpr int STAGE = (BM + BROWS) * kRowB;
+  static_assert(NM == 16 && NR == 8 && QS == 4, "16 MFMAs, 8 fragment reads, 4 pieces per substep");
+  extern __shared__ __align__(16) char smem[];
+
+  const int KTall = K / kBK;
+  WorkItem w;
+  if (!find_item(offsets, E, BM, NT, P, max_split, KTall, blockIdx.x, w)) return;
+  const TileCoord tc = w.tc;
+  int kb = 0, KT = KTall;
+  if (w.split >= 0) {
+    const int ns = make_plan(offsets, E, BM, NT, P, max_split, KTall).s;
+    kb = w.slice * KTall / ns;
+    KT = (w.slice + 1) * KTall / ns - kb;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int n0 = tc.n_tile * BN;
+
+  const size_t rowb = (size_t)K * 2;
+  const int a_rows = min(BM, tc.seg_rows - tc.m0);
+  const int b_rows = min(BN, N - n0);
+  const size_t wrow0 = (size_t)tc.e * N + n0;
+  const auto rb0 = make_rsrc(B0 + wrow0 * K, (uint32_t)(b_rows * rowb));
+  const auto rb1 = make_rsrc((SWIGLU ? B1 : B0) + wrow0 * K, (uint32_t)(b_rows * rowb));
+  const int row0 = tid >> 3, ch = tid & 7;
+  const uint32_t voff = (uint32_t)(row0 * rowb) + ch * 16 + (uint32_t)kb * kRowB;
+  const uint32_t rstep = (uint32_t)(RSTEP * rowb);
+  __amdgpu_buffer_rsrc_t ra;
+  uint32_t aoff[PT];
+  if (a_slot != nullptr) {   // gathered token rows, as in ffn_bf16_reg_kernel
+    ra = make_rsrc(A, a_records);
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int r = row0 + p * RSTEP;
+      aoff[p] = r < a_rows ? ((uint32_t)a_slot[tc.seg_start + tc.m0 + r] / (uint32_t)a_k) * (uint32_t)rowb + ch * 16 +
+                                 (uint32_t)kb * kRowB
+                           : a_records;
+    }
+  } else {
+    ra = make_rsrc(A + (size_t)(tc.seg_start + tc.m0) * K, (uint32_t)(a_rows * rowb));
+#pragma unroll
+    for (int p = 0; p < PT; ++p) aoff[p] = voff + p * rstep;
+  }
+  const int wofs = row0 * kRowB + ((ch ^ dswz(row0)) << 4);   // RSTEP is a multiple of 16: same swizzle
+
+  // piece p < PT: token row row0 + p*RSTEP; p >= PT: weight row row0 + (p-PT)*RSTEP
+  // (SwiGLU tiles: BN gate rows, then BN up rows)
+  u32x4 stg[NP];
+  auto gl = [&](int p, int kt) {
+    const uint32_t ko = (uint32_t)(kt < KT ? kt : KT - 1) * kRowB;
+    if (p < PT) {
+      stg[p] = bload16(ra, aoff[p] + ko);
+    } else {
+      const int i = p - PT;
+      const bool up = SWIGLU && i * RSTEP >= BN;
+      stg[p] = bload16(up ? rb1 : rb0, voff + (up ? i * rstep - BN * (uint32_t)rowb : i * rstep) + ko);
+    }
+  };
+  auto sw = [&](int p, int stage) {
+    char* b = smem + stage * STAGE + wofs;
+    st16(p < PT ? b + p * RSTEP * kRowB : b + BM * kRowB + (p - PT) * RSTEP * kRowB, stg[p]);
+  };
+
+  f32x16 acc[NACC];
+#pragma unroll
+  for (int i = 0; i < NACC; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  bf16x8 fa[2][MB], fb[2][NBF];
+  auto read_frags = [&](int stage, int sub, bf16x8(&A_)[MB], bf16x8(&B_)[NBF]) {
+    const char* buf = smem + stage * STAGE;
+    const int chunk = 2 * sub + (lane >> 5);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      A_[mb] = __builtin_bit_cast(bf16x8, ld16(buf + daddr(wm * WM + mb * 32 + (lane & 31), chunk)));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int row = wn * WN + nb * 32 + (lane & 31);
+      B_[nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(row, chunk)));
+      if (SWIGLU) B_[NB + nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(BN + row, chunk)));
+    }
+  };
+  // MFMAs [i0, i1) of a substep
+  auto mma = [&](const bf16x8(&A_)[MB], const bf16x8(&B_)[NBF], int i0, int i1) {
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i < i0 || i >= i1) continue;
+      const int nb = i / MB, mb = i % MB;
+      const int a = (nb / NB) * MB * NB + mb * NB + (nb % NB);
+      acc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B_[nb], A_[mb], acc[a], 0, 0, 0);
+    }
+  };
+  auto pieces = [&](int q0, int stage, int kt) {
+#pragma unroll
+    for (int j = 0; j < QS; ++j) {
+      wait_vmcnt<NP - 1>();   // piece q0 + j of tile kt-1 has landed (loaded one step ago)
+      sw(q0 + j, stage);
+      gl(q0 + j, kt);         // its register now takes tile kt
+    }
+  };
+
+#pragma unroll
+  for (int p = 0; p < NP; ++p) gl(p, 0);
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int p = 0; p < NP; ++p) sw(p, 0);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) gl(p, 1);
+  wait_lgkm0();
+  __syncthreads();
+  read_frags(0, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < KT - 1; ++kt) {
+    const int cur = kt & 1;
+#pragma unroll
+    for (int sub = 0; sub < 3; ++sub) {
+      read_frags(cur, sub + 1, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
+      mma(fa[sub & 1], fb[sub & 1], 0, NM);
+      pieces(QS * sub, cur ^ 1, kt + 2);
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {                 // the next fragments among the first MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < QS; ++j) {                 // then the write / reload pairs
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - NR - QS, 0);
+    }
+    // substep 3: the last pieces among its first 8 MFMAs, the barrier, then
+    // the next tile's first fragments among its last 8
+    mma(fa[1], fb[1], 0, NM / 2);
+    pieces(3 * QS, cur ^ 1, kt + 2);
+#pragma unroll
+    for (int j = 0; j < QS; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    read_frags(cur ^ 1, 0, fa[0], fb[0]);
+    mma(fa[1], fb[1], NM / 2, NM);
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  }
+  {
+    const int cur = (KT - 1) & 1;
+    read_frags(cur, 1, fa[1], fb[1]);
+    mma(fa[0], fb[0], 0, NM);
+    read_frags(cur, 2, fa[0], fb[0]);
+    mma(fa[1], fb[1], 0, NM);
+    read_frags(cur, 3, fa[1], fb[1]);
+    mma(fa[0], fb[0], 0, NM);
+    mma(fa[1], fb[1], 0, NM);
+  }
+  wait_vmcnt<0>();   // the reload past the last tile
+
+  if constexpr (SWIGLU) {
+    __syncthreads();   // every wavefront is done reading the stages
+    store_tile_lds<EPI_SWIGLU, BM, MB, NB, WM, WN, BN, NT_>(acc, tc, wm, wn, n0, N, ldc, C, smem, tid);
+  } else {
+    float* pt = nullptr;
+    if (w.split >= 0) {
+      const int ns = make_plan(offsets, E, BM, NT, P, max_split, KTall).s;
+      pt = partials + (size_t)(w.split * ns + w.slice) * BM * BN;
+    }
+    store_plain_lds<BN, MB, NB, WN, NT_>(acc, wm, wn, lane, tid, smem, pt, tc, n0, N, ldc, C);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Few rows per expert (decode): the grouped GEMMs read every weight once and
 // the token rows are few, so the time is the weight stream from HBM.
 //
@@ -1105,6 +1384,30 @@ hipError_t launch_reg(int64_t R_max, int E, const int32_t* offsets, int N, int K
   return hipGetLastError();
 }
 
+template <int BN, bool SWIGLU>
+hipError_t launch_w4(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A, const void* B0,
+                     const void* B1, void* C, float* partials, int P, hipStream_t s,
+                     const int32_t* a_slot = nullptr, int a_k = 1, uint32_t a_records = 0) {
+  constexpr int BM = 256;
+  constexpr size_t kLds = 2 * (size_t)(BM + 256) * kRowB;
+  auto kern = &ffn_bf16_w4_kernel<BN, SWIGLU>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (attr != hipSuccess) return attr;
+  const int NT = (N + BN - 1) / BN;
+  const int64_t tiles_ub = ((R_max + BM - 1) / BM + E) * NT;
+  const bool split = !SWIGLU && partials != nullptr && P > 0;
+  const int max_split = split ? kMaxSplit : 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid_blocks(tiles_ub, P, split)), dim3(256), kLds, s, E, offsets, N, K,
+                     reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B0),
+                     reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C), NT, P, max_split,
+                     partials, N, a_slot, a_k, a_records);
+  if (split)
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(P * (BM / 16))), dim3(256), 0, s, E, offsets, N, K, NT,
+                       P, max_split, partials, reinterpret_cast<uint16_t*>(C));
+  return hipGetLastError();
+}
+
 template <int BM, int BN, bool SWIGLU, int NWM = 2, int NWN = 2>
 hipError_t launch_gemm(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A,
                        const void* B0, const void* B1, void* C, hipStream_t s) {
@@ -1170,8 +1473,8 @@ hipError_t launch_gemm_bf16(int which, int64_t R_max, int64_t seg_max, int d, in
     // GEMM1 reading token rows straight from the unpermuted activations
     if (which != 1 || !ffn_bf16_can_gather(R_max, seg_max, d, E, F, gather_T) || gather_k < 1)
       return hipErrorInvalidValue;
-    return launch_reg<128, true>(R_max, E, offsets, F, d, in, w0, w1, out, nullptr, 0, s, 0, nullptr, nullptr,
-                                 nullptr, nullptr, 0, gather_slot, gather_k, (uint32_t)(gather_T * d * 2));
+    return launch_w4<128, true>(R_max, E, offsets, F, d, in, w0, w1, out, nullptr, 0, s, gather_slot, gather_k,
+                                (uint32_t)(gather_T * d * 2));
   }
   // At most 64 rows per expert: stream the weights, no row tiles.
   if (ffn_bf16_skinny(seg_max, d, F)) {
@@ -1181,9 +1484,9 @@ hipError_t launch_gemm_bf16(int which, int64_t R_max, int64_t seg_max, int d, in
   // 256-row tiles once experts average at least 128 rows; below that the
   // 128-row tiles waste less work on the ragged last tile of each expert.
   if (ffn_bf16_big_tiles(R_max, E)) {
-    if (which == 1) return launch_reg<128, true>(R_max, E, offsets, F, d, in, w0, w1, out, nullptr, 0, s);
-    return launch_reg<256, false>(R_max, E, offsets, d, F, in, w0, nullptr, out, reinterpret_cast<float*>(ws),
-                                  ws ? compute_units() : 0, s);
+    if (which == 1) return launch_w4<128, true>(R_max, E, offsets, F, d, in, w0, w1, out, nullptr, 0, s);
+    return launch_w4<256, false>(R_max, E, offsets, d, F, in, w0, nullptr, out, reinterpret_cast<float*>(ws),
+                                 ws ? compute_units() : 0, s);
   }
   if (which == 1) return launch_gemm<128, 64, true>(R_max, E, offsets, F, d, in, w0, w1, out, s);
   return launch_gemm<128, 128, false>(R_max, E, offsets, d, F, in, w0, nullptr, out, s);
