@@ -351,35 +351,39 @@ __device__ __forceinline__ void store_tile_lds(const f32x16* acc, const TileCoor
   lds_store_rows<BM, W, decltype(row_ptr), NTHR>(lds, tid, (N - n0) / 8, row_ptr);
 }
 
-// Plain 256 x BN tiles whose wavefronts own 128 whole rows each (wavefront
-// row wm), through LDS as fp32 in two passes: pass h takes row blocks 2h and
-// 2h+1 of every wavefront (tile rows wm*128 + 64h + 0..63), so all four
-// wavefronts write in both passes; LDS row j ([128][BN] floats, 16-byte
-// chunk c of row r at position c ^ (r mod BN/4)) holds tile row
-// (j / 64) * 128 + 64h + j % 64. After a pass the threads store whole 16-byte
-// pieces: fp32 rows of the partial tile pt of a split tail slice ([256][BN],
-// row-major), or, with pt null, the bf16 tile (8 floats per piece; rows at or
-// past the segment's end and columns at or past N are not stored). Both cases
-// share the writes of the accumulators, so no accumulator is live across a
-// branch (with 256 of them a lane, a branch there made the register
-// allocator spill).
-template <int BN, int MB, int NB, int WN, int NTHR>
+// Plain tiles of MT rows x BN through LDS as fp32, [128][BN] floats at a time
+// (16-byte chunk c of row r at position c ^ (r mod BN/4)). With MT = 256 the
+// wavefronts are 2 x 2 and own 128 rows each (wavefront row wm); pass h takes
+// row blocks 2h and 2h+1 of every wavefront (tile rows wm*128 + 64h + 0..63),
+// so all four wavefronts write in both passes, and LDS row j holds tile row
+// (j / 64) * 128 + 64h + j % 64. With MT <= 128 the wavefronts are 1 x 4 and
+// one pass holds the tile (LDS row j = tile row j). After a pass the threads
+// store whole 16-byte pieces: fp32 rows of the partial tile pt of a split
+// tail slice ([256][BN], row-major), or, with pt null, the bf16 tile (8
+// floats per piece; rows at or past the segment's end and columns at or past
+// N are not stored). Both cases share the writes of the accumulators, so no
+// accumulator is live across a branch (with 256 of them a lane, a branch
+// there made the register allocator spill).
+template <int MT, int BN, int MB, int NB, int WN, int NTHR>
 __device__ __forceinline__ void store_plain_lds(const f32x16* acc, int wm, int wn, int lane, int tid, char* lds,
                                                 float* pt, const TileCoord& tc, int n0, int N, int ldc,
                                                 uint16_t* __restrict__ C) {
   constexpr int CH = BN / 4, RB = BN * 4;
-  static_assert(MB == 4 && 128 * RB <= 2 * 65536, "two row blocks of each wavefront per pass fit in LDS");
-  const int rows = min(256, tc.seg_rows - tc.m0);
+  constexpr int PASSES = MT == 256 ? 2 : 1, PR = MT == 256 ? 128 : MT;   // passes, rows per pass
+  static_assert(128 * RB <= 2 * 65536, "128 fp32 rows of the tile fit in LDS");
+  static_assert(MT == 256 ? MB == 4 : MB * 32 == MT, "2 x 2 wavefronts of 128 rows or 1 x 4 of the whole tile");
+  const int rows = min(MT, tc.seg_rows - tc.m0);
   const int ncols = N - n0;
   uint16_t* c0 = C + (size_t)(tc.seg_start + tc.m0) * ldc + n0;
   auto at = [&](int row, int c) { return lds + row * RB + ((c ^ (row & (CH - 1))) << 4); };
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < PASSES; ++h) {
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < (MT == 256 ? 2 : MB); ++m) {
       __builtin_amdgcn_sched_barrier(0);
-      const int mb = 2 * h + m, row = wm * 64 + m * 32 + (lane & 31);
+      const int mb = MT == 256 ? 2 * h + m : m;
+      const int row = (MT == 256 ? wm * 64 : 0) + m * 32 + (lane & 31);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -391,16 +395,16 @@ __device__ __forceinline__ void store_plain_lds(const f32x16* acc, int wm, int w
         }
     }
     __syncthreads();
-    auto trow = [&](int j) { return (j >> 6) * 128 + 64 * h + (j & 63); };
+    auto trow = [&](int j) { return MT == 256 ? (j >> 6) * 128 + 64 * h + (j & 63) : j; };
     if (pt != nullptr) {
 #pragma unroll 4
-      for (int i = 0; i < 128 * CH / NTHR; ++i) {
+      for (int i = 0; i < PR * CH / NTHR; ++i) {
         const int cidx = tid + i * NTHR, row = cidx / CH, c = cidx % CH;
         st16(pt + (size_t)trow(row) * BN + 4 * c, ld16(at(row, c)));
       }
     } else {
 #pragma unroll 4
-      for (int i = 0; i < 128 * (CH / 2) / NTHR; ++i) {
+      for (int i = 0; i < PR * (CH / 2) / NTHR; ++i) {
         const int cidx = tid + i * NTHR, row = cidx / (CH / 2), c8 = cidx % (CH / 2);
         const f32x4 lo = __builtin_bit_cast(f32x4, ld16(at(row, 2 * c8)));
         const f32x4 hi = __builtin_bit_cast(f32x4, ld16(at(row, 2 * c8 + 1)));
@@ -465,6 +469,41 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(int E, const int32_t*
   const size_t ss = (size_t)BM * BN;
   uint16_t* crow0 = C + (size_t)(tc.seg_start + tc.m0 + row0) * (size_t)N + (size_t)tc.n_tile * BN;
   switch (p.s) {
+    case 2: split_reduce_rows<2>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+    case 3: split_reduce_rows<3>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+    case 4: split_reduce_rows<4>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+    case 5: split_reduce_rows<5>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+    case 6: split_reduce_rows<6>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+    case 7: split_reduce_rows<7>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+    default: split_reduce_rows<kMaxSplit>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
+  }
+}
+
+// The same for the per-XCD plan: one block per (XCD tail tile, 16-row group);
+// XCD x's tail tile t has its partials at slots x Px + t s .. + s - 1.
+__global__ __launch_bounds__(256) void split_reduce_xcd_kernel(int E, const int32_t* __restrict__ offsets, int N,
+                                                               int K, int NT, int P, int max_split,
+                                                               const float* __restrict__ partials,
+                                                               uint16_t* __restrict__ C) {
+  constexpr int BM = 256, BN = 256;
+  __shared__ int ws[24];
+  const int Px = P / kXcds;
+  const int tg = blockIdx.x / (BM / 16), xcd = tg / Px, t = tg % Px;
+  int tiles;
+  const ExpertScan es = expert_scan(offsets, E, NT, ws, tiles);
+  const XcdRun q = xcd_run(tiles, Px, max_split, K / kBK, xcd);
+  if (t >= q.r) return;
+  const TileCoord tc = locate_tile_scan(es, E, NT, q.first + q.full + t, ws + 16);
+  const int lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x % (BM / 16)) * 16 + (threadIdx.x >> 6) * 4;
+  const int rows_left = tc.seg_rows - (tc.m0 + row0);
+  if (rows_left <= 0) return;
+  const int col = lane * 4;
+  const bool col_ok = tc.n_tile * BN + col < N;
+  const float* part = partials + (size_t)(xcd * Px + t * q.s) * BM * BN;
+  const size_t ss = (size_t)BM * BN;
+  uint16_t* crow0 = C + (size_t)(tc.seg_start + tc.m0 + row0) * (size_t)N + (size_t)tc.n_tile * BN;
+  switch (q.s) {
     case 2: split_reduce_rows<2>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
     case 3: split_reduce_rows<3>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
     case 4: split_reduce_rows<4>(part, ss, row0, rows_left, col, col_ok, crow0, N); break;
@@ -840,58 +879,61 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Forward tiles with 4 wavefronts (one per SIMD), each owning 128 token rows x
-// 128 weight rows of the 256 x 256 tile (256 fp32 accumulators a lane, held
-// in the accumulation registers), so a K step reads a third less from LDS
-// than with 8 wavefronts of 128 x 64. With one wavefront per SIMD nothing
-// hides a fragment read that an MFMA waits for, so the reads run one 16-deep
-// substep ahead of the MFMAs, across the K steps too: the 16 pieces a thread
-// stages per K step (8 token rows, 8 weight rows) are written to the other
-// LDS stage four per substep, each reloaded at once with the step after
-// (one K step to land); the last four are written early in substep 3, then
-// the step's one barrier, and the first fragments of the next step are read
-// while the remaining 8 MFMAs of substep 3 run. Stage reuse: a stage is
-// rewritten only after the barrier that follows every wavefront's last read
-// of it. Tile plan, gather, split tail and LDS-staged epilogue as in
+// Forward tiles with 4 wavefronts (one per SIMD). A 256-row tile gives each
+// wavefront 128 token rows x 128 weight rows (2 x 2; 256 fp32 accumulators
+// a lane, held in the accumulation registers), so a K step reads a third
+// less from LDS than with 8 wavefronts of 128 x 64. With one wavefront per
+// SIMD nothing hides a fragment read that an MFMA waits for, so the reads
+// run one 16-deep substep ahead of the MFMAs, across the K steps too: the
+// pieces a thread stages per K step (token rows, then 8 weight rows) are
+// written to the other LDS stage a quarter per substep, each reloaded at
+// once with the step after (one K step to land); the last quarter is
+// written early in substep 3, then the step's one barrier, and the first
+// fragments of the next step are read while the rest of substep 3's MFMAs
+// run. Stage reuse: a stage is rewritten only after the barrier that follows
+// every wavefront's last read of it.
+// An expert's last row tile is ragged. A tile of at most 128 (64) rows runs
+// with the wavefronts side by side (1 x 4, each 128 (64) rows x a quarter of
+// the weight rows) and stages only its token rows, so it costs half (a
+// quarter) of the MFMAs of a full tile (MT: the rows a tile body handles).
+// Tile plan, gather, split tail and LDS-staged epilogues as in
 // ffn_bf16_reg_kernel. Measured against that kernel on a dense 1024 x 65536
 // GEMM: +3% at K = 4096, +5% at K = 14336.
 // ---------------------------------------------------------------------------
-template <int BN, bool SWIGLU>
-__global__ __launch_bounds__(256) void ffn_bf16_w4_kernel(
-    int E, const int32_t* __restrict__ offsets, int N, int K, const uint16_t* __restrict__ A,
-    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT, int P,
-    int max_split, float* __restrict__ partials, int ldc, const int32_t* __restrict__ a_slot, int a_k,
-    uint32_t a_records) {
-  constexpr int BM = 256, NWN = 2, NT_ = 256;
+template <int BN, bool SWIGLU, int MT>
+__device__ __forceinline__ void w4_tile(const XcdItem& w, int KTall, int E, const int32_t* __restrict__ offsets,
+                                        int N, int K, const uint16_t* __restrict__ A,
+                                        const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
+                                        uint16_t* __restrict__ C, int NT, int P, int max_split,
+                                        float* __restrict__ partials, int ldc, const int32_t* __restrict__ a_slot,
+                                        int a_k, uint32_t a_records, char* smem) {
+  constexpr int BM = 256, NT_ = 256;
   constexpr int BROWS = SWIGLU ? 2 * BN : BN;
-  static_assert(BROWS == 256, "both operands are 256-row tiles");
-  constexpr int WM = BM / 2, WN = BN / NWN;
+  static_assert(BROWS == 256, "the weight tile has 256 rows");
+  constexpr int NWM = MT == 256 ? 2 : 1, NWN = 4 / NWM;
+  constexpr int WM = MT / NWM, WN = BN / NWN;
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int NBF = (SWIGLU ? 2 : 1) * NB;
   constexpr int NACC = MB * NBF, NM = NACC, NR = MB + NBF;
-  constexpr int PT = 2048 / NT_;                 // 16-byte pieces per thread per operand per K step
-  constexpr int NP = 2 * PT, QS = NP / 4;        // pieces per thread per K step, per substep
   constexpr int RSTEP = NT_ / 8;                 // rows between a thread's pieces
+  constexpr int PA = MT / RSTEP, PB = BROWS / RSTEP, NP = PA + PB;   // 16-byte pieces per thread per K step
   constexpr int STAGE = (BM + BROWS) * kRowB;
-  static_assert(NM == 16 && NR == 8 && QS == 4, "16 MFMAs, 8 fragment reads, 4 pieces per substep");
-  extern __shared__ __align__(16) char smem[];
+  static_assert(MB >= 1 && NB >= 1 && NM % 2 == 0, "whole 32 x 32 blocks");
 
-  const int KTall = K / kBK;
-  WorkItem w;
-  if (!find_item(offsets, E, BM, NT, P, max_split, KTall, blockIdx.x, w)) return;
   const TileCoord tc = w.tc;
-  int kb = 0, KT = KTall;
-  if (w.split >= 0) {
-    const int ns = make_plan(offsets, E, BM, NT, P, max_split, KTall).s;
-    kb = w.slice * KTall / ns;
-    KT = (w.slice + 1) * KTall / ns - kb;
-  }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kb = w.slice * KTall / w.nslices;
+  const int KT = (w.slice + 1) * KTall / w.nslices - kb;
+  // the thread index through an opaque step: the per-thread address arithmetic
+  // then stays inside the loop over a block's tiles instead of being hoisted
+  // out of it (for three tile shapes), where it would hold registers throughout
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / NWN, wn = wave % NWN;
   const int n0 = tc.n_tile * BN;
 
   const size_t rowb = (size_t)K * 2;
-  const int a_rows = min(BM, tc.seg_rows - tc.m0);
+  const int a_rows = min(MT, tc.seg_rows - tc.m0);
   const int b_rows = min(BN, N - n0);
   const size_t wrow0 = (size_t)tc.e * N + n0;
   const auto rb0 = make_rsrc(B0 + wrow0 * K, (uint32_t)(b_rows * rowb));
@@ -900,11 +942,11 @@ __global__ __launch_bounds__(256) void ffn_bf16_w4_kernel(
   const uint32_t voff = (uint32_t)(row0 * rowb) + ch * 16 + (uint32_t)kb * kRowB;
   const uint32_t rstep = (uint32_t)(RSTEP * rowb);
   __amdgpu_buffer_rsrc_t ra;
-  uint32_t aoff[PT];
+  uint32_t aoff[PA];
   if (a_slot != nullptr) {   // gathered token rows, as in ffn_bf16_reg_kernel
     ra = make_rsrc(A, a_records);
 #pragma unroll
-    for (int p = 0; p < PT; ++p) {
+    for (int p = 0; p < PA; ++p) {
       const int r = row0 + p * RSTEP;
       aoff[p] = r < a_rows ? ((uint32_t)a_slot[tc.seg_start + tc.m0 + r] / (uint32_t)a_k) * (uint32_t)rowb + ch * 16 +
                                  (uint32_t)kb * kRowB
@@ -913,26 +955,26 @@ __global__ __launch_bounds__(256) void ffn_bf16_w4_kernel(
   } else {
     ra = make_rsrc(A + (size_t)(tc.seg_start + tc.m0) * K, (uint32_t)(a_rows * rowb));
 #pragma unroll
-    for (int p = 0; p < PT; ++p) aoff[p] = voff + p * rstep;
+    for (int p = 0; p < PA; ++p) aoff[p] = voff + p * rstep;
   }
   const int wofs = row0 * kRowB + ((ch ^ dswz(row0)) << 4);   // RSTEP is a multiple of 16: same swizzle
 
-  // piece p < PT: token row row0 + p*RSTEP; p >= PT: weight row row0 + (p-PT)*RSTEP
+  // piece p < PA: token row row0 + p*RSTEP; p >= PA: weight row row0 + (p-PA)*RSTEP
   // (SwiGLU tiles: BN gate rows, then BN up rows)
   u32x4 stg[NP];
   auto gl = [&](int p, int kt) {
     const uint32_t ko = (uint32_t)(kt < KT ? kt : KT - 1) * kRowB;
-    if (p < PT) {
+    if (p < PA) {
       stg[p] = bload16(ra, aoff[p] + ko);
     } else {
-      const int i = p - PT;
+      const int i = p - PA;
       const bool up = SWIGLU && i * RSTEP >= BN;
       stg[p] = bload16(up ? rb1 : rb0, voff + (up ? i * rstep - BN * (uint32_t)rowb : i * rstep) + ko);
     }
   };
   auto sw = [&](int p, int stage) {
     char* b = smem + stage * STAGE + wofs;
-    st16(p < PT ? b + p * RSTEP * kRowB : b + BM * kRowB + (p - PT) * RSTEP * kRowB, stg[p]);
+    st16(p < PA ? b + p * RSTEP * kRowB : b + BM * kRowB + (p - PA) * RSTEP * kRowB, stg[p]);
   };
 
   f32x16 acc[NACC];
@@ -964,12 +1006,15 @@ __global__ __launch_bounds__(256) void ffn_bf16_w4_kernel(
       acc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B_[nb], A_[mb], acc[a], 0, 0, 0);
     }
   };
-  auto pieces = [&](int q0, int stage, int kt) {
+  // substep sub writes (and reloads) pieces [q0(sub), q0(sub+1))
+  auto q0 = [](int sub) { return NP * sub / 4; };
+  auto pieces = [&](int sub, int stage, int kt) {
 #pragma unroll
-    for (int j = 0; j < QS; ++j) {
-      wait_vmcnt<NP - 1>();   // piece q0 + j of tile kt-1 has landed (loaded one step ago)
-      sw(q0 + j, stage);
-      gl(q0 + j, kt);         // its register now takes tile kt
+    for (int p = 0; p < NP; ++p) {
+      if (p < q0(sub) || p >= q0(sub + 1)) continue;
+      wait_vmcnt<NP - 1>();   // piece p of tile kt-1 has landed (loaded one step ago)
+      sw(p, stage);
+      gl(p, kt);              // its register now takes tile kt
     }
   };
 
@@ -989,27 +1034,32 @@ __global__ __launch_bounds__(256) void ffn_bf16_w4_kernel(
     for (int sub = 0; sub < 3; ++sub) {
       read_frags(cur, sub + 1, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
       mma(fa[sub & 1], fb[sub & 1], 0, NM);
-      pieces(QS * sub, cur ^ 1, kt + 2);
+      pieces(sub, cur ^ 1, kt + 2);
+      // the next fragments among the first MFMAs, then the write / reload pairs, each with an
+      // MFMA while any is left
+      const int nq = q0(sub + 1) - q0(sub);
 #pragma unroll
-      for (int j = 0; j < NR; ++j) {                 // the next fragments among the first MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int j = 0; j < NR; ++j) {
+        if (j < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
 #pragma unroll
-      for (int j = 0; j < QS; ++j) {                 // then the write / reload pairs
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int j = 0; j < nq; ++j) {
+        if (NR + j < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, NM - NR - QS, 0);
-    }
-    // substep 3: the last pieces among its first 8 MFMAs, the barrier, then
-    // the next tile's first fragments among its last 8
-    mma(fa[1], fb[1], 0, NM / 2);
-    pieces(3 * QS, cur ^ 1, kt + 2);
 #pragma unroll
-    for (int j = 0; j < QS; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      for (int j = NR + nq; j < NM; ++j) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    // substep 3: the last pieces among its first MFMAs, the barrier, then the next tile's
+    // first fragments among the rest
+    mma(fa[1], fb[1], 0, NM / 2);
+    pieces(3, cur ^ 1, kt + 2);
+#pragma unroll
+    for (int j = 0; j < NP - q0(3); ++j) {
+      if (2 * j < NM / 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (2 * j + 1 < NM / 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
@@ -1020,7 +1070,7 @@ __global__ __launch_bounds__(256) void ffn_bf16_w4_kernel(
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (j < NM / 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   }
   {
@@ -1037,14 +1087,42 @@ __global__ __launch_bounds__(256) void ffn_bf16_w4_kernel(
 
   if constexpr (SWIGLU) {
     __syncthreads();   // every wavefront is done reading the stages
-    store_tile_lds<EPI_SWIGLU, BM, MB, NB, WM, WN, BN, NT_>(acc, tc, wm, wn, n0, N, ldc, C, smem, tid);
+    store_tile_lds<EPI_SWIGLU, MT, MB, NB, WM, WN, BN, NT_>(acc, tc, wm, wn, n0, N, ldc, C, smem, tid);
   } else {
-    float* pt = nullptr;
-    if (w.split >= 0) {
-      const int ns = make_plan(offsets, E, BM, NT, P, max_split, KTall).s;
-      pt = partials + (size_t)(w.split * ns + w.slice) * BM * BN;
-    }
-    store_plain_lds<BN, MB, NB, WN, NT_>(acc, wm, wn, lane, tid, smem, pt, tc, n0, N, ldc, C);
+    float* pt = w.slot >= 0 ? partials + (size_t)w.slot * BM * BN : nullptr;
+    store_plain_lds<MT, BN, MB, NB, WN, NT_>(acc, wm, wn, lane, tid, smem, pt, tc, n0, N, ldc, C);
+  }
+}
+
+template <int BN, bool SWIGLU>
+__global__ __launch_bounds__(256) void ffn_bf16_w4_kernel(
+    int E, const int32_t* __restrict__ offsets, int N, int K, const uint16_t* __restrict__ A,
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT, int P,
+    int max_split, float* __restrict__ partials, int ldc, const int32_t* __restrict__ a_slot, int a_k,
+    uint32_t a_records) {
+  extern __shared__ __align__(16) char smem[];
+  int* ws = reinterpret_cast<int*>(smem);   // plan words; the stages are free between tiles
+  const int KTall = K / kBK, xcd = blockIdx.x % kXcds, Px = P / kXcds;
+  int tiles;
+  const ExpertScan es = expert_scan(offsets, E, NT, ws, tiles);
+  const XcdRun q = xcd_run(tiles, Px, max_split, KTall, xcd);
+  const int stride = gridDim.x / kXcds;
+  for (int l = blockIdx.x / kXcds;; l += stride) {
+    XcdItem w;
+    int tile;
+    if (!xcd_item(q, xcd, Px, l, tile, w)) break;
+    w.tc = locate_tile_scan(es, E, NT, tile, ws + 16);
+    __syncthreads();   // every thread has its tile before the stages are written
+    const int rows = w.tc.seg_rows - w.tc.m0;   // the tile's token rows (at most 256 are used)
+    if (rows <= 64)
+      w4_tile<BN, SWIGLU, 64>(w, KTall, E, offsets, N, K, A, B0, B1, C, NT, P, max_split, partials, ldc, a_slot,
+                              a_k, a_records, smem);
+    else if (rows <= 128)
+      w4_tile<BN, SWIGLU, 128>(w, KTall, E, offsets, N, K, A, B0, B1, C, NT, P, max_split, partials, ldc, a_slot,
+                               a_k, a_records, smem);
+    else
+      w4_tile<BN, SWIGLU, 256>(w, KTall, E, offsets, N, K, A, B0, B1, C, NT, P, max_split, partials, ldc, a_slot,
+                               a_k, a_records, smem);
   }
 }
 
@@ -1396,15 +1474,15 @@ hipError_t launch_w4(int64_t R_max, int E, const int32_t* offsets, int N, int K,
   if (attr != hipSuccess) return attr;
   const int NT = (N + BN - 1) / BN;
   const int64_t tiles_ub = ((R_max + BM - 1) / BM + E) * NT;
-  const bool split = !SWIGLU && partials != nullptr && P > 0;
+  const bool split = !SWIGLU && partials != nullptr && P >= kXcds;
   const int max_split = split ? kMaxSplit : 1;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid_blocks(tiles_ub, P, split)), dim3(256), kLds, s, E, offsets, N, K,
-                     reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B0),
+  hipLaunchKernelGGL(kern, dim3((unsigned)xcd_grid_blocks(tiles_ub, P, split)), dim3(256), kLds, s, E,
+                     offsets, N, K, reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B0),
                      reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C), NT, P, max_split,
                      partials, N, a_slot, a_k, a_records);
   if (split)
-    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(P * (BM / 16))), dim3(256), 0, s, E, offsets, N, K, NT,
-                       P, max_split, partials, reinterpret_cast<uint16_t*>(C));
+    hipLaunchKernelGGL(split_reduce_xcd_kernel, dim3((unsigned)(P / kXcds * kXcds * (BM / 16))), dim3(256), 0, s, E,
+                       offsets, N, K, NT, P, max_split, partials, reinterpret_cast<uint16_t*>(C));
   return hipGetLastError();
 }
 
