@@ -189,6 +189,36 @@ def test_grouped_ffn(case):
     assert_close_rows(host(o[:R]), ref["o_rows"], w.dtype, "o")
 
 
+# Expert row counts that give the 256-row-tile GEMMs every tile shape: last
+# row tiles of 1 and 64 rows (the 64-row body), 65 and 128 (the 128-row
+# body), 129, 255 and 256 (full), an empty expert and experts of several
+# tiles; the down projection with and without its split tail (the tail tiles
+# of each XCD cut into K-slices when the workspace is given).
+TILE_COUNTS = [1, 64, 65, 128, 129, 255, 256, 257, 300, 0, 511, 640]
+
+
+@pytest.mark.parametrize("split", [True, False], ids=["split_tail", "whole_tiles"])
+def test_grouped_ffn_tile_shapes(split):
+    E, d, F = len(TILE_COUNTS), 512, 384
+    offsets = np.concatenate([[0], np.cumsum(TILE_COUNTS)]).astype(np.int32)
+    R = int(offsets[-1])
+    assert R >= 128 * E   # the 256-row tiles
+    w = mi.Workload("tile_shapes", T=R, d=d, E=E, k=1, F=F, cf=0.0, dtype="bf16", seed=70)
+    a = mi.generate(w)
+    xp = dev(a["x"])
+    h, o = moe.moe_grouped_ffn_rows(xp, dev(torch.from_numpy(offsets)), dev(a["w_gate"]), dev(a["w_up"]),
+                                    dev(a["w_down"]), R, ws=None if split else False)
+    torch.cuda.synchronize()
+    hs, os_ = [], []
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        he, oe = orc.swiglu_expert(a["x"][lo:hi], a["w_gate"][e], a["w_up"][e], a["w_down"][e], "bf16")
+        hs.append(he)
+        os_.append(oe)
+    assert_close_rows(host(h[:R]), np.concatenate(hs), "bf16", "h")
+    assert_close_rows(host(o[:R]), np.concatenate(os_), "bf16", "o")
+
+
 @pytest.mark.parametrize("case", SMALL + NAMED_SMALL, ids=case_id)
 def test_unpermute_combine(case):
     w, a = workload(case)
