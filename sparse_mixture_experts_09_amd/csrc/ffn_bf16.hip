@@ -1321,7 +1321,14 @@ __global__ __launch_bounds__(512) void wgrad_kernel(int E, const int32_t* __rest
   if (l >= q + (x < rr ? 1 : 0)) return;
   const int tile = x * q + min(x, rr) + l;
   const int e = tile / (MT * NTn), rem = tile % (MT * NTn);
-  const int m0 = (rem % MT) * BM, n0 = (rem / MT) * BN;
+  // Consecutive tiles (the blocks of one XCD at a time) share one operand's
+  // column slab and each read a different slab of the other, which is so
+  // read again for every tile of the shared one: that re-read operand is the
+  // narrower one (A when M <= N), whose rows of an expert stay cached. (Over
+  // [da | db], 2F = 28672 columns, it would be 58 MB an expert, 8 experts at
+  // once: more than the 256 MB Infinity Cache.)
+  const bool m_fast = M <= N;
+  const int m0 = (m_fast ? rem % MT : rem / NTn) * BM, n0 = (m_fast ? rem / MT : rem % NTn) * BN;
   const int lo = offsets[e], cnt = offsets[e + 1] - lo;
   const int KT = (cnt + kBK - 1) / kBK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
