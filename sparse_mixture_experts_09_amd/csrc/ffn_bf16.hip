@@ -1142,9 +1142,11 @@ __global__ __launch_bounds__(256) void ffn_bf16_w4_kernel(
 // The DMA past the last K step uses offsets above every record count, so it
 // fetches nothing and the wait counts stay the same on every step.
 // ---------------------------------------------------------------------------
+// AUX: the cache policy bits of the load (2: nontemporal, for data read once)
+template <int AUX = 0>
 __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, char* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voff, 0, 0, AUX);
 #endif
 }
 
@@ -1185,9 +1187,14 @@ __global__ __launch_bounds__(64 * NW) void ffn_bf16_skinny_kernel(int E, const i
   auto issue = [&](int stage, int kt) {
     char* st = my + stage * STAGE;
     const uint32_t ko = kt < KT ? (uint32_t)kt * kRowB : 0x80000000u;
+    // the weights stream through once: nontemporal; the token rows are read by every block
 #pragma unroll
-    for (int i = 0; i < L; ++i)
-      bdma16(i < 4 ? ((SWIGLU && i >= 2) ? rw1 : rw0) : rx, src[i] + ko, st + i * 1024);
+    for (int i = 0; i < L; ++i) {
+      if (i < 4)
+        bdma16<2>((SWIGLU && i >= 2) ? rw1 : rw0, src[i] + ko, st + i * 1024);
+      else
+        bdma16(rx, src[i] + ko, st + i * 1024);
+    }
   };
   f32x16 acc[MT];
 #pragma unroll
