@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int d, int k,
   for (uint32_t off = (uint32_t)lane * 16; off < row_bytes; off += 64 * 16) {
     u32x4 v[KM];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) v[j] = bload16(src[j], off);
+    for (int j = 0; j < KM; ++j) v[j] = bload16<2>(src[j], off);   // each row is read once: nontemporal
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;

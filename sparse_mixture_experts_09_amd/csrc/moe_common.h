@@ -72,8 +72,10 @@ __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cas
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
+// AUX: the cache policy bits (2: nontemporal, for data read once)
+template <int AUX = 0>
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, AUX));
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
