@@ -219,6 +219,31 @@ def test_grouped_ffn_tile_shapes(split):
     assert_close_rows(host(o[:R]), np.concatenate(os_), "bf16", "o")
 
 
+# The most experts with 256-row tiles (at least 128 rows per expert on
+# average): every thread of the per-XCD plan's block scan holds an expert,
+# and most experts end in a ragged tile of at most 128 rows.
+@pytest.mark.parametrize("E,R,seed", [(256, 32768, 80), (255, 33000, 81)])
+def test_grouped_ffn_many_experts(E, R, seed):
+    d, F = 128, 128
+    rng = np.random.default_rng(seed)
+    counts = rng.multinomial(R, np.full(E, 1.0 / E))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    assert R >= 128 * E   # the 256-row tiles
+    w = mi.Workload("many_experts", T=R, d=d, E=E, k=1, F=F, cf=0.0, dtype="bf16", seed=seed)
+    a = mi.generate(w)
+    h, o = moe.moe_grouped_ffn_rows(dev(a["x"]), dev(torch.from_numpy(offsets)), dev(a["w_gate"]), dev(a["w_up"]),
+                                    dev(a["w_down"]), R)
+    torch.cuda.synchronize()
+    hs, os_ = [], []
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        he, oe = orc.swiglu_expert(a["x"][lo:hi], a["w_gate"][e], a["w_up"][e], a["w_down"][e], "bf16")
+        hs.append(he)
+        os_.append(oe)
+    assert_close_rows(host(h[:R]), np.concatenate(hs), "bf16", "h")
+    assert_close_rows(host(o[:R]), np.concatenate(os_), "bf16", "o")
+
+
 @pytest.mark.parametrize("case", SMALL + NAMED_SMALL, ids=case_id)
 def test_unpermute_combine(case):
     w, a = workload(case)
