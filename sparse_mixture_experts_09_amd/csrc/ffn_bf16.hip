@@ -1306,6 +1306,11 @@ hipError_t launch_skinny(int64_t seg_max, int E, const int32_t* offsets, int N, 
 // record counts end at the expert's last row, so the rows of the last step
 // past it read zeros. Tiles run expert by expert with m-tiles fastest, each
 // XCD a contiguous run of them; an expert with no rows gets a zero gradient.
+// The K extent is an expert's rows (about a thousand), so a tile is only ~16
+// K steps: the blocks stay resident (one per compute unit, stepping through
+// their XCD's run with the grid's stride) and load the next tile's first K
+// step before the current tile's epilogue, so that load's latency and the
+// block launch no longer sit between the tiles.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(512) void wgrad_kernel(int E, const int32_t* __restrict__ offsets, int M, int M1, int N,
                                                     int lda, int ldb, const uint16_t* __restrict__ A,
@@ -1323,11 +1328,11 @@ __global__ __launch_bounds__(512) void wgrad_kernel(int E, const int32_t* __rest
 
   const int MT = (M + BM - 1) / BM, NTn = (N + BN - 1) / BN;
   const int tiles = E * MT * NTn;
-  const int x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
+  const int x = blockIdx.x % kXcds, stride = gridDim.x / kXcds;
   const int q = tiles / kXcds, rr = tiles % kXcds;
-  if (l >= q + (x < rr ? 1 : 0)) return;
-  const int tile = x * q + min(x, rr) + l;
-  const int e = tile / (MT * NTn), rem = tile % (MT * NTn);
+  const int first = x * q + min(x, rr), run = q + (x < rr ? 1 : 0);
+  int l = blockIdx.x / kXcds;
+  if (l >= run) return;
   // Consecutive tiles (the blocks of one XCD at a time) share one operand's
   // column slab and each read a different slab of the other, which is so
   // read again for every tile of the shared one: that re-read operand is the
@@ -1335,95 +1340,130 @@ __global__ __launch_bounds__(512) void wgrad_kernel(int E, const int32_t* __rest
   // [da | db], 2F = 28672 columns, it would be 58 MB an expert, 8 experts at
   // once: more than the 256 MB Infinity Cache.)
   const bool m_fast = M <= N;
-  const int m0 = (m_fast ? rem % MT : rem / NTn) * BM, n0 = (m_fast ? rem / MT : rem % NTn) * BN;
-  const int lo = offsets[e], cnt = offsets[e + 1] - lo;
-  const int KT = (cnt + kBK - 1) / kBK;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / NWN, wn = wave % NWN;
-
-  f32x16 acc[NACC];
-#pragma unroll
-  for (int i = 0; i < NACC; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-
-  if (KT > 0) {
-    // columns past M (N) read the next row and are never stored
-    const auto ra = make_rsrc(A + (size_t)lo * lda + m0, (uint32_t)(((size_t)cnt * lda - m0) * 2));
-    const auto rb = make_rsrc(B + (size_t)lo * ldb + n0, (uint32_t)(((size_t)cnt * ldb - n0) * 2));
-    const int k0 = tid >> 5, c = tid & 31;
-    const uint32_t a_off = (uint32_t)(k0 * lda + c * 8) * 2u, b_off = (uint32_t)(k0 * ldb + c * 8) * 2u;
-    const int wofs = k0 * 512 + ((c ^ ((k0 & 3) << 2)) << 4);   // rows k0 + 16 i share (row & 3)
-    u32x4 stg[NP];
-    auto gl = [&](int p, int kt) {
-      const uint32_t k = (uint32_t)((kt < KT ? kt : KT - 1) * kBK + 16 * (p % PT));
-      stg[p] = p < PT ? bload16(ra, a_off + k * (uint32_t)lda * 2u) : bload16(rb, b_off + k * (uint32_t)ldb * 2u);
-    };
-    auto sw = [&](int p, int stage) {
-      st16(smem + stage * STAGE + (p < PT ? 0 : TILE) + wofs + (p % PT) * 16 * 512, stg[p]);
-    };
+  int e, m0, n0, lo, cnt, KT;
+  auto coords = [&](int tile) {
+    e = tile / (MT * NTn);
+    const int rem = tile % (MT * NTn);
+    m0 = (m_fast ? rem % MT : rem / NTn) * BM;
+    n0 = (m_fast ? rem / MT : rem % NTn) * BN;
+    lo = offsets[e];
+    cnt = offsets[e + 1] - lo;
+    KT = (cnt + kBK - 1) / kBK;
+  };
+  // The per-thread offsets are worked out again for every tile from the
+  // thread index passed through an opaque step: left to itself the compiler
+  // would hoist them out of the loop over tiles, where they would hold
+  // registers through the epilogue and spill.
+  int tid, lane, wave, wm, wn, k0, c, tq, ts, wofs;
+  uint32_t a_off, b_off;
+  auto thread_setup = [&]() {
+    tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63;
+    wave = tid >> 6;
+    wm = wave / NWN;
+    wn = wave % NWN;
+    k0 = tid >> 5;
+    c = tid & 31;
+    a_off = (uint32_t)(k0 * lda + c * 8) * 2u;
+    b_off = (uint32_t)(k0 * ldb + c * 8) * 2u;
+    wofs = k0 * 512 + ((c ^ ((k0 & 3) << 2)) << 4);   // rows k0 + 16 i share (row & 3)
     // lane i of 16-lane group tq gets rows k..k+3 of column (block base + 16 (tq & 1) + i)
-    const int tq = lane >> 4, ts = lane & 15;
-    auto frag = [&](const char* t, int sub, int col0) {
-      const int k = 16 * sub + 8 * (tq >> 1) + (ts >> 2);
-      const int n = col0 + 16 * (tq & 1) + 4 * (ts & 3);
-      const char* at = t + k * 512 + (((n >> 3) ^ ((k & 3) << 2)) << 4) + (n & 4) * 2;
-      const uint2 lo2 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)at));
-      const uint2 hi2 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(at + 4 * 512)));
-      const u32x4 v = {lo2.x, lo2.y, hi2.x, hi2.y};
-      return __builtin_bit_cast(bf16x8, v);
-    };
-    bf16x8 fa[2][MB], fb[2][NB];
-    auto read_frags = [&](int stage, int sub, bf16x8(&A_)[MB], bf16x8(&B_)[NB]) {
-      const char* buf = smem + stage * STAGE;
+    tq = lane >> 4;
+    ts = lane & 15;
+  };
+
+  // columns past M (N) read the next row and are never stored; an expert
+  // without rows has no records, so its loads read zeros
+  __amdgpu_buffer_rsrc_t ra, rb;
+  auto descriptors = [&]() {
+    ra = make_rsrc(A + (size_t)lo * lda + m0, cnt > 0 ? (uint32_t)(((size_t)cnt * lda - m0) * 2) : 0u);
+    rb = make_rsrc(B + (size_t)lo * ldb + n0, cnt > 0 ? (uint32_t)(((size_t)cnt * ldb - n0) * 2) : 0u);
+  };
+  u32x4 stg[NP];
+  // a step past the last one fetches nothing
+  auto gl = [&](int p, int kt) {
+    const uint32_t k = (uint32_t)(kt * kBK + 16 * (p % PT));
+    stg[p] = p < PT ? bload16(ra, kt < KT ? a_off + k * (uint32_t)lda * 2u : 0x80000000u)
+                    : bload16(rb, kt < KT ? b_off + k * (uint32_t)ldb * 2u : 0x80000000u);
+  };
+  auto sw = [&](int p, int stage) {
+    st16(smem + stage * STAGE + (p < PT ? 0 : TILE) + wofs + (p % PT) * 16 * 512, stg[p]);
+  };
+  auto frag = [&](const char* t, int sub, int col0) {
+    const int k = 16 * sub + 8 * (tq >> 1) + (ts >> 2);
+    const int n = col0 + 16 * (tq & 1) + 4 * (ts & 3);
+    const char* at = t + k * 512 + (((n >> 3) ^ ((k & 3) << 2)) << 4) + (n & 4) * 2;
+    const uint2 lo2 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)at));
+    const uint2 hi2 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(at + 4 * 512)));
+    const u32x4 v = {lo2.x, lo2.y, hi2.x, hi2.y};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+  f32x16 acc[NACC];
+  bf16x8 fa[2][MB], fb[2][NB];
+  auto read_frags = [&](int stage, int sub, bf16x8(&A_)[MB], bf16x8(&B_)[NB]) {
+    const char* buf = smem + stage * STAGE;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) A_[mb] = frag(buf, sub, wm * WM + mb * 32);
+    for (int mb = 0; mb < MB; ++mb) A_[mb] = frag(buf, sub, wm * WM + mb * 32);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) B_[nb] = frag(buf + TILE, sub, wn * WN + nb * 32);
-    };
-    auto mma = [&](const bf16x8(&A_)[MB], const bf16x8(&B_)[NB]) {
+    for (int nb = 0; nb < NB; ++nb) B_[nb] = frag(buf + TILE, sub, wn * WN + nb * 32);
+  };
+  auto mma = [&](const bf16x8(&A_)[MB], const bf16x8(&B_)[NB]) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb * NB + nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B_[nb], A_[mb], acc[mb * NB + nb], 0, 0, 0);
-    };
-#pragma unroll
-    for (int p = 0; p < NP; ++p) gl(p, 0);
-    wait_vmcnt<0>();
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb * NB + nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B_[nb], A_[mb], acc[mb * NB + nb], 0, 0, 0);
+  };
+
+  // stage 0 <- step 0 (in registers), registers <- step 1
+  auto start_tile = [&]() {
 #pragma unroll
     for (int p = 0; p < NP; ++p) sw(p, 0);
 #pragma unroll
     for (int p = 0; p < NP; ++p) gl(p, 1);
     wait_lgkm0();
     __syncthreads();
-    for (int kt = 0; kt < KT - 1; ++kt) {
-      const int cur = kt & 1;
-      read_frags(cur, 0, fa[0], fb[0]);
+  };
+  thread_setup();
+  coords(first + l);
+  descriptors();
 #pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        if (sub < 3) read_frags(cur, sub + 1, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
-        mma(fa[sub & 1], fb[sub & 1]);
+  for (int p = 0; p < NP; ++p) gl(p, 0);
+  start_tile();
+  for (;;) {
+    thread_setup();
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int p = 2 * sub + jj;
-          wait_vmcnt<NP - 1>();    // piece p of step kt+1 has landed (loaded one step ago)
-          sw(p, cur ^ 1);
-          gl(p, kt + 2);
+    for (int i = 0; i < NACC; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    if (KT > 0) {
+      for (int kt = 0; kt < KT - 1; ++kt) {
+        const int cur = kt & 1;
+        read_frags(cur, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+          if (sub < 3) read_frags(cur, sub + 1, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
+          mma(fa[sub & 1], fb[sub & 1]);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int p = 2 * sub + jj;
+            wait_vmcnt<NP - 1>();    // piece p of step kt+1 has landed (loaded one step ago)
+            sw(p, cur ^ 1);
+            gl(p, kt + 2);
+          }
+          if (sub < 3) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
-        if (sub < 3) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
       }
-      wait_lgkm0();
-      __builtin_amdgcn_s_barrier();
-    }
-    {
       const int cur = (KT - 1) & 1;
       read_frags(cur, 0, fa[0], fb[0]);
       read_frags(cur, 1, fa[1], fb[1]);
@@ -1434,18 +1474,46 @@ __global__ __launch_bounds__(512) void wgrad_kernel(int E, const int32_t* __rest
       mma(fa[0], fb[0]);
       mma(fa[1], fb[1]);
     }
-    wait_vmcnt<0>();   // the reload past the last step
+    wait_vmcnt<0>();   // the empty loads past the last step
+    thread_setup();    // (nothing derived from the thread index stays live through the K loop)
+    // the tile through LDS: row m < M1 of expert e goes to C0[e][m], m >= M1 to C1[e][m - M1]
+    __syncthreads();
+    lds_put_tile<MB, NB, WM, WN, BN>(smem, wm, wn, lane,
+                                     [&](int mb, int nb, int g, int i) { return acc[mb * NB + nb][4 * g + i]; });
+    // the next tile's first step is loaded while this tile is stored
+    const int e_c = e, m0_c = m0, n0_c = n0;
+    l += stride;
+    const bool more = l < run;
+    if (more) {
+      coords(first + l);
+      descriptors();
+#pragma unroll
+      for (int p = 0; p < NP; ++p) gl(p, 0);
+    }
+    __syncthreads();
+    // Every thread issues the same stores whatever the tile's shape (a piece
+    // of C0 and one of C1, each past its expert's record count where it does
+    // not belong), so the waits for the loads above do not have to cover them.
+    {
+      const auto rc0 = make_rsrc(C0 + (size_t)e_c * M1 * N, (uint32_t)((size_t)M1 * N * 2));
+      const auto rc1 = make_rsrc(M1 < M ? C1 + (size_t)e_c * (M - M1) * N : C0,
+                                 M1 < M ? (uint32_t)((size_t)(M - M1) * N * 2) : 0u);
+#pragma unroll
+      for (int i = 0; i < BM * BN / 8 / 512; ++i) {
+        const int cidx = tid + i * 512, row = cidx >> 5, ch = cidx & 31;
+        const u32x4 v = ld16(smem + row * 512 + ((ch ^ (row & 31)) << 4));
+        const int m = m0_c + row, col = n0_c + ch * 8;
+        const bool in = col < N;
+        // rows m >= M1 fall past C0's records, rows m < M1 or m >= M outside C1's
+        bstore16(rc0, in ? (uint32_t)(m * N + col) * 2u : 0x80000000u, v);
+        bstore16(rc1, in ? (uint32_t)((m - M1) * N + col) * 2u : 0x80000000u, v);
+      }
+    }
+    if (!more) break;
+    wait_lgkm0();
+    __syncthreads();   // every wavefront is done reading the tile out of LDS
+    start_tile();
   }
-  // the tile through LDS: row m < M1 of expert e goes to C0[e][m], m >= M1 to C1[e][m - M1]
-  __syncthreads();
-  lds_put_tile<MB, NB, WM, WN, BN>(smem, wm, wn, lane,
-                                   [&](int mb, int nb, int g, int i) { return acc[mb * NB + nb][4 * g + i]; });
-  __syncthreads();
-  lds_store_rows<BM, BN>(smem, tid, (N - n0) / 8, [&](int row) {
-    const int m = m0 + row;
-    if (m >= M) return static_cast<uint16_t*>(nullptr);
-    return (m < M1 ? C0 + ((size_t)e * M1 + m) * (size_t)N : C1 + ((size_t)e * (M - M1) + (m - M1)) * (size_t)N) + n0;
-  });
 }
 
 template <int BN, bool SWIGLU, int EPI = (SWIGLU ? EPI_SWIGLU : EPI_PLAIN), bool BT = false>
@@ -1630,14 +1698,21 @@ hipError_t launch_bwd_dx_perm(int64_t R_max, int d, int E, int F, const void* da
 
 hipError_t launch_wgrad(int E, const int32_t* offsets, int M, int M1, int N, int lda, int ldb, int64_t R,
                         const void* A, const void* B, void* C0, void* C1, hipStream_t s) {
-  // buffer offsets within one expert's rows must stay below 2^31
+  // buffer offsets within one expert's rows, and within one expert's
+  // gradient, must stay below 2^31
   if (R * (int64_t)(lda > ldb ? lda : ldb) * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if ((int64_t)M * N * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   constexpr size_t kLds = 2 * (size_t)(2 * 64 * 512);
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_kernel),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
+  // one resident block per compute unit of each XCD (at most one per tile)
   const int64_t tiles = (int64_t)E * ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
+  const int P = compute_units();
+  if (P < kXcds) return hipErrorInvalidValue;
+  const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
+  const int64_t grid = (per_xcd < P / kXcds ? per_xcd : P / kXcds) * kXcds;
+  if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)grid), dim3(512), kLds, s, E, offsets, M, M1, N, lda, ldb,
                      reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B),
                      reinterpret_cast<uint16_t*>(C0), reinterpret_cast<uint16_t*>(C1));

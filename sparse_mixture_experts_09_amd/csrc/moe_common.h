@@ -78,6 +78,11 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, AUX));
 }
 
+// A store at or past the record count is dropped.
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t voff, const u32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, 0, 0);
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Sum of V values over the 64 lanes of a wave, spread so that lane L ends up

@@ -94,6 +94,29 @@ def test_backward_empty_expert_has_zero_weight_gradients():
     assert torch.any(out["dw_gate"][3] != 0)
 
 
+def test_backward_empty_experts_between_tiles():
+    """Weight-gradient blocks stay resident and step through several tiles
+    each (64 experts x 4 x 4 tiles of 256 x 256): the odd experts get no rows
+    (W_g[e, 0] is -8 for them, 0 for the even ones, and every token's first
+    feature is large), so tiles of empty experts sit between full ones in every
+    block's sequence and must come out exactly zero."""
+    w, a = mi.random_small(2048, 1024, 64, 2, 512, 0.0, "bf16", 72)
+    a = dict(a)
+    x = a["x"].float() * 0.1
+    x[:, 0] = 4.0
+    wr = a["w_router"].float()
+    wr[:, 0] = torch.where(torch.arange(64) % 2 == 1, -8.0, 0.0)
+    a["x"], a["w_router"] = x.to(torch.bfloat16), wr.to(torch.bfloat16)
+    fw = orc.forward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], w.k, w.cf, "bf16")
+    assert all(fw["demand"][e] == 0 for e in range(1, 64, 2))
+    assert all(fw["demand"][e] > 0 for e in range(0, 64, 2))
+    g = {k_: dev(v) for k_, v in a.items() if v is not None}
+    out = run_and_check(w, a, g, make_dy(w, 72), "odd experts unused")
+    for e in range(1, 64, 2):
+        assert torch.all(out["dw_gate"][e] == 0) and torch.all(out["dw_up"][e] == 0)
+        assert torch.all(out["dw_down"][e] == 0)
+
+
 def test_backward_is_deterministic():
     case = BF16_CASES[0]
     w, _ = workload(case)
