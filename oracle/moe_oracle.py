@@ -489,7 +489,8 @@ def topk_softmax_grad(gates: np.ndarray, dg: np.ndarray) -> np.ndarray:
     return gates * (dg - (gates * dg).sum(axis=1, keepdims=True))
 
 
-def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: str) -> dict:
+def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: str,
+             weight_grad_experts=None) -> dict:
     """Gradients of L = <dy, y> for the token-choice layer with Softmax(TopK)
     gates and token-order capacity, with respect to x and every weight.
 
@@ -507,6 +508,10 @@ def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: 
       dW_down[e] = st(sum_r d_o[r]^T h[r])
       dW_g[e]  = st(sum over (t, j) with S_j = e of dl[t, j] x[t])
       dx[t]    = st(sum_j dl[t, j] W_g[S_j] + sum over kept j of dx_perm[slot (t, j)])
+
+    weight_grad_experts: None for the expert weight gradients of every expert;
+    otherwise a list of experts, and dW_gate, dW_up and dW_down hold only theirs,
+    in that order (the other results are the same either way).
     """
     x64 = as_f64(x)
     T, d = x64.shape
@@ -541,9 +546,10 @@ def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: 
     dg[tt, kk] = np.einsum("ij,ij->i", dy64[tt], o[slot_row[tt, kk]])
     dl = topk_softmax_grad(gates, dg)
     dx_perm = np.empty((R, d))
-    dW_gate = np.zeros((E, F, d))
-    dW_up = np.zeros((E, F, d))
-    dW_down = np.zeros((E, d, F))
+    wg_experts = list(range(E)) if weight_grad_experts is None else [int(e) for e in weight_grad_experts]
+    dW_gate = np.zeros((len(wg_experts), F, d))
+    dW_up = np.zeros((len(wg_experts), F, d))
+    dW_down = np.zeros((len(wg_experts), d, F))
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
@@ -553,10 +559,12 @@ def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: 
         da = store(dh * b_st[lo:hi] * silu_grad(a_st[lo:hi]), storage)
         db = store(dh * sa, storage)
         dx_perm[lo:hi] = store(da @ as_f64(w_gate[e]) + db @ as_f64(w_up[e]), storage)
-        xr = x64[tok[lo:hi]]
-        dW_gate[e] = da.T @ xr
-        dW_up[e] = db.T @ xr
-        dW_down[e] = d_o[lo:hi].T @ h[lo:hi]
+        if e in wg_experts:
+            i = wg_experts.index(e)
+            xr = x64[tok[lo:hi]]
+            dW_gate[i] = da.T @ xr
+            dW_up[i] = db.T @ xr
+            dW_down[i] = d_o[lo:hi].T @ h[lo:hi]
     dW_g = np.zeros((E, d))
     for j in range(k):
         np.add.at(dW_g, idx[:, j].astype(np.int64), dl[:, j][:, None] * x64)

@@ -11,7 +11,7 @@ import moe_inputs as mi
 import sparse_mixture_experts_09_amd as moe
 from oracle import moe_oracle as orc
 from parity import compare_routing, host
-from test_gpu_parity import SMALL, case_id, dev, device_inputs, workload
+from test_gpu_parity import SMALL, case_id, dev, device_inputs, full_reference, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -127,3 +127,44 @@ def test_backward_is_deterministic():
         again = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, w.k, w.cf)
         for key in first:
             assert torch.equal(first[key], again[key]), key
+
+
+@pytest.mark.parametrize("name", ["mixtral_bf16", "finegrained_bf16"])
+def test_full_size_backward(name):
+    """The dropless workloads at full size, in the configuration the benchmark
+    times, on what the oracle can afford: without capacity drops a token's
+    routing and rows depend on that token alone, so dx of sampled tokens comes
+    from the oracle's backward over those tokens, and the weight gradients of
+    one expert (the one with the fewest rows) from its backward over the tokens
+    routed to that expert (both identities are pinned on the CPU)."""
+    w, a = workload(name)
+    assert w.cf == 0.0
+    ref = full_reference(name)
+    g = device_inputs(name)
+    dy = make_dy(w, 90)
+    idx, gate, _ = moe.moe_route(g["x"], g["w_router"], w.k)
+    out = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dev(dy), w.k, w.cf)
+    torch.cuda.synchronize()
+    flips = compare_routing(host(idx), host(gate), ref)
+    same = (host(idx) == ref["topk_idx"]).all(axis=1)
+    dy64 = dy.double().numpy()
+    rng = np.random.default_rng(91)
+    toks = np.unique(np.concatenate([np.arange(8), np.arange(w.T - 8, w.T), rng.integers(0, w.T, 16)]))
+    toks = toks[same[toks]]
+    r = orc.backward(a["x"][toks], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy64[toks], w.k, w.cf,
+                     "bf16", weight_grad_experts=[])
+    rel_dx = check_grad("dx", host(out["dx"])[toks], r["dx"])
+    # an expert none of whose tokens flipped on a near tie
+    counts = np.bincount(ref["topk_idx"].reshape(-1), minlength=w.E)
+    for e in np.argsort(counts, kind="stable"):
+        te = np.nonzero((ref["topk_idx"] == e).any(axis=1) | (host(idx) == e).any(axis=1))[0]
+        if same[te].all():
+            break
+    else:
+        pytest.fail("every expert has a token routed differently")
+    r = orc.backward(a["x"][te], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy64[te], w.k, w.cf,
+                     "bf16", weight_grad_experts=[int(e)])
+    res = {key: check_grad(key, host(out[key][int(e)]), r[rk][0])
+           for key, rk in [("dw_gate", "dW_gate"), ("dw_up", "dW_up"), ("dw_down", "dW_down")]}
+    print(f"{name}: flips {flips}, {len(toks)} tokens dx rel {rel_dx[0]:.3g}; expert {int(e)} ({len(te)} tokens): "
+          + ", ".join(f"{k_} rel {v[0]:.3g}" for k_, v in res.items()))

@@ -632,6 +632,29 @@ def check_backward_storage_rounding():
         assert np.abs(v - g64[name]).max() <= 0.05 * scale, name
 
 
+def check_backward_expert_subset_and_sub_batch():
+    """Two identities the full-size GPU test relies on. (1) Asking for some
+    experts' weight gradients returns exactly theirs. (2) Without capacity
+    drops a token's routing and rows depend on that token alone, so the
+    backward over a sub-batch gives the same dx rows, and over the tokens routed
+    to expert e the same weight gradients of e, as over the whole batch."""
+    x, wr, wg, wu, wd = small_layer(T=40, E=4, k=2, dtype="bf16")
+    dy = torch.from_numpy(np.random.default_rng(6).standard_normal(x.shape)).to(torch.bfloat16).double().numpy()
+    full = orc.backward(x, wr, wg, wu, wd, dy, 2, 0.0, "bf16")
+    part = orc.backward(x, wr, wg, wu, wd, dy, 2, 0.0, "bf16", weight_grad_experts=[3, 1])
+    for name in ("dW_gate", "dW_up", "dW_down"):
+        assert np.array_equal(part[name], full[name][[3, 1]]), name
+    assert np.array_equal(part["dx"], full["dx"]) and np.array_equal(part["dW_g"], full["dW_g"])
+    toks = np.array([0, 7, 21, 39])
+    sub = orc.backward(x[toks], wr, wg, wu, wd, dy[toks], 2, 0.0, "bf16", weight_grad_experts=[])
+    assert np.array_equal(sub["dx"], full["dx"][toks])
+    idx = full["forward"]["topk_idx"]
+    te = np.nonzero((idx == 2).any(axis=1))[0]
+    sub = orc.backward(x[te], wr, wg, wu, wd, dy[te], 2, 0.0, "bf16", weight_grad_experts=[2])
+    for name in ("dW_gate", "dW_up", "dW_down"):
+        assert np.allclose(sub[name][0], full[name][2], rtol=0, atol=1e-12 * np.abs(full[name][2]).max()), name
+
+
 ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
             check_zero_router_closed_form, check_gate_invariants, check_k_equals_E_is_softmax,
             check_printed_gates, check_capacity_values, check_permutation_bruteforce,
@@ -641,7 +664,8 @@ ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
             check_bpr_reduces_to_token_order, check_bpr_float32_decision,
             check_bpr_forward_keeps_high_gates, check_ec_bruteforce, check_ec_selects_by_score_not_logit,
             check_ec_full_capacity_is_dense_gating, check_ec_zero_router, check_ec_float32_decision,
-            check_backward_finite_differences, check_backward_autograd, check_backward_storage_rounding]
+            check_backward_finite_differences, check_backward_autograd, check_backward_storage_rounding,
+            check_backward_expert_subset_and_sub_batch]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
