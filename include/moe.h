@@ -343,9 +343,13 @@ int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float 
  *   dx[t] = bf16(sum_j dl_j W_g[S_j] + sum over kept j of dx_perm[slot (t, j)])
  * All accumulation is fp32. Layouts: dx [T, d], dw_router [E, d],
  * dw_gate / dw_up [E, F, d], dw_down [E, d, F] (as the weights).
- * ws, ws_bytes: scratch of moe_backward_workspace_bytes (recomputed
- * activations, transposed weights and activations for the K-contiguous
- * gradient GEMMs, fp32 partial sums of the router gradient).
+ * ws, ws_bytes: scratch of moe_backward_workspace_bytes (routing and
+ * permutation maps, the recomputed x_perm, a, b, h and o, d_o, [da | db],
+ * dx_perm, fp32 partial sums of the router gradient and the down projection's
+ * split-tail partials); the GEMMs read weights and activations as stored.
+ * Limits (MOE_ERR_UNSUPPORTED beyond): R_max * max(2F, d) * 2 bytes and one
+ * expert's weight (d * F * 2 bytes) below 2^31, R_max the row bound of
+ * moe_rows_max.
  * ------------------------------------------------------------------------- */
 int moe_backward_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
                                  moe_dtype dt, size_t* bytes);

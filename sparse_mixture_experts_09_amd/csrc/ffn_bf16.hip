@@ -1504,9 +1504,8 @@ __global__ __launch_bounds__(512) void wgrad_kernel(int E, const int32_t* __rest
         const u32x4 v = ld16(smem + row * 512 + ((ch ^ (row & 31)) << 4));
         const int m = m0_c + row, col = n0_c + ch * 8;
         const bool in = col < N;
-        // rows m >= M1 fall past C0's records, rows m < M1 or m >= M outside C1's
-        bstore16(rc0, in ? (uint32_t)(m * N + col) * 2u : 0x80000000u, v);
-        bstore16(rc1, in ? (uint32_t)((m - M1) * N + col) * 2u : 0x80000000u, v);
+        bstore16(rc0, in && m < M1 ? (uint32_t)(m * N + col) * 2u : 0x80000000u, v);
+        bstore16(rc1, in && m >= M1 && m < M ? (uint32_t)((m - M1) * N + col) * 2u : 0x80000000u, v);
       }
     }
     if (!more) break;
@@ -1698,10 +1697,10 @@ hipError_t launch_bwd_dx_perm(int64_t R_max, int d, int E, int F, const void* da
 
 hipError_t launch_wgrad(int E, const int32_t* offsets, int M, int M1, int N, int lda, int ldb, int64_t R,
                         const void* A, const void* B, void* C0, void* C1, hipStream_t s) {
-  // buffer offsets within one expert's rows, and within one expert's
-  // gradient, must stay below 2^31
+  // buffer offsets within one expert's rows, and within one expert's C0 or
+  // C1 gradient, must stay below 2^31
   if (R * (int64_t)(lda > ldb ? lda : ldb) * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  if ((int64_t)M * N * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if ((int64_t)(M1 > M - M1 ? M1 : M - M1) * N * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   constexpr size_t kLds = 2 * (size_t)(2 * 64 * 512);
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&wgrad_kernel),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
