@@ -633,11 +633,12 @@ def check_backward_storage_rounding():
 
 
 def check_backward_expert_subset_and_sub_batch():
-    """Two identities the full-size GPU test relies on. (1) Asking for some
-    experts' weight gradients returns exactly theirs. (2) Without capacity
-    drops a token's routing and rows depend on that token alone, so the
-    backward over a sub-batch gives the same dx rows, and over the tokens routed
-    to expert e the same weight gradients of e, as over the whole batch."""
+    """The identities the full-size GPU test relies on. (1) Asking for some
+    experts' weight gradients returns exactly theirs. (2) A token's routing,
+    gates and rows depend on that token alone (only whether a slot is kept
+    depends on the tokens before it), so a drop-free backward over a sub-batch
+    gives the same dx for tokens that kept every slot, and one over the tokens
+    an expert kept gives that expert's weight gradients."""
     x, wr, wg, wu, wd = small_layer(T=40, E=4, k=2, dtype="bf16")
     dy = torch.from_numpy(np.random.default_rng(6).standard_normal(x.shape)).to(torch.bfloat16).double().numpy()
     full = orc.backward(x, wr, wg, wu, wd, dy, 2, 0.0, "bf16")
@@ -653,6 +654,22 @@ def check_backward_expert_subset_and_sub_batch():
     sub = orc.backward(x[te], wr, wg, wu, wd, dy[te], 2, 0.0, "bf16", weight_grad_experts=[2])
     for name in ("dW_gate", "dW_up", "dW_down"):
         assert np.allclose(sub[name][0], full[name][2], rtol=0, atol=1e-12 * np.abs(full[name][2]).max()), name
+    # With capacity drops: a token none of whose slots was dropped has the same
+    # dx as in a drop-free backward over it alone, and expert e's weight
+    # gradients are those of a drop-free backward over the tokens it kept.
+    cf = 0.6
+    full = orc.backward(x, wr, wg, wu, wd, dy, 2, cf, "bf16")
+    srow, idx = full["forward"]["slot_row"], full["forward"]["topk_idx"]
+    kept_all = np.nonzero((srow >= 0).all(axis=1))[0]
+    assert 0 < len(kept_all) < len(x)
+    sub = orc.backward(x[kept_all], wr, wg, wu, wd, dy[kept_all], 2, 0.0, "bf16", weight_grad_experts=[])
+    assert np.array_equal(sub["dx"], full["dx"][kept_all])
+    for e in range(4):
+        te = np.nonzero(((idx == e) & (srow >= 0)).any(axis=1))[0]
+        sub = orc.backward(x[te], wr, wg, wu, wd, dy[te], 2, 0.0, "bf16", weight_grad_experts=[e])
+        for name in ("dW_gate", "dW_up", "dW_down"):
+            scale = max(np.abs(full[name][e]).max(), 1e-300)
+            assert np.allclose(sub[name][0], full[name][e], rtol=0, atol=1e-12 * scale), (name, e)
 
 
 ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
