@@ -251,7 +251,7 @@ def main():
                     "alg_bytes_per_launch": alg["gate_up"]["bytes"], "avg_launch_us": st_ms["gate_up"] * 1e3}
     else:
         achieved = alg["gate_up"]["flops"] / gu_t / 1e12
-        roofline = {"bound": "mfma", "kernel": "ffn_bf16_w4_kernel<128,true> (grouped gate/up GEMM + SwiGLU epilogue)",
+        roofline = {"bound": "mfma", "kernel": "ffn_bf16_w4_kernel<128,true,false> (grouped gate/up GEMM + SwiGLU epilogue)",
                     "achieved": achieved, "peak": peak_mm, "unit": "TFLOP/s", "frac": achieved / peak_mm,
                     "traffic": load_traffic(w.name), "alg_flops_per_launch": alg["gate_up"]["flops"],
                     "avg_launch_us": st_ms["gate_up"] * 1e3}

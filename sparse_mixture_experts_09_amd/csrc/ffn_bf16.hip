@@ -19,10 +19,11 @@
 //   ffn_bf16_w4_kernel      256-row tiles, 4 wavefronts (1 per SIMD) of 128 x 128,
 //                           K step 64, register-staged loads into two LDS
 //                           stages, fragments read a substep ahead (the forward
-//                           main path);
+//                           main path, and the backward pass's dx_perm GEMM over
+//                           K-major weights);
 //   ffn_bf16_reg_kernel     the same tiles with 8 wavefronts (2 per SIMD) of
-//                           128 x 64 (the backward pass's recomputation and data
-//                           gradients, with their epilogues and K-major weights);
+//                           128 x 64 (the backward pass's recomputation and dh
+//                           GEMMs, whose epilogues move three or four tiles);
 //   ffn_bf16_kernel         128-row tiles, 4 wavefronts (experts average fewer
 //                           than 128 rows: big tiles would waste work on the
 //                           ragged last tile of each expert);
@@ -900,21 +901,22 @@ __global__ __launch_bounds__(512) void ffn_bf16_reg_kernel(
 // ffn_bf16_reg_kernel. Measured against that kernel on a dense 1024 x 65536
 // GEMM: +3% at K = 4096, +5% at K = 14336.
 // ---------------------------------------------------------------------------
-template <int BN, bool SWIGLU, int MT>
+template <int BN, bool SWIGLU, int MT, bool BT>
 __device__ __forceinline__ void w4_tile(const XcdItem& w, int KTall, int E, const int32_t* __restrict__ offsets,
                                         int N, int K, const uint16_t* __restrict__ A,
                                         const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1,
                                         uint16_t* __restrict__ C, int NT, int P, int max_split,
                                         float* __restrict__ partials, int ldc, const int32_t* __restrict__ a_slot,
-                                        int a_k, uint32_t a_records, char* smem) {
+                                        int a_k, uint32_t a_records, int ldb, int ksplit, char* smem) {
   constexpr int BM = 256, NT_ = 256;
   constexpr int BROWS = SWIGLU ? 2 * BN : BN;
   static_assert(BROWS == 256, "the weight tile has 256 rows");
+  static_assert(!BT || !SWIGLU, "K-major weights: plain tiles only");
   constexpr int NWM = MT == 256 ? 2 : 1, NWN = 4 / NWM;
   constexpr int WM = MT / NWM, WN = BN / NWN;
   constexpr int MB = WM / 32, NB = WN / 32;
   constexpr int NBF = (SWIGLU ? 2 : 1) * NB;
-  constexpr int NACC = MB * NBF, NM = NACC, NR = MB + NBF;
+  constexpr int NACC = MB * NBF, NM = NACC, NR = MB + (BT ? 2 : 1) * NBF;   // MFMAs, LDS reads a substep
   constexpr int RSTEP = NT_ / 8;                 // rows between a thread's pieces
   constexpr int PA = MT / RSTEP, PB = BROWS / RSTEP, NP = PA + PB;   // 16-byte pieces per thread per K step
   constexpr int STAGE = (BM + BROWS) * kRowB;
@@ -936,8 +938,15 @@ __device__ __forceinline__ void w4_tile(const XcdItem& w, int KTall, int E, cons
   const int a_rows = min(MT, tc.seg_rows - tc.m0);
   const int b_rows = min(BN, N - n0);
   const size_t wrow0 = (size_t)tc.e * N + n0;
-  const auto rb0 = make_rsrc(B0 + wrow0 * K, (uint32_t)(b_rows * rowb));
-  const auto rb1 = make_rsrc((SWIGLU ? B1 : B0) + wrow0 * K, (uint32_t)(b_rows * rowb));
+  // K-major weights (BT) as in ffn_bf16_reg_kernel: expert e's k-rows below
+  // ksplit from B0[e] [ksplit][ldb], the rest from B1[e]; staged as a
+  // [64 k][256 n] tile of 512-byte rows (chunk c of row r at c ^ ((r & 3) << 2)),
+  // piece i of a thread k-row (tid >> 5) + 8 i, chunk tid & 31
+  const auto rb0 = BT ? make_rsrc(B0 + (size_t)tc.e * ksplit * ldb + n0, (uint32_t)(((size_t)ksplit * ldb - n0) * 2))
+                      : make_rsrc(B0 + wrow0 * K, (uint32_t)(b_rows * rowb));
+  const auto rb1 = BT ? make_rsrc((K > ksplit ? B1 : B0) + (size_t)tc.e * (K - ksplit) * ldb + n0,
+                                  (uint32_t)(((size_t)(K - ksplit) * ldb - n0) * 2))
+                      : make_rsrc((SWIGLU ? B1 : B0) + wrow0 * K, (uint32_t)(b_rows * rowb));
   const int row0 = tid >> 3, ch = tid & 7;
   const uint32_t voff = (uint32_t)(row0 * rowb) + ch * 16 + (uint32_t)kb * kRowB;
   const uint32_t rstep = (uint32_t)(RSTEP * rowb);
@@ -961,11 +970,19 @@ __device__ __forceinline__ void w4_tile(const XcdItem& w, int KTall, int E, cons
 
   // piece p < PA: token row row0 + p*RSTEP; p >= PA: weight row row0 + (p-PA)*RSTEP
   // (SwiGLU tiles: BN gate rows, then BN up rows)
+  const int bk0 = tid >> 5, bch = tid & 31;
+  const uint32_t bt_off = (uint32_t)(bk0 * ldb + bch * 8) * 2u;
+  const int bt_wofs = BM * kRowB + bk0 * 512 + ((bch ^ ((bk0 & 3) << 2)) << 4);   // rows bk0 + 8 i: same swizzle
   u32x4 stg[NP];
   auto gl = [&](int p, int kt) {
     const uint32_t ko = (uint32_t)(kt < KT ? kt : KT - 1) * kRowB;
     if (p < PA) {
       stg[p] = bload16(ra, aoff[p] + ko);
+    } else if constexpr (BT) {
+      const int k = ((kt < KT ? kt : KT - 1) + kb) * kBK;   // first k-row of the step (whole in B0 or in B1)
+      const int i = p - PA;
+      stg[p] = k < ksplit ? bload16(rb0, bt_off + (uint32_t)((k + 8 * i) * ldb) * 2u)
+                          : bload16(rb1, bt_off + (uint32_t)((k - ksplit + 8 * i) * ldb) * 2u);
     } else {
       const int i = p - PA;
       const bool up = SWIGLU && i * RSTEP >= BN;
@@ -973,8 +990,11 @@ __device__ __forceinline__ void w4_tile(const XcdItem& w, int KTall, int E, cons
     }
   };
   auto sw = [&](int p, int stage) {
-    char* b = smem + stage * STAGE + wofs;
-    st16(p < PA ? b + p * RSTEP * kRowB : b + BM * kRowB + (p - PA) * RSTEP * kRowB, stg[p]);
+    char* b = smem + stage * STAGE;
+    if (BT && p >= PA)
+      st16(b + bt_wofs + (p - PA) * 8 * 512, stg[p]);
+    else
+      st16(p < PA ? b + wofs + p * RSTEP * kRowB : b + wofs + BM * kRowB + (p - PA) * RSTEP * kRowB, stg[p]);
   };
 
   f32x16 acc[NACC];
@@ -991,9 +1011,20 @@ __device__ __forceinline__ void w4_tile(const XcdItem& w, int KTall, int E, cons
       A_[mb] = __builtin_bit_cast(bf16x8, ld16(buf + daddr(wm * WM + mb * 32 + (lane & 31), chunk)));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int row = wn * WN + nb * 32 + (lane & 31);
-      B_[nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(row, chunk)));
-      if (SWIGLU) B_[NB + nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(BN + row, chunk)));
+      if constexpr (BT) {   // transposing reads, as in ffn_bf16_reg_kernel
+        const int tq = lane >> 4, ts = lane & 15;
+        const int k = 16 * sub + 8 * (tq >> 1) + (ts >> 2);
+        const int n = wn * WN + nb * 32 + 16 * (tq & 1) + 4 * (ts & 3);
+        const char* at = buf + BM * kRowB + k * 512 + (((n >> 3) ^ ((k & 3) << 2)) << 4) + (n & 4) * 2;
+        const uint2 lo = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)at));
+        const uint2 hi = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(at + 4 * 512)));
+        const u32x4 v = {lo.x, lo.y, hi.x, hi.y};
+        B_[nb] = __builtin_bit_cast(bf16x8, v);
+      } else {
+        const int row = wn * WN + nb * 32 + (lane & 31);
+        B_[nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(row, chunk)));
+        if (SWIGLU) B_[NB + nb] = __builtin_bit_cast(bf16x8, ld16(buf + BM * kRowB + daddr(BN + row, chunk)));
+      }
     }
   };
   // MFMAs [i0, i1) of a substep
@@ -1094,12 +1125,12 @@ __device__ __forceinline__ void w4_tile(const XcdItem& w, int KTall, int E, cons
   }
 }
 
-template <int BN, bool SWIGLU>
+template <int BN, bool SWIGLU, bool BT>
 __global__ __launch_bounds__(256) void ffn_bf16_w4_kernel(
     int E, const int32_t* __restrict__ offsets, int N, int K, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int NT, int P,
     int max_split, float* __restrict__ partials, int ldc, const int32_t* __restrict__ a_slot, int a_k,
-    uint32_t a_records) {
+    uint32_t a_records, int ldb, int ksplit) {
   extern __shared__ __align__(16) char smem[];
   int* ws = reinterpret_cast<int*>(smem);   // plan words; the stages are free between tiles
   const int KTall = K / kBK, xcd = blockIdx.x % kXcds, Px = P / kXcds;
@@ -1115,14 +1146,14 @@ __global__ __launch_bounds__(256) void ffn_bf16_w4_kernel(
     __syncthreads();   // every thread has its tile before the stages are written
     const int rows = w.tc.seg_rows - w.tc.m0;   // the tile's token rows (at most 256 are used)
     if (rows <= 64)
-      w4_tile<BN, SWIGLU, 64>(w, KTall, E, offsets, N, K, A, B0, B1, C, NT, P, max_split, partials, ldc, a_slot,
-                              a_k, a_records, smem);
+      w4_tile<BN, SWIGLU, 64, BT>(w, KTall, E, offsets, N, K, A, B0, B1, C, NT, P, max_split, partials, ldc, a_slot,
+                              a_k, a_records, ldb, ksplit, smem);
     else if (rows <= 128)
-      w4_tile<BN, SWIGLU, 128>(w, KTall, E, offsets, N, K, A, B0, B1, C, NT, P, max_split, partials, ldc, a_slot,
-                               a_k, a_records, smem);
+      w4_tile<BN, SWIGLU, 128, BT>(w, KTall, E, offsets, N, K, A, B0, B1, C, NT, P, max_split, partials, ldc, a_slot,
+                               a_k, a_records, ldb, ksplit, smem);
     else
-      w4_tile<BN, SWIGLU, 256>(w, KTall, E, offsets, N, K, A, B0, B1, C, NT, P, max_split, partials, ldc, a_slot,
-                               a_k, a_records, smem);
+      w4_tile<BN, SWIGLU, 256, BT>(w, KTall, E, offsets, N, K, A, B0, B1, C, NT, P, max_split, partials, ldc, a_slot,
+                               a_k, a_records, ldb, ksplit, smem);
   }
 }
 
@@ -1543,13 +1574,14 @@ hipError_t launch_reg(int64_t R_max, int E, const int32_t* offsets, int N, int K
   return hipGetLastError();
 }
 
-template <int BN, bool SWIGLU>
+template <int BN, bool SWIGLU, bool BT = false>
 hipError_t launch_w4(int64_t R_max, int E, const int32_t* offsets, int N, int K, const void* A, const void* B0,
                      const void* B1, void* C, float* partials, int P, hipStream_t s,
-                     const int32_t* a_slot = nullptr, int a_k = 1, uint32_t a_records = 0) {
+                     const int32_t* a_slot = nullptr, int a_k = 1, uint32_t a_records = 0, int ldb = 0,
+                     int ksplit = 0) {
   constexpr int BM = 256;
   constexpr size_t kLds = 2 * (size_t)(BM + 256) * kRowB;
-  auto kern = &ffn_bf16_w4_kernel<BN, SWIGLU>;
+  auto kern = &ffn_bf16_w4_kernel<BN, SWIGLU, BT>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
@@ -1560,7 +1592,7 @@ hipError_t launch_w4(int64_t R_max, int E, const int32_t* offsets, int N, int K,
   hipLaunchKernelGGL(kern, dim3((unsigned)xcd_grid_blocks(tiles_ub, P, split)), dim3(256), kLds, s, E,
                      offsets, N, K, reinterpret_cast<const uint16_t*>(A), reinterpret_cast<const uint16_t*>(B0),
                      reinterpret_cast<const uint16_t*>(B1), reinterpret_cast<uint16_t*>(C), NT, P, max_split,
-                     partials, N, a_slot, a_k, a_records);
+                     partials, N, a_slot, a_k, a_records, ldb, ksplit);
   if (split)
     hipLaunchKernelGGL(split_reduce_xcd_kernel, dim3((unsigned)(P / kXcds * kXcds * (BM / 16))), dim3(256), 0, s, E,
                        offsets, N, K, NT, P, max_split, partials, reinterpret_cast<uint16_t*>(C));
@@ -1690,9 +1722,8 @@ hipError_t launch_bwd_dx_perm(int64_t R_max, int d, int E, int F, const void* da
   if ((int64_t)d * F * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   // dx_perm = [da, db] . [W_gate[e]; W_up[e]] (contraction over 2F): K-major
   // weight rows 0..F-1 from W_gate[e] [F][d], F..2F-1 from W_up[e]
-  return launch_reg<256, false, EPI_PLAIN, true>(R_max, E, offsets, d, 2 * F, dab, w_gate, w_up, dx_perm,
-                                                 reinterpret_cast<float*>(ws), ws ? compute_units() : 0, s, 0,
-                                                 nullptr, nullptr, nullptr, nullptr, 0, nullptr, 1, 0, d, F);
+  return launch_w4<256, false, true>(R_max, E, offsets, d, 2 * F, dab, w_gate, w_up, dx_perm,
+                                     reinterpret_cast<float*>(ws), ws ? compute_units() : 0, s, nullptr, 1, 0, d, F);
 }
 
 hipError_t launch_wgrad(int E, const int32_t* offsets, int M, int M1, int N, int lda, int ldb, int64_t R,
