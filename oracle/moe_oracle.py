@@ -392,16 +392,28 @@ def expert_choice_forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, 
         h, o = swiglu_expert(as_f64(x[tok[e]]), w_gate[e], w_up[e], w_down[e], storage)
         o_rows[e * C:(e + 1) * C] = o
         h_rows[e * C:(e + 1) * C] = h
+    y = expert_choice_combine(o_rows, slot, S, storage, tokens)
+    return dict(logits=logits, scores=S, cap=C, tokens=tok, slot=slot, y=y,
+                o_rows=o_rows, h_rows=h_rows, boundary_tie=expert_choice_boundary_ties(S, C))
+
+
+def expert_choice_combine(o_rows: np.ndarray, slot: np.ndarray, scores: np.ndarray, storage: str,
+                          tokens=None) -> np.ndarray:
+    """y[t] = store(sum over the experts e that chose t, ascending, of
+    score[t, e] * o[slot[t, e]]). The gate is the dense score itself: it is
+    not renormalised over the experts that happened to choose t ([TALK]: a
+    token may get anywhere from zero to all experts), and a token no expert
+    chose gets 0."""
+    T, E = slot.shape
     if tokens is None:
         tokens = np.arange(T)
     tokens = np.asarray(tokens, dtype=np.int64)
-    y = np.zeros((len(tokens), d))
+    y = np.zeros((len(tokens), o_rows.shape[1]))
     for e in range(E):
         r = slot[tokens, e]
         m = r >= 0
-        y[m] += S[tokens[m], e][:, None] * o_rows[r[m]]
-    return dict(logits=logits, scores=S, cap=C, tokens=tok, slot=slot, y=store(y, storage),
-                o_rows=o_rows, h_rows=h_rows, boundary_tie=expert_choice_boundary_ties(S, C))
+        y[m] += scores[tokens[m], e][:, None] * o_rows[r[m]]
+    return store(y, storage)
 
 
 # ---------------------------------------------------------------------------
@@ -489,6 +501,18 @@ def topk_softmax_grad(gates: np.ndarray, dg: np.ndarray) -> np.ndarray:
     return gates * (dg - (gates * dg).sum(axis=1, keepdims=True))
 
 
+BACKWARD_ROUNDING_POINTS = ("a", "b", "d_o", "da", "db", "dx_perm")
+
+
+def hold(v: np.ndarray, storage: str, point: str) -> np.ndarray:
+    """An intermediate of the backward pass as the layer holds it between its
+    steps: written in the storage type like every stored activation. `point`
+    names the rounding point (one of BACKWARD_ROUNDING_POINTS); it changes
+    nothing here and lets a self-check drop one point at a time."""
+    assert point in BACKWARD_ROUNDING_POINTS, point
+    return store(v, storage)
+
+
 def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: str,
              weight_grad_experts=None) -> dict:
     """Gradients of L = <dy, y> for the token-choice layer with Softmax(TopK)
@@ -535,17 +559,19 @@ def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: 
         xr = x64[tok[lo:hi]]
         a = xr @ as_f64(w_gate[e]).T
         b = xr @ as_f64(w_up[e]).T
-        a_st[lo:hi] = store(a, storage)
-        b_st[lo:hi] = store(b, storage)
+        a_st[lo:hi] = hold(a, storage, "a")
+        b_st[lo:hi] = hold(b, storage, "b")
         h[lo:hi] = store(silu(a) * b, storage)
         o[lo:hi] = store(h[lo:hi] @ as_f64(w_down[e]).T, storage)
-    d_o = store(gates[tok, jj][:, None] * dy64[tok], storage)
+    d_o = hold(gates[tok, jj][:, None] * dy64[tok], storage, "d_o")
     dg = np.zeros((T, k))
     kept = slot_row >= 0
     tt, kk = np.nonzero(kept)
     dg[tt, kk] = np.einsum("ij,ij->i", dy64[tt], o[slot_row[tt, kk]])
     dl = topk_softmax_grad(gates, dg)
     dx_perm = np.empty((R, d))
+    da_rows = np.empty((R, F))
+    db_rows = np.empty((R, F))
     wg_experts = list(range(E)) if weight_grad_experts is None else [int(e) for e in weight_grad_experts]
     dW_gate = np.zeros((len(wg_experts), F, d))
     dW_up = np.zeros((len(wg_experts), F, d))
@@ -556,9 +582,11 @@ def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: 
             continue
         dh = d_o[lo:hi] @ as_f64(w_down[e])
         sa = silu(a_st[lo:hi])
-        da = store(dh * b_st[lo:hi] * silu_grad(a_st[lo:hi]), storage)
-        db = store(dh * sa, storage)
-        dx_perm[lo:hi] = store(da @ as_f64(w_gate[e]) + db @ as_f64(w_up[e]), storage)
+        da = hold(dh * b_st[lo:hi] * silu_grad(a_st[lo:hi]), storage, "da")
+        db = hold(dh * sa, storage, "db")
+        da_rows[lo:hi] = da
+        db_rows[lo:hi] = db
+        dx_perm[lo:hi] = hold(da @ as_f64(w_gate[e]) + db @ as_f64(w_up[e]), storage, "dx_perm")
         if e in wg_experts:
             i = wg_experts.index(e)
             xr = x64[tok[lo:hi]]
@@ -574,4 +602,4 @@ def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: 
         dx[m] += dx_perm[slot_row[m, j]]
     return dict(forward=r, dx=store(dx, storage), dW_g=store(dW_g, storage), dW_gate=store(dW_gate, storage),
                 dW_up=store(dW_up, storage), dW_down=store(dW_down, storage), dl=dl, dg=dg, d_o=d_o,
-                a_st=a_st, b_st=b_st, dx_perm=dx_perm)
+                a_st=a_st, b_st=b_st, h=h, o=o, da=da_rows, db=db_rows, dx_perm=dx_perm)

@@ -546,6 +546,37 @@ def check_ec_zero_router():
     assert np.all(r["y"][C:] == 0.0)
 
 
+def check_ec_partial_capacity_dense_eval():
+    """C < T: experts take different numbers of each token, so tokens get
+    zero, one or several experts ([TALK] expert-choice Q&A). The layer must be
+    y[t] = sum over the experts e that chose t of Softmax(x.W_g)[t, e] *
+    FFN_e(x_t): the dense score, not renormalised over the choosing experts.
+    The selection here is a brute-force column sort (float32 scores, lower
+    token first) and the experts run densely in torch (library softmax, silu)."""
+    for (T, E, k, cf, seed) in [(30, 5, 2, 0.5, 11), (24, 4, 1, 1.0, 12), (40, 6, 3, 0.3, 13)]:
+        x, wr, wg, wu, wd = small_layer(T=T, E=E, seed=seed)
+        wr = wr * 3.0                      # sharper scores: choosers differ a lot between tokens
+        r = orc.expert_choice_forward(x, wr, wg, wu, wd, k, cf, "f64")
+        C = r["cap"]
+        assert C == math.ceil(float(np.float32(cf)) * T * k / E) < T
+        xt = torch.from_numpy(x)
+        S = torch.softmax(xt @ torch.from_numpy(wr).T, dim=1)
+        s32 = S.to(torch.float32).tolist()
+        chosen = np.zeros((T, E), dtype=bool)
+        for e in range(E):
+            best = sorted(range(T), key=lambda t: (-s32[t][e], t))[:C]
+            chosen[best, e] = True
+        per_token = chosen.sum(axis=1)
+        assert (per_token == 0).any() and (per_token == 1).any() and (per_token >= 2).any(), per_token
+        y = torch.zeros_like(xt)
+        for e in range(E):
+            h = torch.nn.functional.silu(xt @ torch.from_numpy(wg[e]).T) * (xt @ torch.from_numpy(wu[e]).T)
+            w = S[:, e:e + 1] * torch.from_numpy(chosen[:, e:e + 1].astype(np.float64))
+            y += w * (h @ torch.from_numpy(wd[e]).T)
+        assert np.allclose(r["y"], y.numpy(), rtol=1e-12, atol=1e-13)
+        assert np.all(r["y"][per_token == 0] == 0.0)
+
+
 def check_ec_float32_decision():
     """Scores equal in float32 tie (lower token wins) even if float64 differs."""
     S = np.array([[0.5, 0.5], [0.5 + 1e-12, 0.5 - 1e-12], [0.25, 0.75]])
@@ -632,6 +663,124 @@ def check_backward_storage_rounding():
         assert np.abs(v - g64[name]).max() <= 0.05 * scale, name
 
 
+def bf16_ordinal(v):
+    """Signed position of each bf16 value on the bf16 number line (0 for both
+    zeros), so that adjacent bf16 values differ by 1."""
+    b = (np.asarray(v, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def assert_bf16_close(mine, ref, what, min_equal=0.99):
+    """Both sides hold bf16 values; they differ by at most one bf16 step, and
+    at least `min_equal` of them are identical (the two sides round the same
+    float64 values, which differ only by float64 summation order)."""
+    mine = np.asarray(mine, np.float64)
+    ref = np.asarray(ref, np.float64)
+    as_bf16 = lambda a: torch.from_numpy(a).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(as_bf16(mine), mine), f"{what}: oracle value is not a bf16 value"
+    assert np.array_equal(as_bf16(ref), ref), f"{what}: reference value is not a bf16 value"
+    steps = np.abs(bf16_ordinal(mine) - bf16_ordinal(ref))
+    assert steps.max(initial=0) <= 1, f"{what}: {int(steps.max())} bf16 steps apart"
+    eq = float((steps == 0).mean()) if steps.size else 1.0
+    assert eq >= min_equal, f"{what}: only {eq:.4f} identical"
+
+
+def torch_backward_bf16(x, wr, wg, wu, wd, dy, k, cf):
+    """The backward pass of a bf16 layer, evaluated slot by slot in torch
+    float64, rounding to bf16 (torch's float32 -> bfloat16 conversion) at the
+    points where the layer holds a value in its storage type: a and b as the
+    SwiGLU backward reads them, h and o (recomputed as the forward stores
+    them), d_o = g*dy, da, db, dx_perm, and each returned gradient. The
+    derivatives of silu and of the softmax over the chosen logits come from
+    torch autograd, the routing from a stable torch sort and counting ranks."""
+    bf = lambda v: v.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    X, WR, WG, WU, WD, DY = (torch.from_numpy(np.asarray(a, np.float64)) for a in (x, wr, wg, wu, wd, dy))
+    T, d = X.shape
+    E, F = WG.shape[0], WG.shape[1]
+    l = X @ WR.T
+    idx = torch.sort(l.to(torch.float32), dim=1, descending=True, stable=True).indices[:, :k]
+    lS = torch.gather(l, 1, idx).detach().requires_grad_(True)
+    g = torch.softmax(lS, dim=1)
+    cap = T if np.float32(cf) == 0 else min(T, math.ceil(float(np.float32(cf)) * T * k / E))
+    onehot = torch.zeros((T, E), dtype=torch.int64)
+    onehot.scatter_(1, idx, 1)
+    before = torch.cumsum(onehot, 0) - onehot
+    rank = torch.gather(before, 1, idx)
+    kept = rank < cap
+    gd = g.detach()
+    out = {n: {} for n in ("a", "b", "h", "o", "d_o", "da", "db", "dx_perm")}
+    dg = torch.zeros((T, k), dtype=torch.float64)
+    dWgate = torch.zeros_like(WG)
+    dWup = torch.zeros_like(WU)
+    dWdown = torch.zeros_like(WD)
+    dx = torch.zeros_like(X)
+    for t in range(T):
+        for j in range(k):
+            if not bool(kept[t, j]):
+                continue
+            e = int(idx[t, j])
+            a = WG[e] @ X[t]
+            b = WU[e] @ X[t]
+            h = bf(torch.nn.functional.silu(a) * b)
+            o = bf(WD[e] @ h)
+            d_o = bf(gd[t, j] * DY[t])
+            dg[t, j] = torch.dot(DY[t], o)
+            dh = WD[e].T @ d_o
+            a_st, b_st = bf(a), bf(b)
+            a_req = a_st.clone().requires_grad_(True)
+            s = torch.nn.functional.silu(a_req)
+            s.sum().backward()
+            da = bf(dh * b_st * a_req.grad)
+            db = bf(dh * s.detach())
+            dxp = bf(WG[e].T @ da + WU[e].T @ db)
+            dWgate[e] += torch.outer(da, X[t])
+            dWup[e] += torch.outer(db, X[t])
+            dWdown[e] += torch.outer(d_o, h)
+            dx[t] += dxp
+            for n, v in (("a", a_st), ("b", b_st), ("h", h), ("o", o), ("d_o", d_o), ("da", da), ("db", db),
+                         ("dx_perm", dxp)):
+                out[n][(t, j)] = v.numpy()
+    g.backward(dg)
+    dl = lS.grad
+    dWg = torch.zeros_like(WR)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            dWg[e] += dl[t, j] * X[t]
+            dx[t] += dl[t, j] * WR[e]
+    res = dict(dx=bf(dx).numpy(), dW_g=bf(dWg).numpy(), dW_gate=bf(dWgate).numpy(), dW_up=bf(dWup).numpy(),
+               dW_down=bf(dWdown).numpy(), dl=dl.numpy(), idx=idx.numpy(), kept=kept.numpy())
+    res.update(out)
+    return res
+
+
+def check_backward_rounding_points_bf16():
+    """The bf16 backward's rounding points, pinned by an independent slot-by-slot
+    torch evaluation (torch_backward_bf16): every intermediate the oracle holds
+    (a, b, h, o, d_o, da, db, dx_perm) and every returned gradient are bf16
+    values within one bf16 step of torch's, and almost all identical. With a
+    rounding point left out, the intermediate is no bf16 value, or the
+    gradients drift by more than rounding-order noise."""
+    for (T, E, k, cf, seed) in [(24, 4, 2, 0.75, 21), (16, 3, 1, 0.0, 22), (20, 5, 3, 1.0, 23)]:
+        x, wr, wg, wu, wd = small_layer(T=T, E=E, k=k, seed=seed, dtype="bf16")
+        dy = torch.from_numpy(np.random.default_rng(seed).standard_normal(x.shape)).to(torch.bfloat16).double().numpy()
+        g = orc.backward(x, wr, wg, wu, wd, dy, k, cf, "bf16")
+        ref = torch_backward_bf16(x, wr, wg, wu, wd, dy, k, cf)
+        fw = g["forward"]
+        assert np.array_equal(fw["topk_idx"], ref["idx"])
+        assert np.array_equal(fw["slot_row"] >= 0, ref["kept"])
+        if cf > 0 and k > 1:
+            assert (~ref["kept"]).any()          # the case has drops
+        slots = sorted(ref["a"])
+        rows = np.array([fw["slot_row"][t, j] for (t, j) in slots])
+        for name in ("a", "b", "h", "o", "d_o", "da", "db", "dx_perm"):
+            mine = {"a": g["a_st"], "b": g["b_st"]}.get(name, g.get(name))
+            assert_bf16_close(mine[rows], np.stack([ref[name][s] for s in slots]), name)
+        assert np.allclose(g["dl"], ref["dl"], rtol=1e-9, atol=1e-12)
+        for name in ("dx", "dW_g", "dW_gate", "dW_up", "dW_down"):
+            assert_bf16_close(g[name], ref[name], name)
+
+
 def check_backward_expert_subset_and_sub_batch():
     """The identities the full-size GPU test relies on. (1) Asking for some
     experts' weight gradients returns exactly theirs. (2) A token's routing,
@@ -681,7 +830,9 @@ ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
             check_bpr_reduces_to_token_order, check_bpr_float32_decision,
             check_bpr_forward_keeps_high_gates, check_ec_bruteforce, check_ec_selects_by_score_not_logit,
             check_ec_full_capacity_is_dense_gating, check_ec_zero_router, check_ec_float32_decision,
+            check_ec_partial_capacity_dense_eval,
             check_backward_finite_differences, check_backward_autograd, check_backward_storage_rounding,
+            check_backward_rounding_points_bf16,
             check_backward_expert_subset_and_sub_batch]
 
 
@@ -784,6 +935,30 @@ MUTANTS["softmax_grad_without_the_mean"] = ("topk_softmax_grad", lambda gates, d
                                             [check_backward_autograd])
 MUTANTS["bpr_score_as_float64"] = ("priority_order", lambda score: np.argsort(
     -np.asarray(score, np.float64), kind="stable"), [check_bpr_float32_decision])
+
+
+def _ec_combine_renormalised(o_rows, slot, scores, storage, tokens=None, _o=orc.expert_choice_combine):
+    """Gates renormalised over the experts that chose the token."""
+    chosen = slot >= 0
+    mass = np.where(chosen, scores, 0.0).sum(axis=1, keepdims=True)
+    s = np.where(chosen, scores / np.where(mass > 0, mass, 1.0), 0.0)
+    return _o(o_rows, slot, s, storage, tokens)
+
+
+MUTANTS["ec_combine_renormalised"] = ("expert_choice_combine", _ec_combine_renormalised,
+                                      [check_ec_partial_capacity_dense_eval])
+
+
+def _hold_skipping(skip):
+    def hold(v, storage, point, _o=orc.hold):
+        return np.asarray(v, np.float64) if point in skip else _o(v, storage, point)
+    return hold
+
+
+MUTANTS["backward_no_intermediate_rounding"] = ("hold", _hold_skipping(set(orc.BACKWARD_ROUNDING_POINTS)),
+                                                [check_backward_rounding_points_bf16])
+for _p in orc.BACKWARD_ROUNDING_POINTS:
+    MUTANTS[f"backward_{_p}_unrounded"] = ("hold", _hold_skipping({_p}), [check_backward_rounding_points_bf16])
 
 
 def _ec_reversed(S, C, orig):
