@@ -127,6 +127,22 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+def _new(stream, shape, dtype, device):
+    """A buffer the wrapper allocates for a call enqueued on `stream`. torch's
+    caching allocator ties a block to the stream current at allocation and may
+    hand it out again as soon as the tensor is dropped; when the kernels run
+    on another stream the block is recorded on that one too, so it is not
+    reused before they have finished with it."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None:
+        t.record_stream(stream)
+    return t
+
+
+def _new_like(stream, ref):
+    return _new(stream, ref.shape, ref.dtype, ref.device)
+
+
 def moe_capacity(T: int, E: int, k: int, cf: float) -> int:
     return int(lib().moe_capacity(T, E, k, cf))
 
@@ -164,10 +180,10 @@ def moe_ffn_workspace_bytes(T: int, d: int, E: int, k: int, cf: float, F: int, d
     return int(b.value)
 
 
-def _ffn_ws(ws, T, d, E, k, cf, F, dtype, device):
+def _ffn_ws(ws, T, d, E, k, cf, F, dtype, device, stream):
     if ws is None:
         n = moe_ffn_workspace_bytes(T, d, E, k, cf, F, dtype)
-        ws = torch.empty(n, dtype=torch.uint8, device=device) if n else None
+        ws = _new(stream, n, torch.uint8, device) if n else None
     return ws
 
 
@@ -180,11 +196,11 @@ def moe_route(x, w_router, k: int, topk_idx=None, topk_gate=None, logits=None, w
     E = w_router.shape[0]
     dev = x.device
     if topk_idx is None:
-        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        topk_idx = _new(stream, (T, k), torch.int32, dev)
     if topk_gate is None:
-        topk_gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+        topk_gate = _new(stream, (T, k), torch.float32, dev)
     if logits is None and want_logits:
-        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        logits = _new(stream, (T, E), torch.float32, dev)
     if gating == "topk_softmax":
         st = lib().moe_route(T, d, E, k, _dt(x), _ptr(x), _ptr(w_router), _ptr(topk_idx), _ptr(topk_gate),
                              _ptr(logits), _stream(stream))
@@ -209,7 +225,7 @@ def moe_permute(x, topk_idx, E: int, cf: float, stream=None, out=None, score=Non
 
     def get(name, shape, dtype):
         t = o.get(name)
-        return t if t is not None else torch.empty(shape, dtype=dtype, device=dev)
+        return t if t is not None else _new(stream, shape, dtype, dev)
 
     counts = get("expert_counts", E, torch.int32)
     offsets = get("expert_offsets", E + 1, torch.int32)
@@ -242,10 +258,10 @@ def moe_grouped_ffn(x_perm, expert_offsets, w_gate, w_up, w_down, T: int, k: int
     R_max = moe_rows_max(T, E, k, cf)
     dev = x_perm.device
     if h is None:
-        h = torch.empty((max(R_max, 1), F), dtype=x_perm.dtype, device=dev)
+        h = _new(stream, (max(R_max, 1), F), x_perm.dtype, dev)
     if out_perm is None:
-        out_perm = torch.empty((max(R_max, 1), d), dtype=x_perm.dtype, device=dev)
-    ws = None if ws is False else _ffn_ws(ws, T, d, E, k, cf, F, x_perm.dtype, dev)
+        out_perm = _new(stream, (max(R_max, 1), d), x_perm.dtype, dev)
+    ws = None if ws is False else _ffn_ws(ws, T, d, E, k, cf, F, x_perm.dtype, dev, stream)
     st = lib().moe_grouped_ffn(T, d, E, k, cf, F, _dt(x_perm), _ptr(x_perm), _ptr(expert_offsets),
                                _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(out_perm), _ptr(ws),
                                ws.numel() if ws is not None else 0, _stream(stream))
@@ -258,7 +274,7 @@ def moe_expert_gate_up(x_perm, expert_offsets, w_gate, w_up, T: int, k: int, cf:
     """First grouped GEMM with the SwiGLU epilogue. Returns h [R_max, F]."""
     E, F, d = w_gate.shape
     if h is None:
-        h = torch.empty((max(moe_rows_max(T, E, k, cf), 1), F), dtype=x_perm.dtype, device=x_perm.device)
+        h = _new(stream, (max(moe_rows_max(T, E, k, cf), 1), F), x_perm.dtype, x_perm.device)
     st = lib().moe_expert_gate_up(T, d, E, k, cf, F, _dt(x_perm), _ptr(x_perm), _ptr(expert_offsets),
                                   _ptr(w_gate), _ptr(w_up), _ptr(h), _stream(stream))
     _check("moe_expert_gate_up", st)
@@ -271,8 +287,8 @@ def moe_expert_down(h, expert_offsets, w_down, T: int, k: int, cf: float, out_pe
     (allocated when None; pass False to run without the split tail)."""
     E, d, F = w_down.shape
     if out_perm is None:
-        out_perm = torch.empty((max(moe_rows_max(T, E, k, cf), 1), d), dtype=h.dtype, device=h.device)
-    ws = None if ws is False else _ffn_ws(ws, T, d, E, k, cf, F, h.dtype, h.device)
+        out_perm = _new(stream, (max(moe_rows_max(T, E, k, cf), 1), d), h.dtype, h.device)
+    ws = None if ws is False else _ffn_ws(ws, T, d, E, k, cf, F, h.dtype, h.device, stream)
     st = lib().moe_expert_down(T, d, E, k, cf, F, _dt(h), _ptr(h), _ptr(expert_offsets), _ptr(w_down),
                                _ptr(out_perm), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
     _check("moe_expert_down", st)
@@ -283,7 +299,7 @@ def moe_unpermute_combine(out_perm, slot_row, topk_gate, E: int, cf: float, y=No
     T, k = slot_row.shape
     d = out_perm.shape[1]
     if y is None:
-        y = torch.empty((T, d), dtype=out_perm.dtype, device=out_perm.device)
+        y = _new(stream, (T, d), out_perm.dtype, out_perm.device)
     st = lib().moe_unpermute_combine(T, d, E, k, cf, _dt(out_perm), _ptr(out_perm), _ptr(slot_row),
                                      _ptr(topk_gate), _ptr(y), _stream(stream))
     _check("moe_unpermute_combine", st)
@@ -299,10 +315,9 @@ def moe_forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, y=None, to
     T, d = x.shape
     E, F, _ = w_gate.shape
     if y is None:
-        y = torch.empty_like(x)
+        y = _new_like(stream, x)
     if ws is None:
-        ws = torch.empty(max(moe_workspace_bytes(T, d, E, k, cf, F, x.dtype), 16), dtype=torch.uint8,
-                         device=x.device)
+        ws = _new(stream, max(moe_workspace_bytes(T, d, E, k, cf, F, x.dtype), 16), torch.uint8, x.device)
     if gating == "topk_softmax" and fill_order == "token":
         st = lib().moe_forward(T, d, E, k, cf, F, _dt(x), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
                                _ptr(w_down), _ptr(y), _ptr(topk_idx), _ptr(topk_gate), _ptr(slot_row),
@@ -334,12 +349,11 @@ def moe_route_expert_choice(x, w_router, k: int, cf: float, stream=None):
     E = w_router.shape[0]
     C = moe_capacity(T, E, k, cf)
     dev = x.device
-    out = dict(scores=torch.empty((T, E), dtype=torch.float32, device=dev),
-               expert_tokens=torch.empty(max(E * C, 1), dtype=torch.int32, device=dev),
-               slot=torch.empty((T, E), dtype=torch.int32, device=dev),
-               expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev), C=C)
-    ws = torch.empty(max(_size_query("moe_route_expert_choice_workspace_bytes", T, E), 16), dtype=torch.uint8,
-                     device=dev)
+    out = dict(scores=_new(stream, (T, E), torch.float32, dev),
+               expert_tokens=_new(stream, max(E * C, 1), torch.int32, dev),
+               slot=_new(stream, (T, E), torch.int32, dev),
+               expert_offsets=_new(stream, E + 1, torch.int32, dev), C=C)
+    ws = _new(stream, max(_size_query("moe_route_expert_choice_workspace_bytes", T, E), 16), torch.uint8, dev)
     st = lib().moe_route_expert_choice(T, d, E, k, cf, _dt(x), _ptr(x), _ptr(w_router), _ptr(out["scores"]),
                                        _ptr(out["expert_tokens"]), _ptr(out["slot"]), _ptr(out["expert_offsets"]),
                                        _ptr(ws), ws.numel(), _stream(stream))
@@ -351,7 +365,7 @@ def moe_gather_rows(x, row_token, R: int, x_perm=None, stream=None):
     """x_perm[r] = x[row_token[r]] for r < R."""
     T, d = x.shape
     if x_perm is None:
-        x_perm = torch.empty((max(R, 1), d), dtype=x.dtype, device=x.device)
+        x_perm = _new(stream, (max(R, 1), d), x.dtype, x.device)
     _check("moe_gather_rows", lib().moe_gather_rows(T, d, R, _dt(x), _ptr(x), _ptr(row_token), _ptr(x_perm),
                                                     _stream(stream)))
     return x_perm
@@ -363,12 +377,12 @@ def moe_grouped_ffn_rows(x_perm, expert_offsets, w_gate, w_up, w_down, R_max: in
     E, F, d = w_gate.shape
     dev = x_perm.device
     if h is None:
-        h = torch.empty((max(R_max, 1), F), dtype=x_perm.dtype, device=dev)
+        h = _new(stream, (max(R_max, 1), F), x_perm.dtype, dev)
     if out_perm is None:
-        out_perm = torch.empty((max(R_max, 1), d), dtype=x_perm.dtype, device=dev)
+        out_perm = _new(stream, (max(R_max, 1), d), x_perm.dtype, dev)
     if ws is None:
         n = _size_query("moe_ffn_rows_workspace_bytes", R_max, d, E, F, _dt(x_perm))
-        ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+        ws = _new(stream, n, torch.uint8, dev) if n else None
     elif ws is False:
         ws = None
     st = lib().moe_grouped_ffn_rows(R_max, d, E, F, _dt(x_perm), _ptr(x_perm), _ptr(expert_offsets), _ptr(w_gate),
@@ -382,7 +396,7 @@ def moe_combine_expert_choice(out_perm, slot, scores, k: int, cf: float, y=None,
     T, E = slot.shape
     d = out_perm.shape[1]
     if y is None:
-        y = torch.empty((T, d), dtype=out_perm.dtype, device=out_perm.device)
+        y = _new(stream, (T, d), out_perm.dtype, out_perm.device)
     st = lib().moe_combine_expert_choice(T, d, E, k, cf, _dt(out_perm), _ptr(out_perm), _ptr(slot), _ptr(scores),
                                          _ptr(y), _stream(stream))
     _check("moe_combine_expert_choice", st)
@@ -395,10 +409,10 @@ def moe_forward_expert_choice(x, w_router, w_gate, w_up, w_down, k: int, cf: flo
     T, d = x.shape
     E, F, _ = w_gate.shape
     if y is None:
-        y = torch.empty_like(x)
+        y = _new_like(stream, x)
     if ws is None:
         n = _size_query("moe_forward_expert_choice_workspace_bytes", T, d, E, k, cf, F, _dt(x))
-        ws = torch.empty(max(n, 16), dtype=torch.uint8, device=x.device)
+        ws = _new(stream, max(n, 16), torch.uint8, x.device)
     st = lib().moe_forward_expert_choice(T, d, E, k, cf, F, _dt(x), _ptr(x), _ptr(w_router), _ptr(w_gate),
                                          _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(scores), _ptr(slot), _ptr(ws),
                                          ws.numel(), _stream(stream))
@@ -415,11 +429,11 @@ def moe_backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, ws=No
     dw_router, dw_gate, dw_up, dw_down), shaped like x and the weights."""
     T, d = x.shape
     E, F, _ = w_gate.shape
-    out = dict(dx=torch.empty_like(x), dw_router=torch.empty_like(w_router), dw_gate=torch.empty_like(w_gate),
-               dw_up=torch.empty_like(w_up), dw_down=torch.empty_like(w_down))
+    out = dict(dx=_new_like(stream, x), dw_router=_new_like(stream, w_router), dw_gate=_new_like(stream, w_gate),
+               dw_up=_new_like(stream, w_up), dw_down=_new_like(stream, w_down))
     if ws is None:
         n = _size_query("moe_backward_workspace_bytes", T, d, E, k, cf, F, _dt(x))
-        ws = torch.empty(max(n, 16), dtype=torch.uint8, device=x.device)
+        ws = _new(stream, max(n, 16), torch.uint8, x.device)
     st = lib().moe_backward(T, d, E, k, cf, F, _dt(x), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
                             _ptr(w_down), _ptr(dy), _ptr(out["dx"]), _ptr(out["dw_router"]), _ptr(out["dw_gate"]),
                             _ptr(out["dw_up"]), _ptr(out["dw_down"]), _ptr(ws), ws.numel(), _stream(stream))
