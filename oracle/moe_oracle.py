@@ -263,6 +263,33 @@ def fill_in_order(idx: np.ndarray, E: int, cap: int, order):
             slot_row.astype(np.int32), row_slot.astype(np.int32))
 
 
+def layout_from_slot_rows(idx: np.ndarray, E: int, slot_row) -> tuple:
+    """The permutation given its slot -> row map instead of a fill: a layout
+    decided elsewhere (the routing-conditioned oracle takes the GPU's map where
+    float32 ties leave the fill order open). Checks that every expert's kept
+    slots occupy one contiguous block of rows, in ascending expert order from
+    row 0, and returns (demand, offsets, slot_row, row_slot) like
+    fill_in_order."""
+    idx = np.asarray(idx)
+    slot_row = np.asarray(slot_row, dtype=np.int64)
+    T, k = idx.shape
+    demand = np.bincount(idx.ravel().astype(np.int64), minlength=E)
+    kept_e = np.bincount(idx[slot_row >= 0].astype(np.int64), minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept_e)
+    R = int(offsets[E])
+    row_slot = np.full(R, -1, dtype=np.int64)
+    tt, jj = np.nonzero(slot_row >= 0)
+    rows = slot_row[tt, jj]
+    assert np.all(rows < R), "row beyond the kept rows"
+    row_slot[rows] = tt * k + jj
+    assert np.all(row_slot >= 0), "kept slots do not fill rows 0..R-1 once each"
+    e_of_row = idx[tt, jj]
+    assert np.all((rows >= offsets[e_of_row]) & (rows < offsets[e_of_row + 1])), "row outside its expert's block"
+    return (demand.astype(np.int32), offsets.astype(np.int32), slot_row.astype(np.int32),
+            row_slot.astype(np.int32))
+
+
 def fill_in_token_order(idx: np.ndarray, E: int, cap: int):
     """Buffers fill in token order ([ROUTE] drops land towards the end of the
     sequence): fill_in_order with the identity order."""
@@ -372,18 +399,29 @@ def expert_choice_boundary_ties(scores: np.ndarray, C: int, gap: float = 2e-6) -
 
 
 def expert_choice_forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, storage: str,
-                          tokens=None) -> dict:
+                          tokens=None, slot=None) -> dict:
     """The layer with expert-choice routing. C = capacity(T, E, k, cf) tokens
     per expert (cf == 0: C = T, every expert takes every token).
     y[t] = store(sum over experts e that chose t, ascending, of
                  score[t, e] * FFN_e(x_t)); a token no expert chose gets 0.
-    `tokens` restricts y to those tokens (every expert still runs its rows)."""
+    `tokens` restricts y to those tokens (every expert still runs its rows).
+    `slot` [T, E] optionally replaces the selection (a choice taken elsewhere
+    where float32 scores tie at an expert's C-th place): each expert must take
+    exactly C tokens, on rows e*C .. e*C+C-1 in ascending token order."""
     T = x.shape[0]
     E = w_router.shape[0]
     logits = router_logits(x, w_router)
     S = softmax_scores(logits)
     C = capacity(T, E, k, cf)
-    tok, slot = expert_choice_select(S, C)
+    if slot is None:
+        tok, slot = expert_choice_select(S, C)
+    else:
+        slot = np.asarray(slot, dtype=np.int32)
+        tok = np.empty((E, C), dtype=np.int32)
+        for e in range(E):
+            chosen = np.nonzero(slot[:, e] >= 0)[0]
+            assert len(chosen) == C and np.array_equal(slot[chosen, e], e * C + np.arange(C)), e
+            tok[e] = chosen
     d = x.shape[1]
     F = w_gate.shape[1]
     o_rows = np.empty((E * C, d))
@@ -429,7 +467,8 @@ def route(x, w_router, k: int, gating: str = "topk_softmax"):
 
 
 def forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, storage: str,
-            tokens=None, idx=None, gating: str = "topk_softmax", bpr: bool = False) -> dict:
+            tokens=None, idx=None, gating: str = "topk_softmax", bpr: bool = False,
+            slot_row=None) -> dict:
     """The MoE layer forward pass.
 
     tokens: optional subset of token indices whose outputs are computed (the
@@ -440,6 +479,9 @@ def forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, storage: str,
     gating: one of GATINGS (see gates_for).
     bpr:    Batch Priority Routing: buffers fill in descending order of each
             token's top-1 gate instead of token order.
+    slot_row: optional slot -> row map to use instead of the capacity fill
+            (see layout_from_slot_rows); with idx, the layer conditioned on
+            routing decisions taken elsewhere.
     Returns a dict with logits, topk_idx, topk_gate, near_tie, demand,
     offsets, slot_row, row_slot, cap, y (for `tokens`, or all tokens), and
     o_rows/h_rows (rows actually computed, indexed by permuted row; NaN
@@ -451,7 +493,9 @@ def forward(x, w_router, w_gate, w_up, w_down, k: int, cf: float, storage: str,
         idx = select_topk(logits, k)
     gates = gates_for(logits, idx, gating)
     cap = capacity(T, E, k, cf)
-    if bpr:
+    if slot_row is not None:
+        demand, offsets, slot_row, row_slot = layout_from_slot_rows(idx, E, slot_row)
+    elif bpr:
         demand, offsets, slot_row, row_slot = fill_in_priority_order(idx, E, cap, gates[:, 0])
     else:
         demand, offsets, slot_row, row_slot = fill_in_token_order(idx, E, cap)
@@ -514,7 +558,7 @@ def hold(v: np.ndarray, storage: str, point: str) -> np.ndarray:
 
 
 def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: str,
-             weight_grad_experts=None) -> dict:
+             weight_grad_experts=None, idx=None) -> dict:
     """Gradients of L = <dy, y> for the token-choice layer with Softmax(TopK)
     gates and token-order capacity, with respect to x and every weight.
 
@@ -536,13 +580,15 @@ def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: 
     weight_grad_experts: None for the expert weight gradients of every expert;
     otherwise a list of experts, and dW_gate, dW_up and dW_down hold only theirs,
     in that order (the other results are the same either way).
+    idx: optional top-k indices to use instead of the router's choice (as in
+    `forward`: the layer conditioned on routing decisions taken elsewhere).
     """
     x64 = as_f64(x)
     T, d = x64.shape
     E = w_router.shape[0]
     F = w_gate.shape[1]
     wr = as_f64(w_router)
-    r = forward(x, w_router, w_gate, w_up, w_down, k, cf, storage)
+    r = forward(x, w_router, w_gate, w_up, w_down, k, cf, storage, idx=idx)
     idx, gates, slot_row, offsets, row_slot = r["topk_idx"], r["topk_gate"], r["slot_row"], r["offsets"], r["row_slot"]
     R = int(offsets[E])
     dy64 = as_f64(dy)

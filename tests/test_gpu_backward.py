@@ -132,12 +132,10 @@ def test_backward_is_deterministic():
 @pytest.mark.parametrize("name", ["mixtral_bf16", "openmoe_bf16", "finegrained_bf16"])
 def test_full_size_backward(name):
     """The named workloads at full size, in the configuration the benchmark
-    times, on what the oracle can afford. A token's routing, gates and rows
-    depend on that token alone (only whether a slot is kept depends on the
-    tokens before it), so dx of sampled tokens that kept every slot comes from
-    a drop-free oracle backward over those tokens, and the weight gradients of
-    one expert (the one with the fewest kept rows) from a drop-free backward
-    over the tokens that expert kept (both identities are pinned on the CPU)."""
+    times: every entry of dx, dW_g, dW_gate, dW_up and dW_down against the
+    whole oracle backward (tens of seconds and some tens of GB on the host).
+    A near-tie token the kernel routed the other way conditions the oracle on
+    the kernel's indices instead of being left out."""
     w, a = workload(name)
     ref = full_reference(name)
     g = device_inputs(name)
@@ -146,32 +144,12 @@ def test_full_size_backward(name):
     out = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dev(dy), w.k, w.cf)
     torch.cuda.synchronize()
     flips = compare_routing(host(idx), host(gate), ref)
-    if w.cf > 0:
-        assert flips == 0, "a flipped near tie would shift the kept rows of later tokens"
-    same = (host(idx) == ref["topk_idx"]).all(axis=1)
-    kept = ref["slot_row"] >= 0
-    dy64 = dy.double().numpy()
-    rng = np.random.default_rng(91)
-    toks = np.unique(np.concatenate([np.arange(8), np.arange(w.T - 8, w.T), rng.integers(0, w.T, 16)]))
-    toks = toks[same[toks] & kept[toks].all(axis=1)]
-    assert len(toks) >= 16
-    r = orc.backward(a["x"][toks], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy64[toks], w.k, 0.0,
-                     "bf16", weight_grad_experts=[])
-    rel_dx = check_grad("dx", host(out["dx"])[toks], r["dx"])
-    # an expert none of whose tokens flipped on a near tie, with the fewest kept rows
-    kept_rows = np.bincount(ref["topk_idx"][kept], minlength=w.E)
-    for e in np.argsort(kept_rows, kind="stable"):
-        if kept_rows[e] == 0:
-            continue
-        te = np.nonzero(((ref["topk_idx"] == e) & kept).any(axis=1))[0]
-        near = np.nonzero((ref["topk_idx"] == e).any(axis=1) | (host(idx) == e).any(axis=1))[0]
-        if same[near].all():
-            break
-    else:
-        pytest.fail("every expert has a token routed differently")
-    r = orc.backward(a["x"][te], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy64[te], w.k, 0.0,
-                     "bf16", weight_grad_experts=[int(e)])
-    res = {key: check_grad(key, host(out[key][int(e)]), r[rk][0])
-           for key, rk in [("dw_gate", "dW_gate"), ("dw_up", "dW_up"), ("dw_down", "dW_down")]}
-    print(f"{name}: flips {flips}, {len(toks)} tokens dx rel {rel_dx[0]:.3g}; expert {int(e)} ({len(te)} tokens): "
-          + ", ".join(f"{k_} rel {v[0]:.3g}" for k_, v in res.items()))
+    r = orc.backward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy.double().numpy(), w.k, w.cf,
+                     "bf16", idx=host(idx) if flips else None)
+    res = {}
+    for key, rk in [("dx", "dx"), ("dw_router", "dW_g"), ("dw_gate", "dW_gate"), ("dw_up", "dW_up"),
+                    ("dw_down", "dW_down")]:
+        res[key] = check_grad(key, host(out[key]), r[rk])
+        out[key] = None
+        r[rk] = None
+    print(f"{name}: flips {flips}; " + ", ".join(f"{k_} rel {v[0]:.3g} mae {v[1]:.3g}" for k_, v in res.items()))

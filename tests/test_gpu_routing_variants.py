@@ -12,7 +12,7 @@ import moe_inputs as mi
 import sparse_mixture_experts_09_amd as moe
 from oracle import moe_oracle as orc
 from parity import assert_close_rows, compare_routing, host
-from test_gpu_parity import NAMED_SMALL, SMALL, case_id, dev, device_inputs, sample_tokens, workload
+from test_gpu_parity import NAMED_SMALL, SMALL, case_id, dev, device_inputs, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -189,12 +189,14 @@ def test_forward_ex(case, gating, fill):
         assert np.array_equal(s[~amb], ref["slot_row"][~amb])
         check_rows_valid(s, host(idx), ref["offsets"], w.k)
         assert np.array_equal((s >= 0).sum(), (ref["slot_row"] >= 0).sum())
-        keep = ~amb
         print(f"{case_id(case)} {gating}/{fill}: {int(amb.sum())} ambiguous tokens")
+        if amb.any() and not np.array_equal(s, ref["slot_row"]):
+            # tied priorities: every token against the layer fed the kernel's layout
+            ref = orc.forward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], w.k, w.cf, w.dtype,
+                              gating=gating, idx=host(idx), slot_row=s)
     else:
         assert np.array_equal(s, ref["slot_row"])
-        keep = np.ones(w.T, dtype=bool)
-    assert_close_rows(host(y)[keep], ref["y"][keep], w.dtype)
+    assert_close_rows(host(y), ref["y"], w.dtype)
 
 
 def test_priority_with_equal_gates_is_token_order():
@@ -241,10 +243,11 @@ def test_full_size_forward_ex(name, gating, fill):
     amb = ambiguous_tokens(gates[:, 0], a["x"]) if bpr else np.zeros(w.T, dtype=bool)
     assert np.array_equal(s[~amb], slot_row[~amb])
     check_rows_valid(s, host(idx), offsets, w.k)
-    toks = sample_tokens(w, ref)
-    toks = toks[~amb[toks]]
-    r = orc.forward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], w.k, w.cf, w.dtype, tokens=toks,
-                    gating=gating, bpr=bpr)
-    assert np.array_equal(r["slot_row"][~amb], s[~amb])
-    rel, mae = assert_close_rows(host(y)[toks], r["y"], w.dtype)
-    print(f"{name} {gating}/{fill}: {int(amb.sum())} ambiguous, {len(toks)} sampled, max-rel {rel:.3g}")
+    assert (s >= 0).sum() == (slot_row >= 0).sum()
+    # every token, against the layer fed the kernel's routing and layout (the
+    # two differ only where float32 priorities tie, and the check above bounds that)
+    r = orc.forward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], w.k, w.cf, w.dtype,
+                    gating=gating, idx=host(idx), slot_row=s)
+    rel, mae = assert_close_rows(host(y), r["y"], w.dtype)
+    print(f"{name} {gating}/{fill}: {int(amb.sum())} ambiguous, {int((s != slot_row).any(1).sum())} placed "
+          f"differently, all {w.T} tokens, max-rel {rel:.3g}, MAE {mae:.3g}")

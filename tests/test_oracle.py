@@ -995,3 +995,34 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught = True
     assert caught, f"planted mistake {name} passed every pin"
+
+
+def test_routing_conditioned_oracle_reduces_to_the_oracle():
+    """forward(idx=, slot_row=) with the oracle's own decisions is the oracle;
+    any other valid layout (rows reordered inside each expert's block) gives
+    the same y (the combine follows the slots, not the row order); a layout
+    with a row outside its expert's block is refused. The same for expert
+    choice with its own selection."""
+    x, wr, wg, wu, wd = small_layer(T=40, E=5, k=2)
+    ref = orc.forward(x, wr, wg, wu, wd, 2, 0.75, "f64")
+    again = orc.forward(x, wr, wg, wu, wd, 2, 0.75, "f64", idx=ref["topk_idx"], slot_row=ref["slot_row"])
+    for key in ("demand", "offsets", "slot_row", "row_slot"):
+        assert np.array_equal(again[key], ref[key]), key
+    assert np.array_equal(again["y"], ref["y"])
+    # reverse the rows of every expert's block
+    off = ref["offsets"]
+    new_row = np.arange(int(off[-1]))
+    for e in range(5):
+        new_row[off[e]:off[e + 1]] = new_row[off[e]:off[e + 1]][::-1]
+    srow = np.where(ref["slot_row"] >= 0, new_row[np.maximum(ref["slot_row"], 0)], -1)
+    rev = orc.forward(x, wr, wg, wu, wd, 2, 0.75, "f64", idx=ref["topk_idx"], slot_row=srow)
+    assert np.allclose(rev["y"], ref["y"], rtol=1e-13, atol=1e-14)
+    bad = ref["slot_row"].copy()
+    swap = np.nonzero((bad >= 0) & (ref["topk_idx"] == 0))
+    other = np.nonzero((bad >= 0) & (ref["topk_idx"] == 1))
+    bad[swap[0][0], swap[1][0]], bad[other[0][0], other[1][0]] = bad[other[0][0], other[1][0]], bad[swap[0][0], swap[1][0]]
+    with pytest.raises(AssertionError):
+        orc.forward(x, wr, wg, wu, wd, 2, 0.75, "f64", idx=ref["topk_idx"], slot_row=bad)
+    ec = orc.expert_choice_forward(x, wr, wg, wu, wd, 2, 0.5, "f64")
+    ec2 = orc.expert_choice_forward(x, wr, wg, wu, wd, 2, 0.5, "f64", slot=ec["slot"])
+    assert np.array_equal(ec2["y"], ec["y"]) and np.array_equal(ec2["tokens"], ec["tokens"])
