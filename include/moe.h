@@ -169,6 +169,30 @@ int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype 
                 int32_t* slot_row, int32_t* row_slot, void* x_perm,
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_permute for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Same arguments, arithmetic and outputs as
+ * moe_permute, without ws / ws_bytes: the permutation's scratch (per-chunk
+ * expert histograms, ceil(T / 256) * E * 4 bytes rounded up to 256) is a
+ * file-scope device array of moe_permute_noalloc_scratch_bytes() = 1 MiB
+ * that each GPU holds until the process ends. Problems whose scratch would
+ * exceed it return MOE_ERR_WORKSPACE (E = 256 fits up to 262144 tokens,
+ * E = 8 up to 8388608). The call allocates nothing: its first call on a device looks
+ * up that device's copy of the array (hipGetSymbolAddress, with the device
+ * current; MOE_ERR_HIP if that fails) and keeps the address. Every call on
+ * a GPU shares that GPU's array, and the array keeps the last call's
+ * contents (every histogram entry is rewritten before it is read, so no
+ * clearing is needed): calls that overlap in time on one GPU, on different
+ * streams, race on it and must be serialised by the caller. `stream` must
+ * belong to the current device. */
+int moe_permute_noalloc(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+                        const void* x, const int32_t* topk_idx,
+                        int32_t* expert_counts, int32_t* expert_offsets,
+                        int32_t* slot_row, int32_t* row_slot, void* x_perm, hipStream_t stream);
+
+/* Size in bytes of moe_permute_noalloc's device scratch array (host only). */
+size_t moe_permute_noalloc_scratch_bytes(void);
+
 /* moe_permute with Batch Priority Routing (MOE_FILL_PRIORITY): token t's
  * importance is score[t * score_stride] (fp32, device; pass topk_gate with
  * stride k for the top-1 gate). Each expert keeps, among the tokens that

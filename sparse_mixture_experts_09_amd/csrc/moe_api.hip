@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe.h"
 #include "moe_kernels.h"
 
@@ -120,6 +122,34 @@ ForwardLayout forward_layout(int64_t T, int d, int E, int k, int64_t R_max, int 
   return L;
 }
 
+// Scratch of moe_permute_noalloc: the permutation's per-chunk expert
+// histograms live in this file-scope device array instead of a caller
+// workspace. Every GPU the library runs on holds its own copy until the
+// process ends. On the host the name is only a stand-in: kernels get the
+// device address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kPermuteScratchBytes = (size_t)1 << 20;
+static __device__ __align__(256) char permute_scratch[kPermuteScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of permute_scratch on the current device, looked up once
+// per device (with that device current) and kept.
+int permute_scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(permute_scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -197,22 +227,30 @@ int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, const vo
                           logits_opt, stream);
 }
 
+// static_scratch: take the workspace from permute_scratch (ws / ws_bytes are
+// ignored) instead of the caller's buffer.
 static int permute_impl(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
                         const int32_t* topk_idx, const float* score, int64_t score_stride,
                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot_row,
-                        int32_t* row_slot, void* x_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+                        int32_t* row_slot, void* x_perm, void* ws, size_t ws_bytes, hipStream_t stream,
+                        bool static_scratch = false) {
   int st = check_scalars(T, d, E, k, cf, -1, dt, false);
   if (st != MOE_OK) return st;
   const bool priority = score != nullptr;
   if (priority && score_stride < 1) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
-  if (!x || !topk_idx || !expert_counts || !expert_offsets || !slot_row || !row_slot || !x_perm || !ws)
+  if (!x || !topk_idx || !expert_counts || !expert_offsets || !slot_row || !row_slot || !x_perm ||
+      (!ws && !static_scratch))
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(topk_idx) || !aligned16(expert_counts) || !aligned16(expert_offsets) ||
       !aligned16(slot_row) || !aligned16(row_slot) || !aligned16(x_perm) || !aligned16(ws) ||
       (reinterpret_cast<uintptr_t>(score) & 3u) != 0)
     return MOE_ERR_UNSUPPORTED;
   const size_t need = permute_ws_bytes(T, E, priority);
+  if (static_scratch) {
+    ws = nullptr;                       // looked up after every argument check
+    ws_bytes = kPermuteScratchBytes;
+  }
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   const int64_t cap = capacity_of(T, E, k, cf);
   const int64_t R_max = rows_max_of(T, E, k, cap);
@@ -223,6 +261,10 @@ static int permute_impl(int64_t T, int32_t d, int32_t E, int32_t k, float cf, mo
                        {x, (size_t)T * d * s},          {topk_idx, (size_t)T * k * 4},
                        {score, priority ? (size_t)((T - 1) * score_stride + 1) * 4 : 0}};
   if (any_overlap(all, 6, 9)) return MOE_ERR_INVALID_ARG;
+  if (static_scratch) {
+    st = permute_scratch_address(&ws);
+    if (st != MOE_OK) return st;
+  }
   char* w = reinterpret_cast<char*>(ws);
   int32_t* chunks = reinterpret_cast<int32_t*>(w);
   int32_t* order = nullptr;
@@ -245,6 +287,15 @@ int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype 
   return permute_impl(T, d, E, k, cf, dt, x, topk_idx, nullptr, 0, expert_counts, expert_offsets, slot_row,
                       row_slot, x_perm, ws, ws_bytes, stream);
 }
+
+int moe_permute_noalloc(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
+                        const int32_t* topk_idx, int32_t* expert_counts, int32_t* expert_offsets,
+                        int32_t* slot_row, int32_t* row_slot, void* x_perm, hipStream_t stream) {
+  return permute_impl(T, d, E, k, cf, dt, x, topk_idx, nullptr, 0, expert_counts, expert_offsets, slot_row,
+                      row_slot, x_perm, nullptr, 0, stream, true);
+}
+
+size_t moe_permute_noalloc_scratch_bytes(void) { return kPermuteScratchBytes; }
 
 int moe_permute_priority(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
                          const int32_t* topk_idx, const float* score, int64_t score_stride,

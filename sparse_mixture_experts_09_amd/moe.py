@@ -40,6 +40,9 @@ _SIGS = {
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_permute": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _vp, _vp, _sz, _vp]),
+    "moe_permute_noalloc": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _vp, _vp]),
+    "moe_permute_noalloc_scratch_bytes": (_sz, []),
     "moe_ffn_workspace_bytes": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int,
                                                ctypes.POINTER(_sz)]),
     "moe_grouped_ffn": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp,
@@ -248,6 +251,24 @@ def moe_permute(x, topk_idx, E: int, cf: float, stream=None, out=None, score=Non
         _check("moe_permute_priority", st)
     return dict(expert_counts=counts, expert_offsets=offsets, slot_row=slot_row, row_slot=row_slot,
                 x_perm=x_perm)
+
+
+def moe_permute_noalloc(x, topk_idx, E: int, cf: float, out, stream=None):
+    """moe_permute without a workspace (the library's static device scratch).
+    Every output is caller-supplied in `out` (expert_counts [E], expert_offsets
+    [E+1], slot_row [T,k], row_slot [>= R_max], x_perm [>= R_max, d]), so the
+    call allocates nothing. Returns `out`."""
+    T, d = x.shape
+    k = topk_idx.shape[1]
+    st = lib().moe_permute_noalloc(T, d, E, k, cf, _dt(x), _ptr(x), _ptr(topk_idx), _ptr(out["expert_counts"]),
+                                   _ptr(out["expert_offsets"]), _ptr(out["slot_row"]), _ptr(out["row_slot"]),
+                                   _ptr(out["x_perm"]), _stream(stream))
+    _check("moe_permute_noalloc", st)
+    return out
+
+
+def moe_permute_noalloc_scratch_bytes() -> int:
+    return int(lib().moe_permute_noalloc_scratch_bytes())
 
 
 def moe_grouped_ffn(x_perm, expert_offsets, w_gate, w_up, w_down, T: int, k: int, cf: float,

@@ -27,7 +27,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 27
+    assert len(names) == 29
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -150,6 +150,31 @@ def test_stage_entry_points_validate():
     assert L.moe_workspace_bytes(64, 64, 4, 5, 1.0, 128, F32, ctypes.byref(b)) == INV
     assert L.moe_workspace_bytes(64, 64, 4, 2, 1.0, 128, F32, None) == INV
     assert L.moe_permute_workspace_bytes(64, 300, ctypes.byref(b)) == UNS
+
+
+def test_permute_noalloc_validates_fake_pointers():
+    """The allocation-free permutation checks like moe_permute and rejects a
+    problem whose histograms exceed its 1 MiB static scratch before any HIP
+    call (so these fake pointers are never used)."""
+    L = moe.lib()
+    assert L.moe_permute_noalloc_scratch_bytes() == 1 << 20
+    args = [64, 64, 4, 2, 1.0, F32, A[0], A[1], A[2], A[3], A[4], A[5], A[6], None]
+    a = list(args); a[7] = None                                  # null topk_idx
+    assert L.moe_permute_noalloc(*a) == INV
+    a = list(args); a[12] = A[0]                                 # x_perm overlapping x
+    assert L.moe_permute_noalloc(*a) == INV
+    a = list(args); a[6] = A[0] + 8                              # misaligned x
+    assert L.moe_permute_noalloc(*a) == UNS
+    a = list(args); a[0] = 0
+    assert L.moe_permute_noalloc(*a) == OK
+    # histograms: ceil(T / 256) * E * 4 bytes; E = 256 fits 262144 tokens, not one chunk more
+    a = list(args); a[0] = 262144 + 1; a[2] = 256; a[3] = 1
+    assert L.moe_permute_noalloc(*a) == WS
+    a = list(args); a[0] = 8388608 + 1; a[2] = 8; a[3] = 1; a[1] = 8
+    assert L.moe_permute_noalloc(*a) == WS
+    b = ctypes.c_size_t()
+    assert L.moe_permute_workspace_bytes(262144, 256, ctypes.byref(b)) == OK and b.value == 1 << 20
+    assert L.moe_permute_workspace_bytes(8388608, 8, ctypes.byref(b)) == OK and b.value == 1 << 20
 
 
 def test_gating_and_priority_entry_points_validate():
