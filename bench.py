@@ -62,6 +62,35 @@ def load_traffic(workload):
     return t.get("bytes_per_launch")
 
 
+def clock_during(moe, run, steps, ms_per_step):
+    """The core (shader) clock while `run()` executes `steps` times: clock
+    probes (one wavefront each, waiting 1 ms of the device's constant-rate
+    wall clock and counting core cycles meanwhile) run back to back on a
+    second stream beside the loop, for about 80% of its length so that every
+    probe overlaps it. Returns MHz statistics over the probes."""
+    import torch
+    khz = moe.moe_wall_clock_khz()
+    n = max(1, int(0.8 * steps * ms_per_step))
+    out = torch.zeros((n, 2), dtype=torch.int64, device="cuda")
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()   # default priority, like every stream here
+    start = torch.cuda.Event()
+    start.record(main)
+    side.wait_event(start)
+    for i in range(n):
+        moe.moe_clock_probe(out[i], khz, stream=side)
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    cyc = out[:, 0].double()
+    wall = out[:, 1].double()
+    mhz = (cyc / wall * khz / 1e3).cpu().tolist()
+    return {"mean_mhz": float(cyc.sum() / wall.sum() * khz / 1e3), "min_mhz": min(mhz), "max_mhz": max(mhz),
+            "probes": n, "wall_clock_khz": khz,
+            "source": "core-cycle counter over 1 ms wall-clock windows, probes on a second stream beside "
+                      f"{steps} more moe_forward steps"}
+
+
 def cpu_baseline(w, a, target_s, gating="topk_softmax", bpr=False):
     """The oracle, as it is, on the first S tokens of the workload."""
     from threadpoolctl import threadpool_info
@@ -173,6 +202,10 @@ def main():
     ms_step = (t1 - t0) * 1e3 / K
     gpu_ms_step = e0.elapsed_time(e1) / K
     log(f"moe_forward: {ms_step:.3f} ms/step wall, {gpu_ms_step:.3f} ms/step events")
+    # the core clock during the same loop, measured in K more steps (outside the timed region)
+    clock = clock_during(moe, forward, K, ms_step)
+    log(f"core clock during moe_forward: mean {clock['mean_mhz']:.0f} MHz (min {clock['min_mhz']:.0f}, "
+        f"max {clock['max_mhz']:.0f}, {clock['probes']} probes)")
 
     # ---- stage pass: same kernels, events between launches ----
     R_max = moe.moe_rows_max(T, E, k, cf)
@@ -273,6 +306,7 @@ def main():
         "route_permute_combine_hbm_frac": hbm_frac,
         "layer_tflops": (alg["route"]["flops"] + alg["gate_up"]["flops"] + alg["down"]["flops"]) / (ms_step * 1e-3) / 1e12,
         "gpu_ms_per_step_events": gpu_ms_step,
+        "core_clock": clock,
         "stages": stages,
         "stage_path_equals_forward": same_as_forward,
     }

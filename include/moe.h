@@ -384,6 +384,21 @@ int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F
                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
+/* Measurement aid, not part of the layer: the shader clock while other work
+ * runs. Enqueues one wavefront on `stream` that waits `wall_ticks` ticks of
+ * the device's constant-rate wall clock (see moe_wall_clock_khz) and writes
+ * out[0] = core clock cycles counted meanwhile (s_memtime), out[1] = wall
+ * ticks elapsed, so clock = out[0] / out[1] * wall rate. Run it on a second
+ * stream beside a workload to see the clock the workload runs at (a
+ * power-limited chip lowers it under dense MFMA work).
+ *   out         uint64 [2], device, 16-byte aligned
+ *   wall_ticks  1 .. 100000000 (MOE_ERR_INVALID_ARG otherwise) */
+int moe_clock_probe(uint64_t* out, int64_t wall_ticks, hipStream_t stream);
+
+/* Rate of the wall clock that moe_clock_probe counts, in kHz, for the
+ * current device (hipDeviceAttributeWallClockRate). Host only. */
+int moe_wall_clock_khz(int32_t* khz);
+
 const char* moe_status_string(int status);
 
 #ifdef __cplusplus

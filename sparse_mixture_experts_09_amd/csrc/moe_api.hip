@@ -150,9 +150,47 @@ int permute_scratch_address(void** out) {
   return MOE_OK;
 }
 
+// One wavefront: the shader-clock counter (s_memtime, counts core clock
+// cycles) and the constant-rate wall clock (s_memrealtime) at the start, a
+// wait of `ticks` wall-clock ticks (s_sleep between reads, so the wave takes
+// almost no issue slots from kernels sharing its compute unit), and both
+// counters again; out = {core cycles, wall ticks} over the wait. The wall
+// clock only moves forward, so the wait always ends.
+__global__ __launch_bounds__(64) void clock_probe_kernel(uint64_t* __restrict__ out, uint64_t ticks) {
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  uint64_t r1 = r0;
+  while (r1 - r0 < ticks) {
+    __builtin_amdgcn_s_sleep(8);
+    r1 = __builtin_amdgcn_s_memrealtime();
+  }
+  const uint64_t c1 = __builtin_amdgcn_s_memtime();
+  r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    out[0] = c1 - c0;
+    out[1] = r1 - r0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+int moe_clock_probe(uint64_t* out, int64_t wall_ticks, hipStream_t stream) {
+  if (out == nullptr || wall_ticks < 1 || wall_ticks > 100000000) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(out)) return MOE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(1), dim3(64), 0, stream, out, (uint64_t)wall_ticks);
+  return hip_status(hipGetLastError());
+}
+
+int moe_wall_clock_khz(int32_t* khz) {
+  if (khz == nullptr) return MOE_ERR_INVALID_ARG;
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return MOE_ERR_HIP;
+  *khz = v;
+  return MOE_OK;
+}
 
 int64_t moe_capacity(int64_t T, int32_t E, int32_t k, float cf) {
   if (T < 0 || E < 1 || k < 1 || k > E || !isfinite(cf) || cf < 0.0f) return -1;

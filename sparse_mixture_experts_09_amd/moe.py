@@ -72,6 +72,8 @@ _SIGS = {
                                                     ctypes.POINTER(_sz)]),
     "moe_backward": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_clock_probe": (ctypes.c_int, [_vp, _i64, _vp]),
+    "moe_wall_clock_khz": (ctypes.c_int, [ctypes.POINTER(_i32)]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -460,3 +462,19 @@ def moe_backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, ws=No
                             _ptr(out["dw_up"]), _ptr(out["dw_down"]), _ptr(ws), ws.numel(), _stream(stream))
     _check("moe_backward", st)
     return out
+
+
+# ---------------------------------------------------------------------------
+# measurement aid
+# ---------------------------------------------------------------------------
+
+def moe_clock_probe(out, wall_ticks: int, stream=None):
+    """Enqueue one clock probe writing {core cycles, wall ticks} into out[0:2]
+    (a uint64-sized int64 CUDA tensor of at least 2 elements)."""
+    _check("moe_clock_probe", lib().moe_clock_probe(_ptr(out), wall_ticks, _stream(stream)))
+
+
+def moe_wall_clock_khz() -> int:
+    v = _i32()
+    _check("moe_wall_clock_khz", lib().moe_wall_clock_khz(ctypes.byref(v)))
+    return int(v.value)

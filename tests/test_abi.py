@@ -27,7 +27,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 29
+    assert len(names) == 31
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -150,6 +150,15 @@ def test_stage_entry_points_validate():
     assert L.moe_workspace_bytes(64, 64, 4, 5, 1.0, 128, F32, ctypes.byref(b)) == INV
     assert L.moe_workspace_bytes(64, 64, 4, 2, 1.0, 128, F32, None) == INV
     assert L.moe_permute_workspace_bytes(64, 300, ctypes.byref(b)) == UNS
+
+
+def test_clock_probe_validates_fake_pointers():
+    L = moe.lib()
+    assert L.moe_clock_probe(None, 100, None) == INV
+    assert L.moe_clock_probe(A[0], 0, None) == INV
+    assert L.moe_clock_probe(A[0], 100000001, None) == INV
+    assert L.moe_clock_probe(A[0] + 8, 100, None) == UNS
+    assert L.moe_wall_clock_khz(None) == INV
 
 
 def test_permute_noalloc_validates_fake_pointers():

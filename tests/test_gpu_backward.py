@@ -24,9 +24,13 @@ def make_dy(w, seed):
 
 
 def check_grad(name, got, ref):
-    """Row-wise: max |err| / max |ref| <= 2e-2 per row of the last dimension,
-    and mean |err| <= 1e-2 * mean |ref| over the tensor; rows whose reference
-    is exactly zero must be zero."""
+    """Row-wise: max |err| / max |ref| <= 2e-2 per row of the last dimension
+    (the forward's bound), and mean |err| <= 2e-3 * mean |ref| over the
+    tensor: the forward's mean absolute error bound of 1e-3 on outputs whose
+    mean magnitude is 0.5 to 0.7 at these workloads, carried over to tensors
+    whose scale varies by orders of magnitude (a weight gradient sums over all
+    rows of an expert).
+    Rows whose reference is exactly zero must be zero."""
     g = np.asarray(got, np.float64).reshape(-1, got.shape[-1])
     r = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
     assert np.all(np.isfinite(g)), name
@@ -37,7 +41,7 @@ def check_grad(name, got, ref):
     rel = (err.max(axis=1)[~zero] / rmax[~zero]).max(initial=0.0)
     mae = err.mean() / max(np.abs(r).mean(), 1e-30)
     assert rel <= 2e-2, f"{name}: row max-rel {rel:.3g}"
-    assert mae <= 1e-2, f"{name}: relative MAE {mae:.3g}"
+    assert mae <= 2e-3, f"{name}: relative MAE {mae:.3g}"
     return rel, mae
 
 
