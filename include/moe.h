@@ -51,8 +51,9 @@
  *   - T == 0 is a valid empty problem: the call returns MOE_OK and enqueues
  *     nothing (pointers are not inspected).
  *   - Compiled limits (MOE_ERR_UNSUPPORTED beyond them): E <= 256, k <= 8,
- *     T*k < 2^31; d and F multiples of 8 (bf16) or 4 (fp32); for bf16 the
- *     grouped FFN also needs d and F to be multiples of 64.
+ *     T*k < 2^31, d and F at most 2^24; d and F multiples of 8 (bf16) or 4
+ *     (fp32); for bf16 the grouped FFN also needs d and F to be multiples of
+ *     64. The size queries refuse T >= 2^31 the same way.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -65,6 +66,9 @@
 extern "C" {
 #endif
 
+/* Storage type of activations and weights. Entry points take it as an
+ * int32_t `dt` holding one of these values, so that any other value is a
+ * well-defined MOE_ERR_INVALID_ARG rather than an out-of-range enum. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Gate rule of the router (the chosen experts are the same under every rule;
@@ -106,7 +110,8 @@ typedef enum {
 int64_t moe_capacity(int64_t T, int32_t E, int32_t k, float cf);
 
 /* R_max = min(T*k, E*cap): the row count to allocate for x_perm, h, out_perm
- * and row_slot. Host only. */
+ * and row_slot. Host only. MOE_ERR_INVALID_ARG for invalid scalars (as
+ * moe_capacity), MOE_ERR_UNSUPPORTED for T >= 2^31. */
 int moe_rows_max(int64_t T, int32_t E, int32_t k, float cf, int64_t* rows);
 
 /* Workspace bytes needed by moe_permute (per-chunk expert histograms). */
@@ -121,14 +126,14 @@ int moe_permute_priority_workspace_bytes(int64_t T, int32_t E, size_t* bytes);
  * of the current device at most; 0 when the problem uses no split). Query it
  * with the device the calls will run on current. */
 int moe_ffn_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
-                            moe_dtype dt, size_t* bytes);
+                            int32_t dt, size_t* bytes);
 
 /* Workspace bytes needed by moe_forward and moe_forward_ex (routing outputs,
  * row maps, x_perm, h, out_perm, the permutation's histograms, the priority
  * sort's buffers and the FFN's split-tail partials, each 256-byte aligned;
  * depends on the current device). */
 int moe_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf,
-                        int32_t F, moe_dtype dt, size_t* bytes);
+                        int32_t F, int32_t dt, size_t* bytes);
 
 /* Router: logits l = x . W_g^T (fp32 accumulation), the k largest per token
  * in slot order (descending logit, ties to the lower expert index) and their
@@ -138,7 +143,7 @@ int moe_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf,
  *   topk_idx   [T, k]  int32     out: chosen experts
  *   topk_gate  [T, k]  fp32      out: gates, summing to 1 per token
  *   logits_opt [T, E]  fp32      out (optional, NULL to skip): router logits */
-int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt,
+int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, int32_t dt,
               const void* x, const void* w_router,
               int32_t* topk_idx, float* topk_gate, float* logits_opt,
               hipStream_t stream);
@@ -148,13 +153,19 @@ int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt,
  * softmax-first rules topk_gate[t, j] = p[t, S_j] (times E/k when scaled)
  * with p the softmax over all E logits. An unknown rule is
  * MOE_ERR_INVALID_ARG. */
-int moe_route_gating(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, int32_t gating,
+int moe_route_gating(int64_t T, int32_t d, int32_t E, int32_t k, int32_t dt, int32_t gating,
                      const void* x, const void* w_router,
                      int32_t* topk_idx, float* topk_gate, float* logits_opt,
                      hipStream_t stream);
 
 /* Permutation with token-order capacity (the walkthrough's permute step).
- *   topk_idx        [T, k]      int32  in: from moe_route (values in [0, E))
+ *   topk_idx        [T, k]      int32  in: from moe_route. A token's k ids
+ *                                      must be distinct experts in [0, E)
+ *                                      (moe_route guarantees it); an id
+ *                                      outside [0, E) is a dropped slot; with
+ *                                      a repeated id the call stays inside its
+ *                                      buffers but its counts, row maps and
+ *                                      x_perm are unspecified
  *   expert_counts   [E]         int32  out: demand, tokens that chose e
  *   expert_offsets  [E + 1]     int32  out: exclusive prefix sum of
  *                                      kept_e = min(demand_e, cap)
@@ -163,7 +174,7 @@ int moe_route_gating(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, i
  *   x_perm          [R_max, d]  dt     out: x_perm[slot_row[t,j]] = x[t];
  *                                      expert-major, token order inside an expert
  *   ws, ws_bytes                       scratch, >= moe_permute_workspace_bytes */
-int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t dt,
                 const void* x, const int32_t* topk_idx,
                 int32_t* expert_counts, int32_t* expert_offsets,
                 int32_t* slot_row, int32_t* row_slot, void* x_perm,
@@ -185,7 +196,7 @@ int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype 
  * clearing is needed): calls that overlap in time on one GPU, on different
  * streams, race on it and must be serialised by the caller. `stream` must
  * belong to the current device. */
-int moe_permute_noalloc(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+int moe_permute_noalloc(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t dt,
                         const void* x, const int32_t* topk_idx,
                         int32_t* expert_counts, int32_t* expert_offsets,
                         int32_t* slot_row, int32_t* row_slot, void* x_perm, hipStream_t stream);
@@ -201,7 +212,7 @@ size_t moe_permute_noalloc_scratch_bytes(void);
  * Counts and offsets are as for moe_permute.
  *   score, score_stride  fp32 device array, 4-byte aligned; stride >= 1
  *   ws, ws_bytes         scratch, >= moe_permute_priority_workspace_bytes */
-int moe_permute_priority(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+int moe_permute_priority(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t dt,
                          const void* x, const int32_t* topk_idx,
                          const float* score, int64_t score_stride,
                          int32_t* expert_counts, int32_t* expert_offsets,
@@ -227,7 +238,7 @@ int moe_permute_priority(int64_t T, int32_t d, int32_t E, int32_t k, float cf, m
  * into K-slices whose fp32 partial sums are added in slice order before the
  * single rounding to dt, so results are deterministic. */
 int moe_grouped_ffn(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
-                    moe_dtype dt, const void* x_perm, const int32_t* expert_offsets,
+                    int32_t dt, const void* x_perm, const int32_t* expert_offsets,
                     const void* w_gate, const void* w_up, const void* w_down,
                     void* h_ws, void* out_perm, void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -236,10 +247,10 @@ int moe_grouped_ffn(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_
  *   moe_expert_gate_up: h = store(silu(x_perm . W_gate^T) * (x_perm . W_up^T))
  *   moe_expert_down:    out_perm = store(h . W_down^T)                       */
 int moe_expert_gate_up(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
-                       moe_dtype dt, const void* x_perm, const int32_t* expert_offsets,
+                       int32_t dt, const void* x_perm, const int32_t* expert_offsets,
                        const void* w_gate, const void* w_up, void* h, hipStream_t stream);
 int moe_expert_down(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
-                    moe_dtype dt, const void* h, const int32_t* expert_offsets,
+                    int32_t dt, const void* h, const int32_t* expert_offsets,
                     const void* w_down, void* out_perm, void* ws, size_t ws_bytes,
                     hipStream_t stream);
 
@@ -253,7 +264,7 @@ int moe_expert_down(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_
  *   topk_gate  [T, k]      fp32
  *   y          [T, d]      dt    out */
 int moe_unpermute_combine(int64_t T, int32_t d, int32_t E, int32_t k, float cf,
-                          moe_dtype dt, const void* out_perm, const int32_t* slot_row,
+                          int32_t dt, const void* out_perm, const int32_t* slot_row,
                           const float* topk_gate, void* y, hipStream_t stream);
 
 /* The whole layer: moe_route, moe_permute, moe_grouped_ffn and
@@ -265,7 +276,7 @@ int moe_unpermute_combine(int64_t T, int32_t d, int32_t E, int32_t k, float cf,
  *   slot_row_opt     [T, k]  int32  out (optional)
  *   ws, ws_bytes                    scratch, >= moe_workspace_bytes */
 int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
-                moe_dtype dt, const void* x, const void* w_router,
+                int32_t dt, const void* x, const void* w_router,
                 const void* w_gate, const void* w_up, const void* w_down, void* y,
                 int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* slot_row_opt,
                 void* ws, size_t ws_bytes, hipStream_t stream);
@@ -276,7 +287,7 @@ int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
  * moe_forward is (MOE_GATING_TOPK_SOFTMAX, MOE_FILL_TOKEN_ORDER). Unknown
  * values are MOE_ERR_INVALID_ARG. */
 int moe_forward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
-                   moe_dtype dt, int32_t gating, int32_t fill_order,
+                   int32_t dt, int32_t gating, int32_t fill_order,
                    const void* x, const void* w_router,
                    const void* w_gate, const void* w_up, const void* w_down, void* y,
                    int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* slot_row_opt,
@@ -310,14 +321,14 @@ int moe_route_expert_choice_workspace_bytes(int64_t T, int32_t E, size_t* bytes)
  *   slot            [T, E]     int32  out: row of (t, e), -1 if e did not take t
  *   expert_offsets  [E + 1]    int32  out: e * C (for the grouped FFN)
  *   ws, ws_bytes                      scratch, >= moe_route_expert_choice_workspace_bytes */
-int moe_route_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+int moe_route_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t dt,
                             const void* x, const void* w_router, float* scores,
                             int32_t* expert_tokens, int32_t* slot, int32_t* expert_offsets,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Row gather: x_perm[r, :] = x[row_token[r], :] for r < R (a token index
  * outside [0, T) gives a zero row). x [T, d], x_perm [R, d], both dt. */
-int moe_gather_rows(int64_t T, int32_t d, int64_t R, moe_dtype dt, const void* x,
+int moe_gather_rows(int64_t T, int32_t d, int64_t R, int32_t dt, const void* x,
                     const int32_t* row_token, void* x_perm, hipStream_t stream);
 
 /* The grouped SwiGLU FFN of moe_grouped_ffn over any expert-major row set of
@@ -325,9 +336,9 @@ int moe_gather_rows(int64_t T, int32_t d, int64_t R, moe_dtype dt, const void* x
  * expert_offsets[e+1]-1, offsets non-decreasing, expert_offsets[E] <= R_max).
  * Same arithmetic, layouts and split-tail workspace rules; the workspace
  * size comes from moe_ffn_rows_workspace_bytes. */
-int moe_ffn_rows_workspace_bytes(int64_t R_max, int32_t d, int32_t E, int32_t F, moe_dtype dt,
+int moe_ffn_rows_workspace_bytes(int64_t R_max, int32_t d, int32_t E, int32_t F, int32_t dt,
                                  size_t* bytes);
-int moe_grouped_ffn_rows(int64_t R_max, int32_t d, int32_t E, int32_t F, moe_dtype dt,
+int moe_grouped_ffn_rows(int64_t R_max, int32_t d, int32_t E, int32_t F, int32_t dt,
                          const void* x_perm, const int32_t* expert_offsets,
                          const void* w_gate, const void* w_up, const void* w_down,
                          void* h_ws, void* out_perm, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -335,16 +346,16 @@ int moe_grouped_ffn_rows(int64_t R_max, int32_t d, int32_t E, int32_t F, moe_dty
 /* Combine with a variable fan-in (y as above; rows outside [0, E*C) count as
  * not chosen).
  *   out_perm [E*C, d] dt, slot [T, E] int32, scores [T, E] fp32, y [T, d] dt out */
-int moe_combine_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+int moe_combine_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t dt,
                               const void* out_perm, const int32_t* slot, const float* scores,
                               void* y, hipStream_t stream);
 
 /* The whole expert-choice layer on one stream, intermediates in ws.
  *   scores_opt [T, E] fp32 and slot_opt [T, E] int32 are optional outputs. */
 int moe_forward_expert_choice_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf,
-                                              int32_t F, moe_dtype dt, size_t* bytes);
+                                              int32_t F, int32_t dt, size_t* bytes);
 int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
-                              moe_dtype dt, const void* x, const void* w_router,
+                              int32_t dt, const void* x, const void* w_router,
                               const void* w_gate, const void* w_up, const void* w_down, void* y,
                               float* scores_opt, int32_t* slot_opt,
                               void* ws, size_t ws_bytes, hipStream_t stream);
@@ -376,8 +387,8 @@ int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float 
  * moe_rows_max.
  * ------------------------------------------------------------------------- */
 int moe_backward_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
-                                 moe_dtype dt, size_t* bytes);
-int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+                                 int32_t dt, size_t* bytes);
+int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt,
                  const void* x, const void* w_router, const void* w_gate, const void* w_up,
                  const void* w_down, const void* dy,
                  void* dx, void* dw_router, void* dw_gate, void* dw_up, void* dw_down,

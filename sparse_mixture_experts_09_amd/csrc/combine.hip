@@ -10,6 +10,7 @@
 // One wavefront per token: lane l handles the 16-byte slices l, l+64, ... of
 // the row; for each slice it reads the k expert-output rows (in slot order),
 // accumulates gate * value in fp32 from +0 and writes the rounded sum once.
+// The loads of several slices are issued together before the sums.
 // Each slot reads through a buffer descriptor of its own (base at its row,
 // record count one row, or 0 for a dropped slot, whose gate is taken as 0),
 // so the k loads carry no branch and issue together; a dropped slot adds
@@ -42,22 +43,33 @@ __global__ __launch_bounds__(256) void combine_kernel(int64_t T, int d, int k,
     src[j] = make_rsrc(out_perm + (size_t)(r >= 0 ? r : 0) * row_bytes, r >= 0 ? row_bytes : 0u);
   }
   char* dst = y + (size_t)t * row_bytes;
-#pragma unroll 2
-  for (uint32_t off = (uint32_t)lane * 16; off < row_bytes; off += 64 * 16) {
-    u32x4 v[KM];
+  // U slices (1 KB of the row each) of all k rows are loaded before any is
+  // used: 16 loads of 16 bytes in flight a lane (an 8 KB row at k = 2 in one
+  // batch). Offsets past the row read zeros (the record count) and are not
+  // stored.
+  constexpr int U = KM >= 8 ? 2 : 16 / KM;
+  for (uint32_t base = (uint32_t)lane * 16; base < row_bytes; base += U * 64 * 16) {
+    u32x4 v[U][KM];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) v[j] = bload16<2>(src[j], off);   // each row is read once: nontemporal
-    float acc[V];
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+      for (int j = 0; j < KM; ++j) v[u][j] = bload16<2>(src[j], base + u * 1024);   // read once: nontemporal
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      float f[V];
-      unpack16(S(), v[j], f);
+    for (int u = 0; u < U; ++u) {
+      const uint32_t off = base + u * 1024;
+      if (off >= row_bytes) break;
+      float acc[V];
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = fmaf(g[j], f[i], acc[i]);
+      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        float f[V];
+        unpack16(S(), v[u][j], f);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = fmaf(g[j], f[i], acc[i]);
+      }
+      st16(dst + off, pack16(S(), acc));
     }
-    st16(dst + off, pack16(S(), acc));
   }
 }
 

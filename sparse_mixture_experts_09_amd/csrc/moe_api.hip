@@ -15,6 +15,8 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 8;
+constexpr int kMaxDim = 1 << 24;           // d and F
+constexpr int64_t kMaxTokens = (int64_t)1 << 31;   // T (T * k < 2^31 for the layer entry points)
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -64,7 +66,8 @@ int check_scalars(int64_t T, int d, int E, int k, float cf, int F, int dt, bool 
   if (!isfinite(cf) || cf < 0.0f) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (E > kMaxE || k > kMaxK) return MOE_ERR_UNSUPPORTED;
-  if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (T > ((((int64_t)1 << 31) - 1) / k)) return MOE_ERR_UNSUPPORTED;   // T * k < 2^31, without overflow
+  if (d > kMaxDim || F > kMaxDim) return MOE_ERR_UNSUPPORTED;           // buffer sizes fit 64 bits
   const int vec = dt == MOE_BF16 ? 8 : 4;
   if (d % vec != 0) return MOE_ERR_UNSUPPORTED;
   if (F > 0 && F % vec != 0) return MOE_ERR_UNSUPPORTED;
@@ -201,25 +204,26 @@ int moe_rows_max(int64_t T, int32_t E, int32_t k, float cf, int64_t* rows) {
   if (rows == nullptr) return MOE_ERR_INVALID_ARG;
   const int64_t cap = moe_capacity(T, E, k, cf);
   if (cap < 0) return MOE_ERR_INVALID_ARG;
+  if (T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
   *rows = rows_max_of(T, E, k, cap);
   return MOE_OK;
 }
 
 int moe_permute_workspace_bytes(int64_t T, int32_t E, size_t* bytes) {
   if (bytes == nullptr || T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
-  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (E > kMaxE || T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
   *bytes = permute_ws_bytes(T, E, false);
   return MOE_OK;
 }
 
 int moe_permute_priority_workspace_bytes(int64_t T, int32_t E, size_t* bytes) {
   if (bytes == nullptr || T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
-  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (E > kMaxE || T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
   *bytes = permute_ws_bytes(T, E, true);
   return MOE_OK;
 }
 
-int moe_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+int moe_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt,
                         size_t* bytes) {
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
   const int st = check_scalars(T, d, E, k, cf, F, dt, true);
@@ -229,7 +233,7 @@ int moe_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, in
   return MOE_OK;
 }
 
-int moe_ffn_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+int moe_ffn_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt,
                             size_t* bytes) {
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
   const int st = check_scalars(T, d, E, k, cf, F, dt, true);
@@ -238,7 +242,7 @@ int moe_ffn_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf
   return MOE_OK;
 }
 
-int moe_route_gating(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, int32_t gating,
+int moe_route_gating(int64_t T, int32_t d, int32_t E, int32_t k, int32_t dt, int32_t gating,
                      const void* x, const void* w_router, int32_t* topk_idx, float* topk_gate,
                      float* logits_opt, hipStream_t stream) {
   int st = check_scalars(T, d, E, k, 0.0f, -1, dt, false);
@@ -258,7 +262,7 @@ int moe_route_gating(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, i
                                        logits_opt, stream));
 }
 
-int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, const void* x,
+int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, int32_t dt, const void* x,
               const void* w_router, int32_t* topk_idx, float* topk_gate, float* logits_opt,
               hipStream_t stream) {
   return moe_route_gating(T, d, E, k, dt, MOE_GATING_TOPK_SOFTMAX, x, w_router, topk_idx, topk_gate,
@@ -267,7 +271,7 @@ int moe_route(int64_t T, int32_t d, int32_t E, int32_t k, moe_dtype dt, const vo
 
 // static_scratch: take the workspace from permute_scratch (ws / ws_bytes are
 // ignored) instead of the caller's buffer.
-static int permute_impl(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
+static int permute_impl(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t dt, const void* x,
                         const int32_t* topk_idx, const float* score, int64_t score_stride,
                         int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot_row,
                         int32_t* row_slot, void* x_perm, void* ws, size_t ws_bytes, hipStream_t stream,
@@ -318,7 +322,7 @@ static int permute_impl(int64_t T, int32_t d, int32_t E, int32_t k, float cf, mo
   return hip_status(e);
 }
 
-int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
+int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t dt, const void* x,
                 const int32_t* topk_idx, int32_t* expert_counts, int32_t* expert_offsets,
                 int32_t* slot_row, int32_t* row_slot, void* x_perm, void* ws, size_t ws_bytes,
                 hipStream_t stream) {
@@ -326,7 +330,7 @@ int moe_permute(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype 
                       row_slot, x_perm, ws, ws_bytes, stream);
 }
 
-int moe_permute_noalloc(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
+int moe_permute_noalloc(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t dt, const void* x,
                         const int32_t* topk_idx, int32_t* expert_counts, int32_t* expert_offsets,
                         int32_t* slot_row, int32_t* row_slot, void* x_perm, hipStream_t stream) {
   return permute_impl(T, d, E, k, cf, dt, x, topk_idx, nullptr, 0, expert_counts, expert_offsets, slot_row,
@@ -335,7 +339,7 @@ int moe_permute_noalloc(int64_t T, int32_t d, int32_t E, int32_t k, float cf, mo
 
 size_t moe_permute_noalloc_scratch_bytes(void) { return kPermuteScratchBytes; }
 
-int moe_permute_priority(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
+int moe_permute_priority(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t dt, const void* x,
                          const int32_t* topk_idx, const float* score, int64_t score_stride,
                          int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot_row,
                          int32_t* row_slot, void* x_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -344,7 +348,7 @@ int moe_permute_priority(int64_t T, int32_t d, int32_t E, int32_t k, float cf, m
                       slot_row, row_slot, x_perm, ws, ws_bytes, stream);
 }
 
-int moe_grouped_ffn(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+int moe_grouped_ffn(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt,
                     const void* x_perm, const int32_t* expert_offsets, const void* w_gate,
                     const void* w_up, const void* w_down, void* h_ws, void* out_perm, void* ws,
                     size_t ws_bytes, hipStream_t stream) {
@@ -376,7 +380,7 @@ int moe_grouped_ffn(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_
 }
 
 static int expert_gemm(int which, int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
-                       moe_dtype dt, const void* in, const int32_t* expert_offsets, const void* w0,
+                       int32_t dt, const void* in, const int32_t* expert_offsets, const void* w0,
                        const void* w1, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_scalars(T, d, E, k, cf, F, dt, true);
   if (st != MOE_OK) return st;
@@ -402,20 +406,20 @@ static int expert_gemm(int which, int64_t T, int32_t d, int32_t E, int32_t k, fl
   return hip_status(e);
 }
 
-int moe_expert_gate_up(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+int moe_expert_gate_up(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt,
                        const void* x_perm, const int32_t* expert_offsets, const void* w_gate,
                        const void* w_up, void* h, hipStream_t stream) {
   return expert_gemm(1, T, d, E, k, cf, F, dt, x_perm, expert_offsets, w_gate, w_up, h, nullptr, 0, stream);
 }
 
-int moe_expert_down(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+int moe_expert_down(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt,
                     const void* h, const int32_t* expert_offsets, const void* w_down, void* out_perm,
                     void* ws, size_t ws_bytes, hipStream_t stream) {
   return expert_gemm(2, T, d, E, k, cf, F, dt, h, expert_offsets, w_down, nullptr, out_perm, ws, ws_bytes,
                      stream);
 }
 
-int moe_unpermute_combine(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+int moe_unpermute_combine(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t dt,
                           const void* out_perm, const int32_t* slot_row, const float* topk_gate,
                           void* y, hipStream_t stream) {
   int st = check_scalars(T, d, E, k, cf, -1, dt, false);
@@ -432,7 +436,7 @@ int moe_unpermute_combine(int64_t T, int32_t d, int32_t E, int32_t k, float cf, 
   return hip_status(moe::launch_combine(dt == MOE_BF16, T, d, k, out_perm, slot_row, topk_gate, y, stream));
 }
 
-int moe_forward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+int moe_forward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt,
                    int32_t gating, int32_t fill_order, const void* x, const void* w_router,
                    const void* w_gate, const void* w_up, const void* w_down, void* y, int32_t* topk_idx_opt,
                    float* topk_gate_opt, int32_t* slot_row_opt, void* ws, size_t ws_bytes,
@@ -494,7 +498,7 @@ int moe_forward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t
   return hip_status(e);
 }
 
-int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+int moe_forward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt,
                 const void* x, const void* w_router, const void* w_gate, const void* w_up,
                 const void* w_down, void* y, int32_t* topk_idx_opt, float* topk_gate_opt,
                 int32_t* slot_row_opt, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -516,12 +520,12 @@ static int ec_rows(int64_t T, int E, int k, float cf, int64_t* C, int64_t* R) {
 
 int moe_route_expert_choice_workspace_bytes(int64_t T, int32_t E, size_t* bytes) {
   if (bytes == nullptr || T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
-  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (E > kMaxE || T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
   *bytes = round_up(moe::ec_select_bytes(T, E));
   return MOE_OK;
 }
 
-int moe_route_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt, const void* x,
+int moe_route_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t dt, const void* x,
                             const void* w_router, float* scores, int32_t* expert_tokens, int32_t* slot,
                             int32_t* expert_offsets, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_scalars(T, d, E, k, cf, -1, dt, false);
@@ -545,7 +549,7 @@ int moe_route_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf
   return hip_status(e);
 }
 
-int moe_gather_rows(int64_t T, int32_t d, int64_t R, moe_dtype dt, const void* x, const int32_t* row_token,
+int moe_gather_rows(int64_t T, int32_t d, int64_t R, int32_t dt, const void* x, const int32_t* row_token,
                     void* x_perm, hipStream_t stream) {
   if (T < 0 || d < 1 || R < 0 || (dt != MOE_F32 && dt != MOE_BF16)) return MOE_ERR_INVALID_ARG;
   if (d % (dt == MOE_BF16 ? 8 : 4) != 0) return MOE_ERR_UNSUPPORTED;
@@ -558,15 +562,16 @@ int moe_gather_rows(int64_t T, int32_t d, int64_t R, moe_dtype dt, const void* x
   return hip_status(moe::launch_gather_rows(dt == MOE_BF16, T, R, d, x, row_token, x_perm, stream));
 }
 
-int moe_ffn_rows_workspace_bytes(int64_t R_max, int32_t d, int32_t E, int32_t F, moe_dtype dt, size_t* bytes) {
+int moe_ffn_rows_workspace_bytes(int64_t R_max, int32_t d, int32_t E, int32_t F, int32_t dt, size_t* bytes) {
   if (bytes == nullptr || R_max < 0) return MOE_ERR_INVALID_ARG;
   const int st = check_scalars(0, d, E, 1, 0.0f, F, dt, true);
   if (st != MOE_OK) return st;
+  if (R_max >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   *bytes = ffn_ws_bytes(R_max, E, dt);
   return MOE_OK;
 }
 
-int moe_grouped_ffn_rows(int64_t R_max, int32_t d, int32_t E, int32_t F, moe_dtype dt, const void* x_perm,
+int moe_grouped_ffn_rows(int64_t R_max, int32_t d, int32_t E, int32_t F, int32_t dt, const void* x_perm,
                          const int32_t* expert_offsets, const void* w_gate, const void* w_up, const void* w_down,
                          void* h_ws, void* out_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (R_max < 0) return MOE_ERR_INVALID_ARG;
@@ -596,7 +601,7 @@ int moe_grouped_ffn_rows(int64_t R_max, int32_t d, int32_t E, int32_t F, moe_dty
   return hip_status(e);
 }
 
-int moe_combine_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, moe_dtype dt,
+int moe_combine_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t dt,
                               const void* out_perm, const int32_t* slot, const float* scores, void* y,
                               hipStream_t stream) {
   int st = check_scalars(T, d, E, k, cf, -1, dt, false);
@@ -640,7 +645,7 @@ static EcLayout ec_layout(int64_t T, int d, int E, int64_t R, int F, int dt) {
 }
 
 int moe_forward_expert_choice_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
-                                              moe_dtype dt, size_t* bytes) {
+                                              int32_t dt, size_t* bytes) {
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
   int st = check_scalars(T, d, E, k, cf, F, dt, true);
   if (st != MOE_OK) return st;
@@ -650,7 +655,7 @@ int moe_forward_expert_choice_workspace_bytes(int64_t T, int32_t d, int32_t E, i
   return MOE_OK;
 }
 
-int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt,
                               const void* x, const void* w_router, const void* w_gate, const void* w_up,
                               const void* w_down, void* y, float* scores_opt, int32_t* slot_opt, void* ws,
                               size_t ws_bytes, hipStream_t stream) {
@@ -729,7 +734,7 @@ static BwdLayout bwd_layout(int64_t T, int d, int E, int k, int64_t R_max, int F
   return L;
 }
 
-int moe_backward_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt,
+int moe_backward_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt,
                                  size_t* bytes) {
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
   int st = check_scalars(T, d, E, k, cf, F, dt, true);
@@ -739,7 +744,7 @@ int moe_backward_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, flo
   return MOE_OK;
 }
 
-int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, moe_dtype dt, const void* x,
+int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt, const void* x,
                  const void* w_router, const void* w_gate, const void* w_up, const void* w_down, const void* dy,
                  void* dx, void* dw_router, void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
                  hipStream_t stream) {

@@ -10,23 +10,26 @@
 //
 // The rank of (t, e) is the number of earlier tokens that chose e. It is
 // computed without atomics on the order, so the result is deterministic:
-//   1. hist:    per chunk of 256 tokens, per expert counts (LDS counters;
-//               counts do not depend on the order of the increments).
+//   1. count:   per chunk of 256 tokens: inside each wavefront, for every
+//               expert present, a ballot of the lanes (tokens) that chose it
+//               and a popcount of the lanes below give the in-wave rank; the
+//               wavefront totals in LDS give the in-chunk rank of every slot
+//               and the chunk's count per expert. The in-chunk rank goes to
+//               slot_row for now, packed with its chunk.
 //   2. scan:    one block: per expert, the exclusive prefix of the chunk
 //               counts over chunks, the demand, kept = min(demand, cap), and
 //               the exclusive prefix of kept over experts (the offsets).
-//   3. rank:    per chunk: inside each wavefront, for every expert, a ballot
-//               of the lanes (tokens) that chose it and a popcount of the
-//               lanes below give the in-wave rank; wave totals in LDS give
-//               the in-chunk rank; plus the chunk prefix from step 2. Writes
-//               slot_row (row or -1) and row_slot.
-//   4. scatter: one wavefront per token (per 1 KB piece of its row below
-//               2048 tokens) reads the row once with 16-byte loads and writes
-//               it to each of the token's kept rows.
-// Up to 1024 tokens, steps 1-3 run as one 1024-thread workgroup instead
-// (perm_layout_kernel): the same ballot ranks per wavefront, the per-expert
-// prefix over the wavefronts, the demand and the offsets, all in LDS, so the
-// layout costs one launch.
+//   3. place:   one wavefront per token: its lanes 0..k-1 turn the packed
+//               in-chunk ranks into rows (offsets + chunk prefix + rank, -1
+//               past the capacity) and write slot_row and row_slot, while
+//               the token's row, loaded first, is written to each kept row
+//               with 16-byte stores (the copy is skipped when the grouped
+//               GEMM gathers the rows itself).
+// Up to 1024 tokens, steps 1-2 and the rows run as one 1024-thread workgroup
+// instead (perm_layout_kernel): the same ballot ranks per wavefront, the
+// per-expert prefix over the wavefronts, the demand and the offsets, all in
+// LDS; the copy follows with a wavefront per 1 KB piece of a row
+// (perm_scatter_kernel), for parallelism at few tokens.
 //
 // Batch Priority Routing ("Scaling Vision with Sparse Mixture of Experts",
 // section "Priority Routing": tokens are taken by an importance score rather
@@ -49,25 +52,82 @@ namespace {
 
 constexpr int kChunk = 256;   // tokens per chunk = threads per block in hist / rank
 
-// order: token at each position of the arrival sequence (nullptr: identity)
-__global__ __launch_bounds__(256) void perm_hist_kernel(int64_t T, int E, int k,
-                                                        const int32_t* __restrict__ idx,
-                                                        const int32_t* __restrict__ order,
-                                                        int32_t* __restrict__ chunk_counts) {
-  __shared__ int cnt[256];
-  const int tid = threadIdx.x;
-  cnt[tid] = 0;
-  __syncthreads();
+// In-wavefront ranks of the slots a lane holds: one ballot per distinct
+// expert present among the wavefront's pending slots. ex[j] = -1 for a slot
+// that takes no part. Returns nothing; fills rk[] and, from lane 0, the
+// wavefront's count of each expert it saw into wcnt[e].
+__device__ __forceinline__ void wave_ranks(const int (&ex)[8], int (&rk)[8], int* wcnt) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t pend = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pend |= (ex[j] >= 0 ? 1u : 0u) << j;
+  for (;;) {
+    const uint64_t busy = __ballot(pend != 0);
+    if (busy == 0) break;
+    int mine = -1;
+#pragma unroll
+    for (int j = 7; j >= 0; --j)
+      if ((pend >> j) & 1) mine = ex[j];
+    const int e = __builtin_amdgcn_readlane(mine, __ffsll((long long)busy) - 1);
+    bool has = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) has |= ((pend >> j) & 1) && ex[j] == e;
+    const uint64_t m = __ballot(has);
+    const int r = __popcll(m & below);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (((pend >> j) & 1) && ex[j] == e) {
+        rk[j] = r;
+        pend &= ~(1u << j);
+      }
+    if (lane == 0) wcnt[e] = __popcll(m);
+  }
+}
+
+// Step 1 (chunks of 256 positions of the arrival sequence; order: token at
+// each position, nullptr for token order). Writes chunk_counts[chunk][e] and,
+// for every slot, packed[t * k + j] = (chunk << 8) | in-chunk rank (a chunk
+// holds an expert at most 256 times, so the rank fits 8 bits), -1 for an
+// expert id outside [0, E).
+__global__ __launch_bounds__(256) void perm_count_kernel(int64_t T, int E, int k,
+                                                         const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ order,
+                                                         int32_t* __restrict__ chunk_counts,
+                                                         int32_t* __restrict__ packed) {
+  extern __shared__ int wcnt[];   // [4][E]: wavefront counts, then their prefix over the wavefronts
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t p = (int64_t)blockIdx.x * kChunk + tid;
-  if (p < T) {
-    const int64_t t = order ? (int64_t)order[p] : p;
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j];
-      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  const bool valid = p < T;
+  const int64_t t = valid ? (order ? (int64_t)order[p] : p) : 0;
+  int ex[8], rk[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int e = (valid && j < k) ? idx[t * k + j] : -1;
+    ex[j] = (e >= 0 && e < E) ? e : -1;
+    rk[j] = 0;
+  }
+  for (int i = tid; i < 4 * E; i += 256) wcnt[i] = 0;
+  __syncthreads();
+  wave_ranks(ex, rk, wcnt + wave * E);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = wcnt[w * E + e];
+      wcnt[w * E + e] = run;
+      run += c;
     }
+    chunk_counts[(int64_t)blockIdx.x * E + e] = run;
   }
   __syncthreads();
-  if (tid < E) chunk_counts[(int64_t)blockIdx.x * E + tid] = cnt[tid];
+  if (!valid) return;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    packed[t * k + j] = ex[j] >= 0 ? (int32_t)((blockIdx.x << 8) | (wcnt[wave * E + ex[j]] + rk[j])) : -1;
+  }
 }
 
 // Inclusive scan of one int per thread over a 256-thread block.
@@ -94,10 +154,17 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int nchunks, int E, int6
   const int e = threadIdx.x;
   int running = 0;
   if (e < E) {
-    for (int b = 0; b < nchunks; ++b) {
-      const int c = chunk_counts[(int64_t)b * E + e];
-      chunk_counts[(int64_t)b * E + e] = running;   // becomes the chunk base
-      running += c;
+    // 16 chunks at a time: the loads are issued together, then the prefix
+    // replaces them (one memory round trip per 16 chunks, not per chunk)
+    for (int b0 = 0; b0 < nchunks; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = b0 + i < nchunks ? chunk_counts[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (b0 + i < nchunks) chunk_counts[(int64_t)(b0 + i) * E + e] = running;   // becomes the chunk base
+        running += c[i];
+      }
     }
   }
   const int kept = e < E ? (int)min<int64_t>(running, cap) : 0;
@@ -109,52 +176,64 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(int nchunks, int E, int6
   }
 }
 
-__global__ __launch_bounds__(256) void perm_rank_kernel(int64_t T, int E, int k, int64_t cap,
-                                                        const int32_t* __restrict__ idx,
-                                                        const int32_t* __restrict__ order,
-                                                        const int32_t* __restrict__ chunk_base,
-                                                        const int32_t* __restrict__ expert_offsets,
-                                                        int32_t* __restrict__ slot_row,
-                                                        int32_t* __restrict__ row_slot) {
-  __shared__ int wave_cnt[4][256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t p = (int64_t)blockIdx.x * kChunk + tid;
-  const bool valid = p < T;
-  const int64_t t = !valid ? 0 : (order ? (int64_t)order[p] : p);
-  int ex[8], rk[8];
+// Step 3: one wavefront per token. The token's row (all of it, in groups of
+// 8 KB) is loaded before the row arithmetic so the copy does not wait on it;
+// lanes 0..k-1 then read their slot's packed in-chunk rank (written by step
+// 1 into slot_row, read and replaced by the same lane here), add the chunk
+// prefix and the expert's offset, apply the capacity, and write slot_row and
+// row_slot; the rows are broadcast and the row is stored to each kept one.
+// x_perm == nullptr: the layout only (the grouped GEMM gathers the rows).
+__global__ __launch_bounds__(256) void perm_place_kernel(int64_t T, int E, int k, int64_t cap, size_t row_bytes,
+                                                         const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ chunk_base,
+                                                         const int32_t* __restrict__ expert_offsets,
+                                                         int32_t* __restrict__ slot_row,
+                                                         int32_t* __restrict__ row_slot,
+                                                         const char* __restrict__ x, char* __restrict__ x_perm) {
+  constexpr int G = 8;   // 1 KB pieces per lane group in flight
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const char* src = x + (size_t)t * row_bytes;
+  const size_t first = (size_t)lane * 16;
+  u32x4 v[G];
+  if (x_perm != nullptr) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    ex[j] = (valid && j < k) ? idx[t * k + j] : -1;
-    rk[j] = 0;
+    for (int g = 0; g < G; ++g)
+      if (first + (size_t)g * 1024 < row_bytes) v[g] = ld16(src + first + (size_t)g * 1024);
   }
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int e = 0; e < E; ++e) {
-    bool has = false;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) has |= (ex[j] == e);
-    const uint64_t m = __ballot(has);
-    const int r = __popcll(m & below);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (ex[j] == e) rk[j] = r;
-    if (lane == 0) wave_cnt[wave][e] = __popcll(m);
-  }
-  __syncthreads();
-  if (!valid) return;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    const int e = ex[j];
-    int row = -1;
-    if (e >= 0 && e < E) {
-      int rank = chunk_base[(int64_t)blockIdx.x * E + e] + rk[j];
-      for (int w = 0; w < wave; ++w) rank += wave_cnt[w][e];
+  int row = -1;
+  if (lane < k) {
+    const int e = idx[t * k + lane];
+    const int pk = slot_row[t * k + lane];
+    if (pk >= 0 && e >= 0 && e < E) {
+      const int rank = chunk_base[(int64_t)(pk >> 8) * E + e] + (pk & 255);
       if (rank < cap) {
         row = expert_offsets[e] + rank;
-        row_slot[row] = (int32_t)(t * k + j);
+        row_slot[row] = (int32_t)(t * k + lane);
       }
     }
-    slot_row[t * k + j] = row;
+    slot_row[t * k + lane] = row;
+  }
+  if (x_perm == nullptr) return;
+  int rows[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rows[j] = j < k ? __shfl(row, j) : -1;
+  for (size_t base = 0; base < row_bytes; base += (size_t)G * 1024) {
+    if (base > 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        if (base + first + (size_t)g * 1024 < row_bytes) v[g] = ld16(src + base + first + (size_t)g * 1024);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const size_t off = base + first + (size_t)g * 1024;
+      if (off < row_bytes) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (rows[j] >= 0) st16(x_perm + (size_t)rows[j] * row_bytes + off, v[g]);
+      }
+    }
   }
 }
 
@@ -501,24 +580,23 @@ hipError_t launch_permute(bool bf16, int64_t T, int d, int E, int k, int64_t cap
     const size_t lds = (size_t)(17 * E + 16) * sizeof(int);
     hipLaunchKernelGGL(perm_layout_kernel, dim3(1), dim3(1024), lds, s, (int)T, E, k, cap, idx, order,
                        expert_counts, expert_offsets, slot_row, row_slot);
-  } else {
-    const int64_t nchunks = permute_chunks(T);
-    hipLaunchKernelGGL(perm_hist_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, E, k, idx, order,
-                       chunk_counts);
-    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, s, (int)nchunks, E, cap, chunk_counts,
-                       expert_counts, expert_offsets);
-    hipLaunchKernelGGL(perm_rank_kernel, dim3((unsigned)nchunks), dim3(256), 0, s, T, E, k, cap, idx, order,
-                       chunk_counts, expert_offsets, slot_row, row_slot);
+    if (x_perm == nullptr) return hipGetLastError();   // the layout only: the GEMM gathers the rows
+    const size_t row_bytes = (size_t)d * (bf16 ? 2 : 4);
+    const int pieces = (int)((row_bytes + 1023) / 1024);
+    // few tokens: a wavefront per 1 KB piece, for parallelism
+    const int64_t waves = T * pieces;
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, T, k, row_bytes,
+                       pieces, 1, reinterpret_cast<const char*>(x), slot_row, reinterpret_cast<char*>(x_perm));
+    return hipGetLastError();
   }
-  if (x_perm == nullptr) return hipGetLastError();   // the layout only: the GEMM gathers the rows
-  const size_t row_bytes = (size_t)d * (bf16 ? 2 : 4);
-  const int pieces = (int)((row_bytes + 1023) / 1024);
-  // few tokens: a wavefront per piece, for parallelism; many: a wavefront per
-  // row (measured faster at 4096 tokens of 8 KB)
-  const int ppw = T < 2048 ? 1 : pieces;
-  const int64_t waves = T * (pieces / ppw);
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, T, k, row_bytes,
-                     pieces, ppw, reinterpret_cast<const char*>(x), slot_row, reinterpret_cast<char*>(x_perm));
+  const int64_t nchunks = permute_chunks(T);
+  hipLaunchKernelGGL(perm_count_kernel, dim3((unsigned)nchunks), dim3(256), (size_t)4 * E * sizeof(int), s, T, E,
+                     k, idx, order, chunk_counts, slot_row);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, s, (int)nchunks, E, cap, chunk_counts, expert_counts,
+                     expert_offsets);
+  hipLaunchKernelGGL(perm_place_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, T, E, k, cap,
+                     (size_t)d * (bf16 ? 2 : 4), idx, chunk_counts, expert_offsets, slot_row, row_slot,
+                     reinterpret_cast<const char*>(x), reinterpret_cast<char*>(x_perm));
   return hipGetLastError();
 }
 

@@ -290,3 +290,27 @@ def test_backward_entry_points_validate():
     assert L.moe_backward(*a) == UNS
     a = list(bw); a[0] = 0
     assert L.moe_backward(*a) == OK
+
+
+def test_extreme_scalars_are_rejected_or_exact():
+    """Sizes near the integer limits: refused with a status (the products in
+    the checks must not overflow) or answered exactly."""
+    L = moe.lib()
+    big = 1 << 62
+    assert L.moe_capacity(big, 8, 2, 0.0) == big                 # dropless: cap = T
+    assert L.moe_capacity(big, 8, 2, 1.0) == big // 4
+    r = ctypes.c_int64()
+    assert L.moe_rows_max(big, 8, 2, 1.0, ctypes.byref(r)) == UNS
+    assert L.moe_rows_max((1 << 31) - 1, 8, 2, 1.0, ctypes.byref(r)) == OK and r.value == 2 * ((1 << 31) - 1)
+    b = ctypes.c_size_t()
+    assert L.moe_workspace_bytes(big, 4096, 8, 2, 0.0, 14336, 1, ctypes.byref(b)) == UNS
+    assert L.moe_workspace_bytes((1 << 30) - 1, 4096, 8, 2, 0.0, 14336, 1, ctypes.byref(b)) == OK
+    assert L.moe_workspace_bytes(1 << 30, 4096, 8, 2, 0.0, 14336, 1, ctypes.byref(b)) == UNS   # T * k = 2^31
+    for fn in ("moe_permute_workspace_bytes", "moe_permute_priority_workspace_bytes",
+               "moe_route_expert_choice_workspace_bytes"):
+        assert getattr(L, fn)(big, 8, ctypes.byref(b)) == UNS, fn
+        assert getattr(L, fn)((1 << 63) - 1, 8, ctypes.byref(b)) == UNS, fn
+    assert L.moe_ffn_rows_workspace_bytes(big, 64, 4, 128, BF16, ctypes.byref(b)) == UNS
+    assert L.moe_route(big, 64, 4, 2, F32, A[0], A[1], A[2], A[3], None, None) == UNS
+    assert L.moe_route(8, 1 << 25, 4, 2, F32, A[0], A[1], A[2], A[3], None, None) == UNS
+    assert L.moe_capacity((1 << 63) - 1, 256, 8, 1e30) == (1 << 63) - 1

@@ -171,6 +171,35 @@ def test_permute_layout_sizes(T, d, E, k, cf, dtype, seed):
     assert torch.equal(out["x_perm"][:R].cpu(), a["x"][torch.from_numpy(row_slot.astype(np.int64)) // k])
 
 
+@pytest.mark.parametrize("T", [300, 3000])
+def test_permute_repeated_or_out_of_range_ids_stay_in_bounds(T):
+    """Caller-supplied indices outside the contract (a repeated expert id in a
+    token, ids outside [0, E)): the layout is unspecified, but every row the
+    call reports lies inside x_perm, kept rows are a prefix of it, every kept
+    row holds its token's row of x and an out-of-range id is a dropped slot.
+    Both layout paths (one workgroup up to 1024 tokens, chunked above)."""
+    E, k, d, cf = 8, 3, 64, 0.0
+    rng = np.random.default_rng(T)
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    idx[::7, 1] = idx[::7, 0]                   # repeats
+    idx[::11, 2] = E + 5                        # out of range
+    idx[::13, 0] = -3
+    x = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).to(torch.bfloat16)
+    R_max = moe.moe_rows_max(T, E, k, cf)
+    out = moe.moe_permute(dev(x), dev(torch.from_numpy(idx)), E, cf)
+    torch.cuda.synchronize()
+    off = host(out["expert_offsets"])
+    R = int(off[-1])
+    assert 0 <= R <= R_max and np.all(np.diff(off) >= 0)
+    srow = host(out["slot_row"])
+    assert np.all((srow >= -1) & (srow < R))
+    bad = (idx < 0) | (idx >= E)
+    assert np.all(srow[bad] == -1)
+    tt, jj = np.nonzero(srow >= 0)
+    xp = out["x_perm"][:R].cpu()
+    assert torch.equal(xp[torch.from_numpy(srow[tt, jj].astype(np.int64))], x[torch.from_numpy(tt)])
+
+
 @pytest.mark.parametrize("case", SMALL + NAMED_SMALL, ids=case_id)
 def test_grouped_ffn(case):
     w, a = workload(case)
