@@ -545,6 +545,39 @@ def topk_softmax_grad(gates: np.ndarray, dg: np.ndarray) -> np.ndarray:
     return gates * (dg - (gates * dg).sum(axis=1, keepdims=True))
 
 
+def switch_softmax_grad(logits: np.ndarray, idx: np.ndarray, dg: np.ndarray, scaled: bool) -> np.ndarray:
+    """Gradient through the Switch gates g_j = s p[S_j], p = softmax over all E
+    logits, s = E/k when scaled else 1 ([TALK] upcycling part). With
+    D[e] = dg_j where e = S_j (0 for experts not chosen), the softmax's
+    Jacobian gives, for every expert e (chosen or not):
+        dl[e] = s p[e] (D[e] - sum_j p[S_j] dg_j).
+    Returns the dense [T, E] gradient."""
+    l = np.asarray(logits, np.float64)
+    T, E = l.shape
+    k = idx.shape[1]
+    z = np.exp(l - l.max(axis=1, keepdims=True))
+    p = z / z.sum(axis=1, keepdims=True)
+    D = np.zeros((T, E))
+    np.put_along_axis(D, idx.astype(np.int64), dg, axis=1)
+    s = E / k if scaled else 1.0
+    return s * p * (D - (p * D).sum(axis=1, keepdims=True))
+
+
+def gate_grad_dense(logits: np.ndarray, idx: np.ndarray, gates: np.ndarray, dg: np.ndarray,
+                    gating: str) -> np.ndarray:
+    """dL/dl [T, E] for a gate rule, given dg [T, k] = dL/dg: Softmax(TopK)
+    puts topk_softmax_grad on the chosen logits (the others get 0); the
+    Switch rules spread switch_softmax_grad over every logit."""
+    T, E = logits.shape
+    if gating == "topk_softmax":
+        dl = np.zeros((T, E))
+        np.put_along_axis(dl, idx.astype(np.int64), topk_softmax_grad(gates, dg), axis=1)
+        return dl
+    if gating in ("softmax_topk", "softmax_topk_scaled"):
+        return switch_softmax_grad(logits, idx, dg, gating == "softmax_topk_scaled")
+    raise ValueError(f"unknown gating {gating!r}")
+
+
 BACKWARD_ROUNDING_POINTS = ("a", "b", "d_o", "da", "db", "dx_perm")
 
 
@@ -558,24 +591,28 @@ def hold(v: np.ndarray, storage: str, point: str) -> np.ndarray:
 
 
 def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: str,
-             weight_grad_experts=None, idx=None) -> dict:
-    """Gradients of L = <dy, y> for the token-choice layer with Softmax(TopK)
-    gates and token-order capacity, with respect to x and every weight.
+             weight_grad_experts=None, idx=None, gating: str = "topk_softmax", bpr: bool = False) -> dict:
+    """Gradients of L = <dy, y> for the token-choice layer, with respect to x
+    and every weight. gating and bpr select the gate rule and the capacity
+    fill order as in `forward`; the fill order is a discrete decision of the
+    forward pass and passes no gradient.
 
     Forward (as `forward`): l = x W_g^T; S = TopK(l); g = softmax(l_S);
     a = x_perm W_gate^T, b = x_perm W_up^T; h = st(silu(a) b); o = st(h W_down^T);
     y = st(sum_j g_j o_j).  Backward, per kept row r = slot (t, j) of expert e:
       d_o[r]   = st(g_j dy[t])
       dg[t,j]  = <dy[t], o[r]>                  (0 for a dropped slot)
-      dl[t,S_j]= g_j (dg_j - sum_j' g_j' dg_j')  (softmax over the chosen k)
+      dl[t,:]  = gate_grad_dense(l, S, g, dg, gating): for Softmax(TopK)
+                 dl[t,S_j] = g_j (dg_j - sum_j' g_j' dg_j') and 0 elsewhere;
+                 for the Switch rules every logit gets s p_e (D_e - sum p dg)
       dh[r]    = d_o[r] W_down[e]
       da[r]    = st(dh * b_st * silu'(a_st)),  db[r] = st(dh * silu(a_st))
                  with a_st = st(a), b_st = st(b)
       dx_perm  = st(da W_gate[e] + db W_up[e])
       dW_gate[e] = st(sum_r da[r]^T x_perm[r]),  dW_up[e] = st(sum_r db[r]^T x_perm[r])
       dW_down[e] = st(sum_r d_o[r]^T h[r])
-      dW_g[e]  = st(sum over (t, j) with S_j = e of dl[t, j] x[t])
-      dx[t]    = st(sum_j dl[t, j] W_g[S_j] + sum over kept j of dx_perm[slot (t, j)])
+      dW_g[e]  = st(sum_t dl[t, e] x[t])
+      dx[t]    = st(sum_e dl[t, e] W_g[e] + sum over kept j of dx_perm[slot (t, j)])
 
     weight_grad_experts: None for the expert weight gradients of every expert;
     otherwise a list of experts, and dW_gate, dW_up and dW_down hold only theirs,
@@ -588,7 +625,7 @@ def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: 
     E = w_router.shape[0]
     F = w_gate.shape[1]
     wr = as_f64(w_router)
-    r = forward(x, w_router, w_gate, w_up, w_down, k, cf, storage, idx=idx)
+    r = forward(x, w_router, w_gate, w_up, w_down, k, cf, storage, idx=idx, gating=gating, bpr=bpr)
     idx, gates, slot_row, offsets, row_slot = r["topk_idx"], r["topk_gate"], r["slot_row"], r["offsets"], r["row_slot"]
     R = int(offsets[E])
     dy64 = as_f64(dy)
@@ -614,7 +651,8 @@ def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: 
     kept = slot_row >= 0
     tt, kk = np.nonzero(kept)
     dg[tt, kk] = np.einsum("ij,ij->i", dy64[tt], o[slot_row[tt, kk]])
-    dl = topk_softmax_grad(gates, dg)
+    dl_dense = gate_grad_dense(r["logits"], idx, gates, dg, gating)
+    dl = np.take_along_axis(dl_dense, idx.astype(np.int64), axis=1)   # the chosen experts' entries
     dx_perm = np.empty((R, d))
     da_rows = np.empty((R, F))
     db_rows = np.empty((R, F))
@@ -639,13 +677,11 @@ def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: 
             dW_gate[i] = da.T @ xr
             dW_up[i] = db.T @ xr
             dW_down[i] = d_o[lo:hi].T @ h[lo:hi]
-    dW_g = np.zeros((E, d))
-    for j in range(k):
-        np.add.at(dW_g, idx[:, j].astype(np.int64), dl[:, j][:, None] * x64)
-    dx = np.einsum("tj,tjd->td", dl, wr[idx.astype(np.int64)])
+    dW_g = dl_dense.T @ x64
+    dx = dl_dense @ wr
     for j in range(k):
         m = slot_row[:, j] >= 0
         dx[m] += dx_perm[slot_row[m, j]]
     return dict(forward=r, dx=store(dx, storage), dW_g=store(dW_g, storage), dW_gate=store(dW_gate, storage),
-                dW_up=store(dW_up, storage), dW_down=store(dW_down, storage), dl=dl, dg=dg, d_o=d_o,
+                dW_up=store(dW_up, storage), dW_down=store(dW_down, storage), dl=dl, dl_dense=dl_dense, dg=dg, d_o=d_o,
                 a_st=a_st, b_st=b_st, h=h, o=o, da=da_rows, db=db_rows, dx_perm=dx_perm)

@@ -588,8 +588,32 @@ def check_ec_float32_decision():
 # backward pass
 # ---------------------------------------------------------------------------
 
-def _loss(x, wr, wg, wu, wd, dy, k, cf):
-    return float((orc.forward(x, wr, wg, wu, wd, k, cf, "f64")["y"] * dy).sum())
+def _loss(x, wr, wg, wu, wd, dy, k, cf, gating="topk_softmax", bpr=False):
+    return float((orc.forward(x, wr, wg, wu, wd, k, cf, "f64", gating=gating, bpr=bpr)["y"] * dy).sum())
+
+
+def _fd_check(x, wr, wg, wu, wd, dy, k, cf, gating="topk_softmax", bpr=False, eps=1e-6):
+    """Every gradient entry against a central difference of L = <dy, y>; the
+    routing, the drops and (with bpr) the fill order must not move under the
+    step, which the caller's inputs make sure of and this checks."""
+    g = orc.backward(x, wr, wg, wu, wd, dy, k, cf, "f64", gating=gating, bpr=bpr)
+    base = g["forward"]["slot_row"]
+    params = {"dx": x, "dW_g": wr, "dW_gate": wg, "dW_up": wu, "dW_down": wd}
+    for name, arr in params.items():
+        flat = arr.reshape(-1)
+        num = np.empty(flat.size)
+        for i in range(flat.size):
+            keep = flat[i]
+            vals = []
+            for sgn in (1, -1):
+                flat[i] = keep + sgn * eps
+                vals.append(_loss(x, wr, wg, wu, wd, dy, k, cf, gating, bpr))
+            flat[i] = keep
+            num[i] = (vals[0] - vals[1]) / (2 * eps)
+        assert np.allclose(g[name].reshape(-1), num, rtol=1e-6, atol=1e-7), (name, gating, bpr)
+    again = orc.forward(x, wr, wg, wu, wd, k, cf, "f64", gating=gating, bpr=bpr)
+    assert np.array_equal(again["slot_row"], base)
+    return g
 
 
 def check_backward_finite_differences():
@@ -622,6 +646,60 @@ def check_backward_finite_differences():
                 flat[i] = keep
                 num[i] = (lp - lm) / (2 * eps)
             assert np.allclose(g[name].reshape(-1), num, rtol=1e-6, atol=1e-7), name
+
+
+def check_backward_gating_finite_differences():
+    """The Switch gate rules (every logit gets gradient through the softmax
+    over all experts; rescaled by E/k or not) and Batch Priority Routing
+    (fill order by the top-1 gate: a discrete decision, no gradient), each on
+    tiny layers with capacity drops, against central differences."""
+    for (T, d, E, k, F, cf, seed, gating, bpr) in [
+            (12, 6, 4, 2, 5, 0.75, 31, "softmax_topk", False),
+            (10, 5, 4, 1, 6, 0.5, 32, "softmax_topk_scaled", False),
+            (12, 6, 5, 2, 5, 0.6, 33, "topk_softmax", True),
+            (11, 5, 4, 2, 4, 0.75, 34, "softmax_topk_scaled", True)]:
+        rng = np.random.default_rng(seed)
+        x = rng.standard_normal((T, d))
+        wr = rng.standard_normal((E, d))
+        wg = rng.standard_normal((E, F, d)) / math.sqrt(d)
+        wu = rng.standard_normal((E, F, d)) / math.sqrt(d)
+        wd = rng.standard_normal((E, d, F)) / math.sqrt(F)
+        dy = rng.standard_normal((T, d))
+        g = _fd_check(x, wr, wg, wu, wd, dy, k, cf, gating, bpr)
+        assert (g["forward"]["slot_row"] < 0).any()
+        if gating != "topk_softmax":
+            # under the Switch rules every logit of a token with a kept slot gets gradient,
+            # chosen or not; a token with every slot dropped gets none
+            live = (g["forward"]["slot_row"] >= 0).any(axis=1)
+            assert np.all(np.abs(g["dl_dense"][live]) > 0) and np.all(g["dl_dense"][~live] == 0)
+
+
+def check_backward_gating_autograd():
+    """torch autograd through a dense evaluation with the oracle's routing,
+    fill and drops held fixed, for the Switch rules and Batch Priority
+    Routing (gates s * softmax(l)[S_j] from the library softmax)."""
+    for (T, E, k, cf, gating, bpr) in [(30, 5, 2, 0.75, "softmax_topk", False), (25, 4, 1, 0.5, "softmax_topk_scaled", True),
+                                       (28, 6, 3, 0.8, "topk_softmax", True)]:
+        x, wr, wg, wu, wd = small_layer(T=T, E=E, k=k)
+        dy = np.random.default_rng(7).standard_normal(x.shape)
+        g = orc.backward(x, wr, wg, wu, wd, dy, k, cf, "f64", gating=gating, bpr=bpr)
+        fw = g["forward"]
+        idx = torch.from_numpy(fw["topk_idx"].astype(np.int64))
+        kept = torch.from_numpy(fw["slot_row"] >= 0)
+        tx, twr, twg, twu, twd = (torch.tensor(a, requires_grad=True) for a in (x, wr, wg, wu, wd))
+        l = tx @ twr.T
+        if gating == "topk_softmax":
+            gate = torch.softmax(torch.gather(l, 1, idx), dim=1)
+        else:
+            gate = torch.gather(torch.softmax(l, dim=1), 1, idx) * (E / k if gating.endswith("scaled") else 1.0)
+        y = torch.zeros_like(tx)
+        for e in range(E):
+            h = torch.nn.functional.silu(tx @ twg[e].T) * (tx @ twu[e].T)
+            w = ((idx == e) & kept).double() * gate
+            y = y + w.sum(1, keepdim=True) * (h @ twd[e].T)
+        (y * torch.from_numpy(dy)).sum().backward()
+        for name, t in [("dx", tx), ("dW_g", twr), ("dW_gate", twg), ("dW_up", twu), ("dW_down", twd)]:
+            assert np.allclose(g[name], t.grad.numpy(), rtol=1e-10, atol=1e-12), (name, gating, bpr)
 
 
 def check_backward_autograd():
@@ -685,7 +763,7 @@ def assert_bf16_close(mine, ref, what, min_equal=0.99):
     assert eq >= min_equal, f"{what}: only {eq:.4f} identical"
 
 
-def torch_backward_bf16(x, wr, wg, wu, wd, dy, k, cf):
+def torch_backward_bf16(x, wr, wg, wu, wd, dy, k, cf, gating="topk_softmax", bpr=False):
     """The backward pass of a bf16 layer, evaluated slot by slot in torch
     float64, rounding to bf16 (torch's float32 -> bfloat16 conversion) at the
     points where the layer holds a value in its storage type: a and b as the
@@ -699,12 +777,22 @@ def torch_backward_bf16(x, wr, wg, wu, wd, dy, k, cf):
     E, F = WG.shape[0], WG.shape[1]
     l = X @ WR.T
     idx = torch.sort(l.to(torch.float32), dim=1, descending=True, stable=True).indices[:, :k]
-    lS = torch.gather(l, 1, idx).detach().requires_grad_(True)
-    g = torch.softmax(lS, dim=1)
+    if gating == "topk_softmax":
+        lS = torch.gather(l, 1, idx).detach().requires_grad_(True)
+        g = torch.softmax(lS, dim=1)
+    else:
+        lS = l.detach().clone().requires_grad_(True)
+        g = torch.gather(torch.softmax(lS, dim=1), 1, idx) * (E / k if gating.endswith("scaled") else 1.0)
     cap = T if np.float32(cf) == 0 else min(T, math.ceil(float(np.float32(cf)) * T * k / E))
+    # arrival order: token order, or (BPR) by descending float32 top-1 gate, ties by token
+    order = (torch.sort(-g.detach()[:, 0].to(torch.float32), stable=True).indices if bpr
+             else torch.arange(T))
     onehot = torch.zeros((T, E), dtype=torch.int64)
     onehot.scatter_(1, idx, 1)
-    before = torch.cumsum(onehot, 0) - onehot
+    oh = onehot[order]
+    before_in_order = torch.cumsum(oh, 0) - oh
+    before = torch.empty_like(before_in_order)
+    before[order] = before_in_order
     rank = torch.gather(before, 1, idx)
     kept = rank < cap
     gd = g.detach()
@@ -741,15 +829,16 @@ def torch_backward_bf16(x, wr, wg, wu, wd, dy, k, cf):
                          ("dx_perm", dxp)):
                 out[n][(t, j)] = v.numpy()
     g.backward(dg)
-    dl = lS.grad
-    dWg = torch.zeros_like(WR)
-    for t in range(T):
-        for j in range(k):
-            e = int(idx[t, j])
-            dWg[e] += dl[t, j] * X[t]
-            dx[t] += dl[t, j] * WR[e]
+    dl = torch.zeros((T, E), dtype=torch.float64)
+    if gating == "topk_softmax":
+        dl.scatter_(1, idx, lS.grad)
+    else:
+        dl = lS.grad
+    dWg = dl.T @ X
+    dx += dl @ WR
     res = dict(dx=bf(dx).numpy(), dW_g=bf(dWg).numpy(), dW_gate=bf(dWgate).numpy(), dW_up=bf(dWup).numpy(),
-               dW_down=bf(dWdown).numpy(), dl=dl.numpy(), idx=idx.numpy(), kept=kept.numpy())
+               dW_down=bf(dWdown).numpy(), dl=dl.numpy(), idx=idx.numpy(), kept=kept.numpy(),
+               rank=rank.numpy())
     res.update(out)
     return res
 
@@ -761,11 +850,15 @@ def check_backward_rounding_points_bf16():
     values within one bf16 step of torch's, and almost all identical. With a
     rounding point left out, the intermediate is no bf16 value, or the
     gradients drift by more than rounding-order noise."""
-    for (T, E, k, cf, seed) in [(24, 4, 2, 0.75, 21), (16, 3, 1, 0.0, 22), (20, 5, 3, 1.0, 23)]:
+    for (T, E, k, cf, seed, gating, bpr) in [(24, 4, 2, 0.75, 21, "topk_softmax", False),
+                                             (16, 3, 1, 0.0, 22, "topk_softmax", False),
+                                             (20, 5, 3, 1.0, 23, "topk_softmax", False),
+                                             (24, 4, 2, 0.75, 24, "softmax_topk_scaled", True),
+                                             (20, 5, 2, 0.6, 25, "softmax_topk", False)]:
         x, wr, wg, wu, wd = small_layer(T=T, E=E, k=k, seed=seed, dtype="bf16")
         dy = torch.from_numpy(np.random.default_rng(seed).standard_normal(x.shape)).to(torch.bfloat16).double().numpy()
-        g = orc.backward(x, wr, wg, wu, wd, dy, k, cf, "bf16")
-        ref = torch_backward_bf16(x, wr, wg, wu, wd, dy, k, cf)
+        g = orc.backward(x, wr, wg, wu, wd, dy, k, cf, "bf16", gating=gating, bpr=bpr)
+        ref = torch_backward_bf16(x, wr, wg, wu, wd, dy, k, cf, gating, bpr)
         fw = g["forward"]
         assert np.array_equal(fw["topk_idx"], ref["idx"])
         assert np.array_equal(fw["slot_row"] >= 0, ref["kept"])
@@ -776,7 +869,7 @@ def check_backward_rounding_points_bf16():
         for name in ("a", "b", "h", "o", "d_o", "da", "db", "dx_perm"):
             mine = {"a": g["a_st"], "b": g["b_st"]}.get(name, g.get(name))
             assert_bf16_close(mine[rows], np.stack([ref[name][s] for s in slots]), name)
-        assert np.allclose(g["dl"], ref["dl"], rtol=1e-9, atol=1e-12)
+        assert np.allclose(g["dl_dense"], ref["dl"], rtol=1e-9, atol=1e-12)
         for name in ("dx", "dW_g", "dW_gate", "dW_up", "dW_down"):
             assert_bf16_close(g[name], ref[name], name)
 
@@ -832,7 +925,8 @@ ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
             check_ec_full_capacity_is_dense_gating, check_ec_zero_router, check_ec_float32_decision,
             check_ec_partial_capacity_dense_eval,
             check_backward_finite_differences, check_backward_autograd, check_backward_storage_rounding,
-            check_backward_rounding_points_bf16,
+            check_backward_rounding_points_bf16, check_backward_gating_finite_differences,
+            check_backward_gating_autograd,
             check_backward_expert_subset_and_sub_batch]
 
 
@@ -947,6 +1041,22 @@ def _ec_combine_renormalised(o_rows, slot, scores, storage, tokens=None, _o=orc.
 
 MUTANTS["ec_combine_renormalised"] = ("expert_choice_combine", _ec_combine_renormalised,
                                       [check_ec_partial_capacity_dense_eval])
+
+
+MUTANTS["switch_grad_chosen_logits_only"] = (
+    "switch_softmax_grad",
+    lambda logits, idx, dg, scaled, _o=orc.switch_softmax_grad: _mask_chosen(_o(logits, idx, dg, scaled), idx),
+    [check_backward_gating_finite_differences, check_backward_gating_autograd])
+MUTANTS["switch_grad_without_rescale"] = (
+    "switch_softmax_grad", lambda logits, idx, dg, scaled, _o=orc.switch_softmax_grad: _o(logits, idx, dg, False),
+    [check_backward_gating_finite_differences, check_backward_gating_autograd])
+
+
+def _mask_chosen(dl, idx):
+    """Keep dl only at each token's chosen experts."""
+    m = np.zeros_like(dl, dtype=bool)
+    np.put_along_axis(m, idx.astype(np.int64), True, axis=1)
+    return np.where(m, dl, 0.0)
 
 
 def _hold_skipping(skip):
