@@ -323,10 +323,13 @@ def bench_backward(args, w, a, g, moe, stream):
     dy = torch.from_numpy(np.random.default_rng(0).standard_normal((T, d)).astype(np.float32)).to(g["x"].dtype).cuda()
     n = moe._size_query("moe_backward_workspace_bytes", T, d, E, k, cf, F, moe._dt(g["x"]))
     ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
-    out = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, k, cf, ws=ws)
+    gating, fill = args.gating, args.fill
+    out = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, k, cf, ws=ws,
+                           gating=gating, fill_order=fill)
 
     def step():
-        moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, k, cf, ws=ws)
+        moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, k, cf, ws=ws,
+                         gating=gating, fill_order=fill)
 
     for _ in range(W):
         step()
@@ -336,8 +339,8 @@ def bench_backward(args, w, a, g, moe, stream):
         step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / K
-    idx, gate, _ = moe.moe_route(g["x"], g["w_router"], k)
-    perm = moe.moe_permute(g["x"], idx, E, cf)
+    idx, gate, _ = moe.moe_route(g["x"], g["w_router"], k, gating=gating)
+    perm = moe.moe_permute(g["x"], idx, E, cf, score=gate if fill == "priority" else None, score_stride=k)
     R = int(perm["expert_offsets"][-1].item())
     flops = 18 * d * F * R + 4 * T * d * E
     peak = PEAK["bf16_tflops"]
@@ -348,7 +351,8 @@ def bench_backward(args, w, a, g, moe, stream):
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "pass": "backward", "T": T, "d": d, "E": E, "k": k, "F": F, "cf": cf,
-                   "kept_rows": R, "workspace_bytes": n, "parallelism": "none (1 GPU)"},
+                   "gating": gating, "fill": fill, "kept_rows": R, "workspace_bytes": n,
+                   "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "whole backward (recompute + data and weight gradient GEMMs)",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
                      "alg_flops_per_launch": flops, "avg_launch_us": ms_step * 1e3},

@@ -381,7 +381,8 @@ int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float 
  * ws, ws_bytes: scratch of moe_backward_workspace_bytes (routing and
  * permutation maps, the recomputed x_perm, a, b, h and o, d_o, [da | db],
  * dx_perm, fp32 partial sums of the router gradient and the down projection's
- * split-tail partials); the GEMMs read weights and activations as stored.
+ * split-tail partials; the size covers moe_backward_ex under every gate rule
+ * and fill order); the GEMMs read weights and activations as stored.
  * Limits (MOE_ERR_UNSUPPORTED beyond): R_max * max(2F, d) * 2 bytes and one
  * expert's weight (d * F * 2 bytes) below 2^31, R_max the row bound of
  * moe_rows_max.
@@ -393,6 +394,27 @@ int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F
                  const void* w_down, const void* dy,
                  void* dx, void* dw_router, void* dw_gate, void* dw_up, void* dw_down,
                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_backward for the layer of moe_forward_ex: a gate rule (moe_gating) and a
+ * capacity fill order (moe_fill_order); moe_backward is
+ * (MOE_GATING_TOPK_SOFTMAX, MOE_FILL_TOKEN_ORDER). The routing, the fill and
+ * the activations are recomputed under the same rule and order. The fill
+ * order is a discrete decision of the forward pass and carries no gradient;
+ * it only decides which slots are kept. Under the Switch rules (gates
+ * g_j = s p[S_j], p the softmax over all E logits, s = E/k for
+ * MOE_GATING_SOFTMAX_TOPK_SCALED, else 1; the upcycling talk's Switch order)
+ * every logit receives gradient, chosen or not:
+ *   dl[e] = s p[e] (D[e] - sum_j p[S_j] dg_j),  D[S_j] = dg_j, else 0,
+ *   dw_router[e] = bf16(sum_t dl[t, e] x[t]),
+ *   dx[t] = bf16(sum_e dl[t, e] W_g[e] + sum over kept j of dx_perm[slot (t, j)]).
+ * Everything else, the rounding points and the workspace are as for
+ * moe_backward. Unknown rules or orders are MOE_ERR_INVALID_ARG. */
+int moe_backward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt,
+                    int32_t gating, int32_t fill_order,
+                    const void* x, const void* w_router, const void* w_gate, const void* w_up,
+                    const void* w_down, const void* dy,
+                    void* dx, void* dw_router, void* dw_gate, void* dw_up, void* dw_down,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 /* Measurement aid, not part of the layer: the shader clock while other work

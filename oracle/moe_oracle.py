@@ -591,7 +591,8 @@ def hold(v: np.ndarray, storage: str, point: str) -> np.ndarray:
 
 
 def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: str,
-             weight_grad_experts=None, idx=None, gating: str = "topk_softmax", bpr: bool = False) -> dict:
+             weight_grad_experts=None, idx=None, gating: str = "topk_softmax", bpr: bool = False,
+             slot_row=None) -> dict:
     """Gradients of L = <dy, y> for the token-choice layer, with respect to x
     and every weight. gating and bpr select the gate rule and the capacity
     fill order as in `forward`; the fill order is a discrete decision of the
@@ -617,15 +618,17 @@ def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: 
     weight_grad_experts: None for the expert weight gradients of every expert;
     otherwise a list of experts, and dW_gate, dW_up and dW_down hold only theirs,
     in that order (the other results are the same either way).
-    idx: optional top-k indices to use instead of the router's choice (as in
-    `forward`: the layer conditioned on routing decisions taken elsewhere).
+    idx, slot_row: optional top-k indices and slot -> row layout to use
+    instead of the router's choice and the capacity fill (as in `forward`:
+    the layer conditioned on routing decisions taken elsewhere).
     """
     x64 = as_f64(x)
     T, d = x64.shape
     E = w_router.shape[0]
     F = w_gate.shape[1]
     wr = as_f64(w_router)
-    r = forward(x, w_router, w_gate, w_up, w_down, k, cf, storage, idx=idx, gating=gating, bpr=bpr)
+    r = forward(x, w_router, w_gate, w_up, w_down, k, cf, storage, idx=idx, gating=gating, bpr=bpr,
+                slot_row=slot_row)
     idx, gates, slot_row, offsets, row_slot = r["topk_idx"], r["topk_gate"], r["slot_row"], r["offsets"], r["row_slot"]
     R = int(offsets[E])
     dy64 = as_f64(dy)

@@ -700,8 +700,8 @@ int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float 
 // ---------------------------------------------------------------------------
 
 struct BwdLayout {
-  size_t idx, gate, slot_row, row_slot, counts, offsets, chunks, dl, x_perm, a_st, b_st, h, o, d_o, dab, dx_perm,
-      router_part, ffn, total;
+  size_t idx, gate, slot_row, row_slot, counts, offsets, chunks, dl, logits, order, sort, x_perm, a_st, b_st, h, o,
+      d_o, dab, dx_perm, router_part, ffn, total;
 };
 
 static BwdLayout bwd_layout(int64_t T, int d, int E, int k, int64_t R_max, int F) {
@@ -719,7 +719,10 @@ static BwdLayout bwd_layout(int64_t T, int d, int E, int k, int64_t R_max, int F
   L.counts = take((size_t)E * 4);
   L.offsets = take((size_t)(E + 1) * 4);
   L.chunks = take((size_t)moe::permute_chunks(T) * E * 4);
-  L.dl = take((size_t)T * k * 4);
+  L.dl = take((size_t)T * (E > k ? E : k) * 4);   // [T, k], or [T, E] under the Switch rules
+  L.logits = take((size_t)T * E * 4);             // the Switch rules' softmax input
+  L.order = take((size_t)T * 4);                  // Batch Priority Routing: the fill order
+  L.sort = take(moe::priority_sort_bytes(T));
   L.x_perm = take((size_t)R_max * d * 2);
   L.a_st = take((size_t)R_max * F * 2);
   L.b_st = take((size_t)R_max * F * 2);
@@ -744,12 +747,13 @@ int moe_backward_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, flo
   return MOE_OK;
 }
 
-int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt, const void* x,
-                 const void* w_router, const void* w_gate, const void* w_up, const void* w_down, const void* dy,
-                 void* dx, void* dw_router, void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
-                 hipStream_t stream) {
+int moe_backward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt, int32_t gating,
+                    int32_t fill_order, const void* x, const void* w_router, const void* w_gate, const void* w_up,
+                    const void* w_down, const void* dy, void* dx, void* dw_router, void* dw_gate, void* dw_up,
+                    void* dw_down, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_scalars(T, d, E, k, cf, F, dt, true);
   if (st != MOE_OK) return st;
+  if (!valid_gating(gating) || !valid_fill(fill_order)) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !w_gate || !w_up || !w_down || !dy || !dx || !dw_router || !dw_gate || !dw_up ||
@@ -782,11 +786,17 @@ int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F
   int32_t* offsets = I32(L.offsets);
   float* dl = reinterpret_cast<float*>(w + L.dl);
   void* ffn_ws = ffn_ws_bytes(R_max, E, MOE_BF16) ? w + L.ffn : nullptr;
+  const bool dense = gating != MOE_GATING_TOPK_SOFTMAX;   // the Switch rules: every logit gets gradient
+  float* logits = dense ? reinterpret_cast<float*>(w + L.logits) : nullptr;
+  const float scale = gating == MOE_GATING_SOFTMAX_TOPK_SCALED ? (float)E / (float)k : 1.f;
+  int32_t* order = fill_order == MOE_FILL_PRIORITY ? I32(L.order) : nullptr;
 
-  // recompute: routing, permutation, a, b, h and o
-  hipError_t e = moe::launch_router(true, T, d, E, k, 0, x, w_router, idx, gate, nullptr, stream);
+  // recompute: routing (the same gate rule and fill order), permutation, a, b, h and o
+  hipError_t e = moe::launch_router(true, T, d, E, k, gating, x, w_router, idx, gate, logits, stream);
+  if (e == hipSuccess && order != nullptr)
+    e = moe::launch_priority_order(T, gate, k, order, w + L.sort, stream);   // score: the top-1 gate
   if (e == hipSuccess)
-    e = moe::launch_permute(true, T, d, E, k, cap, x, idx, nullptr, I32(L.counts), offsets, srow, I32(L.row_slot),
+    e = moe::launch_permute(true, T, d, E, k, cap, x, idx, order, I32(L.counts), offsets, srow, I32(L.row_slot),
                             w + L.x_perm, I32(L.chunks), stream);
   if (e == hipSuccess)
     e = moe::launch_bwd_recompute_gate_up(R_max, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w + L.h, w + L.a_st,
@@ -795,7 +805,8 @@ int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F
     e = moe::launch_gemm_bf16(2, R_max, seg_max_of(cap, R_max), d, E, F, w + L.h, offsets, w_down, nullptr, w + L.o,
                               ffn_ws, stream);
   // combine and gate backward: d_o rows, dl
-  if (e == hipSuccess) e = moe::launch_gate_bwd(T, d, k, dy, w + L.o, srow, gate, w + L.d_o, dl, stream);
+  if (e == hipSuccess)
+    e = moe::launch_gate_bwd(T, d, k, dy, w + L.o, srow, gate, w + L.d_o, dl, stream, E, idx, logits, scale);
   // data gradients through the experts (the weights read as stored)
   if (e == hipSuccess)
     e = moe::launch_bwd_dh(R_max, d, E, F, w + L.d_o, offsets, w_down, w + L.a_st, w + L.b_st, w + L.dab, stream);
@@ -809,9 +820,18 @@ int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F
   // router weight and input gradients
   if (e == hipSuccess)
     e = moe::launch_router_wgrad(T, d, E, k, x, idx, dl, reinterpret_cast<float*>(w + L.router_part), dw_router,
-                                 stream);
-  if (e == hipSuccess) e = moe::launch_dx_final(T, d, k, dl, idx, w_router, w + L.dx_perm, srow, dx, stream);
+                                 stream, dense);
+  if (e == hipSuccess)
+    e = moe::launch_dx_final(T, d, k, dl, idx, w_router, w + L.dx_perm, srow, dx, stream, dense ? E : 0);
   return hip_status(e);
+}
+
+int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt, const void* x,
+                 const void* w_router, const void* w_gate, const void* w_up, const void* w_down, const void* dy,
+                 void* dx, void* dw_router, void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  return moe_backward_ex(T, d, E, k, cf, F, dt, MOE_GATING_TOPK_SOFTMAX, MOE_FILL_TOKEN_ORDER, x, w_router, w_gate,
+                         w_up, w_down, dy, dx, dw_router, dw_gate, dw_up, dw_down, ws, ws_bytes, stream);
 }
 
 const char* moe_status_string(int status) {

@@ -85,11 +85,15 @@ hipError_t launch_bwd_dx_perm(int64_t R_max, int d, int E, int F, const void* da
 hipError_t launch_wgrad(int E, const int32_t* offsets, int M, int M1, int N, int lda, int ldb, int64_t R,
                         const void* A, const void* B, void* C0, void* C1, hipStream_t s);
 size_t router_wgrad_partial_bytes(int64_t T, int d, int E);
+// logits == nullptr: Softmax(TopK) gates, dl [T, k]; else the Switch rules
+// (logits [T, E] of the router, gate scale s), dl dense [T, E].
 hipError_t launch_gate_bwd(int64_t T, int d, int k, const void* dy, const void* o, const int32_t* slot_row,
-                           const float* gate, void* d_o, float* dl, hipStream_t s);
+                           const float* gate, void* d_o, float* dl, hipStream_t s, int E = 0,
+                           const int32_t* idx = nullptr, const float* logits = nullptr, float scale = 1.f);
 hipError_t launch_router_wgrad(int64_t T, int d, int E, int k, const void* x, const int32_t* idx, const float* dl,
-                               float* partial, void* dwg, hipStream_t s);
+                               float* partial, void* dwg, hipStream_t s, bool dense = false);
+// dense_E > 0: dl is [T, dense_E]; 0: [T, k] at idx
 hipError_t launch_dx_final(int64_t T, int d, int k, const float* dl, const int32_t* idx, const void* wr,
-                           const void* dx_perm, const int32_t* slot_row, void* dx, hipStream_t s);
+                           const void* dx_perm, const int32_t* slot_row, void* dx, hipStream_t s, int dense_E = 0);
 
 }  // namespace moe

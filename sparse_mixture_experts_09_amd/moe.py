@@ -73,6 +73,8 @@ _SIGS = {
                                                     ctypes.POINTER(_sz)]),
     "moe_backward": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_backward_ex": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _i32, _i32, _vp, _vp, _vp,
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_clock_probe": (ctypes.c_int, [_vp, _i64, _vp]),
     "moe_wall_clock_khz": (ctypes.c_int, [ctypes.POINTER(_i32)]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -448,9 +450,12 @@ def moe_forward_expert_choice(x, w_router, w_gate, w_up, w_down, k: int, cf: flo
 # backward pass
 # ---------------------------------------------------------------------------
 
-def moe_backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, ws=None, stream=None):
+def moe_backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, ws=None, stream=None,
+                 gating: str = "topk_softmax", fill_order: str = "token"):
     """Gradients of <dy, y> for the token-choice layer (bf16). Returns dict(dx,
-    dw_router, dw_gate, dw_up, dw_down), shaped like x and the weights."""
+    dw_router, dw_gate, dw_up, dw_down), shaped like x and the weights. The
+    defaults call moe_backward; another gating or fill_order calls
+    moe_backward_ex."""
     T, d = x.shape
     E, F, _ = w_gate.shape
     out = dict(dx=_new_like(stream, x), dw_router=_new_like(stream, w_router), dw_gate=_new_like(stream, w_gate),
@@ -458,10 +463,14 @@ def moe_backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, ws=No
     if ws is None:
         n = _size_query("moe_backward_workspace_bytes", T, d, E, k, cf, F, _dt(x))
         ws = _new(stream, max(n, 16), torch.uint8, x.device)
-    st = lib().moe_backward(T, d, E, k, cf, F, _dt(x), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
-                            _ptr(w_down), _ptr(dy), _ptr(out["dx"]), _ptr(out["dw_router"]), _ptr(out["dw_gate"]),
-                            _ptr(out["dw_up"]), _ptr(out["dw_down"]), _ptr(ws), ws.numel(), _stream(stream))
-    _check("moe_backward", st)
+    ptrs = (_ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(dy), _ptr(out["dx"]),
+            _ptr(out["dw_router"]), _ptr(out["dw_gate"]), _ptr(out["dw_up"]), _ptr(out["dw_down"]), _ptr(ws),
+            ws.numel(), _stream(stream))
+    if gating == "topk_softmax" and fill_order == "token":
+        _check("moe_backward", lib().moe_backward(T, d, E, k, cf, F, _dt(x), *ptrs))
+    else:
+        _check("moe_backward_ex", lib().moe_backward_ex(T, d, E, k, cf, F, _dt(x), GATINGS[gating],
+                                                        FILL_ORDERS[fill_order], *ptrs))
     return out
 
 

@@ -27,7 +27,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 31
+    assert len(names) == 32
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -290,6 +290,14 @@ def test_backward_entry_points_validate():
     assert L.moe_backward(*a) == UNS
     a = list(bw); a[0] = 0
     assert L.moe_backward(*a) == OK
+    bx = bw[:7] + [0, 0] + bw[7:]
+    for g, f in [(3, 0), (0, 2), (-1, 0)]:
+        a = list(bx); a[7] = g; a[8] = f
+        assert L.moe_backward_ex(*a) == INV
+    a = list(bx); a[7] = 2; a[8] = 1; a[15] = A[0]          # dx overlapping x, under a valid rule and order
+    assert L.moe_backward_ex(*a) == INV
+    a = list(bx); a[7] = 1; a[8] = 1; a[0] = 0
+    assert L.moe_backward_ex(*a) == OK
 
 
 def test_extreme_scalars_are_rejected_or_exact():

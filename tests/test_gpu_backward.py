@@ -45,21 +45,39 @@ def check_grad(name, got, ref):
     return rel, mae
 
 
-def run_and_check(w, a, g, dy, seed_label):
+def gpu_layout(w, g, gating, fill):
+    """The kernels' routing and slot -> row map for a gate rule and fill order
+    (moe_forward_ex recomputes them exactly as moe_backward_ex does)."""
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
+    srow = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    moe.moe_forward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], w.k, w.cf, topk_idx=idx,
+                    topk_gate=gate, slot_row=srow, gating=gating, fill_order=fill)
+    torch.cuda.synchronize()
+    return host(idx), host(gate), host(srow)
+
+
+def run_and_check(w, a, g, dy, seed_label, gating="topk_softmax", fill="token"):
+    bpr = fill == "priority"
     ref = orc.backward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy.double().numpy(), w.k, w.cf,
-                       "bf16")
+                       "bf16", gating=gating, bpr=bpr)
     fw = ref["forward"]
     # routing decisions must match (no near ties in these seeds)
-    idx, gate, _ = moe.moe_route(g["x"], g["w_router"], w.k)
-    torch.cuda.synchronize()
-    assert compare_routing(host(idx), host(gate), fw) == 0
-    out = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dev(dy), w.k, w.cf)
+    idx, gate, srow = gpu_layout(w, g, gating, fill)
+    assert compare_routing(idx, gate, fw) == 0
+    if not np.array_equal(srow, fw["slot_row"]):
+        # equal float32 priorities may fill in another valid order: condition on the kernels' layout
+        assert bpr, "token-order fill must match the oracle bit for bit"
+        ref = orc.backward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy.double().numpy(), w.k,
+                           w.cf, "bf16", gating=gating, bpr=bpr, idx=idx, slot_row=srow)
+    out = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dev(dy), w.k, w.cf,
+                           gating=gating, fill_order=fill)
     torch.cuda.synchronize()
     res = {}
     for key, rk in [("dx", "dx"), ("dw_router", "dW_g"), ("dw_gate", "dW_gate"), ("dw_up", "dW_up"),
                     ("dw_down", "dW_down")]:
         res[key] = check_grad(key, host(out[key]), ref[rk])
-    print(f"{seed_label}: " + ", ".join(f"{k_} rel {v[0]:.3g} mae {v[1]:.3g}" for k_, v in res.items()))
+    print(f"{seed_label} {gating}/{fill}: " + ", ".join(f"{k_} rel {v[0]:.3g} mae {v[1]:.3g}" for k_, v in res.items()))
     return out
 
 
@@ -68,6 +86,19 @@ def test_backward(case):
     w, a = workload(case)
     g = device_inputs(case)
     run_and_check(w, a, g, make_dy(w, case[7]), case_id(case))
+
+
+VARIANTS = [("softmax_topk", "token"), ("softmax_topk_scaled", "priority"), ("topk_softmax", "priority")]
+
+
+@pytest.mark.parametrize("gating,fill", VARIANTS, ids=lambda v: v)
+@pytest.mark.parametrize("case", [c for c in BF16_CASES if c[0] >= 32], ids=case_id)
+def test_backward_gating_and_fill(case, gating, fill):
+    """moe_backward_ex: the Switch gate rules (every logit gets gradient) and
+    Batch Priority Routing (another set of kept slots), against the oracle."""
+    w, a = workload(case)
+    g = device_inputs(case)
+    run_and_check(w, a, g, make_dy(w, case[7]), case_id(case), gating, fill)
 
 
 def test_backward_mid_size():
@@ -131,6 +162,39 @@ def test_backward_is_deterministic():
         again = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, w.k, w.cf)
         for key in first:
             assert torch.equal(first[key], again[key]), key
+
+
+@pytest.mark.parametrize("name,gating,fill", [("openmoe_bf16", "softmax_topk_scaled", "priority"),
+                                              ("finegrained_bf16", "softmax_topk", "token")])
+def test_full_size_backward_gating_and_fill(name, gating, fill):
+    """moe_backward_ex at full size: every entry of the five gradients; where
+    equal float32 priorities let the kernels fill in another valid order, the
+    oracle is conditioned on their layout (checked valid first)."""
+    w, a = workload(name)
+    g = device_inputs(name)
+    dy = make_dy(w, 92)
+    idx, gate, srow = gpu_layout(w, g, gating, fill)
+    out = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dev(dy), w.k, w.cf,
+                           gating=gating, fill_order=fill)
+    torch.cuda.synchronize()
+    r = orc.backward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy.double().numpy(), w.k, w.cf,
+                     "bf16", gating=gating, bpr=fill == "priority")
+    fw = r["forward"]
+    flips = compare_routing(idx, gate, fw)
+    moved = int((srow != fw["slot_row"]).any(axis=1).sum())
+    if flips or moved:
+        kept = (srow >= 0).sum()
+        assert kept == (fw["slot_row"] >= 0).sum()
+        r = orc.backward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy.double().numpy(), w.k, w.cf,
+                         "bf16", gating=gating, bpr=fill == "priority", idx=idx, slot_row=srow)
+    res = {}
+    for key, rk in [("dx", "dx"), ("dw_router", "dW_g"), ("dw_gate", "dW_gate"), ("dw_up", "dW_up"),
+                    ("dw_down", "dW_down")]:
+        res[key] = check_grad(key, host(out[key]), r[rk])
+        out[key] = None
+        r[rk] = None
+    print(f"{name} {gating}/{fill}: flips {flips}, moved {moved}; "
+          + ", ".join(f"{k_} rel {v[0]:.3g} mae {v[1]:.3g}" for k_, v in res.items()))
 
 
 @pytest.mark.parametrize("name", ["mixtral_bf16", "openmoe_bf16", "finegrained_bf16"])
