@@ -362,7 +362,9 @@ int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float 
 
 /* ---------------------------------------------------------------------------
  * Backward pass of the token-choice layer (Softmax(TopK) gates, token-order
- * capacity), bf16 only (MOE_ERR_UNSUPPORTED for MOE_F32).
+ * capacity), bf16 or fp32 storage ("bf16(...)" below is a rounding to the
+ * storage type: a no-op beyond fp32 for MOE_F32, whose products run on the
+ * vector ALUs).
  * Gradients of L = <dy, y> by the chain rule of the forward definition. The
  * routing, the permutation and the expert activations are recomputed from
  * the inputs (the upcycling talk's walkthrough recomputes the permutation in
@@ -383,9 +385,9 @@ int moe_forward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float 
  * dx_perm, fp32 partial sums of the router gradient and the down projection's
  * split-tail partials; the size covers moe_backward_ex under every gate rule
  * and fill order); the GEMMs read weights and activations as stored.
- * Limits (MOE_ERR_UNSUPPORTED beyond): R_max * max(2F, d) * 2 bytes and one
- * expert's weight (d * F * 2 bytes) below 2^31, R_max the row bound of
- * moe_rows_max.
+ * Limits (MOE_ERR_UNSUPPORTED beyond), bf16: R_max * max(2F, d) * 2 bytes
+ * and one expert's weight (d * F * 2 bytes) below 2^31, R_max the row bound
+ * of moe_rows_max.
  * ------------------------------------------------------------------------- */
 int moe_backward_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
                                  int32_t dt, size_t* bytes);

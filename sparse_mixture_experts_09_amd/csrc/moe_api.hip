@@ -704,7 +704,8 @@ struct BwdLayout {
       d_o, dab, dx_perm, router_part, ffn, total;
 };
 
-static BwdLayout bwd_layout(int64_t T, int d, int E, int k, int64_t R_max, int F) {
+static BwdLayout bwd_layout(int64_t T, int d, int E, int k, int64_t R_max, int F, int dt) {
+  const size_t s = elem_bytes(dt);
   BwdLayout L;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -723,16 +724,16 @@ static BwdLayout bwd_layout(int64_t T, int d, int E, int k, int64_t R_max, int F
   L.logits = take((size_t)T * E * 4);             // the Switch rules' softmax input
   L.order = take((size_t)T * 4);                  // Batch Priority Routing: the fill order
   L.sort = take(moe::priority_sort_bytes(T));
-  L.x_perm = take((size_t)R_max * d * 2);
-  L.a_st = take((size_t)R_max * F * 2);
-  L.b_st = take((size_t)R_max * F * 2);
-  L.h = take((size_t)R_max * F * 2);
-  L.o = take((size_t)R_max * d * 2);
-  L.d_o = take((size_t)R_max * d * 2);
-  L.dab = take((size_t)R_max * 2 * F * 2);
-  L.dx_perm = take((size_t)R_max * d * 2);
+  L.x_perm = take((size_t)R_max * d * s);
+  L.a_st = take((size_t)R_max * F * s);
+  L.b_st = take((size_t)R_max * F * s);
+  L.h = take((size_t)R_max * F * s);
+  L.o = take((size_t)R_max * d * s);
+  L.d_o = take((size_t)R_max * d * s);
+  L.dab = take((size_t)R_max * 2 * F * s);
+  L.dx_perm = take((size_t)R_max * d * s);
   L.router_part = take(moe::router_wgrad_partial_bytes(T, d, E));
-  L.ffn = take(ffn_ws_bytes(R_max, E, MOE_BF16));
+  L.ffn = take(ffn_ws_bytes(R_max, E, dt));
   L.total = o;
   return L;
 }
@@ -742,8 +743,7 @@ int moe_backward_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, flo
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
   int st = check_scalars(T, d, E, k, cf, F, dt, true);
   if (st != MOE_OK) return st;
-  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  *bytes = bwd_layout(T, d, E, k, rows_max_of(T, E, k, capacity_of(T, E, k, cf)), F).total;
+  *bytes = bwd_layout(T, d, E, k, rows_max_of(T, E, k, capacity_of(T, E, k, cf)), F, dt).total;
   return MOE_OK;
 }
 
@@ -754,8 +754,9 @@ int moe_backward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_
   int st = check_scalars(T, d, E, k, cf, F, dt, true);
   if (st != MOE_OK) return st;
   if (!valid_gating(gating) || !valid_fill(fill_order)) return MOE_ERR_INVALID_ARG;
-  if (dt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
+  const bool bf16 = dt == MOE_BF16;
+  const size_t s = elem_bytes(dt);
   if (!x || !w_router || !w_gate || !w_up || !w_down || !dy || !dx || !dw_router || !dw_gate || !dw_up ||
       !dw_down || !ws)
     return MOE_ERR_INVALID_ARG;
@@ -765,17 +766,17 @@ int moe_backward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_
     return MOE_ERR_UNSUPPORTED;
   const int64_t cap = capacity_of(T, E, k, cf);
   const int64_t R_max = rows_max_of(T, E, k, cap);
-  // the GEMMs address one expert's weights, and the kept rows of one activation, with 31-bit offsets
+  // the bf16 GEMMs address one expert's weights, and the kept rows of one activation, with 31-bit offsets
   const int64_t widest = 2 * (int64_t)F > d ? 2 * (int64_t)F : d;
-  if (R_max * widest * 2 >= ((int64_t)1 << 31) || (int64_t)d * F * 2 >= ((int64_t)1 << 31))
+  if (bf16 && (R_max * widest * 2 >= ((int64_t)1 << 31) || (int64_t)d * F * 2 >= ((int64_t)1 << 31)))
     return MOE_ERR_UNSUPPORTED;
-  const BwdLayout L = bwd_layout(T, d, E, k, R_max, F);
+  const BwdLayout L = bwd_layout(T, d, E, k, R_max, F, dt);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  const size_t wbytes = (size_t)E * F * d * 2;
-  const Range all[] = {{dx, (size_t)T * d * 2},    {dw_router, (size_t)E * d * 2}, {dw_gate, wbytes},
+  const size_t wbytes = (size_t)E * F * d * s;
+  const Range all[] = {{dx, (size_t)T * d * s},    {dw_router, (size_t)E * d * s}, {dw_gate, wbytes},
                        {dw_up, wbytes},            {dw_down, wbytes},              {ws, L.total},
-                       {x, (size_t)T * d * 2},     {w_router, (size_t)E * d * 2},  {w_gate, wbytes},
-                       {w_up, wbytes},             {w_down, wbytes},               {dy, (size_t)T * d * 2}};
+                       {x, (size_t)T * d * s},     {w_router, (size_t)E * d * s},  {w_gate, wbytes},
+                       {w_up, wbytes},             {w_down, wbytes},               {dy, (size_t)T * d * s}};
   if (any_overlap(all, 6, 12)) return MOE_ERR_INVALID_ARG;
 
   char* w = reinterpret_cast<char*>(ws);
@@ -785,44 +786,56 @@ int moe_backward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_
   int32_t* srow = I32(L.slot_row);
   int32_t* offsets = I32(L.offsets);
   float* dl = reinterpret_cast<float*>(w + L.dl);
-  void* ffn_ws = ffn_ws_bytes(R_max, E, MOE_BF16) ? w + L.ffn : nullptr;
+  void* ffn_ws = ffn_ws_bytes(R_max, E, dt) ? w + L.ffn : nullptr;
   const bool dense = gating != MOE_GATING_TOPK_SOFTMAX;   // the Switch rules: every logit gets gradient
   float* logits = dense ? reinterpret_cast<float*>(w + L.logits) : nullptr;
   const float scale = gating == MOE_GATING_SOFTMAX_TOPK_SCALED ? (float)E / (float)k : 1.f;
   int32_t* order = fill_order == MOE_FILL_PRIORITY ? I32(L.order) : nullptr;
 
   // recompute: routing (the same gate rule and fill order), permutation, a, b, h and o
-  hipError_t e = moe::launch_router(true, T, d, E, k, gating, x, w_router, idx, gate, logits, stream);
+  hipError_t e = moe::launch_router(bf16, T, d, E, k, gating, x, w_router, idx, gate, logits, stream);
   if (e == hipSuccess && order != nullptr)
     e = moe::launch_priority_order(T, gate, k, order, w + L.sort, stream);   // score: the top-1 gate
   if (e == hipSuccess)
-    e = moe::launch_permute(true, T, d, E, k, cap, x, idx, order, I32(L.counts), offsets, srow, I32(L.row_slot),
+    e = moe::launch_permute(bf16, T, d, E, k, cap, x, idx, order, I32(L.counts), offsets, srow, I32(L.row_slot),
                             w + L.x_perm, I32(L.chunks), stream);
   if (e == hipSuccess)
-    e = moe::launch_bwd_recompute_gate_up(R_max, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w + L.h, w + L.a_st,
-                                          w + L.b_st, stream);
+    e = bf16 ? moe::launch_bwd_recompute_gate_up(R_max, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w + L.h,
+                                                 w + L.a_st, w + L.b_st, stream)
+             : moe::launch_bwd_f32_recompute(R_max, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w + L.h,
+                                             w + L.a_st, w + L.b_st, stream);
   if (e == hipSuccess)
-    e = moe::launch_gemm_bf16(2, R_max, seg_max_of(cap, R_max), d, E, F, w + L.h, offsets, w_down, nullptr, w + L.o,
-                              ffn_ws, stream);
+    e = bf16 ? moe::launch_gemm_bf16(2, R_max, seg_max_of(cap, R_max), d, E, F, w + L.h, offsets, w_down, nullptr,
+                                     w + L.o, ffn_ws, stream)
+             : moe::launch_gemm_f32(2, R_max, d, E, F, w + L.h, offsets, w_down, nullptr, w + L.o, stream);
   // combine and gate backward: d_o rows, dl
   if (e == hipSuccess)
-    e = moe::launch_gate_bwd(T, d, k, dy, w + L.o, srow, gate, w + L.d_o, dl, stream, E, idx, logits, scale);
+    e = moe::launch_gate_bwd(T, d, k, dy, w + L.o, srow, gate, w + L.d_o, dl, stream, E, idx, logits, scale, bf16);
   // data gradients through the experts (the weights read as stored)
   if (e == hipSuccess)
-    e = moe::launch_bwd_dh(R_max, d, E, F, w + L.d_o, offsets, w_down, w + L.a_st, w + L.b_st, w + L.dab, stream);
+    e = bf16 ? moe::launch_bwd_dh(R_max, d, E, F, w + L.d_o, offsets, w_down, w + L.a_st, w + L.b_st, w + L.dab,
+                                  stream)
+             : moe::launch_bwd_f32_dh(R_max, d, E, F, w + L.d_o, offsets, w_down, w + L.a_st, w + L.b_st, w + L.dab,
+                                      stream);
   if (e == hipSuccess)
-    e = moe::launch_bwd_dx_perm(R_max, d, E, F, w + L.dab, offsets, w_gate, w_up, w + L.dx_perm, ffn_ws, stream);
+    e = bf16 ? moe::launch_bwd_dx_perm(R_max, d, E, F, w + L.dab, offsets, w_gate, w_up, w + L.dx_perm, ffn_ws,
+                                       stream)
+             : moe::launch_bwd_f32_dx_perm(R_max, d, E, F, w + L.dab, offsets, w_gate, w_up, w + L.dx_perm, stream);
   // weight gradients over each expert's rows (the activations as stored)
   if (e == hipSuccess)
-    e = moe::launch_wgrad(E, offsets, 2 * F, F, d, 2 * F, d, R_max, w + L.dab, w + L.x_perm, dw_gate, dw_up, stream);
+    e = bf16 ? moe::launch_wgrad(E, offsets, 2 * F, F, d, 2 * F, d, R_max, w + L.dab, w + L.x_perm, dw_gate, dw_up,
+                                 stream)
+             : moe::launch_wgrad_f32(E, offsets, 2 * F, F, d, 2 * F, d, w + L.dab, w + L.x_perm, dw_gate, dw_up,
+                                     stream);
   if (e == hipSuccess)
-    e = moe::launch_wgrad(E, offsets, d, d, F, d, F, R_max, w + L.d_o, w + L.h, dw_down, nullptr, stream);
+    e = bf16 ? moe::launch_wgrad(E, offsets, d, d, F, d, F, R_max, w + L.d_o, w + L.h, dw_down, nullptr, stream)
+             : moe::launch_wgrad_f32(E, offsets, d, d, F, d, F, w + L.d_o, w + L.h, dw_down, nullptr, stream);
   // router weight and input gradients
   if (e == hipSuccess)
     e = moe::launch_router_wgrad(T, d, E, k, x, idx, dl, reinterpret_cast<float*>(w + L.router_part), dw_router,
-                                 stream, dense);
+                                 stream, dense, bf16);
   if (e == hipSuccess)
-    e = moe::launch_dx_final(T, d, k, dl, idx, w_router, w + L.dx_perm, srow, dx, stream, dense ? E : 0);
+    e = moe::launch_dx_final(T, d, k, dl, idx, w_router, w + L.dx_perm, srow, dx, stream, dense ? E : 0, bf16);
   return hip_status(e);
 }
 

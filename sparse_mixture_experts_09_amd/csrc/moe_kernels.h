@@ -87,13 +87,31 @@ hipError_t launch_wgrad(int E, const int32_t* offsets, int M, int M1, int N, int
 size_t router_wgrad_partial_bytes(int64_t T, int d, int E);
 // logits == nullptr: Softmax(TopK) gates, dl [T, k]; else the Switch rules
 // (logits [T, E] of the router, gate scale s), dl dense [T, E].
+// Every tensor in the storage type (bf16: true; else fp32); dl, gates, logits fp32.
 hipError_t launch_gate_bwd(int64_t T, int d, int k, const void* dy, const void* o, const int32_t* slot_row,
                            const float* gate, void* d_o, float* dl, hipStream_t s, int E = 0,
-                           const int32_t* idx = nullptr, const float* logits = nullptr, float scale = 1.f);
+                           const int32_t* idx = nullptr, const float* logits = nullptr, float scale = 1.f,
+                           bool bf16 = true);
 hipError_t launch_router_wgrad(int64_t T, int d, int E, int k, const void* x, const int32_t* idx, const float* dl,
-                               float* partial, void* dwg, hipStream_t s, bool dense = false);
+                               float* partial, void* dwg, hipStream_t s, bool dense = false, bool bf16 = true);
 // dense_E > 0: dl is [T, dense_E]; 0: [T, k] at idx
 hipError_t launch_dx_final(int64_t T, int d, int k, const float* dl, const int32_t* idx, const void* wr,
-                           const void* dx_perm, const int32_t* slot_row, void* dx, hipStream_t s, int dense_E = 0);
+                           const void* dx_perm, const int32_t* slot_row, void* dx, hipStream_t s, int dense_E = 0,
+                           bool bf16 = true);
+// fp32 layers: the backward's GEMMs on the vector ALUs (ffn_f32.hip).
+//   recompute: h = silu(a) b with a = x_perm W_gate^T, b = x_perm W_up^T, storing h, a and b
+//   dh:        dh = d_o W_down[e] ([E, d, F] as stored), then da = dh b silu'(a) and
+//              db = dh silu(a) written side by side into dab [R, 2F]
+//   dx_perm:   dab [R, 2F] times [W_gate[e]; W_up[e]] ([F, d] each, as stored)
+//   wgrad:     C[e] = A^T B over expert e's rows, A [R, lda] columns 0..M-1, B [R, ldb]
+//              columns 0..N-1; rows of C below M1 go to C0 ([E, M1, N]), the rest to C1
+hipError_t launch_bwd_f32_recompute(int64_t R_max, int d, int E, int F, const void* x_perm, const int32_t* offsets,
+                                    const void* wg, const void* wu, void* h, void* a, void* b, hipStream_t s);
+hipError_t launch_bwd_f32_dh(int64_t R_max, int d, int E, int F, const void* d_o, const int32_t* offsets,
+                             const void* w_down, const void* a, const void* b, void* dab, hipStream_t s);
+hipError_t launch_bwd_f32_dx_perm(int64_t R_max, int d, int E, int F, const void* dab, const int32_t* offsets,
+                                  const void* w_gate, const void* w_up, void* dx_perm, hipStream_t s);
+hipError_t launch_wgrad_f32(int E, const int32_t* offsets, int M, int M1, int N, int lda, int ldb, const void* A,
+                            const void* B, void* C0, void* C1, hipStream_t s);
 
 }  // namespace moe

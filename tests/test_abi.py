@@ -271,13 +271,17 @@ def test_expert_choice_entry_points_validate():
 def test_backward_entry_points_validate():
     L = moe.lib()
     b = ctypes.c_size_t()
-    assert L.moe_backward_workspace_bytes(64, 64, 4, 2, 1.0, 128, F32, ctypes.byref(b)) == UNS
+    assert L.moe_backward_workspace_bytes(64, 64, 4, 2, 1.0, 128, F32, ctypes.byref(b)) == OK
+    f32_need = b.value
     assert L.moe_backward_workspace_bytes(64, 64, 4, 2, 1.0, 128, BF16, ctypes.byref(b)) == OK
     need = b.value
+    assert f32_need > need      # fp32 activations take twice the bytes
     bw = [64, 64, 4, 2, 1.0, 128, BF16, A[0], A[1], A[2], A[3], A[4], A[5], A[6], A[7], A[8], A[9], A[10], A[11],
           1 << 40, None]
-    a = list(bw); a[6] = F32
+    a = list(bw); a[6] = F32; a[1] = 66           # fp32: d must be a multiple of 4
     assert L.moe_backward(*a) == UNS
+    a = list(bw); a[6] = F32; a[19] = f32_need - 1
+    assert L.moe_backward(*a) == WS
     a = list(bw); a[12] = None                  # dy
     assert L.moe_backward(*a) == INV
     a = list(bw); a[19] = need - 1

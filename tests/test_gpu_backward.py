@@ -16,14 +16,20 @@ from test_gpu_parity import SMALL, case_id, dev, device_inputs, full_reference, 
 pytestmark = pytest.mark.gpu
 
 BF16_CASES = [c for c in SMALL if c[6] == "bf16"]
+F32_CASES = [c for c in SMALL if c[6] == "f32"] + ["tiny_fp32"]
+
+# (row max-rel, mean |err| / mean |ref|): bf16 as below; fp32 layers keep every
+# value in fp32, so only summation order separates kernel and oracle
+GRAD_TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-5)}
 
 
 def make_dy(w, seed):
     rng = np.random.default_rng(1000 + seed)
-    return torch.from_numpy(rng.standard_normal((w.T, w.d)).astype(np.float32)).to(torch.bfloat16)
+    dy = torch.from_numpy(rng.standard_normal((w.T, w.d)).astype(np.float32))
+    return dy.to(torch.bfloat16) if w.dtype == "bf16" else dy
 
 
-def check_grad(name, got, ref):
+def check_grad(name, got, ref, dtype="bf16"):
     """Row-wise: max |err| / max |ref| <= 2e-2 per row of the last dimension
     (the forward's bound), and mean |err| <= 2e-3 * mean |ref| over the
     tensor: the forward's mean absolute error bound of 1e-3 on outputs whose
@@ -40,8 +46,9 @@ def check_grad(name, got, ref):
     assert np.all(g[zero] == 0.0), f"{name}: rows with a zero reference are not zero"
     rel = (err.max(axis=1)[~zero] / rmax[~zero]).max(initial=0.0)
     mae = err.mean() / max(np.abs(r).mean(), 1e-30)
-    assert rel <= 2e-2, f"{name}: row max-rel {rel:.3g}"
-    assert mae <= 2e-3, f"{name}: relative MAE {mae:.3g}"
+    rel_tol, mae_tol = GRAD_TOL[dtype]
+    assert rel <= rel_tol, f"{name}: row max-rel {rel:.3g}"
+    assert mae <= mae_tol, f"{name}: relative MAE {mae:.3g}"
     return rel, mae
 
 
@@ -60,7 +67,7 @@ def gpu_layout(w, g, gating, fill):
 def run_and_check(w, a, g, dy, seed_label, gating="topk_softmax", fill="token"):
     bpr = fill == "priority"
     ref = orc.backward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy.double().numpy(), w.k, w.cf,
-                       "bf16", gating=gating, bpr=bpr)
+                       w.dtype, gating=gating, bpr=bpr)
     fw = ref["forward"]
     # routing decisions must match (no near ties in these seeds)
     idx, gate, srow = gpu_layout(w, g, gating, fill)
@@ -69,14 +76,14 @@ def run_and_check(w, a, g, dy, seed_label, gating="topk_softmax", fill="token"):
         # equal float32 priorities may fill in another valid order: condition on the kernels' layout
         assert bpr, "token-order fill must match the oracle bit for bit"
         ref = orc.backward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy.double().numpy(), w.k,
-                           w.cf, "bf16", gating=gating, bpr=bpr, idx=idx, slot_row=srow)
+                           w.cf, w.dtype, gating=gating, bpr=bpr, idx=idx, slot_row=srow)
     out = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dev(dy), w.k, w.cf,
                            gating=gating, fill_order=fill)
     torch.cuda.synchronize()
     res = {}
     for key, rk in [("dx", "dx"), ("dw_router", "dW_g"), ("dw_gate", "dW_gate"), ("dw_up", "dW_up"),
                     ("dw_down", "dW_down")]:
-        res[key] = check_grad(key, host(out[key]), ref[rk])
+        res[key] = check_grad(key, host(out[key]), ref[rk], w.dtype)
     print(f"{seed_label} {gating}/{fill}: " + ", ".join(f"{k_} rel {v[0]:.3g} mae {v[1]:.3g}" for k_, v in res.items()))
     return out
 
@@ -99,6 +106,18 @@ def test_backward_gating_and_fill(case, gating, fill):
     w, a = workload(case)
     g = device_inputs(case)
     run_and_check(w, a, g, make_dy(w, case[7]), case_id(case), gating, fill)
+
+
+@pytest.mark.parametrize("gating,fill", [("topk_softmax", "token")] + VARIANTS, ids=lambda v: v)
+@pytest.mark.parametrize("case", F32_CASES, ids=case_id)
+def test_backward_f32(case, gating, fill):
+    """fp32 layers: the products on the vector ALUs, every gradient entry
+    against the oracle in fp32 storage mode, under every gate rule and fill
+    order."""
+    w, a = workload(case)
+    g = device_inputs(case)
+    seed = case[7] if not isinstance(case, str) else 0
+    run_and_check(w, a, g, make_dy(w, seed), case_id(case), gating, fill)
 
 
 def test_backward_mid_size():
