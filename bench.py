@@ -202,6 +202,35 @@ def main():
     ms_step = (t1 - t0) * 1e3 / K
     gpu_ms_step = e0.elapsed_time(e1) / K
     log(f"moe_forward: {ms_step:.3f} ms/step wall, {gpu_ms_step:.3f} ms/step events")
+    # the same step captured once in a HIP graph and replayed K times (launch gaps removed); the
+    # replay must reproduce the eager output bit for bit
+    graph = None
+    try:
+        y_eager = y.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            forward()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g_ = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_):
+            forward()
+        torch.cuda.synchronize()
+        y.zero_()
+        g_.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(y, y_eager))
+        t0 = time.perf_counter()
+        for _ in range(K):
+            g_.replay()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - t0) * 1e3 / K
+        graph = {"ms_per_step": g_ms, "tokens_per_s": T / (g_ms * 1e-3), "equals_eager": same}
+        log(f"moe_forward as a replayed HIP graph: {g_ms:.3f} ms/step (output equal to eager: {same})")
+        del g_
+    except Exception as exc:   # capture unsupported here: report, keep the eager figures
+        graph = {"error": repr(exc)[:200]}
     # the core clock during the same loop, measured in K more steps (outside the timed region)
     clock = clock_during(moe, forward, K, ms_step)
     log(f"core clock during moe_forward: mean {clock['mean_mhz']:.0f} MHz (min {clock['min_mhz']:.0f}, "
@@ -306,6 +335,7 @@ def main():
         "route_permute_combine_hbm_frac": hbm_frac,
         "layer_tflops": (alg["route"]["flops"] + alg["gate_up"]["flops"] + alg["down"]["flops"]) / (ms_step * 1e-3) / 1e12,
         "gpu_ms_per_step_events": gpu_ms_step,
+        "graph_replay": graph,
         "core_clock": clock,
         "stages": stages,
         "stage_path_equals_forward": same_as_forward,
