@@ -72,7 +72,9 @@ Readings where the pages are silent (each is listed in the design notes):
     expert-output gradient d_o = g * dy, the SwiGLU input gradients da, db,
     the permuted input gradient dx_perm, and every returned gradient. The
     router gradient includes dropped slots (their gates still enter the
-    softmax of the chosen logits);
+    softmax of the chosen logits). Under expert choice the selection passes
+    no gradient and the gates are the dense scores, so every logit of a
+    token that some expert chose gets gradient through the full softmax;
   * "storage" rounding: the layer stores h, o and y in its storage type. In
     "bf16" mode the float64 value is rounded to float32 and then to bfloat16
     (round to nearest even); in "f32" mode to float32; in "f64" mode not at
@@ -563,6 +565,12 @@ def switch_softmax_grad(logits: np.ndarray, idx: np.ndarray, dg: np.ndarray, sca
     return s * p * (D - (p * D).sum(axis=1, keepdims=True))
 
 
+def softmax_grad(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
+    """Gradient through p = softmax(l) over the last axis, given dp = dL/dp:
+    dl = p (dp - sum p dp) (the softmax's Jacobian diag(p) - p p^T)."""
+    return p * (dp - (p * dp).sum(axis=-1, keepdims=True))
+
+
 def gate_grad_dense(logits: np.ndarray, idx: np.ndarray, gates: np.ndarray, dg: np.ndarray,
                     gating: str) -> np.ndarray:
     """dL/dl [T, E] for a gate rule, given dg [T, k] = dL/dg: Softmax(TopK)
@@ -687,4 +695,81 @@ def backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: 
         dx[m] += dx_perm[slot_row[m, j]]
     return dict(forward=r, dx=store(dx, storage), dW_g=store(dW_g, storage), dW_gate=store(dW_gate, storage),
                 dW_up=store(dW_up, storage), dW_down=store(dW_down, storage), dl=dl, dl_dense=dl_dense, dg=dg, d_o=d_o,
+                a_st=a_st, b_st=b_st, h=h, o=o, da=da_rows, db=db_rows, dx_perm=dx_perm)
+
+
+def expert_choice_backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, storage: str,
+                           weight_grad_experts=None, slot=None) -> dict:
+    """Gradients of L = <dy, y> for the expert-choice layer (as
+    `expert_choice_forward`), with respect to x and every weight. Which tokens
+    an expert takes is a discrete decision of the forward pass and passes no
+    gradient; the gate of (t, e) is the dense score S[t, e] = softmax(l[t])[e]
+    over all E logits ([MATH] dense gating), so every logit of a token that
+    some expert chose gets gradient through the softmax.
+
+    Per row r = slot[t, e] (expert e, token t):
+      a, b, h, o  recomputed as in the forward (a and b held as stored)
+      d_o[r]    = st(S[t, e] dy[t])
+      dS[t, e]  = <dy[t], o[r]>                       (0 where e did not choose t)
+      dl[t, :]  = S[t, :] (dS[t, :] - sum_e' S[t, e'] dS[t, e'])
+      dh, da, db, dx_perm and the expert weight gradients as in `backward`
+      dW_g      = st(dl^T x)
+      dx[t]     = st(dl[t] W_g + sum over the experts e that chose t of dx_perm[slot[t, e]])
+
+    weight_grad_experts: as in `backward`. slot: optional [T, E] selection to
+    use instead of the scores' (as in `expert_choice_forward`)."""
+    x64 = as_f64(x)
+    T, d = x64.shape
+    E = w_router.shape[0]
+    F = w_gate.shape[1]
+    wr = as_f64(w_router)
+    r = expert_choice_forward(x, w_router, w_gate, w_up, w_down, k, cf, storage, slot=slot)
+    S, C, tok, slot = r["scores"], r["cap"], r["tokens"], r["slot"]
+    R = E * C
+    dy64 = as_f64(dy)
+    row_tok = tok.reshape(-1).astype(np.int64)   # row e*C + i holds token tokens[e, i]
+    row_exp = np.repeat(np.arange(E), C)
+    a_st = np.empty((R, F))
+    b_st = np.empty((R, F))
+    h = np.empty((R, F))
+    o = np.empty((R, d))
+    for e in range(E):
+        lo, hi = e * C, (e + 1) * C
+        xr = x64[row_tok[lo:hi]]
+        a = xr @ as_f64(w_gate[e]).T
+        b = xr @ as_f64(w_up[e]).T
+        a_st[lo:hi] = hold(a, storage, "a")
+        b_st[lo:hi] = hold(b, storage, "b")
+        h[lo:hi] = store(silu(a) * b, storage)
+        o[lo:hi] = store(h[lo:hi] @ as_f64(w_down[e]).T, storage)
+    d_o = hold(S[row_tok, row_exp][:, None] * dy64[row_tok], storage, "d_o")
+    dS = np.zeros((T, E))
+    dS[row_tok, row_exp] = np.einsum("ij,ij->i", dy64[row_tok], o)
+    dl = softmax_grad(S, dS)
+    dx_perm = np.empty((R, d))
+    da_rows = np.empty((R, F))
+    db_rows = np.empty((R, F))
+    wg_experts = list(range(E)) if weight_grad_experts is None else [int(e) for e in weight_grad_experts]
+    dW_gate = np.zeros((len(wg_experts), F, d))
+    dW_up = np.zeros((len(wg_experts), F, d))
+    dW_down = np.zeros((len(wg_experts), d, F))
+    for e in range(E):
+        lo, hi = e * C, (e + 1) * C
+        dh = d_o[lo:hi] @ as_f64(w_down[e])
+        da = hold(dh * b_st[lo:hi] * silu_grad(a_st[lo:hi]), storage, "da")
+        db = hold(dh * silu(a_st[lo:hi]), storage, "db")
+        da_rows[lo:hi] = da
+        db_rows[lo:hi] = db
+        dx_perm[lo:hi] = hold(da @ as_f64(w_gate[e]) + db @ as_f64(w_up[e]), storage, "dx_perm")
+        if e in wg_experts:
+            i = wg_experts.index(e)
+            xr = x64[row_tok[lo:hi]]
+            dW_gate[i] = da.T @ xr
+            dW_up[i] = db.T @ xr
+            dW_down[i] = d_o[lo:hi].T @ h[lo:hi]
+    dW_g = dl.T @ x64
+    dx = dl @ wr
+    np.add.at(dx, row_tok, dx_perm)
+    return dict(forward=r, dx=store(dx, storage), dW_g=store(dW_g, storage), dW_gate=store(dW_gate, storage),
+                dW_up=store(dW_up, storage), dW_down=store(dW_down, storage), dl=dl, dS=dS, d_o=d_o,
                 a_st=a_st, b_st=b_st, h=h, o=o, da=da_rows, db=db_rows, dx_perm=dx_perm)

@@ -914,6 +914,162 @@ def check_backward_expert_subset_and_sub_batch():
             assert np.allclose(sub[name][0], full[name][e], rtol=0, atol=1e-12 * scale), (name, e)
 
 
+def _ec_loss(x, wr, wg, wu, wd, dy, k, cf):
+    return float((orc.expert_choice_forward(x, wr, wg, wu, wd, k, cf, "f64")["y"] * dy).sum())
+
+
+def check_ec_backward_finite_differences():
+    """Expert choice: every gradient entry of tiny layers (experts taking part
+    of the tokens, and all of them) against a central difference of
+    L = <dy, y> through the forward oracle (float64). The step is far below
+    every score gap at an expert's C-th place, so the selection stays fixed,
+    which this checks."""
+    for (T, d, E, k, F, cf, seed) in [(10, 4, 3, 1, 4, 0.5, 41), (8, 5, 4, 2, 3, 0.0, 42), (12, 4, 3, 2, 5, 0.6, 43)]:
+        rng = np.random.default_rng(seed)
+        x = rng.standard_normal((T, d))
+        wr = rng.standard_normal((E, d))
+        wg = rng.standard_normal((E, F, d)) / math.sqrt(d)
+        wu = rng.standard_normal((E, F, d)) / math.sqrt(d)
+        wd = rng.standard_normal((E, d, F)) / math.sqrt(F)
+        dy = rng.standard_normal((T, d))
+        g = orc.expert_choice_backward(x, wr, wg, wu, wd, dy, k, cf, "f64")
+        base = g["forward"]["slot"]
+        if cf > 0:
+            assert (base < 0).any()
+        params = {"dx": x, "dW_g": wr, "dW_gate": wg, "dW_up": wu, "dW_down": wd}
+        eps = 1e-6
+        for name, arr in params.items():
+            flat = arr.reshape(-1)
+            num = np.empty(flat.size)
+            for i in range(flat.size):
+                keep = flat[i]
+                flat[i] = keep + eps
+                lp = _ec_loss(x, wr, wg, wu, wd, dy, k, cf)
+                flat[i] = keep - eps
+                lm = _ec_loss(x, wr, wg, wu, wd, dy, k, cf)
+                flat[i] = keep
+                num[i] = (lp - lm) / (2 * eps)
+            assert np.allclose(g[name].reshape(-1), num, rtol=1e-6, atol=1e-7), (name, T, E, cf)
+        assert np.array_equal(orc.expert_choice_forward(x, wr, wg, wu, wd, k, cf, "f64")["slot"], base)
+
+
+def check_ec_backward_autograd():
+    """Expert choice: torch autograd through a dense evaluation (every expert
+    on every token, masked by the oracle's selection, gates from torch's
+    softmax over all experts) gives the same five gradients. The cases give
+    tokens no expert, one expert and several experts."""
+    for (T, E, k, cf, seed) in [(30, 5, 2, 0.6, 44), (24, 4, 1, 0.0, 45), (20, 6, 3, 0.4, 46)]:
+        x, wr, wg, wu, wd = small_layer(T=T, E=E, k=k, seed=seed)
+        dy = np.random.default_rng(seed).standard_normal(x.shape)
+        g = orc.expert_choice_backward(x, wr, wg, wu, wd, dy, k, cf, "f64")
+        chosen = g["forward"]["slot"] >= 0
+        per_token = chosen.sum(axis=1)
+        if cf > 0:
+            assert (per_token == 0).any() and (per_token == 1).any() and (per_token >= 2).any()
+        mask = torch.from_numpy(chosen).double()
+        tx, twr, twg, twu, twd = (torch.tensor(a, requires_grad=True) for a in (x, wr, wg, wu, wd))
+        S = torch.softmax(tx @ twr.T, dim=1)
+        y = torch.zeros_like(tx)
+        for e in range(E):
+            h = torch.nn.functional.silu(tx @ twg[e].T) * (tx @ twu[e].T)
+            y = y + (mask[:, e] * S[:, e])[:, None] * (h @ twd[e].T)
+        (y * torch.from_numpy(dy)).sum().backward()
+        for name, t in [("dx", tx), ("dW_g", twr), ("dW_gate", twg), ("dW_up", twu), ("dW_down", twd)]:
+            assert np.allclose(g[name], t.grad.numpy(), rtol=1e-10, atol=1e-12), (name, cf)
+
+
+def check_ec_backward_full_capacity_is_switch_backward():
+    """With C = T every expert takes every token, so the expert-choice layer is
+    the dense-gated layer: the token-choice layer with k = E under the Switch
+    rule without rescale (gates p[e], nothing dropped). Their gradients agree
+    (they differ only in row order, hence summation order)."""
+    x, wr, wg, wu, wd = small_layer(T=18, E=4, k=2, seed=47)
+    dy = np.random.default_rng(47).standard_normal(x.shape)
+    ec = orc.expert_choice_backward(x, wr, wg, wu, wd, dy, 2, 0.0, "f64")
+    tc = orc.backward(x, wr, wg, wu, wd, dy, 4, 0.0, "f64", gating="softmax_topk")
+    assert (ec["forward"]["slot"] >= 0).all()
+    for name in ("dx", "dW_g", "dW_gate", "dW_up", "dW_down"):
+        assert np.allclose(ec[name], tc[name], rtol=1e-12, atol=1e-13), name
+
+
+def torch_ec_backward_bf16(x, wr, wg, wu, wd, dy, k, cf):
+    """The expert-choice backward of a bf16 layer, evaluated pair by pair in
+    torch float64 and rounded to bf16 where the layer holds a value in its
+    storage type (as torch_backward_bf16). The selection (each expert's C
+    largest float32 scores, ties to the lower token) comes from a stable torch
+    sort, the softmax's derivative from torch autograd."""
+    bf = lambda v: v.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    X, WR, WG, WU, WD, DY = (torch.from_numpy(np.asarray(a, np.float64)) for a in (x, wr, wg, wu, wd, dy))
+    T, d = X.shape
+    E = WG.shape[0]
+    lS = (X @ WR.T).detach().requires_grad_(True)
+    S = torch.softmax(lS, dim=1)
+    C = T if np.float32(cf) == 0 else min(T, math.ceil(float(np.float32(cf)) * T * k / E))
+    chosen = torch.zeros((T, E), dtype=torch.bool)
+    for e in range(E):
+        chosen[torch.sort(-S.detach()[:, e].to(torch.float32), stable=True).indices[:C], e] = True
+    out = {n: {} for n in ("a", "b", "h", "o", "d_o", "da", "db", "dx_perm")}
+    dS = torch.zeros((T, E), dtype=torch.float64)
+    dWgate = torch.zeros_like(WG)
+    dWup = torch.zeros_like(WU)
+    dWdown = torch.zeros_like(WD)
+    dx = torch.zeros_like(X)
+    for t in range(T):
+        for e in range(E):
+            if not bool(chosen[t, e]):
+                continue
+            a = WG[e] @ X[t]
+            b = WU[e] @ X[t]
+            h = bf(torch.nn.functional.silu(a) * b)
+            o = bf(WD[e] @ h)
+            d_o = bf(S.detach()[t, e] * DY[t])
+            dS[t, e] = torch.dot(DY[t], o)
+            dh = WD[e].T @ d_o
+            a_st, b_st = bf(a), bf(b)
+            a_req = a_st.clone().requires_grad_(True)
+            s = torch.nn.functional.silu(a_req)
+            s.sum().backward()
+            da = bf(dh * b_st * a_req.grad)
+            db = bf(dh * s.detach())
+            dxp = bf(WG[e].T @ da + WU[e].T @ db)
+            dWgate[e] += torch.outer(da, X[t])
+            dWup[e] += torch.outer(db, X[t])
+            dWdown[e] += torch.outer(d_o, h)
+            dx[t] += dxp
+            for n, v in (("a", a_st), ("b", b_st), ("h", h), ("o", o), ("d_o", d_o), ("da", da), ("db", db),
+                         ("dx_perm", dxp)):
+                out[n][(t, e)] = v.numpy()
+    S.backward(dS)
+    dl = lS.grad
+    dx += dl @ WR
+    res = dict(dx=bf(dx).numpy(), dW_g=bf(dl.T @ X).numpy(), dW_gate=bf(dWgate).numpy(),
+               dW_up=bf(dWup).numpy(), dW_down=bf(dWdown).numpy(), dl=dl.numpy(), chosen=chosen.numpy())
+    res.update(out)
+    return res
+
+
+def check_ec_backward_rounding_points_bf16():
+    """The bf16 expert-choice backward's rounding points, pinned by the
+    independent pair-by-pair torch evaluation: every held intermediate and
+    every returned gradient within one bf16 step of torch's, almost all
+    identical."""
+    for (T, E, k, cf, seed) in [(24, 4, 2, 0.5, 48), (16, 3, 1, 0.0, 49), (20, 5, 2, 0.8, 50)]:
+        x, wr, wg, wu, wd = small_layer(T=T, E=E, k=k, seed=seed, dtype="bf16")
+        dy = torch.from_numpy(np.random.default_rng(seed).standard_normal(x.shape)).to(torch.bfloat16).double().numpy()
+        g = orc.expert_choice_backward(x, wr, wg, wu, wd, dy, k, cf, "bf16")
+        ref = torch_ec_backward_bf16(x, wr, wg, wu, wd, dy, k, cf)
+        slot = g["forward"]["slot"]
+        assert np.array_equal(slot >= 0, ref["chosen"])
+        pairs = sorted(ref["a"])
+        rows = np.array([slot[t, e] for (t, e) in pairs])
+        for name in ("a", "b", "h", "o", "d_o", "da", "db", "dx_perm"):
+            mine = {"a": g["a_st"], "b": g["b_st"]}.get(name, g.get(name))
+            assert_bf16_close(mine[rows], np.stack([ref[name][p] for p in pairs]), name)
+        assert np.allclose(g["dl"], ref["dl"], rtol=1e-9, atol=1e-12)
+        for name in ("dx", "dW_g", "dW_gate", "dW_up", "dW_down"):
+            assert_bf16_close(g[name], ref[name], name)
+
+
 ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
             check_zero_router_closed_form, check_gate_invariants, check_k_equals_E_is_softmax,
             check_printed_gates, check_capacity_values, check_permutation_bruteforce,
@@ -927,7 +1083,9 @@ ALL_PINS = [check_bf16_rounding, check_silu_library, check_topk_bruteforce,
             check_backward_finite_differences, check_backward_autograd, check_backward_storage_rounding,
             check_backward_rounding_points_bf16, check_backward_gating_finite_differences,
             check_backward_gating_autograd,
-            check_backward_expert_subset_and_sub_batch]
+            check_backward_expert_subset_and_sub_batch,
+            check_ec_backward_finite_differences, check_ec_backward_autograd,
+            check_ec_backward_full_capacity_is_switch_backward, check_ec_backward_rounding_points_bf16]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -1069,6 +1227,15 @@ MUTANTS["backward_no_intermediate_rounding"] = ("hold", _hold_skipping(set(orc.B
                                                 [check_backward_rounding_points_bf16])
 for _p in orc.BACKWARD_ROUNDING_POINTS:
     MUTANTS[f"backward_{_p}_unrounded"] = ("hold", _hold_skipping({_p}), [check_backward_rounding_points_bf16])
+
+
+MUTANTS["ec_grad_chosen_logits_only"] = (
+    "softmax_grad", lambda p, dp, _o=orc.softmax_grad: np.where(dp != 0, _o(p, dp), 0.0),
+    [check_ec_backward_finite_differences, check_ec_backward_autograd])
+MUTANTS["ec_grad_without_the_mean"] = ("softmax_grad", lambda p, dp: p * dp,
+                                       [check_ec_backward_finite_differences, check_ec_backward_autograd])
+for _p in orc.BACKWARD_ROUNDING_POINTS:
+    MUTANTS[f"ec_backward_{_p}_unrounded"] = ("hold", _hold_skipping({_p}), [check_ec_backward_rounding_points_bf16])
 
 
 def _ec_reversed(S, C, orig):
