@@ -21,7 +21,8 @@ includes the priority sort. --routing expert_choice times
 moe_forward_expert_choice instead (each expert takes C = capacity tokens);
 its stages are route (scores and selection), gather, ffn and combine.
 --pass backward times moe_backward (gradients of <dy, y> for x and all
-weights, with the forward recomputed inside) instead of the forward.
+weights, with the forward recomputed inside) instead of the forward, or
+moe_backward_expert_choice with --routing expert_choice.
 Prints one JSON line on stdout (progress goes to stderr).
 """
 import argparse
@@ -170,11 +171,11 @@ def main():
     g = {n: v.cuda() for n, v in a.items() if v is not None and n != "token_ids"}
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    if args.routing == "expert_choice":
-        print(json.dumps(bench_expert_choice(args, w, a, g, moe, stream)), flush=True)
-        return
     if args.which == "backward":
         print(json.dumps(bench_backward(args, w, a, g, moe, stream)), flush=True)
+        return
+    if args.routing == "expert_choice":
+        print(json.dumps(bench_expert_choice(args, w, a, g, moe, stream)), flush=True)
         return
 
     # ---- headline: K x moe_forward ----
@@ -344,22 +345,29 @@ def main():
 
 
 def bench_backward(args, w, a, g, moe, stream):
-    """Backward pass: K timed moe_backward steps (forward recomputed inside)."""
+    """Backward pass: K timed moe_backward (or, with --routing expert_choice,
+    moe_backward_expert_choice) steps, the forward recomputed inside."""
     import numpy as np
     import torch
 
     T, d, E, k, F, cf = w.T, w.d, w.E, w.k, w.F, w.cf
     K, W = args.steps, args.warmup
     dy = torch.from_numpy(np.random.default_rng(0).standard_normal((T, d)).astype(np.float32)).to(g["x"].dtype).cuda()
-    n = moe._size_query("moe_backward_workspace_bytes", T, d, E, k, cf, F, moe._dt(g["x"]))
-    ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
+    ec = args.routing == "expert_choice"
     gating, fill = args.gating, args.fill
-    out = moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, k, cf, ws=ws,
-                           gating=gating, fill_order=fill)
+    if ec:
+        n = moe._size_query("moe_backward_expert_choice_workspace_bytes", T, d, E, k, cf, F, moe._dt(g["x"]))
+    else:
+        n = moe._size_query("moe_backward_workspace_bytes", T, d, E, k, cf, F, moe._dt(g["x"]))
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
 
     def step():
-        moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, k, cf, ws=ws,
-                         gating=gating, fill_order=fill)
+        if ec:
+            moe.moe_backward_expert_choice(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, k, cf,
+                                           ws=ws)
+        else:
+            moe.moe_backward(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, k, cf, ws=ws,
+                             gating=gating, fill_order=fill)
 
     for _ in range(W):
         step()
@@ -369,19 +377,24 @@ def bench_backward(args, w, a, g, moe, stream):
         step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / K
-    idx, gate, _ = moe.moe_route(g["x"], g["w_router"], k, gating=gating)
-    perm = moe.moe_permute(g["x"], idx, E, cf, score=gate if fill == "priority" else None, score_stride=k)
-    R = int(perm["expert_offsets"][-1].item())
+    if ec:
+        R = E * moe.moe_capacity(T, E, k, cf)
+    else:
+        idx, gate, _ = moe.moe_route(g["x"], g["w_router"], k, gating=gating)
+        perm = moe.moe_permute(g["x"], idx, E, cf, score=gate if fill == "priority" else None, score_stride=k)
+        R = int(perm["expert_offsets"][-1].item())
     flops = 18 * d * F * R + 4 * T * d * E
     peak = PEAK["bf16_tflops"]
     achieved = flops / (ms_step * 1e-3) / 1e12
-    log(f"moe_backward: {ms_step:.3f} ms/step, {achieved:.0f} TFLOP/s over the layer ({R} rows), workspace {n / 2**30:.2f} GiB")
+    name = "moe_backward_expert_choice" if ec else "moe_backward"
+    log(f"{name}: {ms_step:.3f} ms/step, {achieved:.0f} TFLOP/s over the layer ({R} rows), workspace {n / 2**30:.2f} GiB")
     return {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "pass": "backward", "T": T, "d": d, "E": E, "k": k, "F": F, "cf": cf,
-                   "gating": gating, "fill": fill, "kept_rows": R, "workspace_bytes": n,
+                   "routing": args.routing, "gating": None if ec else gating, "fill": None if ec else fill,
+                   "kept_rows": R, "workspace_bytes": n,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "whole backward (recompute + data and weight gradient GEMMs)",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,

@@ -418,7 +418,39 @@ int moe_backward_ex(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_
                     void* dx, void* dw_router, void* dw_gate, void* dw_up, void* dw_down,
                     void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Static, NUL-terminated description of a status code. */
+/* ---------------------------------------------------------------------------
+ * Backward pass of the expert-choice layer (moe_forward_expert_choice), bf16
+ * or fp32 storage. Gradients of L = <dy, y> by the chain rule of that
+ * layer's definition. The selection (which tokens each expert takes) is a
+ * discrete decision of the forward pass and carries no gradient; the gate of
+ * (t, e) is the dense score S[t, e] = Softmax(x_t . W_g^T)[e] ("How do
+ * Mixture of Expert Models Work?", "The Math Behind MoEs"), so every logit of
+ * a token that some expert chose receives gradient through the softmax over
+ * all E experts. The scores, the selection, the gathered rows and the expert
+ * activations are recomputed from the inputs, then, per row r = slot[t, e]:
+ *   d_o[r] = bf16(S[t, e] dy[t]);  dS[t, e] = <dy[t], o[r]> (0 if e did not take t)
+ *   dl[t, :] = S[t, :] (dS[t, :] - sum_e S[t, e] dS[t, e])
+ *   da, db, dx_perm, dw_gate, dw_up, dw_down as for moe_backward, over the
+ *   E * C selected rows (every expert has C rows)
+ *   dw_router[e] = bf16(sum_t dl[t, e] x[t])
+ *   dx[t] = bf16(sum_e dl[t, e] W_g[e] + sum over the experts e that took t
+ *                of dx_perm[slot[t, e]])   (0 for a token no expert took:
+ *                its dS, and so its dl, is 0)
+ * All accumulation is fp32; layouts as for moe_backward.
+ * ws, ws_bytes: scratch of moe_backward_expert_choice_workspace_bytes (scores,
+ * selection, the recomputed rows and activations, d_o, [da | db], dx_perm,
+ * dl [T, E], router-gradient partial sums, split-tail partials).
+ * Limits (MOE_ERR_UNSUPPORTED beyond): E * C < 2^31; bf16: E * C * max(2F, d)
+ * * 2 bytes and one expert's weight (d * F * 2 bytes) below 2^31.
+ * ------------------------------------------------------------------------- */
+int moe_backward_expert_choice_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf,
+                                               int32_t F, int32_t dt, size_t* bytes);
+int moe_backward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
+                               int32_t dt, const void* x, const void* w_router, const void* w_gate,
+                               const void* w_up, const void* w_down, const void* dy,
+                               void* dx, void* dw_router, void* dw_gate, void* dw_up, void* dw_down,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Measurement aid, not part of the layer: the shader clock while other work
  * runs. Enqueues one wavefront on `stream` that waits `wall_ticks` ticks of
  * the device's constant-rate wall clock (see moe_wall_clock_khz) and writes
@@ -434,6 +466,7 @@ int moe_clock_probe(uint64_t* out, int64_t wall_ticks, hipStream_t stream);
  * current device (hipDeviceAttributeWallClockRate). Host only. */
 int moe_wall_clock_khz(int32_t* khz);
 
+/* Static, NUL-terminated description of a status code. */
 const char* moe_status_string(int status);
 
 #ifdef __cplusplus

@@ -847,6 +847,134 @@ int moe_backward(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F
                          w_up, w_down, dy, dx, dw_router, dw_gate, dw_up, dw_down, ws, ws_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// backward pass of the expert-choice layer
+// ---------------------------------------------------------------------------
+
+struct EcBwdLayout {
+  size_t scores, tokens, slot, offsets, select, dl, x_perm, a_st, b_st, h, o, d_o, dab, dx_perm, router_part, ffn,
+      total;
+};
+
+static EcBwdLayout ec_bwd_layout(int64_t T, int d, int E, int64_t R, int F, int dt) {
+  const size_t s = elem_bytes(dt);
+  EcBwdLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round_up(bytes);
+    return at;
+  };
+  L.scores = take((size_t)T * E * 4);
+  L.tokens = take((size_t)R * 4);
+  L.slot = take((size_t)T * E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.select = take(moe::ec_select_bytes(T, E));
+  L.dl = take((size_t)T * E * 4);
+  L.x_perm = take((size_t)R * d * s);
+  L.a_st = take((size_t)R * F * s);
+  L.b_st = take((size_t)R * F * s);
+  L.h = take((size_t)R * F * s);
+  L.o = take((size_t)R * d * s);
+  L.d_o = take((size_t)R * d * s);
+  L.dab = take((size_t)R * 2 * F * s);
+  L.dx_perm = take((size_t)R * d * s);
+  L.router_part = take(moe::router_wgrad_partial_bytes(T, d, E));
+  L.ffn = take(ffn_ws_bytes(R, E, dt));
+  L.total = o;
+  return L;
+}
+
+int moe_backward_expert_choice_workspace_bytes(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F,
+                                               int32_t dt, size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  int st = check_scalars(T, d, E, k, cf, F, dt, true);
+  if (st != MOE_OK) return st;
+  int64_t C, R;
+  if ((st = ec_rows(T, E, k, cf, &C, &R)) != MOE_OK) return st;
+  *bytes = ec_bwd_layout(T, d, E, R, F, dt).total;
+  return MOE_OK;
+}
+
+int moe_backward_expert_choice(int64_t T, int32_t d, int32_t E, int32_t k, float cf, int32_t F, int32_t dt,
+                               const void* x, const void* w_router, const void* w_gate, const void* w_up,
+                               const void* w_down, const void* dy, void* dx, void* dw_router, void* dw_gate,
+                               void* dw_up, void* dw_down, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_scalars(T, d, E, k, cf, F, dt, true);
+  if (st != MOE_OK) return st;
+  int64_t C, R;
+  if ((st = ec_rows(T, E, k, cf, &C, &R)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  const bool bf16 = dt == MOE_BF16;
+  const size_t s = elem_bytes(dt);
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !dy || !dx || !dw_router || !dw_gate || !dw_up ||
+      !dw_down || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(dy) || !aligned16(dx) || !aligned16(dw_router) || !aligned16(dw_gate) || !aligned16(dw_up) ||
+      !aligned16(dw_down) || !aligned16(ws))
+    return MOE_ERR_UNSUPPORTED;
+  // the bf16 GEMMs address one expert's weights, and the rows of one activation, with 31-bit offsets
+  const int64_t widest = 2 * (int64_t)F > d ? 2 * (int64_t)F : d;
+  if (bf16 && (R * widest * 2 >= ((int64_t)1 << 31) || (int64_t)d * F * 2 >= ((int64_t)1 << 31)))
+    return MOE_ERR_UNSUPPORTED;
+  const EcBwdLayout L = ec_bwd_layout(T, d, E, R, F, dt);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const size_t wbytes = (size_t)E * F * d * s;
+  const Range all[] = {{dx, (size_t)T * d * s},    {dw_router, (size_t)E * d * s}, {dw_gate, wbytes},
+                       {dw_up, wbytes},            {dw_down, wbytes},              {ws, L.total},
+                       {x, (size_t)T * d * s},     {w_router, (size_t)E * d * s},  {w_gate, wbytes},
+                       {w_up, wbytes},             {w_down, wbytes},               {dy, (size_t)T * d * s}};
+  if (any_overlap(all, 6, 12)) return MOE_ERR_INVALID_ARG;
+
+  char* w = reinterpret_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(w + L.scores);
+  int32_t* tokens = reinterpret_cast<int32_t*>(w + L.tokens);
+  int32_t* slot = reinterpret_cast<int32_t*>(w + L.slot);
+  int32_t* offsets = reinterpret_cast<int32_t*>(w + L.offsets);
+  float* dl = reinterpret_cast<float*>(w + L.dl);
+  void* ffn_ws = ffn_ws_bytes(R, E, dt) ? w + L.ffn : nullptr;
+
+  // recompute: scores, selection, gathered rows, a, b, h and o
+  hipError_t e = moe::launch_router(bf16, T, d, E, k, 3, x, w_router, nullptr, nullptr, scores, stream);
+  if (e == hipSuccess) e = moe::launch_ec_select(T, E, (int)C, scores, w + L.select, tokens, slot, offsets, stream);
+  if (e == hipSuccess) e = moe::launch_gather_rows(bf16, T, R, d, x, tokens, w + L.x_perm, stream);
+  if (e == hipSuccess)
+    e = bf16 ? moe::launch_bwd_recompute_gate_up(R, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w + L.h,
+                                                 w + L.a_st, w + L.b_st, stream)
+             : moe::launch_bwd_f32_recompute(R, d, E, F, w + L.x_perm, offsets, w_gate, w_up, w + L.h, w + L.a_st,
+                                             w + L.b_st, stream);
+  if (e == hipSuccess)
+    e = bf16 ? moe::launch_gemm_bf16(2, R, C, d, E, F, w + L.h, offsets, w_down, nullptr, w + L.o, ffn_ws, stream)
+             : moe::launch_gemm_f32(2, R, d, E, F, w + L.h, offsets, w_down, nullptr, w + L.o, stream);
+  // combine and gate backward: d_o rows, dl over all E logits
+  if (e == hipSuccess)
+    e = moe::launch_ec_gate_bwd(bf16, T, d, E, R, dy, w + L.o, slot, scores, w + L.d_o, dl, stream);
+  // data gradients through the experts, then the weight gradients over each expert's rows
+  if (e == hipSuccess)
+    e = bf16 ? moe::launch_bwd_dh(R, d, E, F, w + L.d_o, offsets, w_down, w + L.a_st, w + L.b_st, w + L.dab, stream)
+             : moe::launch_bwd_f32_dh(R, d, E, F, w + L.d_o, offsets, w_down, w + L.a_st, w + L.b_st, w + L.dab,
+                                      stream);
+  if (e == hipSuccess)
+    e = bf16 ? moe::launch_bwd_dx_perm(R, d, E, F, w + L.dab, offsets, w_gate, w_up, w + L.dx_perm, ffn_ws, stream)
+             : moe::launch_bwd_f32_dx_perm(R, d, E, F, w + L.dab, offsets, w_gate, w_up, w + L.dx_perm, stream);
+  if (e == hipSuccess)
+    e = bf16 ? moe::launch_wgrad(E, offsets, 2 * F, F, d, 2 * F, d, R, w + L.dab, w + L.x_perm, dw_gate, dw_up,
+                                 stream)
+             : moe::launch_wgrad_f32(E, offsets, 2 * F, F, d, 2 * F, d, w + L.dab, w + L.x_perm, dw_gate, dw_up,
+                                     stream);
+  if (e == hipSuccess)
+    e = bf16 ? moe::launch_wgrad(E, offsets, d, d, F, d, F, R, w + L.d_o, w + L.h, dw_down, nullptr, stream)
+             : moe::launch_wgrad_f32(E, offsets, d, d, F, d, F, w + L.d_o, w + L.h, dw_down, nullptr, stream);
+  // router weight and input gradients (dl is dense [T, E])
+  if (e == hipSuccess)
+    e = moe::launch_router_wgrad(T, d, E, k, x, nullptr, dl, reinterpret_cast<float*>(w + L.router_part), dw_router,
+                                 stream, true, bf16);
+  if (e == hipSuccess)
+    e = moe::launch_ec_dx_final(bf16, T, d, E, R, dl, w_router, w + L.dx_perm, slot, dx, stream);
+  return hip_status(e);
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -98,6 +98,12 @@ hipError_t launch_router_wgrad(int64_t T, int d, int E, int k, const void* x, co
 hipError_t launch_dx_final(int64_t T, int d, int k, const float* dl, const int32_t* idx, const void* wr,
                            const void* dx_perm, const int32_t* slot_row, void* dx, hipStream_t s, int dense_E = 0,
                            bool bf16 = true);
+// Expert-choice backward (ec_backward.hip): dS, d_o = S dy and dl [T, E]
+// from the [T, E] slots and scores; dx from dl, W_g and the dx_perm rows.
+hipError_t launch_ec_gate_bwd(bool bf16, int64_t T, int d, int E, int64_t R, const void* dy, const void* o,
+                              const int32_t* slot, const float* scores, void* d_o, float* dl, hipStream_t s);
+hipError_t launch_ec_dx_final(bool bf16, int64_t T, int d, int E, int64_t R, const float* dl, const void* wr,
+                              const void* dx_perm, const int32_t* slot, void* dx, hipStream_t s);
 // fp32 layers: the backward's GEMMs on the vector ALUs (ffn_f32.hip).
 //   recompute: h = silu(a) b with a = x_perm W_gate^T, b = x_perm W_up^T, storing h, a and b
 //   dh:        dh = d_o W_down[e] ([E, d, F] as stored), then da = dh b silu'(a) and

@@ -75,6 +75,10 @@ _SIGS = {
                                     _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_backward_ex": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _i32, _i32, _vp, _vp, _vp,
                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_backward_expert_choice_workspace_bytes": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32,
+                                                                  ctypes.c_int, ctypes.POINTER(_sz)]),
+    "moe_backward_expert_choice": (ctypes.c_int, [_i64, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, _vp, _vp, _vp,
+                                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_clock_probe": (ctypes.c_int, [_vp, _i64, _vp]),
     "moe_wall_clock_khz": (ctypes.c_int, [ctypes.POINTER(_i32)]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -471,6 +475,23 @@ def moe_backward(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, ws=No
     else:
         _check("moe_backward_ex", lib().moe_backward_ex(T, d, E, k, cf, F, _dt(x), GATINGS[gating],
                                                         FILL_ORDERS[fill_order], *ptrs))
+    return out
+
+
+def moe_backward_expert_choice(x, w_router, w_gate, w_up, w_down, dy, k: int, cf: float, ws=None, stream=None):
+    """Gradients of <dy, y> for the expert-choice layer. Returns dict(dx,
+    dw_router, dw_gate, dw_up, dw_down), shaped like x and the weights."""
+    T, d = x.shape
+    E, F, _ = w_gate.shape
+    out = dict(dx=_new_like(stream, x), dw_router=_new_like(stream, w_router), dw_gate=_new_like(stream, w_gate),
+               dw_up=_new_like(stream, w_up), dw_down=_new_like(stream, w_down))
+    if ws is None:
+        n = _size_query("moe_backward_expert_choice_workspace_bytes", T, d, E, k, cf, F, _dt(x))
+        ws = _new(stream, max(n, 16), torch.uint8, x.device)
+    _check("moe_backward_expert_choice", lib().moe_backward_expert_choice(
+        T, d, E, k, cf, F, _dt(x), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(dy),
+        _ptr(out["dx"]), _ptr(out["dw_router"]), _ptr(out["dw_gate"]), _ptr(out["dw_up"]), _ptr(out["dw_down"]),
+        _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

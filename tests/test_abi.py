@@ -27,7 +27,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 32
+    assert len(names) == 34
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -302,6 +302,36 @@ def test_backward_entry_points_validate():
     assert L.moe_backward_ex(*a) == INV
     a = list(bx); a[7] = 1; a[8] = 1; a[0] = 0
     assert L.moe_backward_ex(*a) == OK
+
+
+def test_expert_choice_backward_validates():
+    L = moe.lib()
+    b = ctypes.c_size_t()
+    assert L.moe_backward_expert_choice_workspace_bytes(64, 64, 4, 2, 1.0, 128, BF16, ctypes.byref(b)) == OK
+    need = b.value
+    assert L.moe_backward_expert_choice_workspace_bytes(64, 64, 4, 2, 1.0, 128, BF16, None) == INV
+    assert L.moe_backward_expert_choice_workspace_bytes(64, 64, 300, 2, 1.0, 128, BF16, ctypes.byref(b)) == UNS
+    # C = T at cf = 0: every expert takes every token, so more rows than at cf = 1
+    assert L.moe_backward_expert_choice_workspace_bytes(64, 64, 4, 2, 0.0, 128, BF16, ctypes.byref(b)) == OK
+    assert b.value > need
+    bw = [64, 64, 4, 2, 1.0, 128, BF16, A[0], A[1], A[2], A[3], A[4], A[5], A[6], A[7], A[8], A[9], A[10], A[11],
+          1 << 40, None]
+    a = list(bw); a[12] = None                  # dy
+    assert L.moe_backward_expert_choice(*a) == INV
+    a = list(bw); a[19] = need - 1
+    assert L.moe_backward_expert_choice(*a) == WS
+    a = list(bw); a[13] = A[0]                  # dx overlapping x
+    assert L.moe_backward_expert_choice(*a) == INV
+    a = list(bw); a[18] = A[3]                  # workspace overlapping w_up
+    assert L.moe_backward_expert_choice(*a) == INV
+    a = list(bw); a[5] = 72                     # F not a multiple of 64
+    assert L.moe_backward_expert_choice(*a) == UNS
+    a = list(bw); a[6] = 7                      # unknown storage type
+    assert L.moe_backward_expert_choice(*a) == INV
+    a = list(bw); a[13] = A[6] + 4              # dx not 16-byte aligned
+    assert L.moe_backward_expert_choice(*a) == UNS
+    a = list(bw); a[0] = 0
+    assert L.moe_backward_expert_choice(*a) == OK
 
 
 def test_extreme_scalars_are_rejected_or_exact():

@@ -240,3 +240,86 @@ def test_full_size_backward(name):
         out[key] = None
         r[rk] = None
     print(f"{name}: flips {flips}; " + ", ".join(f"{k_} rel {v[0]:.3g} mae {v[1]:.3g}" for k_, v in res.items()))
+
+
+# ---------------------------------------------------------------------------
+# expert choice
+# ---------------------------------------------------------------------------
+
+def run_and_check_ec(w, a, g, dy, label):
+    """moe_backward_expert_choice against the oracle fed the kernels' selection,
+    which is checked first: bit-exact outside float32 near-tie bands at an
+    expert's C-th place, and valid (C tokens per expert, ascending rows) inside."""
+    from test_gpu_expert_choice import check_selection
+    sel = moe.moe_route_expert_choice(g["x"], g["w_router"], w.k, w.cf)
+    out = moe.moe_backward_expert_choice(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dev(dy), w.k,
+                                         w.cf)
+    torch.cuda.synchronize()
+    S = orc.softmax_scores(orc.router_logits(a["x"], a["w_router"]))
+    C = orc.capacity(w.T, w.E, w.k, w.cf)
+    assert sel["C"] == C
+    tok_ref, slot_ref = orc.expert_choice_select(S, C)
+    slot = host(sel["slot"])
+    check_selection(S, C, host(sel["expert_tokens"]), slot, host(sel["expert_offsets"]), tok_ref, slot_ref)
+    ref = orc.expert_choice_backward(a["x"], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy.double().numpy(),
+                                     w.k, w.cf, w.dtype, slot=slot)
+    res = {}
+    for key, rk in [("dx", "dx"), ("dw_router", "dW_g"), ("dw_gate", "dW_gate"), ("dw_up", "dW_up"),
+                    ("dw_down", "dW_down")]:
+        res[key] = check_grad(key, host(out[key]), ref[rk], w.dtype)
+        ref[rk] = None
+    per_token = (slot >= 0).sum(axis=1)
+    print(f"{label} expert choice: C={C}, tokens with 0 / 1 / more experts "
+          f"{int((per_token == 0).sum())} / {int((per_token == 1).sum())} / {int((per_token > 1).sum())}, "
+          f"{int((slot != slot_ref).any(axis=1).sum())} selected differently; "
+          + ", ".join(f"{k_} rel {v[0]:.3g} mae {v[1]:.3g}" for k_, v in res.items()))
+    return out, slot
+
+
+@pytest.mark.parametrize("case", BF16_CASES + F32_CASES, ids=case_id)
+def test_ec_backward(case):
+    w, a = workload(case)
+    g = device_inputs(case)
+    seed = case[7] if not isinstance(case, str) else 0
+    run_and_check_ec(w, a, g, make_dy(w, seed), case_id(case))
+
+
+def test_ec_backward_mid_size_and_token_without_expert():
+    """Several 256-row tiles per expert and K ranges of many steps; at
+    cf = 0.5 some tokens are taken by no expert: their dx must be exactly 0."""
+    w, a = mi.random_small(2048, 1024, 8, 2, 2048, 0.5, "bf16", 73)
+    g = {k_: dev(v) for k_, v in a.items() if v is not None}
+    out, slot = run_and_check_ec(w, a, g, make_dy(w, 73), "T2048_d1024_E8_k2_F2048_cf0.5")
+    none = np.nonzero((slot < 0).all(axis=1))[0]
+    assert len(none) > 0
+    assert torch.all(out["dx"][torch.from_numpy(none).cuda()] == 0)
+
+
+def test_ec_backward_dense_capacity():
+    """cf = 0: C = T, every expert takes every token (dense softmax gating)."""
+    w, a = mi.random_small(300, 128, 4, 2, 128, 0.0, "bf16", 74)
+    g = {k_: dev(v) for k_, v in a.items() if v is not None}
+    _, slot = run_and_check_ec(w, a, g, make_dy(w, 74), "T300_E4_cf0")
+    assert (slot >= 0).all()
+
+
+def test_ec_backward_is_deterministic():
+    case = BF16_CASES[0]
+    w, _ = workload(case)
+    g = device_inputs(case)
+    dy = dev(make_dy(w, 2))
+    first = moe.moe_backward_expert_choice(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, w.k, w.cf)
+    for _ in range(3):
+        again = moe.moe_backward_expert_choice(g["x"], g["w_router"], g["w_gate"], g["w_up"], g["w_down"], dy, w.k,
+                                               w.cf)
+        for key in first:
+            assert torch.equal(first[key], again[key]), key
+
+
+def test_full_size_ec_backward():
+    """Expert choice at the OpenMoE shape (C = 640 tokens for each of 32
+    experts): every entry of the five gradients against the oracle fed the
+    kernels' selection."""
+    w, a = workload("openmoe_bf16")
+    g = device_inputs("openmoe_bf16")
+    run_and_check_ec(w, a, g, make_dy(w, 93), "openmoe_bf16")
