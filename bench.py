@@ -300,6 +300,35 @@ def main():
                      "TFLOP/s": alg[n]["flops"] / t / 1e12,
                      "hbm_frac": alg[n]["bytes"] / t / 1e9 / PEAK["hbm_gbs"]}
         log(f"  {n:8s} {st_ms[n] * 1e3:9.1f} us  {stages[n]['GB/s']:8.0f} GB/s  {stages[n]['TFLOP/s']:8.1f} TFLOP/s")
+    # ---- what a plain memory-bound torch kernel reaches on the same byte counts, timed the same
+    # way (flushed caches, events around one launch): a device copy moving each stage's algorithmic
+    # bytes, half read and half written. It shows what a kernel of that size reaches here, launch
+    # included.
+    half = {n: alg[n]["bytes"] // 2 for n in ("route", "permute", "combine")}
+    ref_src = torch.empty(max(half.values()) + 64, dtype=torch.uint8, device="cuda")
+    ref_dst = torch.empty_like(ref_src)
+    ref_ops = {n: (2 * half[n], (lambda m: lambda: ref_dst[:m].copy_(ref_src[:m]))(half[n])) for n in half}
+    ref_samples = {n: [] for n in ref_ops}
+    for it in range(W + K):
+        for n, (_, op) in ref_ops.items():
+            if flush is not None:
+                flush.sum()
+            e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e_a.record(stream)
+            op()
+            e_b.record(stream)
+            if it >= W:
+                ref_samples[n].append((e_a, e_b))
+    torch.cuda.synchronize()
+    hbm_ref = {}
+    for n, (nbytes, _) in ref_ops.items():
+        if ref_samples[n]:
+            us = float(np.mean([a_.elapsed_time(b_) for a_, b_ in ref_samples[n]])) * 1e3
+            hbm_ref[n] = {"us": us, "bytes": nbytes, "GB/s": nbytes / us / 1e3, "stage_us": st_ms[n] * 1e3}
+    del ref_src, ref_dst
+    if hbm_ref:
+        log("  plain torch kernels on the same bytes: " + ", ".join(
+            f"{n} {v['us']:.1f} us ({v['GB/s']:.0f} GB/s)" for n, v in hbm_ref.items()))
     ffn_t = (st_ms["gate_up"] + st_ms["down"]) * 1e-3
     ffn_frac = (alg["gate_up"]["flops"] + alg["down"]["flops"]) / ffn_t / 1e12 / peak_mm
     hbm_t = (st_ms["route"] + st_ms["permute"] + st_ms["combine"]) * 1e-3
@@ -334,6 +363,12 @@ def main():
         "cpu_baseline": cpu,
         "ffn_mfma_frac": ffn_frac,
         "route_permute_combine_hbm_frac": hbm_frac,
+        "hbm_stage_reference": {
+            "method": "torch device copy of each stage's algorithmic bytes (half read, half written), flushed "
+                      "caches, events around one launch, as the stages",
+            "stages": hbm_ref,
+            "hbm_frac": (sum(v["bytes"] for v in hbm_ref.values()) / (sum(v["us"] for v in hbm_ref.values()) * 1e-6)
+                         / 1e9 / PEAK["hbm_gbs"]) if hbm_ref else None},
         "layer_tflops": (alg["route"]["flops"] + alg["gate_up"]["flops"] + alg["down"]["flops"]) / (ms_step * 1e-3) / 1e12,
         "gpu_ms_per_step_events": gpu_ms_step,
         "graph_replay": graph,

@@ -210,8 +210,9 @@ hipError_t launch_router_tw(int64_t T, int d, int E, int k, int gating, const vo
 // bf16 router on the matrix cores. The logits are a [T, d] x [d, E] product
 // with E small, so the work is bound by reading x from HBM once. A block owns
 // BT = 16 * MT tokens; its NW wavefronts split d: the 128-column steps of d go
-// round-robin to the wavefronts, which issue the x loads of D steps at once
-// before computing on them. In a step, lane l of a wavefront holds row l % 16
+// round-robin to the wavefronts, which issue the W_g loads of D steps and then
+// the x loads of those steps at once before computing on them (W_g comes from
+// L2 and lands first, so a step's MFMAs start as soon as its x pieces arrive). In a step, lane l of a wavefront holds row l % 16
 // of each 16-token tile and of each 16-expert tile of W_g, with the 16-byte
 // pieces at columns 32 j + 8 (l / 16) (j = 0..3), which is the operand layout
 // of v_mfma_f32_16x16x32_bf16 for the 32 columns of piece j. W_g is the first
@@ -273,7 +274,21 @@ __global__ __launch_bounds__(NW * 64) void router_mfma_kernel(int64_t T, int d, 
 
   const u32x4 zero = {0u, 0u, 0u, 0u};
   const int S = (d + kRStep - 1) / kRStep;
+  // W_g pieces of all D steps up front while they fit in registers (up to 32
+  // pieces a lane); beyond that, per step and expert tile after the x loads
+  constexpr bool kPre = D * NT <= 8;
   for (int s0 = wave; s0 < S; s0 += NW * D) {
+    bf16x8 bw[kPre ? D : 1][kPre ? NT : 1][4];
+#pragma unroll
+    for (int i = 0; i < (kPre ? D : 0); ++i) {
+      const int c = (s0 + i * NW) * kRStep + 8 * g;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bw[i][nt][j] = __builtin_bit_cast(
+              bf16x8, (s0 + i * NW < S && c + 32 * j < d) ? ld16(wrow[nt] + (size_t)(c + 32 * j) * 2) : zero);
+    }
     bf16x8 a[D][MT][4];
 #pragma unroll
     for (int i = 0; i < D; ++i) {
@@ -292,10 +307,13 @@ __global__ __launch_bounds__(NW * 64) void router_mfma_kernel(int64_t T, int d, 
       const int c = (s0 + i * NW) * kRStep + 8 * g;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        bf16x8 b[4];
+        bf16x8 bl[4];
+        if constexpr (!kPre) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          b[j] = __builtin_bit_cast(bf16x8, c + 32 * j < d ? ld16(wrow[nt] + (size_t)(c + 32 * j) * 2) : zero);
+          for (int j = 0; j < 4; ++j)
+            bl[j] = __builtin_bit_cast(bf16x8, c + 32 * j < d ? ld16(wrow[nt] + (size_t)(c + 32 * j) * 2) : zero);
+        }
+        const bf16x8* b = kPre ? bw[kPre ? i : 0][kPre ? nt : 0] : bl;   // (indices 0 when unused)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
