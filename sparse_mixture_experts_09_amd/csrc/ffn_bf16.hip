@@ -516,9 +516,12 @@ __global__ __launch_bounds__(256) void split_reduce_xcd_kernel(int E, const int3
 }
 
 // ---------------------------------------------------------------------------
-// Main path: 256 x BN tiles (256 weight rows: BN gate + BN up rows in GEMM1),
-// wavefronts split 2 x 4, the LDS layout and bank swizzle above and the
-// LDS-staged epilogues, with register-staged loads:
+// 8-wavefront tiles (the backward pass's recomputation and dh GEMMs, whose
+// epilogues move three or four tiles; the plain and SwiGLU epilogues and the
+// split tail serve the same tiles in the forward layout): 256 x BN tiles
+// (256 weight rows: BN gate + BN up rows in GEMM1), wavefronts split 2 x 4,
+// the LDS layout and bank swizzle above and the LDS-staged epilogues, with
+// register-staged loads:
 // each thread fetches four 16-byte pieces of each operand per K step with
 // buffer loads (whole 128-byte rows across 8 lanes; the descriptors' record
 // counts end at the expert's last row and at the weight's last row, so
