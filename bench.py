@@ -121,6 +121,37 @@ def cpu_baseline(w, a, target_s, gating="topk_softmax", bpr=False):
                       f"numpy (BLAS matmul), {t:.1f} s"}
 
 
+def library_gemm(args, w, mi, torch):
+    """torch.matmul on the dense shapes of the layer's two GEMMs: the T k token rows (x repeated k
+    times) against one expert's [W_gate; W_up], and h = SiLU(x W_gate^T) * (x W_up^T) of those rows
+    against its W_down, both with the weight as stored (K-major rows, as the grouped kernels read
+    it). The same flops as the grouped GEMMs of a dropless batch, with no routing: a reference
+    for what the vendor library reaches on these shapes, not part of the hot path."""
+    a = mi.generate(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    x = a["x"].to("cuda")
+    wg, wu, wd = (a[n][0].to("cuda") for n in ("w_gate", "w_up", "w_down"))
+    a1 = x.repeat(w.k, 1).contiguous()
+    b1 = torch.cat([wg, wu]).contiguous()
+    h = (torch.nn.functional.silu((a1 @ wg.t()).float()) * (a1 @ wu.t()).float()).to(dt)
+    out = {}
+    for name, lhs, rhs in (("gate_up", a1, b1), ("down", h, wd)):
+        for _ in range(args.warmup):
+            torch.matmul(lhs, rhs.t())
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(args.steps):
+            torch.matmul(lhs, rhs.t())
+        ev[1].record()
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) / args.steps * 1e3
+        flops = 2.0 * lhs.shape[0] * lhs.shape[1] * rhs.shape[0]
+        out[name] = {"m": lhs.shape[0], "n": rhs.shape[0], "k": lhs.shape[1], "us": round(us, 1),
+                     "tflops": round(flops / us / 1e6, 1)}
+    return {"library_gemm": out, "workload": w.name, "dtype": w.dtype, "steps": args.steps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +167,9 @@ def main():
     ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"])
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run K device-to-device copies of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time torch.matmul (the vendor GEMM library) on dense GEMMs of the workload's FFN "
+                         "shapes (T k rows, one expert's weights), as a reference for the grouped kernels")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -157,6 +191,9 @@ def main():
         return
 
     import moe_inputs as mi
+    if args.library_gemm:
+        print(json.dumps(library_gemm(args, mi.WORKLOADS[args.workload], mi, torch)), flush=True)
+        return
     from sparse_mixture_experts_09_amd import moe
 
     if not os.path.exists(moe.LIB_PATH):
