@@ -38,16 +38,23 @@ if ROOT not in sys.path:
 
 METRIC = "MoE layer fwd tokens/s + % bf16 MFMA peak (grouped FFN), Mixtral-shape, 1 GPU"
 PEAK = {"bf16_tflops": 2500.0, "f32_tflops": 157.3, "hbm_gbs": 8000.0}
-DOMINANT_KERNEL_SRC = os.path.join(ROOT, "sparse_mixture_experts_09_amd", "csrc", "ffn_bf16.hip")
+# The gate/up kernel's source: its file and the headers it includes (a change to any of them can
+# change the kernel, and counters taken before it no longer describe it).
+DOMINANT_KERNEL_SRC = [os.path.join(ROOT, "sparse_mixture_experts_09_amd", "csrc", n)
+                       for n in ("ffn_bf16.hip", "ffn_sched.h", "moe_common.h", "moe_kernels.h")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_digest(paths):
+    """SHA-256 over the files in order."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic(workload):
