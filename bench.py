@@ -23,6 +23,9 @@ its stages are route (scores and selection), gather, ffn and combine.
 --pass backward times moe_backward (gradients of <dy, y> for x and all
 weights, with the forward recomputed inside) instead of the forward, or
 moe_backward_expert_choice with --routing expert_choice.
+Two reference modes print their own JSON line instead: --library-gemm times the
+vendor GEMM library on dense GEMMs of the workload's FFN shapes, --copy-probe
+runs plain device copies (the calibration of the HBM byte counters).
 Prints one JSON line on stdout (progress goes to stderr).
 """
 import argparse
