@@ -102,10 +102,14 @@ def clock_during(moe, run, steps, ms_per_step):
                       f"{steps} more moe_forward steps"}
 
 
+def blas_threads():
+    """Threads of the BLAS library numpy calls (the oracle's matmuls run there)."""
+    from threadpoolctl import threadpool_info
+    return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+
+
 def cpu_baseline(w, a, target_s, gating="topk_softmax", bpr=False):
     """The oracle, as it is, on the first S tokens of the workload."""
-    from threadpoolctl import threadpool_info
-
     from oracle import moe_oracle as orc
 
     def run(S):
@@ -123,7 +127,7 @@ def cpu_baseline(w, a, target_s, gating="topk_softmax", bpr=False):
         S = min(w.T, 4 * S)
         t = run(S)
         log(f"cpu oracle: {S} tokens in {t:.2f} s")
-    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    threads = blas_threads()
     drop = "dropless, so routing and outputs equal the full layer's for these tokens" if w.cf == 0 else \
         f"capacity recomputed for {S} tokens"
     return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -560,7 +564,7 @@ def bench_expert_choice(args, w, a, g, moe, stream):
         S = min(T, 1024)
         orc.expert_choice_forward(a["x"][:S], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], k, cf, w.dtype)
         t = time.perf_counter() - t0
-        cpu = {"value": S / t, "unit": "tokens/s", "cores": None, "kind": "oracle",
+        cpu = {"value": S / t, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
                "sample": f"expert-choice layer on the first {S} of {T} tokens (selection recomputed for them), {t:.1f} s"}
     return {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
