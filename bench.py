@@ -135,6 +135,39 @@ def cpu_baseline(w, a, target_s, gating="topk_softmax", bpr=False):
                       f"numpy (BLAS matmul), {t:.1f} s"}
 
 
+def cpu_baseline_backward(w, a, target_s, ec, gating="topk_softmax", bpr=False):
+    """The oracle's backward pass, as it is, on the first S tokens of the workload (routing and
+    capacity recomputed for them), gradients of <dy, y> for x and every weight."""
+    import numpy as np
+
+    from oracle import moe_oracle as orc
+
+    def run(S):
+        dy = np.random.default_rng(0).standard_normal((S, w.d))
+        t = time.perf_counter()
+        if ec:
+            orc.expert_choice_backward(a["x"][:S], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy, w.k,
+                                       w.cf, w.dtype)
+        else:
+            orc.backward(a["x"][:S], a["w_router"], a["w_gate"], a["w_up"], a["w_down"], dy, w.k, w.cf, w.dtype,
+                         gating=gating, bpr=bpr)
+        return time.perf_counter() - t
+
+    # grow the sample (x4) until it takes about target_s or covers the whole batch; each run
+    # includes the oracle's fixed cost of widening the weights and their gradients to float64
+    S = min(w.T, 64)
+    t = run(S)
+    log(f"cpu oracle backward: {S} tokens in {t:.2f} s")
+    while S < w.T and t < target_s / 2:
+        S = min(w.T, 4 * S)
+        t = run(S)
+        log(f"cpu oracle backward: {S} tokens in {t:.2f} s")
+    rule = "expert choice" if ec else f"{gating}, {'priority' if bpr else 'token'} fill"
+    return {"value": S / t, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"backward ({rule}) on the first {S} of {w.T} tokens of {w.name}, routing and capacity "
+                      f"recomputed for them; float64 numpy (BLAS matmul), {t:.1f} s"}
+
+
 def library_gemm(args, w, mi, torch):
     """torch.matmul on the dense shapes of the layer's two GEMMs: the T k token rows (x repeated k
     times) against one expert's [W_gate; W_up], and h = SiLU(x W_gate^T) * (x W_up^T) of those rows
@@ -474,6 +507,10 @@ def bench_backward(args, w, a, g, moe, stream):
     achieved = flops / (ms_step * 1e-3) / 1e12
     name = "moe_backward_expert_choice" if ec else "moe_backward"
     log(f"{name}: {ms_step:.3f} ms/step, {achieved:.0f} TFLOP/s over the layer ({R} rows), workspace {n / 2**30:.2f} GiB")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle's backward ...")
+        cpu = cpu_baseline_backward(w, a, args.cpu_seconds, ec, gating, fill == "priority")
     return {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -485,7 +522,7 @@ def bench_backward(args, w, a, g, moe, stream):
         "roofline": {"bound": "mfma", "kernel": "whole backward (recompute + data and weight gradient GEMMs)",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
                      "alg_flops_per_launch": flops, "avg_launch_us": ms_step * 1e3},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
 
 
